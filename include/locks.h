@@ -1,0 +1,173 @@
+/*
+ * locks.h -- C ABI of the LOCKS decode hot path on MI355X (gfx950).
+ *
+ * LOCKS ("LOCKS: Page-Local Compact Key Summaries for Efficient Long-Context
+ * Decoding"; gist.science explainer, technical summary sec. 2, and the
+ * paper's abstract) keeps the full paged KV cache, gives every page a small
+ * spectral summary of its keys, estimates each page's attention mass from the
+ * summaries alone, and runs attention over only the top pages.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *    memory; the library allocates nothing, never synchronizes and never
+ *    reads device memory on the host, so every call may be captured in a
+ *    HIP graph.
+ *  - `stream` is a hipStream_t passed as void*.  Work is enqueued on it and
+ *    the call returns at once.
+ *  - Arguments are validated on the host before anything is launched; on
+ *    failure a negative status is returned and nothing is launched.  A launch
+ *    error returns LOCKS_ERR_LAUNCH.  Faults inside kernels surface at the
+ *    caller's next synchronization.
+ *  - Supported shape: head_dim 128, page_size 16, rank 8, and
+ *    num_q_heads = 4 * num_kv_heads (GQA group of 4); anything else returns
+ *    LOCKS_ERR_UNSUPPORTED.
+ *  - bf16 tensors are raw bfloat16 bit patterns (uint16).
+ *  - Device-side data (seq_lens, block tables, selections) is range-checked
+ *    in the kernels: a sequence length is clamped to max_pages * 16, and a
+ *    block id outside [0, num_blocks) makes that page count as absent.
+ *  - The library keeps no state and is safe to call from several threads.
+ */
+#ifndef LOCKS_H
+#define LOCKS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t locks_status;
+#define LOCKS_OK 0
+#define LOCKS_ERR_NULL (-1)        /* a required pointer is NULL            */
+#define LOCKS_ERR_SHAPE (-2)       /* a size or stride is out of range     */
+#define LOCKS_ERR_UNSUPPORTED (-3) /* dims outside the supported shape     */
+#define LOCKS_ERR_WORKSPACE (-4)   /* workspace missing or too small       */
+#define LOCKS_ERR_LAUNCH (-5)      /* the HIP runtime refused a launch     */
+
+typedef struct {
+  int32_t num_q_heads;  /* Hq                                      */
+  int32_t num_kv_heads; /* Hkv; Hq / Hkv is the GQA group size G   */
+  int32_t head_dim;     /* d (128)                                 */
+  int32_t page_size;    /* B, tokens per KV page (16)              */
+  int32_t rank;         /* r, basis vectors per page summary (8)   */
+} locks_dims;
+
+/* Element strides (bf16 elements) of one layer's paged K or V cache:
+ * element (block, kv_head, token, dim) sits at
+ *   block*block_stride + kv_head*head_stride + token*token_stride + dim. */
+typedef struct {
+  int64_t block_stride;
+  int64_t head_stride;
+  int64_t token_stride;
+} locks_kv_layout;
+
+/* Bytes of one summary record per (page, KV head): 832 at d=128, B=16, r=8
+ * (codes 768 B + 17 fp16 scales + padding to 64-byte lines; about 10% of
+ * the page-head's 8192 K+V bytes, sec. 2 quantization paragraph).
+ * Returns 0 for unsupported dims. */
+size_t locks_summary_bytes(const locks_dims* dims);
+
+/* Workspace sizes (bytes).  max_pages is the block-table row length; the
+ * budget is in pages. */
+size_t locks_score_workspace_bytes(const locks_dims* dims, int32_t batch,
+                                   int32_t max_pages, int32_t budget_pages);
+size_t locks_attend_workspace_bytes(const locks_dims* dims, int32_t batch,
+                                    int32_t max_attended_pages);
+
+/* Build the summaries of whole pages ("page finalization", sec. 2 core
+ * mechanism: centroid, a small eigendecomposition of the centered keys, the
+ * top-r eigenvectors and one coefficient vector per token; int4 basis, int8
+ * coefficients and centroid).
+ *   k_cache    : bf16 K of one layer, strides `layout`.
+ *   block_ids  : [n_blocks] physical blocks to summarize (all KV heads).
+ *   num_blocks : physical blocks in the layer (record array extent).
+ *   summaries  : [Hkv][num_blocks][locks_summary_bytes] records, written for
+ *                the listed blocks only.
+ *   raw_debug  : nullable; fp32 [n_blocks][Hkv][1280] unquantized summary
+ *                (mu[128], V as [r][128], C as [16][r]) for testing.
+ * Record layout (little-endian):
+ *   [0,512)   basis codes, int4 two's complement in [-7,7]: column k owns
+ *             bytes [64k, 64k+64); 32-bit word w covers dims [8w, 8w+8);
+ *             byte m of the word holds dim 8w+m in its low nibble and dim
+ *             8w+4+m in its high nibble.
+ *   [512,640) coefficient codes int8 [16 tokens][8 columns].
+ *   [640,768) centroid codes int8 [128].
+ *   [768,784) fp16 basis scales s_V[8]; [784,800) fp16 coefficient scales
+ *             s_c[8]; [800,802) fp16 centroid scale; [802,832) zero.
+ *   Dequantized: mu = s_mu*mu_q, v_k = s_V[k]*V_q[:,k], c_ik = s_c[k]*C_q[i,k].
+ */
+locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
+                                   locks_kv_layout layout, const int32_t* block_ids,
+                                   int32_t n_blocks, int32_t num_blocks, void* summaries,
+                                   float* raw_debug, void* stream);
+
+/* Score every finalized page of every sequence from its summary alone
+ * (sec. 2 reconstruction and selection, the equation for s_hat_j(q)):
+ *   s_hat[b][h][j] = LSE_i ( (q_h.mu_j + (V_j^T q_h).c_i) / sqrt(d) ),
+ * natural log, for query head h and logical page j < seq_lens[b] / 16.
+ *   q           : bf16 [batch][Hq][d].
+ *   summaries   : this layer's records, [Hkv][num_blocks][832].
+ *   block_table : [batch][max_pages] physical block of each logical page.
+ *   seq_lens    : [batch] tokens per sequence.
+ *   page_lse    : fp32 [batch][Hq][max_pages]; entries for pages that are not
+ *                 finalized (or whose block id is out of range) get -inf.
+ *   workspace   : >= locks_score_workspace_bytes(dims, batch, max_pages, 0).
+ * No candidate key or value is read. */
+locks_status locks_score_pages(const locks_dims* dims, const void* q, const void* summaries,
+                               int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
+                               const int32_t* seq_lens, int32_t batch, float* page_lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Select pages from scores (sec. 2 group-shared selection): for each
+ * (sequence, KV head) the mass share of page j for query head h is
+ * exp(s_hat_hj - LSE_j' s_hat_hj'); shares are averaged over the G query
+ * heads of the group and the k = min(budget_pages, finalized pages) largest
+ * are kept (ties to the lower page index).
+ *   page_lse  : fp32 [batch][Hq][max_pages] as written by locks_score_pages.
+ *   sel       : int32 [batch][Hkv][budget_pages] logical page ids in
+ *               ascending order, padded with -1.
+ *   sel_count : int32 [batch][Hkv] number of valid entries of sel. */
+locks_status locks_select_pages(const locks_dims* dims, const float* page_lse, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t batch, int32_t budget_pages,
+                                int32_t* sel, int32_t* sel_count, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* locks_score_pages followed by locks_select_pages in one call (the decode
+ * step's selection half).  page_lse is nullable: when NULL the scores live
+ * in the workspace. */
+locks_status locks_score_select(const locks_dims* dims, const void* q, const void* summaries,
+                                int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t batch, int32_t budget_pages,
+                                int32_t* sel, int32_t* sel_count, float* page_lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention of each query head over the selected pages' tokens plus the
+ * partial tail page (tokens past the last full page), an ordinary softmax
+ * renormalized over those tokens (abstract: attend only the top pages).
+ *   k_cache, v_cache : bf16 caches of this layer, strides `layout`.
+ *   sel, sel_count   : as written by locks_select_pages; sel == NULL means
+ *                      every finalized page (dense attention).
+ *   budget_pages     : row length of sel (ignored when sel is NULL).
+ *   softmax_scale    : logit scale, normally 1/sqrt(d).
+ *   out              : bf16 [batch][Hq][d].
+ *   out_lse          : nullable fp32 [batch][Hq], natural-log LSE of the
+ *                      scaled logits over the attended tokens.
+ *   workspace        : >= locks_attend_workspace_bytes(dims, batch, n) with
+ *                      n = budget_pages + 1 (or max_pages + 1 when dense). */
+locks_status locks_sparse_attend(const locks_dims* dims, const void* q, const void* k_cache,
+                                 const void* v_cache, locks_kv_layout layout, int32_t num_blocks,
+                                 const int32_t* block_table, int32_t max_pages,
+                                 const int32_t* seq_lens, int32_t batch, const int32_t* sel,
+                                 const int32_t* sel_count, int32_t budget_pages,
+                                 float softmax_scale, void* out, float* out_lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string, host). */
+const char* locks_status_str(locks_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOCKS_H */

@@ -1,0 +1,232 @@
+// Sparse decode attention over the selected pages (LOCKS abstract: attend only
+// the top pages; technical summary sec. 2: every query head of a GQA group
+// attends the same page set).
+//
+// Split-K: the attended page list of a (sequence, KV head) -- the selected
+// pages in ascending order, then the partial tail page -- is cut into splits
+// of `pages_per_split` pages, one wave each.  The 4 query heads of the group
+// share every K/V load.
+//  * QK^T on the matrix cores: rows = the 16 tokens of a page, K = head dim,
+//    columns = the 4 heads repeated 4 times; lane l gets the logits of tokens
+//    4*(l/16) + r (r = 0..3) for head l%4.
+//  * softmax in base 2 with an online maximum per 4-page group.
+//  * P.V on the vector units: lane l keeps the same 4 tokens and 8 of the
+//    128 dims; the 4 heads' probabilities come from its quad by DPP broadcast.
+// A second kernel merges the splits by log-sum-exp into bf16 output.
+#include "locks_device.h"
+#include "locks_internal.h"
+
+namespace locks {
+
+namespace {
+
+constexpr int kWaves = 4;
+
+struct AttendParams {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  int64_t bs, hs, ts;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* sel;
+  const int32_t* sel_count;
+  float* part_o;
+  float2* part_ml;
+  float scale2;
+  int32_t num_blocks, max_pages, budget, hq, hkv, pages_per_split, n_splits;
+};
+
+__global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int split = blockIdx.x * kWaves + wave;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  if (split >= p.n_splits) return;
+  const int row = lane >> 4, col = lane & 15, h = lane & 3;
+  const int qhead0 = kvh * kG;
+
+  int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
+  const int n_fin = seq / kB;
+  const int tail = seq - n_fin * kB;
+  int count = n_fin;
+  const int32_t* selrow = nullptr;
+  if (p.sel) {
+    count = max(0, min(p.sel_count[(size_t)b * p.hkv + kvh], p.budget));
+    selrow = p.sel + ((size_t)b * p.hkv + kvh) * p.budget;
+  }
+  const int n_att = count + (tail > 0 ? 1 : 0);
+  const int e0 = split * p.pages_per_split;
+  const int e1 = min(e0 + p.pages_per_split, n_att);
+
+  const uint16_t* qrow = p.q + ((size_t)b * p.hq + qhead0 + h) * kD + 32 * row;
+  bf16x8 bq[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 8 * s));
+
+  const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
+  float M = -INFINITY, lsum = 0.f;
+  float acc[4][8];
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+
+  for (int eg = e0; eg < e1; eg += 4) {
+    float S[4][4];
+    size_t off[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const int e = eg + pp;
+      int ntok = 0, j = -1;
+      if (e < e1) {
+        if (e < count) {
+          j = selrow ? selrow[e] : e;
+          ntok = kB;
+          if (j < 0 || j >= n_fin) ntok = 0;
+        } else {
+          j = n_fin;
+          ntok = tail;
+        }
+      }
+      int bid = (ntok > 0) ? bt[j] : 0;
+      if ((unsigned)bid >= (unsigned)p.num_blocks) {
+        bid = 0;
+        ntok = 0;
+      }
+      off[pp] = (size_t)bid * p.bs + (size_t)kvh * p.hs;
+      const uint16_t* kr = p.kc + off[pp] + (size_t)col * p.ts + 32 * row;
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        a = mfma16x16x32(as_bf16x8(*reinterpret_cast<const uint4*>(kr + 8 * s)), bq[s], a);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[pp][r] = (4 * row + r < ntok) ? a[r] * p.scale2 : -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[pp][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float Mn = fmaxf(M, mx);
+    const float alpha = (Mn == -INFINITY) ? 1.f : fast_exp2(M - Mn);
+    float P[4][4];
+    float ps = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        P[pp][r] = (S[pp][r] == -INFINITY) ? 0.f : fast_exp2(S[pp][r] - Mn);
+        ps += P[pp][r];
+      }
+    lsum = lsum * alpha + ps;
+    M = Mn;
+    const float al[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha),
+                         quad_bcast<3>(alpha)};
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] *= al[hh];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p.vc + off[pp] +
+                                                        (size_t)(4 * row + r) * p.ts + 8 * col);
+        const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                             bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        const float p0 = quad_bcast<0>(P[pp][r]), p1 = quad_bcast<1>(P[pp][r]);
+        const float p2 = quad_bcast<2>(P[pp][r]), p3 = quad_bcast<3>(P[pp][r]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          acc[0][e] = fmaf(p0, vf[e], acc[0][e]);
+          acc[1][e] = fmaf(p1, vf[e], acc[1][e]);
+          acc[2][e] = fmaf(p2, vf[e], acc[2][e]);
+          acc[3][e] = fmaf(p3, vf[e], acc[3][e]);
+        }
+      }
+    }
+  }
+  // each row of lanes holds a quarter of the tokens: sum the rows
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[hh][e] += __shfl_xor(acc[hh][e], 16);
+      acc[hh][e] += __shfl_xor(acc[hh][e], 32);
+    }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (row == 0) {
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      float* o = p.part_o + (((size_t)b * p.hq + qhead0 + hh) * p.n_splits + split) * kD + 8 * col;
+      *reinterpret_cast<float4*>(o) = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
+    }
+    if (col < 4)
+      p.part_ml[((size_t)b * p.hq + qhead0 + col) * p.n_splits + split] = make_float2(M, lsum);
+  }
+}
+
+__global__ __launch_bounds__(128) void attend_merge_kernel(const float* part_o, const float2* part_ml,
+                                                           int32_t n_splits, int32_t hq,
+                                                           uint16_t* out, float* out_lse) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const size_t row = (size_t)b * hq + h;
+  const float2* ml = part_ml + row * n_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, ml[s].x);
+  float L = 0.f, o = 0.f;
+  if (M > -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const float2 v = ml[s];
+      if (v.x == -INFINITY) continue;
+      const float w = fast_exp2(v.x - M);
+      L += w * v.y;
+      o += w * part_o[(row * n_splits + s) * kD + d];
+    }
+  }
+  const float res = (L > 0.f) ? o / L : 0.f;
+  out[row * kD + d] = (uint16_t)f32_to_bf16(res);
+  if (out_lse && d == 0) out_lse[row] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+AttendPlan plan_attend(int32_t batch, int32_t hkv, int32_t max_attended) {
+  AttendPlan pl;
+  const long long groups = (long long)batch * hkv;
+  long long per = 2048 / (groups > 0 ? groups : 1);
+  if (per < 1) per = 1;
+  long long pages = (max_attended + per - 1) / per;
+  pages = ((pages + 3) / 4) * 4;
+  if (pages < 4) pages = 4;
+  pl.pages_per_split = (int32_t)pages;
+  pl.n_splits = (int32_t)((max_attended + pages - 1) / pages);
+  if (pl.n_splits < 1) pl.n_splits = 1;
+  return pl;
+}
+
+hipError_t launch_attend(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                         int64_t block_stride, int64_t head_stride, int64_t token_stride,
+                         int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
+                         const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
+                         const int32_t* sel, const int32_t* sel_count, int32_t budget_pages,
+                         float scale, float* part_o, float2* part_ml, const AttendPlan& plan,
+                         uint16_t* out, float* out_lse, hipStream_t stream) {
+  AttendParams p{q, k_cache, v_cache, block_stride, head_stride, token_stride, block_table,
+                 seq_lens, sel, sel_count, part_o, part_ml, scale * kLog2e, num_blocks,
+                 max_pages, budget_pages, hq, hkv, plan.pages_per_split, plan.n_splits};
+  dim3 grid((plan.n_splits + kWaves - 1) / kWaves, hkv, batch);
+  hipLaunchKernelGGL(attend_kernel, grid, dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attend_merge_kernel, dim3(hq, batch), dim3(128), 0, stream, part_o, part_ml,
+                     plan.n_splits, hq, out, out_lse);
+  return hipGetLastError();
+}
+
+}  // namespace locks

@@ -1,0 +1,352 @@
+// Page-summary builder: runs when a page is finalized, off the decode path
+// (LOCKS explainer, technical summary sec. 2, core mechanism: the centroid,
+// a small eigendecomposition of the page's centered keys, the top-r
+// eigenvectors and one coefficient vector per token; int4 basis, int8
+// coefficients and centroid).
+//
+// One wave per (page, KV head):
+//  1. load the 16x128 bf16 keys, centroid mu by DPP row sums, X = K - mu in fp32;
+//  2. Gram matrix X X^T (16x16) on the matrix cores (fp32 16x16x4);
+//  3. cyclic Jacobi on the Gram matrix in LDS: pairs (i, i^m) for m = 1..15
+//     form 8 disjoint rotations per step; each lane owns one 2x2 block of the
+//     matrix and one row-pair of the eigenvector matrix;
+//  4. the top-8 eigenpairs (descending, ties to the lower index) give the
+//     basis v_k = X^T u_k normalized to unit length (the dual of the d x d
+//     scatter's eigenproblem), zeroed when lambda_k <= 1e-5 lambda_1 or when
+//     the page is constant to rounding;
+//  5. sign: the largest-|entry| component of v_k is made positive (lowest dim
+//     on ties); coefficients c_i = V^T x_i are projections on the unquantized
+//     basis;
+//  6. symmetric quantization with fp16 scales (max|x|/7 for the basis,
+//     max|x|/127 for coefficients and centroid, round half to even) and
+//     packing into the 832-byte record.
+#include "locks_device.h"
+#include "locks_internal.h"
+
+namespace locks {
+
+namespace {
+
+constexpr int kSweeps = 10;
+constexpr float kTau = 1e-5f;
+constexpr float kEpsConst = 1e-12f;
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// fp16 scale of a max-magnitude: round to nearest even, saturate at 65504.
+__device__ __forceinline__ float fp16_scale(float m, float qmax) {
+  float s = m / qmax;
+  s = fminf(s, 65504.f);
+  return (float)(_Float16)s;
+}
+__device__ __forceinline__ uint32_t fp16_bits(float s) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s);
+}
+__device__ __forceinline__ int quant(float x, float s, int qmax) {
+  if (!(s > 0.f)) return 0;
+  float v = rintf(x / s);
+  v = fminf(fmaxf(v, (float)-qmax), (float)qmax);
+  return (int)v;
+}
+
+// Rotation (c, s) that zeroes G[p][q] of the 2x2 block [[app, apq], [apq, aqq]]
+// (classical symmetric Schur decomposition).
+__device__ __forceinline__ void jacobi_rot(float app, float apq, float aqq, float& c, float& s) {
+  if (fabsf(apq) <= 1e-30f * (fabsf(app) + fabsf(aqq)) || apq == 0.f) {
+    c = 1.f;
+    s = 0.f;
+    return;
+  }
+  const float theta = (aqq - app) / (2.f * apq);
+  float t;
+  if (fabsf(theta) > 1e15f) {
+    t = 0.5f / theta;
+  } else {
+    t = 1.f / (fabsf(theta) + sqrtf(theta * theta + 1.f));
+    if (theta < 0.f) t = -t;
+  }
+  c = 1.f / sqrtf(t * t + 1.f);
+  s = t * c;
+}
+
+struct BuildSmem {
+  float X[kB][kD + 4];     // centered keys
+  float G[kB][kB + 1];     // Gram matrix -> eigenvalues on the diagonal
+  float U[kB][kB + 1];     // eigenvectors (columns)
+  float cs[8][2];          // rotations of the current step
+  float V[kR][kD + 4];     // unquantized basis, [k][d]
+  float C[kB][kR];         // unquantized coefficients
+  float mu[kD];
+  int order[kB];
+  int8_t vq[kR][kD];
+  uint32_t rec[kRec / 4];
+};
+
+__global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ kc, int64_t bs,
+                                                   int64_t hs, int64_t ts,
+                                                   const int32_t* __restrict__ block_ids,
+                                                   int32_t n_blocks, int32_t num_blocks,
+                                                   int32_t hkv, uint8_t* __restrict__ summ,
+                                                   float* __restrict__ raw) {
+  __shared__ BuildSmem sm;
+  const int lane = threadIdx.x;
+  const int bi = blockIdx.x, kvh = blockIdx.y;
+  const int blk = block_ids[bi];
+  if ((unsigned)blk >= (unsigned)num_blocks) return;   // whole workgroup, uniform
+  const int t = lane & 15, g = lane >> 4;
+
+  // ---- 1. keys, centroid, deviations ----
+  const uint16_t* kp = kc + (size_t)blk * bs + (size_t)kvh * hs + (size_t)t * ts + 32 * g;
+  float x[32];
+  float ksq = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint4 v = *reinterpret_cast<const uint4*>(kp + 8 * s);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * s + 2 * e] = bf16_lo(w[e]);
+      x[8 * s + 2 * e + 1] = bf16_hi(w[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    ksq = fmaf(x[e], x[e], ksq);
+    const float m = row_sum16(x[e]) * (1.f / 16.f);
+    x[e] -= m;
+    if (t == 0) sm.mu[32 * g + e] = m;
+  }
+  ksq = wave_sum(ksq);
+#pragma unroll
+  for (int e = 0; e < 32; ++e) sm.X[t][32 * g + e] = x[e];
+
+  // ---- 2. Gram matrix on the matrix cores: K index (step s, group g) = dim 32g+s ----
+  f32x4v gacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 32; ++s) gacc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], x[s], gacc, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sm.G[4 * g + r][t] = gacc[r];
+  for (int i = lane; i < kB * kB; i += 64) sm.U[i >> 4][i & 15] = ((i >> 4) == (i & 15)) ? 1.f : 0.f;
+  __syncthreads();
+  // symmetrize (the product is symmetric up to rounding order)
+  for (int i = lane; i < kB * kB; i += 64) {
+    const int a = i >> 4, b = i & 15;
+    if (a < b) {
+      const float v = 0.5f * (sm.G[a][b] + sm.G[b][a]);
+      sm.G[a][b] = v;
+      sm.G[b][a] = v;
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. cyclic Jacobi ----
+  const int ia = lane >> 3, ib = lane & 7;   // row pair, column pair of this lane's block
+  const int urow = lane & 15, upair0 = 2 * (lane >> 4);
+  for (int sweep = 0; sweep < kSweeps; ++sweep) {
+    for (int m = 1; m < 16; ++m) {
+      const int hb = 31 - __clz(m);
+      auto pair_p = [&](int pi) { return ((pi >> hb) << (hb + 1)) | (pi & ((1 << hb) - 1)); };
+      const int a0 = pair_p(ia), a1 = a0 ^ m, b0 = pair_p(ib), b1 = b0 ^ m;
+      const float g00 = sm.G[a0][b0], g01 = sm.G[a0][b1], g10 = sm.G[a1][b0], g11 = sm.G[a1][b1];
+      if (ia == ib) {
+        float c, s;
+        jacobi_rot(g00, 0.5f * (g01 + g10), g11, c, s);
+        sm.cs[ia][0] = c;
+        sm.cs[ia][1] = s;
+      }
+      __syncthreads();
+      const float ca = sm.cs[ia][0], sa = sm.cs[ia][1], cb = sm.cs[ib][0], sb = sm.cs[ib][1];
+      // T = G J (columns b0, b1), then G' = J^T T (rows a0, a1)
+      const float t00 = g00 * cb - g01 * sb, t01 = g00 * sb + g01 * cb;
+      const float t10 = g10 * cb - g11 * sb, t11 = g10 * sb + g11 * cb;
+      float n00 = ca * t00 - sa * t10, n01 = ca * t01 - sa * t11;
+      float n10 = sa * t00 + ca * t10, n11 = sa * t01 + ca * t11;
+      if (ia == ib) {
+        n01 = 0.f;
+        n10 = 0.f;
+      }
+      sm.G[a0][b0] = n00;
+      sm.G[a0][b1] = n01;
+      sm.G[a1][b0] = n10;
+      sm.G[a1][b1] = n11;
+      // U' = U J for row urow and pairs upair0, upair0 + 1
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int pi = upair0 + u;
+        const int p0 = pair_p(pi), p1 = p0 ^ m;
+        const float c = sm.cs[pi][0], s = sm.cs[pi][1];
+        const float up = sm.U[urow][p0], uq = sm.U[urow][p1];
+        sm.U[urow][p0] = c * up - s * uq;
+        sm.U[urow][p1] = s * up + c * uq;
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- 4. order eigenpairs: descending eigenvalue, ties to the lower index ----
+  if (lane < 16) {
+    const float lj = sm.G[lane][lane];
+    int rank = 0;
+    for (int i = 0; i < 16; ++i) {
+      const float li = sm.G[i][i];
+      rank += (li > lj) || (li == lj && i < lane);
+    }
+    sm.order[rank] = lane;
+  }
+  __syncthreads();
+  const float lam1 = sm.G[sm.order[0]][sm.order[0]];
+  const bool page_has_basis = lam1 > kEpsConst * ksq;
+
+  // basis v_k = X^T u_k / |X^T u_k|; lane owns dims 2*lane, 2*lane+1
+  const int d0 = 2 * lane;
+#pragma unroll
+  for (int k = 0; k < kR; ++k) {
+    const int j = sm.order[k];
+    const float lk = sm.G[j][j];
+    const bool keep = page_has_basis && (lk > kTau * lam1);
+    float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < kB; ++tt) {
+      const float u = sm.U[tt][j];
+      v0 = fmaf(sm.X[tt][d0], u, v0);
+      v1 = fmaf(sm.X[tt][d0 + 1], u, v1);
+    }
+    const float nrm2 = wave_sum(v0 * v0 + v1 * v1);
+    const float inv = (keep && nrm2 > 0.f) ? 1.f / sqrtf(nrm2) : 0.f;
+    v0 *= inv;
+    v1 *= inv;
+    // sign: largest |v| (lowest dim on ties) positive
+    float best = fabsf(v0);
+    int bidx = d0;
+    float bval = v0;
+    if (fabsf(v1) > best) {
+      best = fabsf(v1);
+      bidx = d0 + 1;
+      bval = v1;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float ob = __shfl_xor(best, o);
+      const int oi = __shfl_xor(bidx, o);
+      const float ov = __shfl_xor(bval, o);
+      if (ob > best || (ob == best && oi < bidx)) {
+        best = ob;
+        bidx = oi;
+        bval = ov;
+      }
+    }
+    if (bval < 0.f) {
+      v0 = -v0;
+      v1 = -v1;
+    }
+    sm.V[k][d0] = v0;
+    sm.V[k][d0 + 1] = v1;
+  }
+  __syncthreads();
+
+  // coefficients c_ik = v_k . x_i : lane -> token t, columns 2*(lane>>4) .. +1
+  {
+    const int tk = lane & 15, k0 = 2 * (lane >> 4);
+    float c0 = 0.f, c1 = 0.f;
+    for (int d = 0; d < kD; ++d) {
+      const float xv = sm.X[tk][d];
+      c0 = fmaf(xv, sm.V[k0][d], c0);
+      c1 = fmaf(xv, sm.V[k0 + 1][d], c1);
+    }
+    sm.C[tk][k0] = c0;
+    sm.C[tk][k0 + 1] = c1;
+  }
+  __syncthreads();
+
+  // ---- 6. quantize + pack ----
+  // centroid
+  const float mu0 = sm.mu[d0], mu1 = sm.mu[d0 + 1];
+  const float s_mu = fp16_scale(wave_max(fmaxf(fabsf(mu0), fabsf(mu1))), 127.f);
+  const int mq0 = quant(mu0, s_mu, 127), mq1 = quant(mu1, s_mu, 127);
+  // basis scales and codes
+  float s_v[kR];
+#pragma unroll
+  for (int k = 0; k < kR; ++k) {
+    const float a = sm.V[k][d0], b2 = sm.V[k][d0 + 1];
+    s_v[k] = fp16_scale(wave_max(fmaxf(fabsf(a), fabsf(b2))), 7.f);
+    sm.vq[k][d0] = (int8_t)quant(a, s_v[k], 7);
+    sm.vq[k][d0 + 1] = (int8_t)quant(b2, s_v[k], 7);
+  }
+  // coefficient scales: column k max over the 16 tokens
+  float s_c[kR];
+#pragma unroll
+  for (int k = 0; k < kR; ++k) {
+    const float a = (lane < 16) ? fabsf(sm.C[lane][k]) : 0.f;
+    s_c[k] = fp16_scale(wave_max(a), 127.f);
+  }
+  __syncthreads();
+  // record words: [0,128) basis, [128,160) coefficients, [160,192) centroid,
+  // [192,196) s_V, [196,200) s_c, [200] s_mu, [201,208) zero
+  uint8_t* mub = reinterpret_cast<uint8_t*>(&sm.rec[160]);
+  mub[d0] = (uint8_t)(int8_t)mq0;
+  mub[d0 + 1] = (uint8_t)(int8_t)mq1;
+  for (int wi = lane; wi < 128; wi += 64) {
+    const int k = wi >> 4, w = wi & 15;
+    uint32_t word = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t lo = (uint32_t)sm.vq[k][8 * w + m] & 0xFu;
+      const uint32_t hi = (uint32_t)sm.vq[k][8 * w + 4 + m] & 0xFu;
+      word |= (lo | (hi << 4)) << (8 * m);
+    }
+    sm.rec[wi] = word;
+  }
+  if (lane < 32) {
+    const int tk = lane >> 1, kh = 4 * (lane & 1);
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      word |= ((uint32_t)(uint8_t)(int8_t)quant(sm.C[tk][kh + e], s_c[kh + e], 127)) << (8 * e);
+    sm.rec[128 + lane] = word;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sm.rec[192 + i] = fp16_bits(s_v[2 * i]) | (fp16_bits(s_v[2 * i + 1]) << 16);
+      sm.rec[196 + i] = fp16_bits(s_c[2 * i]) | (fp16_bits(s_c[2 * i + 1]) << 16);
+    }
+    sm.rec[200] = fp16_bits(s_mu);
+    for (int i = 201; i < kRec / 4; ++i) sm.rec[i] = 0u;
+  }
+  __syncthreads();
+  uint32_t* dst = reinterpret_cast<uint32_t*>(summ + ((size_t)kvh * num_blocks + blk) * kRec);
+  for (int wi = lane; wi < kRec / 4; wi += 64) dst[wi] = sm.rec[wi];
+
+  if (raw) {
+    float* r = raw + ((size_t)bi * hkv + kvh) * 1280;
+    for (int i = lane; i < kD; i += 64) r[i] = sm.mu[i];
+    for (int i = lane; i < kR * kD; i += 64) r[kD + i] = sm.V[i >> 7][i & 127];
+    for (int i = lane; i < kB * kR; i += 64) r[kD + kR * kD + i] = sm.C[i >> 3][i & 7];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_build(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
+                        int64_t token_stride, const int32_t* block_ids, int32_t n_blocks,
+                        int32_t num_blocks, int32_t hkv, uint8_t* summaries, float* raw_debug,
+                        hipStream_t stream) {
+  if (n_blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(build_kernel, dim3(n_blocks, hkv), dim3(64), 0, stream, k_cache,
+                     block_stride, head_stride, token_stride, block_ids, n_blocks, num_blocks,
+                     hkv, summaries, raw_debug);
+  return hipGetLastError();
+}
+
+}  // namespace locks

@@ -1,0 +1,240 @@
+// C ABI entry points: host-side validation, workspace carving, launches.
+// Nothing here allocates, synchronizes or touches device memory from the host.
+#include <hip/hip_runtime.h>
+
+#include "../../include/locks.h"
+#include "locks_internal.h"
+
+using namespace locks;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+locks_status check_dims(const locks_dims* d) {
+  if (!d) return LOCKS_ERR_NULL;
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0) return LOCKS_ERR_SHAPE;
+  if (d->head_dim != 128 || d->page_size != 16 || d->rank != 8) return LOCKS_ERR_UNSUPPORTED;
+  if (d->num_q_heads != 4 * d->num_kv_heads) return LOCKS_ERR_UNSUPPORTED;
+  return LOCKS_OK;
+}
+
+// The page grid is indexed with 32-bit integers on the device.
+constexpr int64_t kMaxPages = (int64_t)1 << 26;
+
+struct ScoreWs {
+  size_t lse_off, part_off, key_off, idx_off, total;
+  ScorePlan sp;
+  SelectPlan sel;
+};
+
+ScoreWs score_ws_layout(const locks_dims* d, int32_t batch, int32_t max_pages, int32_t budget,
+                        bool need_lse) {
+  ScoreWs w{};
+  w.sp = plan_score(batch, d->num_kv_heads, max_pages);
+  w.sel = plan_select(max_pages, budget > 0 ? budget : 1);
+  size_t off = 0;
+  w.lse_off = off;
+  if (need_lse) off += align_up((size_t)batch * d->num_q_heads * max_pages * sizeof(float));
+  w.part_off = off;
+  // partials serve the scorer's chunking and the standalone-select chunking
+  const int32_t n_part = w.sp.n_chunks > w.sel.n_chunks ? w.sp.n_chunks : w.sel.n_chunks;
+  off += align_up((size_t)batch * d->num_q_heads * n_part * sizeof(float2));
+  const size_t ncand = (size_t)batch * d->num_kv_heads * w.sel.n_chunks * w.sel.slots;
+  w.key_off = off;
+  off += align_up(ncand * sizeof(uint32_t));
+  w.idx_off = off;
+  off += align_up(ncand * sizeof(int32_t));
+  w.total = off;
+  return w;
+}
+
+struct AttendWs {
+  size_t o_off, ml_off, total;
+  AttendPlan ap;
+};
+
+AttendWs attend_ws_layout(const locks_dims* d, int32_t batch, int32_t max_attended) {
+  AttendWs w{};
+  w.ap = plan_attend(batch, d->num_kv_heads, max_attended);
+  const size_t rows = (size_t)batch * d->num_q_heads * w.ap.n_splits;
+  w.o_off = 0;
+  w.ml_off = align_up(rows * 128 * sizeof(float));
+  w.total = w.ml_off + align_up(rows * sizeof(float2));
+  return w;
+}
+
+inline char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+}  // namespace
+
+extern "C" {
+
+size_t locks_summary_bytes(const locks_dims* dims) {
+  return check_dims(dims) == LOCKS_OK ? (size_t)832 : 0;
+}
+
+size_t locks_score_workspace_bytes(const locks_dims* dims, int32_t batch, int32_t max_pages,
+                                   int32_t budget_pages) {
+  if (check_dims(dims) != LOCKS_OK || batch <= 0 || max_pages <= 0 || max_pages > kMaxPages)
+    return 0;
+  return score_ws_layout(dims, batch, max_pages, budget_pages, true).total;
+}
+
+size_t locks_attend_workspace_bytes(const locks_dims* dims, int32_t batch,
+                                    int32_t max_attended_pages) {
+  if (check_dims(dims) != LOCKS_OK || batch <= 0 || max_attended_pages <= 0) return 0;
+  return attend_ws_layout(dims, batch, max_attended_pages).total;
+}
+
+locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
+                                   locks_kv_layout layout, const int32_t* block_ids,
+                                   int32_t n_blocks, int32_t num_blocks, void* summaries,
+                                   float* raw_debug, void* stream) {
+  locks_status st = check_dims(dims);
+  if (st != LOCKS_OK) return st;
+  if (n_blocks < 0 || num_blocks <= 0) return LOCKS_ERR_SHAPE;
+  if (n_blocks == 0) return LOCKS_OK;
+  if (!k_cache || !block_ids || !summaries) return LOCKS_ERR_NULL;
+  if (layout.token_stride < 128 || layout.block_stride <= 0 || layout.head_stride <= 0 ||
+      (layout.token_stride % 8) || (layout.head_stride % 8) || (layout.block_stride % 8))
+    return LOCKS_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(k_cache) & 15) || (reinterpret_cast<uintptr_t>(summaries) & 15))
+    return LOCKS_ERR_SHAPE;
+  hipError_t e = launch_build(static_cast<const uint16_t*>(k_cache), layout.block_stride,
+                              layout.head_stride, layout.token_stride, block_ids, n_blocks,
+                              num_blocks, dims->num_kv_heads, static_cast<uint8_t*>(summaries),
+                              raw_debug, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
+}
+
+static locks_status score_checks(const locks_dims* dims, const void* q, const void* summaries,
+                                 int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
+                                 const int32_t* seq_lens, int32_t batch) {
+  locks_status st = check_dims(dims);
+  if (st != LOCKS_OK) return st;
+  if (!q || !summaries || !block_table || !seq_lens) return LOCKS_ERR_NULL;
+  if (batch <= 0 || max_pages <= 0 || max_pages > kMaxPages || num_blocks <= 0)
+    return LOCKS_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(summaries) & 15))
+    return LOCKS_ERR_SHAPE;
+  if (batch > 65535 || dims->num_kv_heads > 65535) return LOCKS_ERR_SHAPE;
+  return LOCKS_OK;
+}
+
+locks_status locks_score_pages(const locks_dims* dims, const void* q, const void* summaries,
+                               int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
+                               const int32_t* seq_lens, int32_t batch, float* page_lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  locks_status st = score_checks(dims, q, summaries, num_blocks, block_table, max_pages, seq_lens, batch);
+  if (st != LOCKS_OK) return st;
+  if (!page_lse) return LOCKS_ERR_NULL;
+  const ScoreWs w = score_ws_layout(dims, batch, max_pages, 0, true);
+  if (!workspace || workspace_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  hipError_t e = launch_score(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
+                              num_blocks, block_table, max_pages, seq_lens, batch,
+                              dims->num_q_heads, dims->num_kv_heads, page_lse,
+                              reinterpret_cast<float2*>(ws_at(workspace, w.part_off)), w.sp,
+                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
+}
+
+locks_status locks_select_pages(const locks_dims* dims, const float* page_lse, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t batch, int32_t budget_pages,
+                                int32_t* sel, int32_t* sel_count, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  locks_status st = check_dims(dims);
+  if (st != LOCKS_OK) return st;
+  if (!page_lse || !seq_lens || !sel || !sel_count) return LOCKS_ERR_NULL;
+  if (batch <= 0 || max_pages <= 0 || max_pages > kMaxPages || budget_pages <= 0)
+    return LOCKS_ERR_SHAPE;
+  const ScoreWs w = score_ws_layout(dims, batch, max_pages, budget_pages, true);
+  if (!workspace || workspace_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float2* part = reinterpret_cast<float2*>(ws_at(workspace, w.part_off));
+  hipError_t e = launch_lse_partials(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, part,
+                                     w.sel.n_chunks, kSelChunk, s);
+  if (e == hipSuccess)
+    e = launch_select(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, dims->num_kv_heads,
+                      budget_pages, part, w.sel.n_chunks,
+                      reinterpret_cast<uint32_t*>(ws_at(workspace, w.key_off)),
+                      reinterpret_cast<int32_t*>(ws_at(workspace, w.idx_off)), w.sel, sel,
+                      sel_count, s);
+  return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
+}
+
+locks_status locks_score_select(const locks_dims* dims, const void* q, const void* summaries,
+                                int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t batch, int32_t budget_pages,
+                                int32_t* sel, int32_t* sel_count, float* page_lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  locks_status st = score_checks(dims, q, summaries, num_blocks, block_table, max_pages, seq_lens, batch);
+  if (st != LOCKS_OK) return st;
+  if (!sel || !sel_count) return LOCKS_ERR_NULL;
+  if (budget_pages <= 0) return LOCKS_ERR_SHAPE;
+  const ScoreWs w = score_ws_layout(dims, batch, max_pages, budget_pages, true);
+  if (!workspace || workspace_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* lse = page_lse ? page_lse : reinterpret_cast<float*>(ws_at(workspace, w.lse_off));
+  float2* part = reinterpret_cast<float2*>(ws_at(workspace, w.part_off));
+  hipError_t e = launch_score(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
+                              num_blocks, block_table, max_pages, seq_lens, batch,
+                              dims->num_q_heads, dims->num_kv_heads, lse, part, w.sp, s);
+  if (e == hipSuccess)
+    e = launch_select(lse, max_pages, seq_lens, batch, dims->num_q_heads, dims->num_kv_heads,
+                      budget_pages, part, w.sp.n_chunks,
+                      reinterpret_cast<uint32_t*>(ws_at(workspace, w.key_off)),
+                      reinterpret_cast<int32_t*>(ws_at(workspace, w.idx_off)), w.sel, sel,
+                      sel_count, s);
+  return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
+}
+
+locks_status locks_sparse_attend(const locks_dims* dims, const void* q, const void* k_cache,
+                                 const void* v_cache, locks_kv_layout layout, int32_t num_blocks,
+                                 const int32_t* block_table, int32_t max_pages,
+                                 const int32_t* seq_lens, int32_t batch, const int32_t* sel,
+                                 const int32_t* sel_count, int32_t budget_pages,
+                                 float softmax_scale, void* out, float* out_lse,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  locks_status st = check_dims(dims);
+  if (st != LOCKS_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return LOCKS_ERR_NULL;
+  if (sel && !sel_count) return LOCKS_ERR_NULL;
+  if (batch <= 0 || batch > 65535 || max_pages <= 0 || max_pages > kMaxPages || num_blocks <= 0)
+    return LOCKS_ERR_SHAPE;
+  if (sel && budget_pages <= 0) return LOCKS_ERR_SHAPE;
+  if (layout.token_stride < 128 || layout.block_stride <= 0 || layout.head_stride <= 0 ||
+      (layout.token_stride % 8) || (layout.head_stride % 8) || (layout.block_stride % 8))
+    return LOCKS_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(k_cache) & 15) ||
+      (reinterpret_cast<uintptr_t>(v_cache) & 15))
+    return LOCKS_ERR_SHAPE;
+  if (!(softmax_scale > 0.f) || softmax_scale != softmax_scale) return LOCKS_ERR_SHAPE;
+  const int32_t max_att = (sel ? budget_pages : max_pages) + 1;
+  const AttendWs w = attend_ws_layout(dims, batch, max_att);
+  if (!workspace || workspace_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  hipError_t e = launch_attend(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+      static_cast<const uint16_t*>(v_cache), layout.block_stride, layout.head_stride,
+      layout.token_stride, num_blocks, block_table, max_pages, seq_lens, batch, dims->num_q_heads,
+      dims->num_kv_heads, sel, sel_count, budget_pages, softmax_scale,
+      reinterpret_cast<float*>(ws_at(workspace, w.o_off)),
+      reinterpret_cast<float2*>(ws_at(workspace, w.ml_off)), w.ap, static_cast<uint16_t*>(out),
+      out_lse, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
+}
+
+const char* locks_status_str(locks_status status) {
+  switch (status) {
+    case LOCKS_OK: return "ok";
+    case LOCKS_ERR_NULL: return "required pointer is NULL";
+    case LOCKS_ERR_SHAPE: return "size, stride or alignment out of range";
+    case LOCKS_ERR_UNSUPPORTED: return "unsupported dims (need d=128, page 16, rank 8, GQA 4)";
+    case LOCKS_ERR_WORKSPACE: return "workspace missing or too small";
+    case LOCKS_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

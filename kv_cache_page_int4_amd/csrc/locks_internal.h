@@ -1,0 +1,63 @@
+// Host-side launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace locks {
+
+// ---- scoring ---------------------------------------------------------------
+struct ScorePlan {
+  int32_t pages_per_chunk;   // pages handled by one workgroup
+  int32_t blocks16_per_wave; // 16-page blocks per wave
+  int32_t n_chunks;          // chunks per (sequence, KV head)
+};
+ScorePlan plan_score(int32_t batch, int32_t hkv, int32_t max_pages);
+
+hipError_t launch_score(const uint16_t* q, const uint8_t* summ, int32_t num_blocks,
+                        const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                        int32_t batch, int32_t hq, int32_t hkv, float* page_lse,
+                        float2* partials, const ScorePlan& plan, hipStream_t stream);
+
+// ---- selection -------------------------------------------------------------
+constexpr int32_t kSelChunk = 2048;   // pages per first-stage select workgroup
+struct SelectPlan {
+  int32_t n_chunks;     // first-stage chunks per (sequence, KV head)
+  int32_t slots;        // candidates kept per chunk = min(budget, kSelChunk)
+};
+SelectPlan plan_select(int32_t max_pages, int32_t budget_pages);
+
+// Per-head (max, sum) base-2 partials straight from page scores.
+hipError_t launch_lse_partials(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
+                               int32_t batch, int32_t hq, float2* partials, int32_t n_chunks,
+                               int32_t pages_per_chunk, hipStream_t stream);
+
+hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
+                         int32_t batch, int32_t hq, int32_t hkv, int32_t budget_pages,
+                         const float2* partials, int32_t n_partials, uint32_t* cand_key,
+                         int32_t* cand_idx, const SelectPlan& plan, int32_t* sel,
+                         int32_t* sel_count, hipStream_t stream);
+
+// ---- sparse attention ---------------------------------------------------------
+struct AttendPlan {
+  int32_t pages_per_split;  // multiple of 4
+  int32_t n_splits;         // splits per (sequence, KV head)
+};
+AttendPlan plan_attend(int32_t batch, int32_t hkv, int32_t max_attended);
+
+hipError_t launch_attend(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                         int64_t block_stride, int64_t head_stride, int64_t token_stride,
+                         int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
+                         const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
+                         const int32_t* sel, const int32_t* sel_count, int32_t budget_pages,
+                         float scale, float* part_o, float2* part_ml, const AttendPlan& plan,
+                         uint16_t* out, float* out_lse, hipStream_t stream);
+
+// ---- summary build -----------------------------------------------------------
+hipError_t launch_build(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
+                        int64_t token_stride, const int32_t* block_ids, int32_t n_blocks,
+                        int32_t num_blocks, int32_t hkv, uint8_t* summaries, float* raw_debug,
+                        hipStream_t stream);
+
+}  // namespace locks

@@ -1,0 +1,200 @@
+"""Python binding of liblocks.so (argument marshalling only).
+
+Every function forwards to the C entry point of the same name in
+include/locks.h.  Tensors supply device pointers and the current torch stream;
+no computation happens here.  If the shared library is missing the import of
+this module still works but every call raises, so nothing can silently fall
+back to a host path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblocks.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4, -5
+SUMMARY_BYTES = 832
+
+
+class LocksError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({status_str(status)})")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("rank", ctypes.c_int32)]
+
+
+class KVLayout(ctypes.Structure):
+    _fields_ = [("block_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("token_stride", ctypes.c_int64)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_DP = ctypes.POINTER(Dims)
+
+_SIGS = {
+    "locks_summary_bytes": (_SZ, [_DP]),
+    "locks_score_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I32]),
+    "locks_attend_workspace_bytes": (_SZ, [_DP, _I32, _I32]),
+    "locks_build_summaries": (_I32, [_DP, _P, KVLayout, _P, _I32, _I32, _P, _P, _P]),
+    "locks_score_pages": (_I32, [_DP, _P, _P, _I32, _P, _I32, _P, _I32, _P, _P, _SZ, _P]),
+    "locks_select_pages": (_I32, [_DP, _P, _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "locks_score_select": (_I32, [_DP, _P, _P, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P,
+                                  _SZ, _P]),
+    "locks_sparse_attend": (_I32, [_DP, _P, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32, _P, _P,
+                                   _I32, ctypes.c_float, _P, _P, _P, _SZ, _P]),
+    "locks_status_str": (ctypes.c_char_p, [_I32]),
+}
+
+
+def lib():
+    """Load liblocks.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype, f.argtypes = res, args
+        _lib = h
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().locks_status_str(int(status)).decode()
+
+
+def _check(fn, st):
+    if st != OK:
+        raise LocksError(fn, st)
+
+
+def dims(num_q_heads, num_kv_heads, head_dim=128, page_size=16, rank=8) -> Dims:
+    return Dims(num_q_heads, num_kv_heads, head_dim, page_size, rank)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, cuda=True):
+    if t is None:
+        return
+    if cuda and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def kv_layout(cache: torch.Tensor) -> KVLayout:
+    """Strides of a [num_blocks, num_kv_heads, page, head_dim] cache view."""
+    if cache.dim() != 4 or cache.stride(3) != 1:
+        raise ValueError("cache must be a [blocks, kv_heads, page, dim] view with unit dim stride")
+    return KVLayout(cache.stride(0), cache.stride(1), cache.stride(2))
+
+
+def summary_bytes(d: Dims) -> int:
+    return lib().locks_summary_bytes(ctypes.byref(d))
+
+
+def score_workspace_bytes(d: Dims, batch, max_pages, budget_pages=0) -> int:
+    return lib().locks_score_workspace_bytes(ctypes.byref(d), batch, max_pages, budget_pages)
+
+
+def attend_workspace_bytes(d: Dims, batch, max_attended_pages) -> int:
+    return lib().locks_attend_workspace_bytes(ctypes.byref(d), batch, max_attended_pages)
+
+
+def build_summaries(d: Dims, k_cache, block_ids, summaries, raw_debug=None, stream=None):
+    """k_cache: bf16 [num_blocks, Hkv, 16, 128] (one layer); block_ids: int32
+    [n]; summaries: uint8 [Hkv, num_blocks, 832]; raw_debug: fp32 [n, Hkv, 1280]."""
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(block_ids, "block_ids", torch.int32)
+    _need(summaries, "summaries", torch.uint8)
+    _need(raw_debug, "raw_debug", torch.float32)
+    st = lib().locks_build_summaries(ctypes.byref(d), _ptr(k_cache), kv_layout(k_cache),
+                                     _ptr(block_ids), block_ids.numel(), k_cache.shape[0],
+                                     _ptr(summaries), _ptr(raw_debug), _stream(stream))
+    _check("locks_build_summaries", st)
+
+
+def score_pages(d: Dims, q, summaries, num_blocks, block_table, seq_lens, page_lse, workspace,
+                stream=None):
+    _need(q, "q", torch.bfloat16)
+    _need(summaries, "summaries", torch.uint8)
+    _need(block_table, "block_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(page_lse, "page_lse", torch.float32)
+    st = lib().locks_score_pages(ctypes.byref(d), _ptr(q), _ptr(summaries), num_blocks,
+                                 _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                 block_table.shape[0], _ptr(page_lse), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("locks_score_pages", st)
+
+
+def select_pages(d: Dims, page_lse, seq_lens, budget_pages, sel, sel_count, workspace, stream=None):
+    _need(page_lse, "page_lse", torch.float32)
+    _need(sel, "sel", torch.int32)
+    _need(sel_count, "sel_count", torch.int32)
+    st = lib().locks_select_pages(ctypes.byref(d), _ptr(page_lse), page_lse.shape[-1],
+                                  _ptr(seq_lens), page_lse.shape[0], budget_pages, _ptr(sel),
+                                  _ptr(sel_count), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("locks_select_pages", st)
+
+
+def score_select(d: Dims, q, summaries, num_blocks, block_table, seq_lens, budget_pages, sel,
+                 sel_count, workspace, page_lse=None, stream=None):
+    _need(q, "q", torch.bfloat16)
+    _need(summaries, "summaries", torch.uint8)
+    _need(block_table, "block_table", torch.int32)
+    _need(sel, "sel", torch.int32)
+    _need(page_lse, "page_lse", torch.float32)
+    st = lib().locks_score_select(ctypes.byref(d), _ptr(q), _ptr(summaries), num_blocks,
+                                  _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                  block_table.shape[0], budget_pages, _ptr(sel), _ptr(sel_count),
+                                  _ptr(page_lse), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("locks_score_select", st)
+
+
+def sparse_attend(d: Dims, q, k_cache, v_cache, block_table, seq_lens, sel, sel_count,
+                  budget_pages, out, workspace, out_lse=None, softmax_scale=None, stream=None):
+    """sel=None attends every finalized page (dense attention)."""
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(v_cache, "v_cache", torch.bfloat16)
+    _need(out, "out", torch.bfloat16)
+    _need(out_lse, "out_lse", torch.float32)
+    lay = kv_layout(k_cache)
+    lv = kv_layout(v_cache)
+    if (lay.block_stride, lay.head_stride, lay.token_stride) != (
+            lv.block_stride, lv.head_stride, lv.token_stride):
+        raise ValueError("k_cache and v_cache must share one layout")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / (d.head_dim ** 0.5)
+    st = lib().locks_sparse_attend(ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), lay,
+                                   k_cache.shape[0], _ptr(block_table), block_table.shape[1],
+                                   _ptr(seq_lens), block_table.shape[0], _ptr(sel),
+                                   _ptr(sel_count), budget_pages if sel is not None else 0,
+                                   float(softmax_scale), _ptr(out), _ptr(out_lse),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream))
+    _check("locks_sparse_attend", st)

@@ -1,0 +1,159 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the library,
+compare with the oracle at the stated tolerances."""
+
+import math
+
+import numpy as np
+import torch
+
+import oracle as O
+from kv_cache_page_int4_amd import locks as L
+
+LSE_TOL = 1e-3        # page LSE, absolute, against fp64 on the same codes
+OUT_TOL = 2e-2        # sparse attention output, max-abs
+WINDOW = 1e-4         # relative mass window around the k-th page
+
+
+def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def from_dev_bf16(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class Layer:
+    """Device copies of one layer of a generated workload."""
+
+    def __init__(self, x, layer=0):
+        w = x.w
+        self.x, self.w, self.layer = x, w, layer
+        self.d = L.dims(w.hq, w.hkv)
+        self.k = to_dev_bf16(x.k_cache[layer])      # [nb, hkv, 16, 128]
+        self.v = to_dev_bf16(x.v_cache[layer])
+        self.q = to_dev_bf16(x.q[layer])            # [b, hq, 128]
+        self.bt = torch.from_numpy(x.block_table).cuda()
+        self.seq = torch.from_numpy(x.seq_lens).cuda()
+        self.nb = w.num_blocks
+        self.summ = torch.zeros((w.hkv, self.nb, O.RECORD_BYTES), dtype=torch.uint8, device="cuda")
+
+    # -- oracle-built records (host), uploaded ---------------------------------
+    def upload_oracle_records(self):
+        x, w = self.x, self.w
+        recs = np.zeros((w.hkv, self.nb, O.RECORD_BYTES), dtype=np.uint8)
+        for b in range(w.batch):
+            n = int(x.seq_lens[b]) // 16
+            if n == 0:
+                continue
+            blk = x.block_table[b, :n]
+            for g in range(w.hkv):
+                K = O.bf16_to_f64(x.k_cache[self.layer][blk, g])
+                r, _, _ = O.build_records(K)
+                recs[g, blk] = r
+        self.summ.copy_(torch.from_numpy(recs))
+        return recs
+
+    def gpu_build(self, raw=False):
+        blocks = torch.arange(self.nb, dtype=torch.int32, device="cuda")
+        rd = torch.zeros((self.nb, self.w.hkv, 1280), dtype=torch.float32, device="cuda") if raw else None
+        L.build_summaries(self.d, self.k, blocks, self.summ, raw_debug=rd)
+        return rd
+
+    def score(self):
+        w = self.w
+        P = self.bt.shape[1]
+        lse = torch.empty((w.batch, w.hq, P), dtype=torch.float32, device="cuda")
+        ws = torch.empty(L.score_workspace_bytes(self.d, w.batch, P, 0), dtype=torch.uint8, device="cuda")
+        L.score_pages(self.d, self.q, self.summ, self.nb, self.bt, self.seq, lse, ws)
+        return lse
+
+    def score_select(self, budget, with_lse=True):
+        w = self.w
+        P = self.bt.shape[1]
+        sel = torch.full((w.batch, w.hkv, budget), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((w.batch, w.hkv), -7, dtype=torch.int32, device="cuda")
+        lse = torch.empty((w.batch, w.hq, P), dtype=torch.float32, device="cuda") if with_lse else None
+        ws = torch.empty(L.score_workspace_bytes(self.d, w.batch, P, budget), dtype=torch.uint8,
+                         device="cuda")
+        L.score_select(self.d, self.q, self.summ, self.nb, self.bt, self.seq, budget, sel, cnt, ws,
+                       page_lse=lse)
+        return sel, cnt, lse
+
+    def select(self, lse, budget):
+        w = self.w
+        sel = torch.full((w.batch, w.hkv, budget), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((w.batch, w.hkv), -7, dtype=torch.int32, device="cuda")
+        ws = torch.empty(L.score_workspace_bytes(self.d, w.batch, lse.shape[-1], budget),
+                         dtype=torch.uint8, device="cuda")
+        L.select_pages(self.d, lse, self.seq, budget, sel, cnt, ws)
+        return sel, cnt
+
+    def attend(self, sel, cnt, budget, dense=False):
+        w = self.w
+        out = torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda")
+        olse = torch.empty((w.batch, w.hq), dtype=torch.float32, device="cuda")
+        n_att = (self.bt.shape[1] if dense else budget) + 1
+        ws = torch.empty(L.attend_workspace_bytes(self.d, w.batch, n_att), dtype=torch.uint8,
+                         device="cuda")
+        L.sparse_attend(self.d, self.q, self.k, self.v, self.bt, self.seq,
+                        None if dense else sel, None if dense else cnt, budget, out, ws,
+                        out_lse=olse)
+        return out, olse
+
+
+def oracle_scores(x, recs, layer, b, g):
+    """fp64 page LSE of the group's heads from records (host array [hkv, nb, 832])."""
+    n = int(x.seq_lens[b]) // 16
+    G = x.w.group
+    q = O.bf16_to_f64(x.q[layer, b, g * G:(g + 1) * G])
+    return O.score_records(q, recs[g, x.block_table[b, :n]])
+
+
+def check_selection(gpu_sel, oracle_log_m, budget):
+    """Selected set must equal the oracle's except for pages whose mass is
+    within WINDOW (relative) of the k-th largest mass.  Returns the number of
+    pages inside that window."""
+    n = oracle_log_m.shape[0]
+    k = min(budget, n)
+    want = O.select_top_pages(oracle_log_m, budget)
+    got = np.asarray(gpu_sel)
+    assert got.shape[0] == k, (got.shape, k)
+    assert np.all(np.diff(got) > 0), "selection not strictly ascending"
+    if k == 0 or k == n:
+        assert list(got) == list(range(n)) if k == n else True
+        return 0
+    lm_k = np.sort(oracle_log_m)[::-1][k - 1]
+    # |m_j - m_k| <= WINDOW * m_k  <=>  |exp(lm_j - lm_k) - 1| <= WINDOW
+    near = np.abs(np.expm1(oracle_log_m - lm_k)) <= WINDOW
+    g_set, w_set = set(got.tolist()), set(want.tolist())
+    diff = g_set ^ w_set
+    bad = [j for j in diff if not near[j]]
+    assert not bad, f"selection differs outside the tie window at pages {sorted(bad)[:10]}"
+    if not (near.sum() > 1):
+        assert list(got) == list(want)
+    return int(near.sum())
+
+
+def dequant_recon(qz):
+    mu, V, C = O.dequantize_summary(qz)
+    return mu[..., None, :] + C @ np.swapaxes(V, -1, -2)
+
+
+def fp16_ulp(x):
+    x = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
+def scores_of(x, layer, b, g, lse_dev):
+    G = x.w.group
+    n = int(x.seq_lens[b]) // 16
+    return lse_dev[b, g * G:(g + 1) * G, :n].double().cpu().numpy()
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def softmax_scale():
+    return 1.0 / math.sqrt(128)

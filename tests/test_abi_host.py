@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/locks.h declares, and rejects bad arguments before
+launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "locks.h")
+
+L = pytest.importorskip("kv_cache_page_int4_amd.locks")
+
+
+def _lib_or_skip():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("liblocks.so not built")
+    return L.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(locks_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ["locks_build_summaries", "locks_score_select", "locks_sparse_attend",
+                 "locks_score_pages", "locks_select_pages", "locks_summary_bytes",
+                 "locks_score_workspace_bytes", "locks_attend_workspace_bytes",
+                 "locks_status_str"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib_or_skip()
+    h = ctypes.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(h, name), name
+
+
+def test_summary_bytes_and_unsupported_dims():
+    _lib_or_skip()
+    assert L.summary_bytes(L.dims(32, 8)) == 832
+    assert L.summary_bytes(L.dims(32, 8, head_dim=64)) == 0
+    assert L.summary_bytes(L.dims(32, 8, rank=4)) == 0
+    assert L.summary_bytes(L.dims(16, 8)) == 0       # group of 2 not supported
+
+
+def test_workspace_sizes_monotone():
+    _lib_or_skip()
+    d = L.dims(32, 8)
+    a = L.score_workspace_bytes(d, 1, 2048, 128)
+    b = L.score_workspace_bytes(d, 1, 65536, 128)
+    assert 0 < a < b
+    assert L.score_workspace_bytes(d, 0, 2048, 128) == 0
+    assert L.attend_workspace_bytes(d, 1, 129) > 0
+    assert L.attend_workspace_bytes(d, 8, 129) >= L.attend_workspace_bytes(d, 1, 129)
+
+
+def _raw_score(lib, d, **kw):
+    args = dict(q=1, summ=1, num_blocks=1, bt=1, max_pages=1, seq=1, batch=1, lse=1, ws=1,
+                ws_bytes=1 << 40)
+    args.update(kw)
+    P = lambda v: ctypes.c_void_p(v) if v else None  # noqa: E731
+    return lib.locks_score_pages(ctypes.byref(d), P(args["q"] and 256), P(args["summ"] and 256),
+                                 args["num_blocks"], P(args["bt"] and 256), args["max_pages"],
+                                 P(args["seq"] and 256), args["batch"], P(args["lse"] and 256),
+                                 P(args["ws"] and 256), args["ws_bytes"], None)
+
+
+def test_validation_errors_launch_nothing():
+    lib = _lib_or_skip()
+    d = L.dims(32, 8)
+    assert _raw_score(lib, d, q=0) == L.ERR_NULL
+    assert _raw_score(lib, d, lse=0) == L.ERR_NULL
+    assert _raw_score(lib, d, batch=0) == L.ERR_SHAPE
+    assert _raw_score(lib, d, max_pages=0) == L.ERR_SHAPE
+    assert _raw_score(lib, d, num_blocks=0) == L.ERR_SHAPE
+    assert _raw_score(lib, d, ws=0) == L.ERR_WORKSPACE
+    assert _raw_score(lib, d, ws_bytes=16) == L.ERR_WORKSPACE
+    assert _raw_score(lib, L.dims(32, 8, page_size=32)) == L.ERR_UNSUPPORTED
+    assert lib.locks_score_pages(None, None, None, 0, None, 0, None, 0, None, None, 0, None) == L.ERR_NULL
+    # misaligned q
+    P = ctypes.c_void_p
+    assert lib.locks_score_pages(ctypes.byref(d), P(258), P(256), 1, P(256), 1, P(256), 1, P(256),
+                                 P(256), 1 << 40, None) == L.ERR_SHAPE
+
+
+def test_attend_and_build_validation():
+    lib = _lib_or_skip()
+    d = L.dims(4, 1)
+    P = ctypes.c_void_p
+    lay = L.KVLayout(2048, 2048, 128)
+    # sel given without sel_count
+    st = lib.locks_sparse_attend(ctypes.byref(d), P(256), P(256), P(256), lay, 4, P(256), 4,
+                                 P(256), 1, P(256), None, 4, 0.1, P(256), None, P(256), 1 << 40, None)
+    assert st == L.ERR_NULL
+    # non-positive softmax scale
+    st = lib.locks_sparse_attend(ctypes.byref(d), P(256), P(256), P(256), lay, 4, P(256), 4,
+                                 P(256), 1, None, None, 0, -1.0, P(256), None, P(256), 1 << 40, None)
+    assert st == L.ERR_SHAPE
+    # token stride shorter than a row
+    bad = L.KVLayout(2048, 2048, 64)
+    st = lib.locks_sparse_attend(ctypes.byref(d), P(256), P(256), P(256), bad, 4, P(256), 4,
+                                 P(256), 1, None, None, 0, 0.1, P(256), None, P(256), 1 << 40, None)
+    assert st == L.ERR_SHAPE
+    # too small workspace
+    st = lib.locks_sparse_attend(ctypes.byref(d), P(256), P(256), P(256), lay, 4, P(256), 4,
+                                 P(256), 1, None, None, 0, 0.1, P(256), None, P(256), 8, None)
+    assert st == L.ERR_WORKSPACE
+    # build: empty list is a no-op, null summaries rejected
+    assert lib.locks_build_summaries(ctypes.byref(d), P(256), lay, P(256), 0, 4, None, None, None) == L.OK
+    assert lib.locks_build_summaries(ctypes.byref(d), P(256), lay, P(256), 3, 4, None, None, None) == L.ERR_NULL
+    assert lib.locks_build_summaries(ctypes.byref(d), P(256), lay, P(256), -1, 4, P(256), None, None) == L.ERR_SHAPE
+    # select: zero budget rejected
+    st = lib.locks_select_pages(ctypes.byref(d), P(256), 16, P(256), 1, 0, P(256), P(256), P(256),
+                                1 << 40, None)
+    assert st == L.ERR_SHAPE
+
+
+def test_status_strings():
+    _lib_or_skip()
+    for st in (L.OK, L.ERR_NULL, L.ERR_SHAPE, L.ERR_UNSUPPORTED, L.ERR_WORKSPACE, L.ERR_LAUNCH):
+        assert len(L.status_str(st)) > 0
+    assert L.status_str(-99) == "unknown status"

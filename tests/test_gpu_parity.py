@@ -1,0 +1,264 @@
+"""GPU parity of every step of the LOCKS decode path against the fp64 oracle,
+through the C ABI, on seeded synthetic inputs.
+
+Tolerances (stated targets): page LSE 1e-3 absolute on the same codes;
+selected sets identical except pages within 1e-4 (relative) of the k-th
+mass, indices bit-exact when untied; sparse output 2e-2 max-abs; summary
+codes within 1 LSB after the sign convention, scales within 1 fp16 ulp,
+with near-degenerate eigenpairs exempted (their reconstruction compared
+instead)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import get_workload
+from synth.host import generate
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from tests.gpu_common import (LSE_TOL, OUT_TOL, Layer, check_selection, dequant_recon,  # noqa: E402
+                              fp16_ulp, log, oracle_scores, scores_of)
+
+_CACHE = {}
+
+
+def gen(name, **kw):
+    key = (name, tuple(sorted((k, tuple(v) if isinstance(v, list) else v) for k, v in kw.items())))
+    if key not in _CACHE:
+        seq = kw.pop("seq_lens", None)
+        w = get_workload(name, **kw)
+        _CACHE[key] = generate(w, seq_lens=seq)
+    return _CACHE[key]
+
+
+def run_and_check(x, budget=None, gpu_records=False, check_build=False):
+    w = x.w
+    budget = w.budget_pages if budget is None else budget
+    lay = Layer(x, 0)
+    if gpu_records:
+        lay.gpu_build()
+        torch.cuda.synchronize()
+        recs = lay.summ.cpu().numpy()
+    else:
+        recs = lay.upload_oracle_records()
+    lse = lay.score()
+    sel, cnt, lse2 = lay.score_select(budget)
+    out, olse = lay.attend(sel, cnt, budget)
+    sel_sa, cnt_sa = lay.select(lse, budget)
+    torch.cuda.synchronize()
+    assert torch.equal(lse, lse2), "score_pages and score_select disagree on page LSE"
+    worst_lse, worst_out, ties = 0.0, 0.0, 0
+    for b in range(w.batch):
+        n = int(x.seq_lens[b]) // 16
+        for g in range(w.hkv):
+            G = w.group
+            if n:
+                s_gpu = scores_of(x, 0, b, g, lse)
+                s_ref = oracle_scores(x, recs, 0, b, g)
+                err = np.abs(s_gpu - s_ref).max()
+                worst_lse = max(worst_lse, err)
+                assert err <= LSE_TOL, f"page LSE off by {err} (b={b}, g={g})"
+                tail = lse[b, g * G:(g + 1) * G, n:]
+                assert torch.all(torch.isneginf(tail)), "non-finalized pages must score -inf"
+                _, log_m, _ = O.group_mass(s_gpu)
+            else:
+                log_m = np.zeros(0)
+            c = int(cnt[b, g])
+            got = sel[b, g, :c].cpu().numpy()
+            assert torch.all(sel[b, g, c:] == -1)
+            ties += check_selection(got, log_m, budget)
+            assert torch.equal(sel[b, g], sel_sa[b, g]) and int(cnt_sa[b, g]) == c
+            q = O.bf16_to_f64(x.q[0, b, g * G:(g + 1) * G])
+            o_ref, l_ref = O.sparse_attention(q, x.k_cache[0], x.v_cache[0], x.block_table[b], g,
+                                              got, int(x.seq_lens[b]))
+            o_gpu = out[b, g * G:(g + 1) * G].float().cpu().numpy()
+            if o_ref.shape[0] and np.isfinite(l_ref).all():
+                e = np.abs(o_gpu - o_ref).max()
+                worst_out = max(worst_out, e)
+                assert e <= OUT_TOL, f"attention output off by {e}"
+                assert np.abs(olse[b, g * G:(g + 1) * G].cpu().numpy() - l_ref).max() <= LSE_TOL
+    log(f"[{w.name} b={w.batch} budget={budget}] max|dLSE|={worst_lse:.2e} "
+        f"max|dOut|={worst_out:.2e} tie-window pages={ties}")
+    return lay, recs
+
+
+@pytest.mark.parametrize("name", ["tiny-4k", "llama8b-32k"])
+def test_pipeline_on_oracle_records(name):
+    run_and_check(gen(name))
+
+
+@pytest.mark.parametrize("name", ["tiny-4k", "llama8b-32k"])
+def test_pipeline_on_gpu_records(name):
+    run_and_check(gen(name), gpu_records=True)
+
+
+def test_ragged_batch_tail_pages_and_shuffled_blocks():
+    x = gen("tiny-4k", batch=3, shuffled_blocks=True, seq_lens=[4096 - 5, 16 * 37 + 9, 7])
+    run_and_check(x, budget=32)
+
+
+@pytest.mark.parametrize("budget", [1, 3, 255, 256, 1000])
+def test_budget_edges(budget):
+    run_and_check(gen("tiny-4k"), budget=budget)
+
+
+def test_dense_attention_matches_oracle():
+    x = gen("tiny-4k", seq_lens=[4096 - 3])
+    lay = Layer(x, 0)
+    out, olse = lay.attend(None, None, 0, dense=True)
+    torch.cuda.synchronize()
+    q = O.bf16_to_f64(x.q[0, 0])
+    o_ref, l_ref = O.sparse_attention(q, x.k_cache[0], x.v_cache[0], x.block_table[0], 0,
+                                      list(range((4096 - 3) // 16)), 4096 - 3)
+    assert np.abs(out[0].float().cpu().numpy() - o_ref).max() <= OUT_TOL
+    assert np.abs(olse[0].cpu().numpy() - l_ref).max() <= 1e-3
+
+
+def test_full_budget_equals_dense_on_gpu():
+    x = gen("tiny-4k")
+    lay = Layer(x, 0)
+    lay.upload_oracle_records()
+    sel, cnt, _ = lay.score_select(10 ** 4)
+    o1, l1 = lay.attend(sel, cnt, 10 ** 4)
+    o2, l2 = lay.attend(None, None, 0, dense=True)
+    torch.cuda.synchronize()
+    assert int(cnt[0, 0]) == 256
+    assert torch.equal(sel[0, 0, :256].cpu(), torch.arange(256, dtype=torch.int32))
+    assert (o1.float() - o2.float()).abs().max().item() <= 1e-2
+    assert (l1 - l2).abs().max().item() <= 1e-4
+
+
+def test_invalid_block_ids_are_absent():
+    x = gen("tiny-4k")
+    lay = Layer(x, 0)
+    lay.upload_oracle_records()
+    bt = lay.bt.clone()
+    bt[0, 5] = -1
+    bt[0, 9] = lay.nb + 3
+    lay.bt = bt
+    lse = lay.score()
+    sel, cnt, _ = lay.score_select(32)
+    out, _ = lay.attend(sel, cnt, 32)
+    torch.cuda.synchronize()
+    assert torch.isneginf(lse[0, :, 5]).all() and torch.isneginf(lse[0, :, 9]).all()
+    s = set(sel[0, 0, :int(cnt[0, 0])].tolist())
+    assert 5 not in s and 9 not in s and int(cnt[0, 0]) == 32
+    assert torch.isfinite(out.float()).all()
+
+
+def test_short_sequences_without_finalized_pages():
+    x = gen("tiny-4k", batch=2, seq_lens=[0, 11])
+    lay = Layer(x, 0)
+    lay.upload_oracle_records()
+    sel, cnt, lse = lay.score_select(32)
+    out, olse = lay.attend(sel, cnt, 32)
+    torch.cuda.synchronize()
+    assert int(cnt[0, 0]) == 0 and int(cnt[1, 0]) == 0
+    assert torch.isneginf(olse[0]).all() and torch.all(out[0].float() == 0)
+    q = O.bf16_to_f64(x.q[0, 1])
+    o_ref, l_ref = O.sparse_attention(q, x.k_cache[0], x.v_cache[0], x.block_table[1], 0, [], 11)
+    assert np.abs(out[1].float().cpu().numpy() - o_ref).max() <= OUT_TOL
+
+
+# ---------------------------------------------------------------------------
+# summary builder codes
+# ---------------------------------------------------------------------------
+
+def _exempt_columns(lam, V):
+    """Columns whose codes are not unique under rounding: near-degenerate
+    eigenvalues, a near-tie for the sign pivot, or an eigenvalue near the
+    rank floor."""
+    r = V.shape[-1]
+    lam1 = lam[0]
+    ex = np.zeros(r, dtype=bool)
+    for k in range(r):
+        gaps = []
+        if k > 0:
+            gaps.append(lam[k - 1] - lam[k])
+        gaps.append(lam[k] - lam[k + 1])
+        if min(gaps) < 1e-3 * lam1:
+            ex[k] = True
+        a = np.sort(np.abs(V[:, k]))[::-1]
+        if a[0] > 0 and (a[0] - a[1]) <= 1e-4 * a[0]:
+            ex[k] = True
+        if 0.5 * O.TAU * lam1 <= lam[k] <= 2 * O.TAU * lam1:
+            ex[k] = True
+    return ex
+
+
+@pytest.mark.parametrize("name", ["tiny-4k", "llama8b-32k"])
+def test_builder_codes(name):
+    x = gen(name)
+    w = x.w
+    lay = Layer(x, 0)
+    raw = lay.gpu_build(raw=True)
+    torch.cuda.synchronize()
+    recs = lay.summ.cpu().numpy()
+    raw = raw.cpu().numpy()
+    n_cols = n_ex = 0
+    worst_rec = 0.0
+    for g in range(w.hkv):
+        blk = x.block_table[0, :w.pages]
+        K = O.bf16_to_f64(x.k_cache[0][blk, g])
+        mu, V, C, lam = O.page_summary(K)
+        qo = O.quantize_summary(mu, V, C)
+        qg = O.unpack_records(recs[g, blk])
+        # centroid: codes within 1 LSB, scale within 1 fp16 ulp
+        assert np.abs(qg["mu_q"].astype(int) - qo["mu_q"]).max() <= 1
+        assert np.all(np.abs(qg["s_mu"] - qo["s_mu"]) <= fp16_ulp(qo["s_mu"]))
+        # unquantized debug output reproduces the centroid and the subspace
+        rmu = raw[blk, g, :128]
+        assert np.abs(rmu - mu).max() <= 1e-5 * (1 + np.abs(mu).max())
+        for i in range(len(blk)):
+            ex = _exempt_columns(lam[i], V[i])
+            n_cols += len(ex)
+            n_ex += int(ex.sum())
+            ok = ~ex
+            dv = np.abs(qg["v_q"][i][:, ok].astype(int) - qo["v_q"][i][:, ok])
+            dc = np.abs(qg["c_q"][i][:, ok].astype(int) - qo["c_q"][i][:, ok])
+            assert dv.max(initial=0) <= 1, f"basis codes off by {dv.max()} (g={g}, page={i})"
+            assert dc.max(initial=0) <= 1, f"coefficient codes off by {dc.max()} (g={g}, page={i})"
+            assert np.all(np.abs(qg["s_v"][i][ok] - qo["s_v"][i][ok]) <= fp16_ulp(qo["s_v"][i][ok]))
+            assert np.all(np.abs(qg["s_c"][i][ok] - qo["s_c"][i][ok]) <= fp16_ulp(qo["s_c"][i][ok]))
+            if ex.any():
+                Rg = dequant_recon({k: v[i] for k, v in qg.items()})
+                Ro = dequant_recon({k: v[i] for k, v in qo.items()})
+                X = K[i] - mu[i]
+                rel = np.linalg.norm(Rg - Ro) / max(np.linalg.norm(X), 1e-30)
+                worst_rec = max(worst_rec, rel)
+                assert rel <= 0.15, f"reconstruction of an exempt page differs by {rel}"
+    log(f"[{name}] builder: {n_ex}/{n_cols} columns exempt, worst exempt-page recon diff {worst_rec:.3f}")
+    assert n_ex <= 0.02 * n_cols
+
+
+def test_builder_exact_low_rank_pages():
+    """Pages whose keys vary in only 5 coordinates: the GPU's unquantized
+    summary reproduces the keys exactly (up to fp32), and the record's
+    estimate matches the exact page LSE to quantization accuracy."""
+    w = get_workload("tiny-4k")
+    x = generate(w)
+    rng = np.random.default_rng(3)
+    from synth.host import f32_to_bf16_bits
+    nb = w.num_blocks
+    k = np.zeros((nb, 1, 16, 128))
+    for p in range(nb):
+        mu = rng.standard_normal(128)
+        kk = np.tile(mu, (16, 1))
+        coords = rng.choice(128, 5, replace=False)
+        kk[:, coords] += rng.standard_normal((16, 5)) * 2
+        k[p, 0] = kk
+    x.k_cache[0] = f32_to_bf16_bits(k)
+    lay = Layer(x, 0)
+    raw = lay.gpu_build(raw=True)
+    torch.cuda.synchronize()
+    raw = raw.cpu().numpy()
+    K = O.bf16_to_f64(x.k_cache[0][:, 0])
+    mu, V, C = raw[:, 0, :128], raw[:, 0, 128:1152].reshape(-1, 8, 128), raw[:, 0, 1152:].reshape(-1, 16, 8)
+    recon = mu[:, None, :] + C @ V
+    assert np.abs(recon - K).max() <= 2e-4 * np.abs(K).max()
+    assert np.all(np.abs(V[:, 5:]) == 0)
