@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""LOCKS decode-step benchmark on one MI355X.
+
+One step = the whole decode hot path for every layer: page scoring from the
+summaries, GQA-shared top-k selection and split-K sparse attention, replayed
+from one HIP graph.  The default workload is the 1M-token, 32-layer
+Llama-3.1-8B-shaped cache (batch 1, 32 query / 8 KV heads, 2048-token
+budget); the 32K single-layer workload is timed beside it.  Inputs are
+synthetic and resident in HBM before timing starts.
+
+Printed: one JSON line with microseconds per decode step per layer (the
+headline), the scorer's and the attention kernel's achieved HBM bandwidth
+(algorithmic bytes / kernel time, HIP events on the launch stream), the
+dense-attention comparator on the same KV, summary-build throughput and the
+CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LOCKS decode-step µs/layer + achieved HBM GB/s (% of peak), 32K–1M ctx"
+PEAK_HBM_GBS = 8000.0                 # MI355X HBM3E
+SCORE_BYTES_PER_PAGE_HEAD = 832 + 16  # record read + 4 fp32 page LSEs written
+ATTEND_BYTES_PER_PAGE_HEAD = 8192     # 16 tokens x 128 dims x bf16, K and V
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_llama8b-1m_traffic.json")
+SCORE_SRC = os.path.join(ROOT, "kv_cache_page_int4_amd", "csrc", "score.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b-1m")
+    ap.add_argument("--small-workload", default="llama8b-32k")
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-small", action="store_true")
+    ap.add_argument("--no-build", action="store_true", help="skip the summary-build timing")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="also run a plain 1 GiB copy kernel (byte-counter calibration)")
+    ap.add_argument("--kernel-reps", type=int, default=3,
+                    help="rounds of per-layer scorer / attention launches timed in isolation")
+    return ap.parse_args()
+
+
+def timed(fn, reps, warm=1):
+    """Average ms of fn() replayed from a captured graph (device time, not host
+    launch rate), HIP events on the launch stream."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / reps
+
+
+def setup(w, build=True):
+    import torch
+    from kv_cache_page_int4_amd import locks as L
+    from kv_cache_page_int4_amd.step import build_all_layers
+    from synth.device import generate_device
+
+    t0 = time.time()
+    inp = generate_device(w)
+    torch.cuda.synchronize()
+    log(f"[{w.name}] inputs on device in {time.time() - t0:.1f}s "
+        f"(KV {2 * inp.k.numel() * 2 / 2**30:.1f} GiB)")
+    d = L.dims(w.hq, w.hkv)
+    summ = torch.empty((w.layers, w.hkv, w.num_blocks, L.summary_bytes(d)), dtype=torch.uint8,
+                       device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    build_all_layers(d, inp.k, summ)
+    e1.record()
+    torch.cuda.synchronize()
+    build_ms = e0.elapsed_time(e1)
+    log(f"[{w.name}] summaries built: {w.layers * w.num_blocks * w.hkv} page-heads in {build_ms:.1f} ms")
+    return d, inp, summ, build_ms
+
+
+def time_step(step, steps, warmup):
+    import torch
+    step.capture()
+    for _ in range(warmup):
+        step.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(w, inp, summ, budget):
+    """The oracle on one (layer 0, sequence 0, KV head 0) group, scaled to a layer."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    n = w.pages
+    G = w.group
+    blk = inp.block_table[0, :n].cpu().numpy()
+    recs = summ[0, 0].cpu().numpy()[blk]
+    qbits = inp.q[0, 0, :G].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    with threadpool_limits(1):
+        t = time.perf_counter()
+        q = O.bf16_to_f64(qbits)
+        s = O.score_records(q, recs)
+        _, log_m, _ = O.group_mass(s)
+        sel = O.select_top_pages(log_m, budget)
+        t_sel = time.perf_counter() - t
+    kmini = inp.k[0][torch.as_tensor(blk[sel], device="cuda").long(), 0:1]
+    vmini = inp.v[0][torch.as_tensor(blk[sel], device="cuda").long(), 0:1]
+    kb = kmini.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    vb = vmini.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    row = np.full(n + 1, -1, dtype=np.int64)
+    row[sel] = np.arange(len(sel))
+    with threadpool_limits(1):
+        t = time.perf_counter()
+        O.sparse_attention(q, kb, vb, row, 0, sel, n * w.page)
+        t_att = time.perf_counter() - t
+    groups = w.batch * w.hkv
+    per_layer_us = (t_sel + t_att) * groups * 1e6
+    return {"value": per_layer_us, "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "sample": (f"layer 0, sequence 0, KV head 0 of {w.name}: score {n} summary records, "
+                       f"GQA share, top-{budget}, attend {len(sel)} pages; measured "
+                       f"{(t_sel + t_att):.2f} s, scaled x{groups} (sequences x KV heads) to one layer")}
+
+
+def traffic_if_current():
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        sha = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
+        if rec.get("score_hip_sha256") != sha:
+            return None
+        return rec.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported: the LOCKS decode path here runs on a single MI355X.", flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_page_int4_amd import locks as L
+    from kv_cache_page_int4_amd.step import DecodeStep
+    from synth import get_workload
+
+    torch.cuda.set_device(0)
+    w = get_workload(args.workload)
+    if args.layers:
+        w = w.with_(layers=args.layers)
+    d, inp, summ, build_ms = setup(w)
+    budget = w.budget_pages
+
+    step = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, inp.seq_lens, budget)
+    torch.cuda.synchronize()
+    ms_step = time_step(step, args.steps, args.warmup)
+    us_layer = ms_step * 1e3 / w.layers
+    log(f"[{w.name}] decode step {ms_step:.3f} ms = {us_layer:.2f} us/layer")
+
+    # --- dominant kernel: the scorer, timed in isolation on the launch stream ---
+    P = inp.block_table.shape[1]
+    lse_buf = torch.empty((w.batch, w.hq, P), dtype=torch.float32, device="cuda")
+
+    def score_all_layers():
+        for layer in range(w.layers):
+            L.score_pages(d, inp.q[layer], summ[layer], w.num_blocks, inp.block_table,
+                          inp.seq_lens, lse_buf, step.ws_score)
+
+    score_ms = timed(score_all_layers, args.kernel_reps) / w.layers
+    page_heads = w.batch * w.hkv * w.pages
+    score_gbs = page_heads * SCORE_BYTES_PER_PAGE_HEAD / (score_ms * 1e-3) / 1e9
+
+    def attend_all_layers():
+        for layer in range(w.layers):
+            L.sparse_attend(d, inp.q[layer], inp.k[layer], inp.v[layer], inp.block_table,
+                            inp.seq_lens, step.sel[layer], step.cnt[layer], budget,
+                            step.out[layer], step.ws_att)
+
+    attend_ms = timed(attend_all_layers, args.kernel_reps) / w.layers
+    att_units = int(step.cnt.sum().item()) / w.layers
+    attend_gbs = att_units * ATTEND_BYTES_PER_PAGE_HEAD / (attend_ms * 1e-3) / 1e9
+    log(f"[{w.name}] scorer {score_ms * 1e3:.2f} us/launch = {score_gbs:.0f} GB/s; "
+        f"attention {attend_ms * 1e3:.2f} us/launch = {attend_gbs:.0f} GB/s")
+
+    extra = {}
+    if not args.no_dense:
+        dense = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, inp.seq_lens, 1,
+                           dense=True)
+        dense_ms = time_step(dense, max(2, args.steps // 5), 1)
+        extra["dense_us_per_layer"] = dense_ms * 1e3 / w.layers
+        extra["speedup_vs_dense"] = dense_ms / ms_step
+        dense_bytes = w.batch * w.hkv * w.pages * ATTEND_BYTES_PER_PAGE_HEAD
+        extra["dense_attention_gbs"] = dense_bytes / (dense_ms * 1e-3 / w.layers) / 1e9
+        locks_bytes = page_heads * 832 + att_units * ATTEND_BYTES_PER_PAGE_HEAD
+        extra["kv_bytes_ratio_dense_over_locks"] = dense_bytes / locks_bytes
+        log(f"[{w.name}] dense {extra['dense_us_per_layer']:.2f} us/layer, "
+            f"speedup {extra['speedup_vs_dense']:.2f}x")
+        del dense
+
+    # achievable streaming-read bandwidth (context for the roofline)
+    from synth.device import device_read
+    rbuf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(4 * 8192, dtype=torch.int32, device="cuda")
+    read_ms = timed(lambda: device_read(rbuf, sink), 5)
+    stream_read_gbs = rbuf.numel() / (read_ms * 1e-3) / 1e9
+    del rbuf, sink
+    log(f"streaming read of 2 GiB: {stream_read_gbs:.0f} GB/s")
+
+    if args.copy_calibrate:
+        from synth.device import device_copy
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        device_copy(dst, src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp, summ, budget)
+        log(f"[{w.name}] oracle {cpu['value']:.0f} us/layer on {cpu['cores']} core")
+
+    also = {}
+    if not args.no_small and args.small_workload:
+        del step
+        ws = get_workload(args.small_workload)
+        d2, inp2, summ2, _ = setup(ws)
+        st2 = DecodeStep(d2, inp2.k, inp2.v, summ2, inp2.q, inp2.block_table, inp2.seq_lens,
+                         ws.budget_pages)
+        ms2 = time_step(st2, max(args.steps, 50), args.warmup)
+        also[ws.name] = {"us_per_layer": ms2 * 1e3 / ws.layers,
+                         "note": "working set fits the 256 MB Infinity Cache; latency-bound"}
+        log(f"[{ws.name}] decode step {ms2 * 1e3:.2f} us/layer")
+
+    result = {
+        "metric": METRIC,
+        "value": round(us_layer, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "batch": w.batch, "ctx": w.ctx,
+                   "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d, "page": w.page,
+                   "rank": w.rank, "budget_tokens": w.budget_tokens,
+                   "carriers_per_kv_head": w.carriers, "graph": "one hipGraph per step"},
+        "roofline": {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(score_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_if_current(), "kernel": "score_kernel",
+                     "kernel_us": round(score_ms * 1e3, 3),
+                     "bytes_per_launch": page_heads * SCORE_BYTES_PER_PAGE_HEAD},
+        "attention": {"achieved": round(attend_gbs, 1), "unit": "GB/s",
+                      "frac": round(attend_gbs / PEAK_HBM_GBS, 4),
+                      "kernel_us": round(attend_ms * 1e3, 3)},
+        "stream_read_gbs": round(stream_read_gbs, 1),
+        "pages_scored_per_s": page_heads / (score_ms * 1e-3),
+        "build_page_heads_per_s": w.layers * w.num_blocks * w.hkv / (build_ms * 1e-3),
+        "cpu_baseline": cpu,
+    }
+    result.update(extra)
+    if also:
+        result["also"] = also
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -69,7 +69,8 @@ typedef struct {
 size_t locks_summary_bytes(const locks_dims* dims);
 
 /* Workspace sizes (bytes).  max_pages is the block-table row length; the
- * budget is in pages. */
+ * budget is in pages.  Workspace contents need no initialization; a
+ * workspace must not be shared by calls that may run concurrently. */
 size_t locks_score_workspace_bytes(const locks_dims* dims, int32_t batch,
                                    int32_t max_pages, int32_t budget_pages);
 size_t locks_attend_workspace_bytes(const locks_dims* dims, int32_t batch,

@@ -49,7 +49,7 @@ constexpr int kRowHalfMirror = 0x141;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // Value of lane (4*(lane/4) + H) within each quad.

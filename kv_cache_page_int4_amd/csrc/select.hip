@@ -8,11 +8,11 @@
 // and the k = min(budget, valid pages) largest m_j are kept, ties to the lower
 // page index, listed in ascending page order.
 //
-// Two stages.  Stage 1: one workgroup per 2048-page chunk turns scores into
-// order-preserving 32-bit keys in LDS and radix-selects the chunk's top
-// min(k, 2048) (8-bit digits, LDS histograms); survivors are written in page
-// order.  Stage 2: one workgroup per (sequence, KV head) radix-selects the
-// global top k over the candidates.  Because each chunk emits its survivors
+// Two kernels.  Stage 1: one workgroup per 2048-page chunk turns scores into
+// order-preserving 32-bit keys and radix-selects the chunk's top min(k, 2048)
+// (8-bit digits, LDS histograms); survivors are written in page order.
+// Stage 2: one workgroup per (sequence, KV head) radix-selects the global top
+// k over all candidates, staged in LDS when they fit.  Because each chunk emits its survivors
 // in page order and chunks are in page order, stream compaction of the
 // winners yields ascending page ids directly, and "lowest index among equal
 // keys" is "first in candidate order".
@@ -23,9 +23,8 @@ namespace locks {
 
 namespace {
 
-constexpr int kSelThreads = 256;
-constexpr int kPerThread = kSelChunk / kSelThreads;  // 8
-constexpr int kMergeThreads = 1024;
+constexpr int kSelThreads = 1024;   // 16 waves: 4 per SIMD hide the latency chains
+constexpr int kPerThread = kSelChunk / kSelThreads;  // 2
 
 // Inclusive prefix sum over a workgroup (blockDim.x <= 1024), returns the
 // exclusive prefix and the total through `total`.
@@ -56,6 +55,31 @@ __device__ int block_exclusive_scan(int v, int* total, int* smem /* >= NT/64 + 1
   return excl;
 }
 
+// Block-wide min and max (result in every thread); smem >= NT/64 + 1 ints.
+template <int NT>
+__device__ void block_minmax(uint32_t& mn, uint32_t& mx, int* smem) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  }
+  __shared__ uint32_t red[2][NT / 64];
+  if (lane == 0) {
+    red[0][wave] = mn;
+    red[1][wave] = mx;
+  }
+  __syncthreads();
+  mn = red[0][0];
+  mx = red[1][0];
+  for (int w = 1; w < NT / 64; ++w) {
+    mn = min(mn, red[0][w]);
+    mx = max(mx, red[1][w]);
+  }
+  __syncthreads();
+  (void)smem;
+}
+
 // Find the digit bucket holding the rem-th largest key among those counted in
 // hist[256] (called by one full wave).  Exactly one lane finds it and stores
 // the digit and the rank left inside that bucket.
@@ -82,6 +106,57 @@ __device__ void pick_digit(const int* hist, int rem, int* sh_digit, int* sh_rem)
     }
     above += c[e];
   }
+}
+
+// Threshold T of the k-th largest key and the number `rem` of keys equal to T
+// that belong to the top k.  The radix passes cover only the bits in which
+// the keys differ (from the block-wide min and max of the valid keys), eight
+// at a time from the top, so the first digit already spreads the keys over
+// the histogram; a wave whose keys all share one digit adds it with a single
+// atomic.  Histograms are double-buffered so a pass needs two barriers.
+// for_each(f) calls f(key, valid) for each of this thread's slots, the same
+// number of times in every thread.  hist: [2][256]; sh: [2][2].
+template <int NT, typename ForEach>
+__device__ void radix_threshold(ForEach for_each, int k, uint32_t kmin, uint32_t kmax,
+                                int (*hist)[256], int (*sh)[2], uint32_t* T_out, int* rem_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t diff = kmin ^ kmax;
+  if (diff == 0u) {           // every valid key is equal
+    *T_out = kmin;
+    *rem_out = k;
+    return;
+  }
+  const int hb = 31 - __clz(diff);
+  uint32_t pmask = (hb == 31) ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = kmin & pmask;
+  int rem = k;
+  for (int i = tid; i < 512; i += NT) hist[i >> 8][i & 255] = 0;
+  __syncthreads();
+  int buf = 0;
+  for (int hi = hb; hi >= 0; hi -= 8) {
+    const int lo = hi >= 7 ? hi - 7 : 0;
+    const uint32_t dmask = (2u << (hi - lo)) - 1u;
+    for_each([&](uint32_t key, bool valid) {
+      const bool in = valid && (key & pmask) == prefix;
+      const int dg = in ? (int)((key >> lo) & dmask) : -1;
+      const int d0 = __builtin_amdgcn_readfirstlane(dg);
+      if (__all(dg == d0)) {
+        if (lane == 0 && d0 >= 0) atomicAdd(&hist[buf][d0], 64);
+      } else if (in) {
+        atomicAdd(&hist[buf][dg], 1);
+      }
+    });
+    __syncthreads();
+    if (wave == 0) pick_digit(hist[buf], rem, &sh[buf][0], &sh[buf][1]);
+    for (int i = tid; i < 256; i += NT) hist[buf ^ 1][i] = 0;   // next pass's buffer
+    __syncthreads();
+    prefix |= (uint32_t)sh[buf][0] << lo;
+    pmask |= dmask << lo;
+    rem = sh[buf][1];
+    buf ^= 1;
+  }
+  *T_out = prefix;
+  *rem_out = rem;
 }
 
 __global__ __launch_bounds__(kSelThreads) void lse_partials_kernel(
@@ -122,6 +197,161 @@ struct SelParams {
   int32_t max_pages, hq, hkv, budget, n_partials, n_chunks, slots;
 };
 
+// Stage 2 over candidates held in registers: thread t owns the contiguous
+// run [t*per, t*per + per) of the page-ordered candidate list (per <= RUN), so
+// runs are in page order and the ordered compaction is one exclusive scan.
+template <int RUN>
+__global__ __launch_bounds__(kSelThreads) void select_merge_kernel(SelParams p) {
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  __shared__ int hist[2][256];
+  __shared__ int sh[2][2];
+  __shared__ int scan_smem[kSelThreads / 64 + 1];
+  const int n_cand = p.n_chunks * p.slots;
+  const size_t gbase = ((size_t)b * p.hkv + kvh) * (size_t)n_cand;
+  const uint32_t* gk = p.cand_key + gbase;
+  const int32_t* gi = p.cand_idx + gbase;
+  const int per = (n_cand + kSelThreads - 1) / kSelThreads;
+  const int c0 = tid * per;
+  uint32_t key[RUN];
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) {
+    const int c = c0 + i;
+    key[i] = (i < per && c < n_cand) ? gk[c] : 0u;
+  }
+  int nv = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < RUN; ++i)
+    if (key[i] != 0u) {
+      ++nv;
+      kmin = min(kmin, key[i]);
+      kmax = max(kmax, key[i]);
+    }
+  int total_valid;
+  (void)block_exclusive_scan<kSelThreads>(nv, &total_valid, scan_smem);
+  block_minmax<kSelThreads>(kmin, kmax, scan_smem);
+  const int k = min(p.budget, total_valid);
+  const bool all = (k >= total_valid);
+  uint32_t T = 0u;
+  int rem = k;
+  if (k > 0 && !all)
+    radix_threshold<kSelThreads>(
+        [&](auto f) {
+#pragma unroll
+          for (int i = 0; i < RUN; ++i) f(key[i], key[i] != 0u);
+        },
+        k, kmin, kmax, hist, sh, &T, &rem);
+  int neq = 0;
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) neq += (!all && key[i] != 0u && key[i] == T);
+  int tot_eq;
+  const int eq_before = block_exclusive_scan<kSelThreads>(neq, &tot_eq, scan_smem);
+  uint32_t take = 0u;   // bit i: slot i is a winner
+  int ntake = 0;
+  {
+    int eqr = eq_before;
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) {
+      bool tk = false;
+      if (key[i] != 0u && k > 0) {
+        if (all || key[i] > T) tk = true;
+        else if (key[i] == T) tk = (eqr++ < rem);
+      }
+      take |= (tk ? 1u : 0u) << i;
+      ntake += tk;
+    }
+  }
+  int tot_take;
+  int pos = block_exclusive_scan<kSelThreads>(ntake, &tot_take, scan_smem);
+  int32_t* out = p.sel + ((size_t)b * p.hkv + kvh) * p.budget;
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) {
+    if ((take >> i) & 1u) {
+      if (pos < p.budget) out[pos] = gi[c0 + i];
+      ++pos;
+    }
+  }
+  const int written = min(tot_take, p.budget);
+  for (int s2 = written + tid; s2 < p.budget; s2 += kSelThreads) out[s2] = -1;
+  if (tid == 0) p.sel_count[(size_t)b * p.hkv + kvh] = written;
+}
+
+// Stage 2 for candidate lists longer than kSelThreads * 32: the same steps with the
+// candidates re-read from memory in every pass (correct, slower).
+__global__ __launch_bounds__(kSelThreads) void select_merge_big_kernel(SelParams p) {
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  __shared__ int hist[2][256];
+  __shared__ int sh[2][2];
+  __shared__ int scan_smem[kSelThreads / 64 + 1];
+  const int n_cand = p.n_chunks * p.slots;
+  const size_t gbase = ((size_t)b * p.hkv + kvh) * (size_t)n_cand;
+  const uint32_t* gk = p.cand_key + gbase;
+  const int32_t* gi = p.cand_idx + gbase;
+  const int per = (n_cand + kSelThreads - 1) / kSelThreads;
+  const int c0 = min(n_cand, tid * per), c1 = min(n_cand, c0 + per);
+  int nv = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int c = c0; c < c1; ++c) {
+    const uint32_t kk = gk[c];
+    if (kk != 0u) {
+      ++nv;
+      kmin = min(kmin, kk);
+      kmax = max(kmax, kk);
+    }
+  }
+  int total_valid;
+  (void)block_exclusive_scan<kSelThreads>(nv, &total_valid, scan_smem);
+  block_minmax<kSelThreads>(kmin, kmax, scan_smem);
+  const int k = min(p.budget, total_valid);
+  const bool all = (k >= total_valid);
+  uint32_t T = 0u;
+  int rem = k;
+  if (k > 0 && !all)
+    radix_threshold<kSelThreads>(
+        [&](auto f) {
+          for (int i = 0; i < per; ++i) {
+            const int c = c0 + i;
+            const uint32_t kk = (c < c1) ? gk[c] : 0u;
+            f(kk, kk != 0u);
+          }
+        },
+        k, kmin, kmax, hist, sh, &T, &rem);
+  int neq = 0;
+  for (int c = c0; c < c1; ++c) {
+    const uint32_t kk = gk[c];
+    neq += (!all && kk != 0u && kk == T);
+  }
+  int tot_eq;
+  const int eq_before = block_exclusive_scan<kSelThreads>(neq, &tot_eq, scan_smem);
+  auto winner = [&](uint32_t kk, int& eqr) -> bool {
+    if (kk == 0u || k == 0) return false;
+    if (all || kk > T) return true;
+    if (kk == T) return eqr++ < rem;
+    return false;
+  };
+  int ntake = 0;
+  {
+    int eqr = eq_before;
+    for (int c = c0; c < c1; ++c) ntake += winner(gk[c], eqr);
+  }
+  int tot_take;
+  int pos = block_exclusive_scan<kSelThreads>(ntake, &tot_take, scan_smem);
+  int32_t* out = p.sel + ((size_t)b * p.hkv + kvh) * p.budget;
+  {
+    int eqr = eq_before;
+    for (int c = c0; c < c1; ++c)
+      if (winner(gk[c], eqr)) {
+        if (pos < p.budget) out[pos] = gi[c];
+        ++pos;
+      }
+  }
+  const int written = min(tot_take, p.budget);
+  for (int s2 = written + tid; s2 < p.budget; s2 += kSelThreads) out[s2] = -1;
+  if (tid == 0) p.sel_count[(size_t)b * p.hkv + kvh] = written;
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) {
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -129,15 +359,25 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
   const int n_fin = seq / kB;
 
   __shared__ float L2[kG];
-  __shared__ int hist[256];
+  __shared__ int hist[2][256];
+  __shared__ int sh[2][2];
   __shared__ int scan_smem[kSelThreads / 64 + 1];
-  __shared__ int sh_digit, sh_rem;
 
   // per-head normalizer from the scoring partials (wave w -> head w)
-  {
+  if (wave < kG) {
     const float2* pp = p.partials + ((size_t)b * p.hq + kvh * kG + wave) * p.n_partials;
     float m = -INFINITY, s = 0.f;
-    for (int c = lane; c < p.n_partials; c += 64) lse2_merge(m, s, pp[c].x, pp[c].y);
+    // independent loads, 8 in flight per lane, then merge
+    for (int c0 = lane; c0 < p.n_partials; c0 += 8 * 64) {
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + 64 * u;
+        v[u] = (c < p.n_partials) ? pp[c] : make_float2(-INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) lse2_merge(m, s, v[u].x, v[u].y);
+    }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
@@ -152,22 +392,27 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
   uint32_t key[kPerThread];
   int nvalid = 0;
   {
+    // all 4 x 8 scores are loaded (clamped in-bounds index) before any use
+    float sv[kG][kPerThread];
+    const int jmax = max(n_fin - 1, 0);
+#pragma unroll
+    for (int hh = 0; hh < kG; ++hh) {
+      const float* s = p.page_lse + ((size_t)b * p.hq + kvh * kG + hh) * p.max_pages;
+#pragma unroll
+      for (int t = 0; t < kPerThread; ++t) sv[hh][t] = s[min(jbase + t, jmax)];
+    }
     float lm[kPerThread];
 #pragma unroll
     for (int t = 0; t < kPerThread; ++t) lm[t] = -INFINITY;
 #pragma unroll
     for (int hh = 0; hh < kG; ++hh) {
-      const float* s = p.page_lse + ((size_t)b * p.hq + kvh * kG + hh) * p.max_pages;
       const float l2 = L2[hh];
 #pragma unroll
       for (int t = 0; t < kPerThread; ++t) {
-        const int j = jbase + t;
-        if (j < n_fin) {
-          const float a = s[j] * kLog2e - l2;
-          // log2(2^lm + 2^a) without overflow
-          const float hi = fmaxf(lm[t], a), lo = fminf(lm[t], a);
-          lm[t] = (hi == -INFINITY) ? -INFINITY : hi + fast_log2(1.f + fast_exp2(lo - hi));
-        }
+        const float a = sv[hh][t] * kLog2e - l2;
+        // log2(2^lm + 2^a) without overflow
+        const float hi = fmaxf(lm[t], a), lo = fminf(lm[t], a);
+        lm[t] = (hi == -INFINITY) ? -INFINITY : hi + fast_log2(1.f + fast_exp2(lo - hi));
       }
     }
 #pragma unroll
@@ -182,26 +427,25 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
   const int kc = min(p.budget, total_valid);
 
   // radix select of the kc-th largest key
-  uint32_t prefix = 0, pmask = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int t = 0; t < kPerThread; ++t)
+    if (key[t] != 0u) {
+      kmin = min(kmin, key[t]);
+      kmax = max(kmax, key[t]);
+    }
+  block_minmax<kSelThreads>(kmin, kmax, scan_smem);
+  uint32_t T = 0u;
   int rem = kc;
   if (kc > 0 && kc < total_valid) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
-      __syncthreads();
+    radix_threshold<kSelThreads>(
+        [&](auto f) {
 #pragma unroll
-      for (int t = 0; t < kPerThread; ++t)
-        if (key[t] != 0u && (key[t] & pmask) == prefix) atomicAdd(&hist[(key[t] >> shift) & 255], 1);
-      __syncthreads();
-      if (wave == 0) pick_digit(hist, rem, &sh_digit, &sh_rem);
-      __syncthreads();
-      prefix |= (uint32_t)sh_digit << shift;
-      pmask |= 0xFFu << shift;
-      rem = sh_rem;
-      __syncthreads();
-    }
+          for (int t = 0; t < kPerThread; ++t) f(key[t], key[t] != 0u);
+        },
+        kc, kmin, kmax, hist, sh, &T, &rem);
   }
   // winners: key > T, or key == T among the first `rem` in page order
-  const uint32_t T = prefix;
   const bool all = (kc >= total_valid);
   int neq = 0;
 #pragma unroll
@@ -223,7 +467,8 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
   }
   int tot_take;
   int pos = block_exclusive_scan<kSelThreads>(ntake, &tot_take, scan_smem);
-  const size_t cbase = (((size_t)b * p.hkv + kvh) * p.n_chunks + chunk) * p.slots;
+  const size_t gbase = ((size_t)b * p.hkv + kvh) * (size_t)p.n_chunks * p.slots;
+  const size_t cbase = gbase + (size_t)chunk * p.slots;
 #pragma unroll
   for (int t = 0; t < kPerThread; ++t) {
     if (take[t]) {
@@ -236,71 +481,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
     p.cand_key[cbase + s] = 0u;
     p.cand_idx[cbase + s] = -1;
   }
-}
 
-__global__ __launch_bounds__(kMergeThreads) void select_merge_kernel(SelParams p) {
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_cand = p.n_chunks * p.slots;
-  const size_t cbase = ((size_t)b * p.hkv + kvh) * (size_t)n_cand;
-  const uint32_t* ck = p.cand_key + cbase;
-  const int32_t* ci = p.cand_idx + cbase;
-
-  __shared__ int hist[256];
-  __shared__ int scan_smem[kMergeThreads / 64 + 1];
-  __shared__ int sh_digit, sh_rem;
-
-  int nv = 0;
-  for (int c = tid; c < n_cand; c += kMergeThreads) nv += (ck[c] != 0u);
-  int total_valid;
-  (void)block_exclusive_scan<kMergeThreads>(nv, &total_valid, scan_smem);
-  const int k = min(p.budget, total_valid);
-
-  uint32_t prefix = 0, pmask = 0;
-  int rem = k;
-  const bool all = (k >= total_valid);
-  if (k > 0 && !all) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      for (int c = tid; c < n_cand; c += kMergeThreads) {
-        const uint32_t kk = ck[c];
-        if (kk != 0u && (kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & 255], 1);
-      }
-      __syncthreads();
-      if (wave == 0) pick_digit(hist, rem, &sh_digit, &sh_rem);
-      __syncthreads();
-      prefix |= (uint32_t)sh_digit << shift;
-      pmask |= 0xFFu << shift;
-      rem = sh_rem;
-      __syncthreads();
-    }
-  }
-  const uint32_t T = prefix;
-  int32_t* out = p.sel + ((size_t)b * p.hkv + kvh) * p.budget;
-  // ordered compaction, one tile of kMergeThreads candidates at a time
-  int written = 0, eq_seen = 0;
-  for (int base = 0; base < n_cand; base += kMergeThreads) {
-    const int c = base + tid;
-    const uint32_t kk = (c < n_cand) ? ck[c] : 0u;
-    const bool is_eq = (!all && kk != 0u && kk == T);
-    int tot_eq;
-    const int eq_rank = eq_seen + block_exclusive_scan<kMergeThreads>(is_eq ? 1 : 0, &tot_eq, scan_smem);
-    bool tk = false;
-    if (kk != 0u) {
-      if (all) tk = true;
-      else if (kk > T) tk = true;
-      else if (is_eq) tk = eq_rank < rem;
-    }
-    if (k == 0) tk = false;
-    int tot_take;
-    const int pos = written + block_exclusive_scan<kMergeThreads>(tk ? 1 : 0, &tot_take, scan_smem);
-    if (tk && pos < p.budget) out[pos] = ci[c];
-    written += tot_take;
-    eq_seen += tot_eq;
-  }
-  for (int s = min(written, p.budget) + tid; s < p.budget; s += kMergeThreads) out[s] = -1;
-  if (tid == 0) p.sel_count[(size_t)b * p.hkv + kvh] = min(written, p.budget);
 }
 
 }  // namespace
@@ -332,7 +513,13 @@ hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_merge_kernel, dim3(hkv, batch), dim3(kMergeThreads), 0, stream, p);
+  const int per = (plan.n_chunks * plan.slots + kSelThreads - 1) / kSelThreads;
+  if (per <= 8)
+    hipLaunchKernelGGL(select_merge_kernel<8>, dim3(hkv, batch), dim3(kSelThreads), 0, stream, p);
+  else if (per <= 32)
+    hipLaunchKernelGGL(select_merge_kernel<32>, dim3(hkv, batch), dim3(kSelThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(select_merge_big_kernel, dim3(hkv, batch), dim3(kSelThreads), 0, stream, p);
   return hipGetLastError();
 }
 

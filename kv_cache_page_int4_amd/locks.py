@@ -122,6 +122,12 @@ def attend_workspace_bytes(d: Dims, batch, max_attended_pages) -> int:
     return lib().locks_attend_workspace_bytes(ctypes.byref(d), batch, max_attended_pages)
 
 
+def attend_workspace(d: Dims, batch, max_attended_pages, device="cuda") -> torch.Tensor:
+    """An attend workspace of the required size."""
+    return torch.empty(attend_workspace_bytes(d, batch, max_attended_pages), dtype=torch.uint8,
+                       device=device)
+
+
 def build_summaries(d: Dims, k_cache, block_ids, summaries, raw_debug=None, stream=None):
     """k_cache: bf16 [num_blocks, Hkv, 16, 128] (one layer); block_ids: int32
     [n]; summaries: uint8 [Hkv, num_blocks, 832]; raw_debug: fp32 [n, Hkv, 1280]."""

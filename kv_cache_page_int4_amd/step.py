@@ -1,0 +1,84 @@
+"""A whole LOCKS decode step over all layers, captured in one HIP graph.
+
+The decode step (technical summary sec. 2, implementation paragraph: scoring,
+selection and sparse attention run inside one full graph with no Python
+dispatch) is, per layer, locks_score_select followed by locks_sparse_attend.
+This module only allocates the per-layer outputs and the workspaces, issues
+the library calls in order on the current stream and records them into a
+torch.cuda.CUDAGraph (a hipGraph on ROCm).  Layers run in sequence because in
+a model layer l+1's query depends on layer l's output.
+"""
+
+import torch
+
+from . import locks as L
+
+
+class DecodeStep:
+    """k, v: bf16 [layers, blocks, hkv, 16, 128]; summaries: uint8
+    [layers, hkv, blocks, 832]; q: bf16 [layers, batch, hq, 128];
+    block_table: int32 [batch, max_pages]; seq_lens: int32 [batch].
+    dense=True attends every finalized page instead (no scoring/selection)."""
+
+    def __init__(self, d, k, v, summaries, q, block_table, seq_lens, budget_pages, dense=False):
+        self.d, self.k, self.v, self.summ, self.q = d, k, v, summaries, q
+        self.bt, self.seq, self.budget, self.dense = block_table, seq_lens, budget_pages, dense
+        n_layers, batch = q.shape[0], q.shape[1]
+        P = block_table.shape[1]
+        dev = q.device
+        self.layers = n_layers
+        self.num_blocks = k.shape[1]
+        self.sel = torch.full((n_layers, batch, d.num_kv_heads, budget_pages), -1,
+                              dtype=torch.int32, device=dev)
+        self.cnt = torch.zeros((n_layers, batch, d.num_kv_heads), dtype=torch.int32, device=dev)
+        self.out = torch.zeros((n_layers, batch, d.num_q_heads, d.head_dim), dtype=torch.bfloat16,
+                               device=dev)
+        self.out_lse = torch.zeros((n_layers, batch, d.num_q_heads), dtype=torch.float32, device=dev)
+        self.ws_score = torch.empty(max(1, L.score_workspace_bytes(d, batch, P, budget_pages)),
+                                    dtype=torch.uint8, device=dev)
+        n_att = (P if dense else budget_pages) + 1
+        self.ws_att = L.attend_workspace(d, batch, n_att, device=dev)
+        self.graph = None
+
+    def run_layer(self, layer, stream=None):
+        d = self.d
+        if not self.dense:
+            L.score_select(d, self.q[layer], self.summ[layer], self.num_blocks, self.bt, self.seq,
+                           self.budget, self.sel[layer], self.cnt[layer], self.ws_score,
+                           stream=stream)
+        L.sparse_attend(d, self.q[layer], self.k[layer], self.v[layer], self.bt, self.seq,
+                        None if self.dense else self.sel[layer],
+                        None if self.dense else self.cnt[layer], self.budget, self.out[layer],
+                        self.ws_att, out_lse=self.out_lse[layer], stream=stream)
+
+    def run(self):
+        for layer in range(self.layers):
+            self.run_layer(layer)
+
+    def capture(self):
+        """Record one full step into a graph (after one eager warm-up run)."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.run()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()
+
+
+def build_all_layers(d, k, summaries, n_fin_blocks=None):
+    """Summarize every block of every layer (prefill finalization)."""
+    n_layers, nb = k.shape[0], k.shape[1]
+    blocks = torch.arange(nb, dtype=torch.int32, device=k.device)
+    if n_fin_blocks is not None:
+        blocks = n_fin_blocks
+    for layer in range(n_layers):
+        L.build_summaries(d, k[layer], blocks, summaries[layer])

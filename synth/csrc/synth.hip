@@ -117,19 +117,6 @@ __global__ __launch_bounds__(64) void fill_pages_kernel(
     u0[k] = g0 * inv;
     u1[k] = g1 * inv;
   }
-  // coefficients a_ik (same draws in every lane)
-  float a[16][8];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float z[8];
-    nrm4(kCoef, 2u * i, z);
-    nrm4(kCoef, 2u * i + 1u, z + 4);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float sd = coef_inv_k ? rsqrtf((float)(k + 1)) : 1.f / (float)(k + 1);
-      a[i][k] = z[k] * sd;
-    }
-  }
   uint16_t* kp = kc + (size_t)blk * bs + (size_t)kvh * hs + d0;
   uint16_t* vp = vc + (size_t)blk * bs + (size_t)kvh * hs + d0;
 #pragma unroll
@@ -137,11 +124,16 @@ __global__ __launch_bounds__(64) void fill_pages_kernel(
     float n0, n1, w0, w1;
     pick2(kNoise, 32u * i, n0, n1);
     pick2(kValue, 32u * i, w0, w1);
+    // coefficients a_ik of token i (the same draws in every lane)
+    float z[8];
+    nrm4(kCoef, 2u * i, z);
+    nrm4(kCoef, 2u * i + 1u, z + 4);
     float k0 = cen0 + n0 * noise_sd, k1 = cen1 + n1 * noise_sd;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      k0 = fmaf(a[i][k], u0[k], k0);
-      k1 = fmaf(a[i][k], u1[k], k1);
+      const float sd = coef_inv_k ? rsqrtf((float)(k + 1)) : 1.f / (float)(k + 1);
+      k0 = fmaf(z[k] * sd, u0[k], k0);
+      k1 = fmaf(z[k] * sd, u1[k], k1);
     }
     const bool ok = i < valid;
     const uint32_t kw = ok ? ((uint32_t)to_bf16(k0) | ((uint32_t)to_bf16(k1) << 16)) : 0u;
@@ -180,9 +172,29 @@ __global__ void copy_kernel(uint4* __restrict__ dst, const uint4* __restrict__ s
     dst[i] = src[i];
 }
 
+// Plain streaming read (16-byte words) reduced to one word per workgroup:
+// the achievable HBM read bandwidth of this device.
+__global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                   uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint4 v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  for (int o = 1; o < 64; o <<= 1) acc ^= __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+int synth_read(const void* src, int64_t bytes, void* sink, int32_t blocks, void* stream) {
+  hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const uint4*)src, bytes / 16, (uint32_t*)sink);
+  return (int)hipGetLastError();
+}
 
 int synth_fill_q(void* q, int64_t n, uint32_t seed, uint32_t layer, void* stream) {
   const int64_t n4 = (n + 3) / 4;

@@ -32,7 +32,9 @@ def lib():
         h.synth_fill_pages.argtypes = [P, P, I64, I64, I64, P, P, I32, I32, I32, U32, U32, F, I32, P]
         h.synth_plant_carriers.argtypes = [P, I64, I64, I64, P, I32, P, I32, P, I32, U32, U32, F, P]
         h.synth_copy.argtypes = [P, P, I64, P]
-        for f in (h.synth_fill_q, h.synth_fill_pages, h.synth_plant_carriers, h.synth_copy):
+        h.synth_read.argtypes = [P, I64, P, I32, P]
+        for f in (h.synth_fill_q, h.synth_fill_pages, h.synth_plant_carriers, h.synth_copy,
+                  h.synth_read):
             f.restype = I32
         _lib = h
     return _lib
@@ -103,4 +105,11 @@ def device_copy(dst: torch.Tensor, src: torch.Tensor):
     """Plain streaming copy of src into dst (same byte size)."""
     n = src.numel() * src.element_size()
     st = lib().synth_copy(_p(dst), _p(src), n, _s())
+    assert st == 0, st
+
+
+def device_read(src: torch.Tensor, sink: torch.Tensor, blocks: int = 8192):
+    """Plain streaming read of src (reduced into sink, >= 4*blocks uint32)."""
+    n = src.numel() * src.element_size()
+    st = lib().synth_read(_p(src), n, _p(sink), blocks, _s())
     assert st == 0, st

@@ -93,8 +93,7 @@ class Layer:
         out = torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda")
         olse = torch.empty((w.batch, w.hq), dtype=torch.float32, device="cuda")
         n_att = (self.bt.shape[1] if dense else budget) + 1
-        ws = torch.empty(L.attend_workspace_bytes(self.d, w.batch, n_att), dtype=torch.uint8,
-                         device="cuda")
+        ws = L.attend_workspace(self.d, w.batch, n_att)
         L.sparse_attend(self.d, self.q, self.k, self.v, self.bt, self.seq,
                         None if dense else sel, None if dense else cnt, budget, out, ws,
                         out_lse=olse)

@@ -262,3 +262,48 @@ def test_builder_exact_low_rank_pages():
     recon = mu[:, None, :] + C @ V
     assert np.abs(recon - K).max() <= 2e-4 * np.abs(K).max()
     assert np.all(np.abs(V[:, 5:]) == 0)
+
+
+# ---------------------------------------------------------------------------
+# exact ties: selection must keep the lowest page indices
+# ---------------------------------------------------------------------------
+
+def test_zero_query_all_ties_select_first_pages():
+    x = gen("llama8b-32k")
+    lay = Layer(x, 0)
+    lay.upload_oracle_records()
+    lay.q.zero_()
+    sel, cnt, lse = lay.score_select(128)
+    torch.cuda.synchronize()
+    n = x.w.pages
+    assert torch.allclose(lse[0, :, :n], torch.full_like(lse[0, :, :n], float(np.log(16.0))), atol=1e-6)
+    for g in range(x.w.hkv):
+        assert int(cnt[0, g]) == 128
+        assert torch.equal(sel[0, g].cpu(), torch.arange(128, dtype=torch.int32))
+
+
+def test_repeated_pages_exact_ties():
+    """Pages repeat with period 7, so scores tie exactly in groups; the GPU must
+    pick exactly the oracle's pages (lowest index among equal masses)."""
+    x = gen("tiny-4k")
+    x2 = generate(x.w)
+    blk = x2.block_table[0]
+    for j in range(x.w.pages):
+        x2.k_cache[0][blk[j]] = x2.k_cache[0][blk[j % 7]]
+    lay = Layer(x2, 0)
+    lay.upload_oracle_records()
+    for budget in (1, 5, 32, 100):
+        sel, cnt, lse = lay.score_select(budget)
+        torch.cuda.synchronize()
+        s_gpu = scores_of(x2, 0, 0, 0, lse)
+        _, log_m, _ = O.group_mass(s_gpu)
+        want = O.select_top_pages(log_m, budget)
+        got = sel[0, 0, :int(cnt[0, 0])].cpu().numpy()
+        assert list(got) == list(want), (budget, got[:10], want[:10])
+
+
+@pytest.mark.parametrize("ctx,budget", [(16 * 8192, 600), (16 * 12000 + 7, 2000)])
+def test_long_candidate_lists(ctx, budget):
+    """Selection merge paths with ~10 and >32 candidates per thread."""
+    x = gen("tiny-4k", ctx=ctx, carriers=8)
+    run_and_check(x, budget=budget, gpu_records=True)
