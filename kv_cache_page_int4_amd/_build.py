@@ -13,6 +13,8 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     # never emit packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep matrix-core accumulators in VGPRs (no AGPR round trips)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-result",
 ]
 

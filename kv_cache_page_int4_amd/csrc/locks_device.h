@@ -46,6 +46,8 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 constexpr int qp(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
 constexpr int kRowMirror = 0x140;
 constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowRor4 = 0x124;   // rotate the 16 lanes of each row by 4
+constexpr int kRowRor8 = 0x128;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {

@@ -8,10 +8,9 @@
 namespace locks {
 
 // ---- scoring ---------------------------------------------------------------
+constexpr int32_t kScoreSteps = 4;     // 4-page steps per scoring wave
 struct ScorePlan {
-  int32_t pages_per_chunk;   // pages handled by one workgroup
-  int32_t blocks16_per_wave; // 16-page blocks per wave
-  int32_t n_chunks;          // chunks per (sequence, KV head)
+  int32_t n_chunks;          // workgroups per (sequence, KV head); one partial each
 };
 ScorePlan plan_score(int32_t batch, int32_t hkv, int32_t max_pages);
 

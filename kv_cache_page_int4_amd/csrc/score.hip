@@ -1,44 +1,50 @@
 // Page scoring from summaries: s_hat_j(q) = LSE_i((q.mu_j + (V_j^T q).c_i)/sqrt(d))
 // (LOCKS explainer, technical summary sec. 2, reconstruction and selection).
 //
-// Work split.  A workgroup (one wave) owns a contiguous chunk of logical
-// pages of one (sequence, KV head) and walks it in 16-page blocks, 4 pages
-// per step; the records of the next step (and the block ids of the next
-// block) are loaded while the current step computes.  Every record is read
-// exactly once, with 16-byte loads.
+// Work split.  The pages of one (sequence, KV head) are cut into 4-page
+// steps; a launch has a fixed number W of one-wave workgroups per
+// (sequence, KV head), and workgroup w takes steps w, w + W, w + 2W, ...
+// so that at any moment the workgroups sweep neighbouring parts of the
+// summary array.  Waves are short (a few steps): many dispatch rounds keep
+// the end-of-launch tail small.
 //
-// Per 4-page step one wave does:
+// Data movement.  The four 832-byte records of a step are copied straight
+// from HBM into a ring of LDS slots with global->LDS DMA (one 816-byte
+// instruction per record: 51 lanes x 16 B; the trailing pad is skipped).
+// The next step is in flight while one is computed, at no VGPR cost; with
+// 6.5 KB of LDS per wave, six waves share each SIMD.  The compiler does not track these copies, so the issue and the
+// waits are written out: every step issues exactly 4 copies, copies of one
+// wave complete in order, and waiting for "at most 4 outstanding" with one
+// younger step issued therefore means this step has landed.  Any other
+// memory instruction in flight only makes such a wait stricter.
+//
+// Per step one wave does:
 //  * V^T q on the matrix cores: rows = (page, basis) pairs, K = head dim,
 //    columns = the 4 query heads of the group repeated 4 times.  The int4
 //    basis codes become bf16 values 136+n exactly (byte permute onto the
 //    exponent of 128); the accumulator starts at -136*sum(q).  With the
 //    rows ordered (page = lane/16, basis = register), lane l ends up holding
 //    w[page l/16][k][head l%4] for all 8 k.
-//  * the coefficient term on the vector units: lane l takes token l%16 of
-//    page l/16 and pulls w[.][k][h] for the 4 heads from its own quad with DPP
-//    broadcasts, so one int8->f32 conversion of c_ik serves all 4 heads.
-//  * the page LSE over the 16 tokens of a page = one DPP row reduction.
-// q.mu for a whole 16-page block is one more matrix-core product (int8
-// centroid codes are exact in bf16), ordered so that each row of lanes finds
-// its page's value in a register and its quad.
+//  * q.mu on the matrix cores: rows (page p, dim group s''), columns
+//    (dim group s', head h), K over the 4 dim quarters; the diagonal
+//    s'' = s' summed over s' is q_h.mu_p.  Lane l picks its diagonal entry
+//    and the 4 lanes 4 apart in the row add up the rest.
+//  * the coefficient term on the vector units: lane l keeps its own head
+//    h = l%4 and page l/16 and takes the 4 tokens 4*cg..4*cg+3 of that page
+//    (cg = (l%16)/4).
+//  * the page LSE over 16 tokens: 4 exponentials in the lane, then the 4
+//    lanes of the same (page, head) -- 4 and 8 apart in the row -- are summed
+//    with two DPP row rotations.
 #include "locks_device.h"
 #include "locks_internal.h"
+
+#include <algorithm>
 
 namespace locks {
 
 namespace {
 
 constexpr uint32_t kMagic = 0x43434343u;  // bf16 high byte of 128.0
-
-struct ScoreParams {
-  const uint16_t* q;
-  const uint8_t* summ;
-  const int32_t* block_table;
-  const int32_t* seq_lens;
-  float* page_lse;
-  float2* partials;
-  int32_t num_blocks, max_pages, hq, hkv, n_chunks, pages_per_chunk;
-};
 
 // 8 int4 codes (two's complement, layout of the record) -> 8 bf16 = 136 + code.
 __device__ __forceinline__ bf16x8 nib8_to_bf16(uint32_t x) {
@@ -64,52 +70,74 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16(uint2 v) {
   return r;
 }
 
-struct StepLoads {
-  uint4 va, vb;   // basis codes of (page tok/4, basis tok%4 and tok%4+4), dims 32*row..+32
-  uint4 sv, sc;   // fp16 scales of page `row`
-  uint2 cc;       // coefficient codes of token tok of page `row`
+constexpr int kRing = 2;           // LDS record slots (steps) per wave: 1 in flight
+constexpr int kUnits = 51;         // 16-byte units copied per record (bytes [0, 816))
+constexpr int kSlotRec = 16 * kUnits;
+constexpr int kStepBytes = 4 * kSlotRec;
+
+struct ScoreParams {
+  const uint16_t* q;
+  const uint8_t* summ;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* page_lse;
+  float2* partials;
+  int32_t num_blocks, max_pages, hq, hkv, n_wg;
 };
 
-struct MuLoads {
-  uint4 m0, m1;   // centroid codes of page pi(tok), dims 32*row..+32
-  float smu[4];   // centroid scales of pages 4r + row
-};
+// Global -> LDS copy of 16 bytes per active lane: lane l writes LDS bytes
+// [lds + 16 l, lds + 16 l + 16) from sbase + voff.  M0 carries the LDS
+// address; the compiler treats M0 as reserved and this kernel has no other
+// user of it.
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(sbase), "s"(lds)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kStepBytes];
+
   const int lane = threadIdx.x;
-  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int w = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int W = p.n_wg;
   const int qhead0 = kvh * kG;
-  const int row = lane >> 4;   // page slot of this lane in a 4-page step
-  const int tok = lane & 15;   // token (coefficient lane) / MFMA row index
+  const int row = lane >> 4;   // page slot of this lane in a step
+  const int tok = lane & 15;
+  const int h = lane & 3;      // query head of this lane within the group
 
   int seq = p.seq_lens[b];
   seq = max(0, min(seq, p.max_pages * kB));
   const int n_fin = seq / kB;
+  const int nsteps = (n_fin + 3) / 4;
+  const int n = w < nsteps ? (nsteps - 1 - w) / W + 1 : 0;
 
   const uint8_t* __restrict__ summ_h = p.summ + (size_t)kvh * p.num_blocks * kRec;
   const int32_t* __restrict__ bt = p.block_table + (size_t)b * p.max_pages;
   float* __restrict__ lse_out = p.page_lse + ((size_t)b * p.hq + qhead0) * p.max_pages;
 
-  const int jbeg = chunk * p.pages_per_chunk;
-  const int jend = min(jbeg + p.pages_per_chunk, p.max_pages);
-  const int jreal = min(jend, n_fin);
-  const int n_blk = jreal > jbeg ? (jreal - jbeg + 15) / 16 : 0;
+  // pages that are not finalized score -inf
+  for (int j = n_fin + 64 * w + lane; j < p.max_pages; j += 64 * W)
+#pragma unroll
+    for (int hh = 0; hh < kG; ++hh) lse_out[(size_t)hh * p.max_pages + j] = -INFINITY;
 
-  // pages of this chunk past the covered blocks: not finalized
-  for (int j = jbeg + 16 * n_blk + row; j < jend; j += 4)
-    if (tok < 4) lse_out[(size_t)tok * p.max_pages + j] = -INFINITY;
-
-  float pm = -INFINITY, ps = 0.f;   // running base-2 (max, sum) of head tok (tok < 4)
-  if (n_blk > 0) {
-    // q as MFMA B operands: column (lane%16) is head lane%4; K element
+  float pm = -INFINITY, ps = 0.f;   // running base-2 (max, sum) of head h (lanes tok < 4)
+  if (n > 0) {
+    // q as MFMA B operands for V^T q: column (lane%16) is head lane%4; K element
     // (step s, lane group g, e) is dim 32g + 8s + e.
-    const int h = lane & 3;
-    const uint16_t* qrow = p.q + ((size_t)b * p.hq + qhead0 + h) * kD + 32 * row;
+    const uint16_t* qh = p.q + ((size_t)b * p.hq + qhead0 + h) * kD;
     bf16x8 bq[4];
     float qsum = 0.f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 8 * s);
+      const uint4 v = *reinterpret_cast<const uint4*>(qh + 32 * row + 8 * s);
       bq[s] = as_bf16x8(v);
       qsum += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
               bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
@@ -118,185 +146,179 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
     qsum += __shfl_xor(qsum, 32);
     // the codes enter the product as 136 + n: start the accumulator at -136 sum(q)
     const float acc0_init = -136.f * qsum;
+    // q as the B operand of q.mu: column (lane%16) = (dim group s' = (lane/4)%4,
+    // head lane%4), K element (lane group g, e) is dim 32g + 8s' + e
+    const int sq = (lane >> 2) & 3;
+    const uint4 qm_raw = *reinterpret_cast<const uint4*>(qh + 32 * row + 8 * sq);
+    const bf16x8 bqm = as_bf16x8(qm_raw);
+    // consume the q loads here, so that the compiler's wait for them comes
+    // before the first record copies are issued rather than behind them
+    asm volatile("" ::"v"(qm_raw.x), "v"(qm_raw.y), "v"(qm_raw.z), "v"(qm_raw.w), "v"(acc0_init));
     const float c0 = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
 
-    // block ids of a 16-page block, one per lane (replicated in each row);
-    // -1 marks a page that is not finalized or has an out-of-range block id
-    auto load_bids = [&](int jb) -> int {
-      const int j = jb + tok;
-      const int v = bt[min(j, n_fin - 1)];
-      return (j < n_fin && (unsigned)v < (unsigned)p.num_blocks) ? v : -1;
-    };
-    auto rec_of = [&](int bid) -> const uint8_t* {
-      return summ_h + (size_t)(bid < 0 ? 0 : bid) * kRec;
-    };
-    auto issue_step = [&](int bids, int it) -> StepLoads {
-      StepLoads L;
-      const uint8_t* rv = rec_of(__shfl(bids, 4 * it + (tok >> 2))) + 64 * (lane & 3) + 16 * row;
-      L.va = *reinterpret_cast<const uint4*>(rv);
-      L.vb = *reinterpret_cast<const uint4*>(rv + 256);
-      const uint8_t* rp = rec_of(__shfl(bids, 4 * it + row));
-      L.sv = *reinterpret_cast<const uint4*>(rp + kOffSv);
-      L.sc = *reinterpret_cast<const uint4*>(rp + kOffSc);
-      L.cc = *reinterpret_cast<const uint2*>(rp + kOffC + 8 * tok);
-      return L;
-    };
-    auto issue_mu = [&](int bids) -> MuLoads {
-      MuLoads M;
-      const int pm_ = 4 * (tok & 3) + (tok >> 2);
-      const uint8_t* rm = rec_of(__shfl(bids, pm_)) + kOffMu + 32 * row;
-      M.m0 = *reinterpret_cast<const uint4*>(rm);
-      M.m1 = *reinterpret_cast<const uint4*>(rm + 16);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        M.smu[r] = half_lo(*reinterpret_cast<const uint16_t*>(rec_of(__shfl(bids, 4 * r + row)) + kOffSmu));
-      return M;
-    };
-
-    int bids_cur = load_bids(jbeg);
-    int bids_next = (n_blk > 1) ? load_bids(jbeg + 16) : -1;
-    StepLoads nxt = issue_step(bids_cur, 0);
-    MuLoads mu = issue_mu(bids_cur);
-
-    for (int bk = 0; bk < n_blk; ++bk) {
-      const int jb = jbeg + 16 * bk;
-      // ---- q.mu for the 16 pages of this block (rows ordered page = 4r + g) ----
-      float qmu[4];
-      {
-        f32x4 dm = {0.f, 0.f, 0.f, 0.f};
-        dm = mfma16x16x32(i8x8_to_bf16(make_uint2(mu.m0.x, mu.m0.y)), bq[0], dm);
-        dm = mfma16x16x32(i8x8_to_bf16(make_uint2(mu.m0.z, mu.m0.w)), bq[1], dm);
-        dm = mfma16x16x32(i8x8_to_bf16(make_uint2(mu.m1.x, mu.m1.y)), bq[2], dm);
-        dm = mfma16x16x32(i8x8_to_bf16(make_uint2(mu.m1.z, mu.m1.w)), bq[3], dm);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) qmu[r] = dm[r] * mu.smu[r] * c0;
+    const uint32_t ring0 =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&ring[0][0];
+    // block ids of step k (scalar loads through the constant address space);
+    // -1 marks a page past the finalized ones or with an out-of-range block id
+    // (its record 0 is copied and its score dropped)
+    const __attribute__((address_space(4))) int32_t* btc =
+        (const __attribute__((address_space(4))) int32_t*)bt;
+    auto step_bids = [&](int k) -> int4 {
+      const int j0 = 4 * (w + k * W);
+      const unsigned nbk = (unsigned)p.num_blocks;
+      int4 v;
+      if (j0 + 4 <= n_fin) {
+        v.x = btc[j0];
+        v.y = btc[j0 + 1];
+        v.z = btc[j0 + 2];
+        v.w = btc[j0 + 3];
+      } else {
+        v.x = btc[min(j0, n_fin - 1)];
+        v.y = (j0 + 1 < n_fin) ? btc[j0 + 1] : -1;
+        v.z = (j0 + 2 < n_fin) ? btc[j0 + 2] : -1;
+        v.w = (j0 + 3 < n_fin) ? btc[j0 + 3] : -1;
       }
-      const int okrow_bids = bids_cur;
-      float blk_lse[4];
+      v.x = ((unsigned)v.x < nbk) ? v.x : -1;
+      v.y = ((unsigned)v.y < nbk) ? v.y : -1;
+      v.z = ((unsigned)v.z < nbk) ? v.z : -1;
+      v.w = ((unsigned)v.w < nbk) ? v.w : -1;
+      return v;
+    };
+    auto issue = [&](int k, int4 bb) {
+      const uint32_t slot = ring0 + (uint32_t)((k & 1) * kStepBytes);
+      const int bi[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const StepLoads cur = nxt;
-        // prefetch the next step (next block's first step and centroids at it == 3)
-        if (it < 3) {
-          nxt = issue_step(bids_cur, it + 1);
-        } else if (bk + 1 < n_blk) {
-          nxt = issue_step(bids_next, 0);
-          mu = issue_mu(bids_next);
-        }
-        const bool okp = __shfl(okrow_bids, 4 * it + row) >= 0;
-
-        f32x4 acc0 = {acc0_init, acc0_init, acc0_init, acc0_init};
-        f32x4 acc1 = acc0;
-        acc0 = mfma16x16x32(nib8_to_bf16(cur.va.x), bq[0], acc0);
-        acc1 = mfma16x16x32(nib8_to_bf16(cur.vb.x), bq[0], acc1);
-        acc0 = mfma16x16x32(nib8_to_bf16(cur.va.y), bq[1], acc0);
-        acc1 = mfma16x16x32(nib8_to_bf16(cur.vb.y), bq[1], acc1);
-        acc0 = mfma16x16x32(nib8_to_bf16(cur.va.z), bq[2], acc0);
-        acc1 = mfma16x16x32(nib8_to_bf16(cur.vb.z), bq[2], acc1);
-        acc0 = mfma16x16x32(nib8_to_bf16(cur.va.w), bq[3], acc0);
-        acc1 = mfma16x16x32(nib8_to_bf16(cur.vb.w), bq[3], acc1);
-
-        // w[k] = (q.v_k) * s_V[k] * s_c[k] for head lane%4 (log2(e)/sqrt(d) applied later)
-        const uint32_t svw[4] = {cur.sv.x, cur.sv.y, cur.sv.z, cur.sv.w};
-        const uint32_t scw[4] = {cur.sc.x, cur.sc.y, cur.sc.z, cur.sc.w};
-        float wk[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int k0 = r, k1 = r + 4;
-          const float f0 = ((k0 & 1) ? half_hi(svw[k0 >> 1]) : half_lo(svw[k0 >> 1])) *
-                           ((k0 & 1) ? half_hi(scw[k0 >> 1]) : half_lo(scw[k0 >> 1]));
-          const float f1 = ((k1 & 1) ? half_hi(svw[k1 >> 1]) : half_lo(svw[k1 >> 1])) *
-                           ((k1 & 1) ? half_hi(scw[k1 >> 1]) : half_lo(scw[k1 >> 1]));
-          wk[k0] = acc0[r] * f0;
-          wk[k1] = acc1[r] * f1;
-        }
-        float cf[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          cf[e] = (float)(int8_t)(cur.cc.x >> (8 * e));
-          cf[4 + e] = (float)(int8_t)(cur.cc.y >> (8 * e));
-        }
-        // deviation logits (without q.mu) of token `tok`, 4 heads, base 2
-        float dl[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          dl[0] = fmaf(quad_bcast<0>(wk[k]), cf[k], dl[0]);
-          dl[1] = fmaf(quad_bcast<1>(wk[k]), cf[k], dl[1]);
-          dl[2] = fmaf(quad_bcast<2>(wk[k]), cf[k], dl[2]);
-          dl[3] = fmaf(quad_bcast<3>(wk[k]), cf[k], dl[3]);
-        }
-#pragma unroll
-        for (int hh = 0; hh < 4; ++hh) dl[hh] *= c0;
-        // page LSE over the 16 tokens: no shift unless a sum leaves the safe range
-        float sm[4];
-        bool bad = false;
-#pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
-          sm[hh] = row_sum16(fast_exp2(dl[hh]));
-          bad |= !(sm[hh] >= 1e-30f && sm[hh] <= 1e30f);
-        }
-        float lse2[4];
-        if (__any(bad)) {
-#pragma unroll
-          for (int hh = 0; hh < 4; ++hh) {
-            const float mx = row_max16(dl[hh]);
-            lse2[hh] = mx + fast_log2(row_sum16(fast_exp2(dl[hh] - mx)));
-          }
-        } else {
-#pragma unroll
-          for (int hh = 0; hh < 4; ++hh) lse2[hh] = fast_log2(sm[hh]);
-        }
-        const float qm0 = quad_bcast<0>(qmu[it]), qm1 = quad_bcast<1>(qmu[it]);
-        const float qm2 = quad_bcast<2>(qmu[it]), qm3 = quad_bcast<3>(qmu[it]);
-        const float s2 = (tok == 0) ? qm0 + lse2[0] : (tok == 1) ? qm1 + lse2[1]
-                       : (tok == 2) ? qm2 + lse2[2] : qm3 + lse2[3];
-        blk_lse[it] = okp ? s2 * kLn2 : -INFINITY;
-        if (tok < 4 && okp) lse2_merge(pm, ps, s2, 1.f);
+      for (int i = 0; i < 4; ++i) {
+        const uint8_t* base = summ_h + (size_t)max(bi[i], 0) * kRec;
+        if (lane < kUnits)
+          dma16(16u * lane, base, __builtin_amdgcn_readfirstlane(slot + kSlotRec * i));
       }
-      // one coalesced store per block: lane 16h + i takes page jb + i of head
-      // h, computed at step i/4 by lane 16*(i%4) + h
-      {
-        const int hh = lane >> 4, i = lane & 15;
-        const int src = 16 * (i & 3) + hh;
-        const float v0 = __shfl(blk_lse[0], src), v1 = __shfl(blk_lse[1], src);
-        const float v2 = __shfl(blk_lse[2], src), v3 = __shfl(blk_lse[3], src);
-        const int st = i >> 2;
-        const float v = (st == 0) ? v0 : (st == 1) ? v1 : (st == 2) ? v2 : v3;
-        const int j = jb + i;
-        if (j < jend) lse_out[(size_t)hh * p.max_pages + j] = v;
+    };
+
+    // block ids of step k (b0) and k+1 (b1, the next one to issue)
+    static_assert(kRing == 2, "the block-id pipeline below holds two steps");
+    const int4 none = make_int4(-1, -1, -1, -1);
+    int4 b0 = step_bids(0);
+    int4 b1 = (n > 1) ? step_bids(1) : none;
+    issue(0, b0);
+    for (int k = 0; k < n; ++k) {
+      // every LDS read of step k-1 has returned: its slot may be refilled
+      wait_lgkm0();
+      const int4 bcur = b0;
+      const bool more = k + 1 < n;
+      if (more) issue(k + 1, b1);
+      b0 = b1;
+      b1 = (k + 2 < n) ? step_bids(k + 2) : none;
+      if (more) wait_vm<4>();
+      else wait_vm<0>();
+
+      const uint8_t* S = &ring[k & 1][0];
+      const uint8_t* Sr = S + kSlotRec * row;          // record of this lane's page
+      const int jpg = 4 * (w + k * W) + row;           // this lane's page
+      const int bid_row = (row == 0) ? bcur.x : (row == 1) ? bcur.y : (row == 2) ? bcur.z : bcur.w;
+      const bool okp = bid_row >= 0;
+
+      // ---- V^T q: A rows (page tok/4, basis tok%4 [+4]), dims 32 row + 8s + e ----
+      const uint8_t* av = S + kSlotRec * (tok >> 2) + 64 * (lane & 3) + 16 * row;
+      const uint4 va = lds16(av), vb = lds16(av + 256);
+      f32x4 acc0 = {acc0_init, acc0_init, acc0_init, acc0_init};
+      f32x4 acc1 = acc0;
+      acc0 = mfma16x16x32(nib8_to_bf16(va.x), bq[0], acc0);
+      acc1 = mfma16x16x32(nib8_to_bf16(vb.x), bq[0], acc1);
+      acc0 = mfma16x16x32(nib8_to_bf16(va.y), bq[1], acc0);
+      acc1 = mfma16x16x32(nib8_to_bf16(vb.y), bq[1], acc1);
+      acc0 = mfma16x16x32(nib8_to_bf16(va.z), bq[2], acc0);
+      acc1 = mfma16x16x32(nib8_to_bf16(vb.z), bq[2], acc1);
+      acc0 = mfma16x16x32(nib8_to_bf16(va.w), bq[3], acc0);
+      acc1 = mfma16x16x32(nib8_to_bf16(vb.w), bq[3], acc1);
+
+      // ---- q.mu: A row (page (lane/4)%4, dim group lane%4), K (lane group g, e) ----
+      const uint2 mq = *reinterpret_cast<const uint2*>(S + kSlotRec * sq + kOffMu + 32 * row +
+                                                       8 * (lane & 3));
+      f32x4 dmu = {0.f, 0.f, 0.f, 0.f};
+      dmu = mfma16x16x32(i8x8_to_bf16(mq), bqm, dmu);
+      // lane (page row, s' = sq, head h) holds D[(row, r)][(sq, h)] in register r
+      float qmu = (sq == 0) ? dmu[0] : (sq == 1) ? dmu[1] : (sq == 2) ? dmu[2] : dmu[3];
+      qmu += dpp<kRowRor4>(qmu);
+      qmu += dpp<kRowRor8>(qmu);
+      const float smu = half_lo(*reinterpret_cast<const uint16_t*>(Sr + kOffSmu));
+      const float qmu2 = qmu * smu * c0;
+
+      // ---- w[k] = (q_h.v_k) * s_V[k] * s_c[k] for this lane's page and head ----
+      const uint4 sv = lds16(Sr + kOffSv), sc = lds16(Sr + kOffSc);
+      const uint32_t svw[4] = {sv.x, sv.y, sv.z, sv.w};
+      const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
+      // fp16 operand times fp32 with a +0 addend: one mixed-precision FMA each
+      auto hmul = [](uint32_t pair, int hi, float x) {
+        return __builtin_fmaf(hi ? half_hi(pair) : half_lo(pair), x, 0.0f);
+      };
+      float wk[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int k0 = r, k1 = r + 4;
+        wk[k0] = hmul(scw[k0 >> 1], k0 & 1, hmul(svw[k0 >> 1], k0 & 1, acc0[r]));
+        wk[k1] = hmul(scw[k1 >> 1], k1 & 1, hmul(svw[k1 >> 1], k1 & 1, acc1[r]));
       }
-      if (bk + 1 < n_blk) {
-        bids_cur = bids_next;
-        bids_next = (bk + 2 < n_blk) ? load_bids(jb + 32) : -1;
+      // ---- deviation logits (base 2, without q.mu) of tokens 4cg..4cg+3 ----
+      const uint8_t* cp = Sr + kOffC + 32 * (tok >> 2);
+      const uint4 cc0 = lds16(cp), cc1 = lds16(cp + 16);
+      const uint32_t cw[8] = {cc0.x, cc0.y, cc0.z, cc0.w, cc1.x, cc1.y, cc1.z, cc1.w};
+      float dl[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float a = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+          a = fmaf(wk[kk], (float)(int8_t)(cw[2 * t + (kk >> 2)] >> (8 * (kk & 3))), a);
+        dl[t] = a * c0;
+      }
+      // page LSE over 16 tokens: 4 in this lane, the rest in the lanes 4 and 8
+      // apart in this row (same page and head, other token quarters)
+      float sm = fast_exp2(dl[0]) + fast_exp2(dl[1]) + fast_exp2(dl[2]) + fast_exp2(dl[3]);
+      sm += dpp<kRowRor4>(sm);
+      sm += dpp<kRowRor8>(sm);
+      float lse2;
+      if (__any(!(sm >= 1e-30f && sm <= 1e30f))) {
+        float mx = fmaxf(fmaxf(dl[0], dl[1]), fmaxf(dl[2], dl[3]));
+        mx = fmaxf(mx, dpp<kRowRor4>(mx));
+        mx = fmaxf(mx, dpp<kRowRor8>(mx));
+        float s3 = fast_exp2(dl[0] - mx) + fast_exp2(dl[1] - mx) + fast_exp2(dl[2] - mx) +
+                   fast_exp2(dl[3] - mx);
+        s3 += dpp<kRowRor4>(s3);
+        s3 += dpp<kRowRor8>(s3);
+        lse2 = mx + fast_log2(s3);
+      } else {
+        lse2 = fast_log2(sm);
+      }
+      const float s2 = qmu2 + lse2;
+      if (tok < 4 && jpg < n_fin) {
+        lse_out[(size_t)h * p.max_pages + jpg] = okp ? s2 * kLn2 : -INFINITY;
+        if (okp) lse2_merge(pm, ps, s2, 1.f);
       }
     }
   }
 
-  // ---- per-chunk (max, sum) of each head, for the page-mass normalization ----
+  // ---- per-workgroup (max, sum) of each head, for the page-mass normalization ----
   float m2 = __shfl_xor(pm, 16), s2 = __shfl_xor(ps, 16);
   lse2_merge(pm, ps, m2, s2);
   m2 = __shfl_xor(pm, 32);
   s2 = __shfl_xor(ps, 32);
   lse2_merge(pm, ps, m2, s2);
   if (lane < 4 && p.partials)
-    p.partials[((size_t)b * p.hq + qhead0 + lane) * p.n_chunks + chunk] = make_float2(pm, ps);
+    p.partials[((size_t)b * p.hq + qhead0 + lane) * W + w] = make_float2(pm, ps);
 }
 
 }  // namespace
 
 ScorePlan plan_score(int32_t batch, int32_t hkv, int32_t max_pages) {
-  // one wave per workgroup; aim for >= ~8k workgroups at long context
+  // short-lived waves of about kScoreSteps steps each: many dispatch rounds
+  // keep the end-of-launch tail small
+  (void)batch;
+  (void)hkv;
   ScorePlan pl;
-  int bpw = 1;
-  const long long groups = (long long)batch * hkv;
-  while (bpw < 8) {
-    const long long chunk = 16LL * bpw * 2;
-    if (groups * ((max_pages + chunk - 1) / chunk) < 8192) break;
-    bpw *= 2;
-  }
-  pl.blocks16_per_wave = bpw;
-  pl.pages_per_chunk = 16 * bpw;
-  pl.n_chunks = (max_pages + pl.pages_per_chunk - 1) / pl.pages_per_chunk;
+  const long long steps = kScoreSteps;
+  const long long nsteps = ((long long)max_pages + 3) / 4;
+  pl.n_chunks = (int32_t)std::max(1LL, (nsteps + steps - 1) / steps);
   return pl;
 }
 
@@ -305,7 +327,7 @@ hipError_t launch_score(const uint16_t* q, const uint8_t* summ, int32_t num_bloc
                         int32_t batch, int32_t hq, int32_t hkv, float* page_lse,
                         float2* partials, const ScorePlan& plan, hipStream_t stream) {
   ScoreParams p{q, summ, block_table, seq_lens, page_lse, partials, num_blocks, max_pages, hq,
-                hkv, plan.n_chunks, plan.pages_per_chunk};
+                hkv, plan.n_chunks};
   dim3 grid(plan.n_chunks, hkv, batch);
   hipLaunchKernelGGL(score_kernel, grid, dim3(64), 0, stream, p);
   return hipGetLastError();

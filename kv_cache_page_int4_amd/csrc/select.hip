@@ -359,41 +359,16 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
   const int n_fin = seq / kB;
 
   __shared__ float L2[kG];
+  __shared__ float2 wpart[kSelThreads / 64];
   __shared__ int hist[2][256];
   __shared__ int sh[2][2];
   __shared__ int scan_smem[kSelThreads / 64 + 1];
 
-  // per-head normalizer from the scoring partials (wave w -> head w)
-  if (wave < kG) {
-    const float2* pp = p.partials + ((size_t)b * p.hq + kvh * kG + wave) * p.n_partials;
-    float m = -INFINITY, s = 0.f;
-    // independent loads, 8 in flight per lane, then merge
-    for (int c0 = lane; c0 < p.n_partials; c0 += 8 * 64) {
-      float2 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int c = c0 + 64 * u;
-        v[u] = (c < p.n_partials) ? pp[c] : make_float2(-INFINITY, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) lse2_merge(m, s, v[u].x, v[u].y);
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-      lse2_merge(m, s, m2, s2);
-    }
-    if (lane == 0) L2[wave] = (s > 0.f) ? m + fast_log2(s) : -INFINITY;
-  }
-  __syncthreads();
-
-  // keys of this thread's 8 consecutive pages
+  // scores of this thread's pages: 4 x kPerThread loads (clamped in-bounds
+  // index), issued before the normalizer so that both are in flight together
   const int jbase = chunk * kSelChunk + kPerThread * tid;
-  uint32_t key[kPerThread];
-  int nvalid = 0;
+  float sv[kG][kPerThread];
   {
-    // all 4 x 8 scores are loaded (clamped in-bounds index) before any use
-    float sv[kG][kPerThread];
     const int jmax = max(n_fin - 1, 0);
 #pragma unroll
     for (int hh = 0; hh < kG; ++hh) {
@@ -401,6 +376,49 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
 #pragma unroll
       for (int t = 0; t < kPerThread; ++t) sv[hh][t] = s[min(jbase + t, jmax)];
     }
+  }
+
+  // per-head normalizer from the scoring partials: waves 4h..4h+3 merge head
+  // h's partials, 16 independent loads per lane per round
+  {
+    constexpr int kWavesPerHead = kSelThreads / 64 / kG;
+    constexpr int kU = 16;
+    const int hh = wave / kWavesPerHead, part = wave % kWavesPerHead;
+    const float2* pp = p.partials + ((size_t)b * p.hq + kvh * kG + hh) * p.n_partials;
+    float m = -INFINITY, s = 0.f;
+    for (int c0 = part * 64 + lane; c0 < p.n_partials; c0 += kU * kWavesPerHead * 64) {
+      float2 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int c = c0 + kWavesPerHead * 64 * u;
+        v[u] = (c < p.n_partials) ? pp[c] : make_float2(-INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) lse2_merge(m, s, v[u].x, v[u].y);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+      lse2_merge(m, s, m2, s2);
+    }
+    if (lane == 0) wpart[wave] = make_float2(m, s);
+    __syncthreads();
+    if (tid < kG) {
+      float mm = -INFINITY, ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < kWavesPerHead; ++i) {
+        const float2 v = wpart[tid * kWavesPerHead + i];
+        lse2_merge(mm, ss, v.x, v.y);
+      }
+      L2[tid] = (ss > 0.f) ? mm + fast_log2(ss) : -INFINITY;
+    }
+    __syncthreads();
+  }
+
+  // keys of this thread's consecutive pages
+  uint32_t key[kPerThread];
+  int nvalid = 0;
+  {
     float lm[kPerThread];
 #pragma unroll
     for (int t = 0; t < kPerThread; ++t) lm[t] = -INFINITY;
