@@ -156,3 +156,62 @@ def log(msg):
 
 def softmax_scale():
     return 1.0 / math.sqrt(128)
+
+
+# ---------------------------------------------------------------------------
+# summary builder codes against the oracle on the same keys
+# ---------------------------------------------------------------------------
+
+def exempt_columns(lam, V):
+    """Columns whose codes are not unique under rounding: near-degenerate
+    eigenvalues, a near-tie for the sign pivot, or an eigenvalue near the
+    rank floor."""
+    r = V.shape[-1]
+    lam1 = lam[0]
+    ex = np.zeros(r, dtype=bool)
+    for k in range(r):
+        gaps = []
+        if k > 0:
+            gaps.append(lam[k - 1] - lam[k])
+        gaps.append(lam[k] - lam[k + 1])
+        if min(gaps) < 1e-3 * lam1:
+            ex[k] = True
+        a = np.sort(np.abs(V[:, k]))[::-1]
+        if a[0] > 0 and (a[0] - a[1]) <= 1e-4 * a[0]:
+            ex[k] = True
+        if 0.5 * O.TAU * lam1 <= lam[k] <= 2 * O.TAU * lam1:
+            ex[k] = True
+    return ex
+
+
+def compare_build_codes(K, recs_gpu, where=""):
+    """K: fp64 keys [n, 16, 128]; recs_gpu: the GPU's records [n, 832] for
+    the same page-heads.  Codes within 1 LSB and scales within 1 fp16 ulp
+    outside the exempt columns; exempt pages compared by reconstruction.
+    Returns (columns, exempt columns, worst exempt-page reconstruction diff)."""
+    mu, V, C, lam = O.page_summary(K)
+    qo = O.quantize_summary(mu, V, C)
+    qg = O.unpack_records(recs_gpu)
+    assert np.abs(qg["mu_q"].astype(int) - qo["mu_q"]).max() <= 1, where
+    assert np.all(np.abs(qg["s_mu"] - qo["s_mu"]) <= fp16_ulp(qo["s_mu"])), where
+    n_cols = n_ex = 0
+    worst_rec = 0.0
+    for i in range(K.shape[0]):
+        ex = exempt_columns(lam[i], V[i])
+        n_cols += len(ex)
+        n_ex += int(ex.sum())
+        ok = ~ex
+        dv = np.abs(qg["v_q"][i][:, ok].astype(int) - qo["v_q"][i][:, ok])
+        dc = np.abs(qg["c_q"][i][:, ok].astype(int) - qo["c_q"][i][:, ok])
+        assert dv.max(initial=0) <= 1, f"basis codes off by {dv.max()} ({where}, page {i})"
+        assert dc.max(initial=0) <= 1, f"coefficient codes off by {dc.max()} ({where}, page {i})"
+        assert np.all(np.abs(qg["s_v"][i][ok] - qo["s_v"][i][ok]) <= fp16_ulp(qo["s_v"][i][ok]))
+        assert np.all(np.abs(qg["s_c"][i][ok] - qo["s_c"][i][ok]) <= fp16_ulp(qo["s_c"][i][ok]))
+        if ex.any():
+            Rg = dequant_recon({k: v[i] for k, v in qg.items()})
+            Ro = dequant_recon({k: v[i] for k, v in qo.items()})
+            X = K[i] - mu[i]
+            rel = np.linalg.norm(Rg - Ro) / max(np.linalg.norm(X), 1e-30)
+            worst_rec = max(worst_rec, rel)
+            assert rel <= 0.15, f"reconstruction of an exempt page differs by {rel} ({where})"
+    return n_cols, n_ex, worst_rec
