@@ -24,7 +24,7 @@ locks_status check_dims(const locks_dims* d) {
 constexpr int64_t kMaxPages = (int64_t)1 << 26;
 
 struct ScoreWs {
-  size_t lse_off, part_off, key_off, idx_off, total;
+  size_t lse_off, part_off, l2_off, key_off, idx_off, total;
   ScorePlan sp;
   SelectPlan sel;
 };
@@ -41,6 +41,8 @@ ScoreWs score_ws_layout(const locks_dims* d, int32_t batch, int32_t max_pages, i
   // partials serve the scorer's chunking and the standalone-select chunking
   const int32_t n_part = w.sp.n_chunks > w.sel.n_chunks ? w.sp.n_chunks : w.sel.n_chunks;
   off += align_up((size_t)batch * d->num_q_heads * n_part * sizeof(float2));
+  w.l2_off = off;
+  off += align_up((size_t)batch * d->num_q_heads * sizeof(float));
   const size_t ncand = (size_t)batch * d->num_kv_heads * w.sel.n_chunks * w.sel.slots;
   w.key_off = off;
   off += align_up(ncand * sizeof(uint32_t));
@@ -158,6 +160,7 @@ locks_status locks_select_pages(const locks_dims* dims, const float* page_lse, i
   if (e == hipSuccess)
     e = launch_select(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, dims->num_kv_heads,
                       budget_pages, part, w.sel.n_chunks,
+                      reinterpret_cast<float*>(ws_at(workspace, w.l2_off)),
                       reinterpret_cast<uint32_t*>(ws_at(workspace, w.key_off)),
                       reinterpret_cast<int32_t*>(ws_at(workspace, w.idx_off)), w.sel, sel,
                       sel_count, s);
@@ -184,6 +187,7 @@ locks_status locks_score_select(const locks_dims* dims, const void* q, const voi
   if (e == hipSuccess)
     e = launch_select(lse, max_pages, seq_lens, batch, dims->num_q_heads, dims->num_kv_heads,
                       budget_pages, part, w.sp.n_chunks,
+                      reinterpret_cast<float*>(ws_at(workspace, w.l2_off)),
                       reinterpret_cast<uint32_t*>(ws_at(workspace, w.key_off)),
                       reinterpret_cast<int32_t*>(ws_at(workspace, w.idx_off)), w.sel, sel,
                       sel_count, s);

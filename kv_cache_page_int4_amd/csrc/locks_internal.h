@@ -34,9 +34,9 @@ hipError_t launch_lse_partials(const float* page_lse, int32_t max_pages, const i
 
 hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
                          int32_t batch, int32_t hq, int32_t hkv, int32_t budget_pages,
-                         const float2* partials, int32_t n_partials, uint32_t* cand_key,
-                         int32_t* cand_idx, const SelectPlan& plan, int32_t* sel,
-                         int32_t* sel_count, hipStream_t stream);
+                         const float2* partials, int32_t n_partials, float* head_l2,
+                         uint32_t* cand_key, int32_t* cand_idx, const SelectPlan& plan, int32_t* sel, int32_t* sel_count,
+                         hipStream_t stream);
 
 // ---- sparse attention ---------------------------------------------------------
 struct AttendPlan {

@@ -8,14 +8,15 @@
 // and the k = min(budget, valid pages) largest m_j are kept, ties to the lower
 // page index, listed in ascending page order.
 //
-// Two kernels.  Stage 1: one workgroup per 2048-page chunk turns scores into
+// Three kernels.  First L_h per query head from the scorer's (max, sum)
+// partials.  Stage 1: one workgroup per 2048-page chunk turns scores into
 // order-preserving 32-bit keys and radix-selects the chunk's top min(k, 2048)
-// (8-bit digits, LDS histograms); survivors are written in page order.
-// Stage 2: one workgroup per (sequence, KV head) radix-selects the global top
-// k over all candidates, staged in LDS when they fit.  Because each chunk emits its survivors
-// in page order and chunks are in page order, stream compaction of the
-// winners yields ascending page ids directly, and "lowest index among equal
-// keys" is "first in candidate order".
+// (8-bit digits, LDS histograms); survivors are written in page
+// order.  Stage 2: one workgroup per (sequence, KV head) radix-selects the
+// global top k over all candidates.  Because each chunk emits its survivors in
+// page order and chunks are in page order, stream compaction of the winners
+// yields ascending page ids directly, and "lowest index among equal keys" is
+// "first in candidate order".
 #include "locks_device.h"
 #include "locks_internal.h"
 
@@ -26,10 +27,12 @@ namespace {
 constexpr int kSelThreads = 1024;   // 16 waves: 4 per SIMD hide the latency chains
 constexpr int kPerThread = kSelChunk / kSelThreads;  // 2
 
-// Inclusive prefix sum over a workgroup (blockDim.x <= 1024), returns the
-// exclusive prefix and the total through `total`.
+// Exclusive prefix sum over the workgroup of one int per thread; the total
+// comes back through `total`.  The cross-wave step is a shuffle scan of the
+// wave totals in every wave (no serial loop).  smem >= NT/64 ints.
 template <int NT>
-__device__ int block_exclusive_scan(int v, int* total, int* smem /* >= NT/64 + 1 */) {
+__device__ int block_exclusive_scan(int v, int* total, int* smem) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -39,58 +42,60 @@ __device__ int block_exclusive_scan(int v, int* total, int* smem /* >= NT/64 + 1
   }
   if (lane == 63) smem[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < NT / 64; ++w) {
-      const int t = smem[w];
-      smem[w] = run;
-      run += t;
-    }
-    smem[NT / 64] = run;
+  const int t = (lane < NW) ? smem[lane] : 0;
+  int u = t;
+#pragma unroll
+  for (int o = 1; o < NW; o <<= 1) {
+    const int y = __shfl_up(u, o);
+    if (lane >= o) u += y;
   }
-  __syncthreads();
-  const int excl = smem[wave] + x - v;
-  *total = smem[NT / 64];
-  __syncthreads();
-  return excl;
+  const int before = __shfl(u, wave) - __shfl(t, wave);   // totals of the waves below
+  *total = __shfl(u, NW - 1);
+  __syncthreads();   // smem is reused by the next call
+  return before + x - v;
 }
 
-// Block-wide min and max (result in every thread); smem >= NT/64 + 1 ints.
+// Workgroup sum of an int and min / max of a uint32 (results in every
+// thread).  smem >= 3 * NT/64 words.
 template <int NT>
-__device__ void block_minmax(uint32_t& mn, uint32_t& mx, int* smem) {
+__device__ void block_sum_minmax(int& sum, uint32_t& mn, uint32_t& mx, uint32_t* smem) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
+    sum += __shfl_xor(sum, o);
     mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
   }
-  __shared__ uint32_t red[2][NT / 64];
   if (lane == 0) {
-    red[0][wave] = mn;
-    red[1][wave] = mx;
+    smem[wave] = (uint32_t)sum;
+    smem[NW + wave] = mn;
+    smem[2 * NW + wave] = mx;
   }
   __syncthreads();
-  mn = red[0][0];
-  mx = red[1][0];
-  for (int w = 1; w < NT / 64; ++w) {
-    mn = min(mn, red[0][w]);
-    mx = max(mx, red[1][w]);
+  int a = (lane < NW) ? (int)smem[lane] : 0;
+  uint32_t b = (lane < NW) ? smem[NW + lane] : 0xFFFFFFFFu;
+  uint32_t c = (lane < NW) ? smem[2 * NW + lane] : 0u;
+#pragma unroll
+  for (int o = 1; o < NW; o <<= 1) {
+    a += __shfl_xor(a, o);
+    b = min(b, (uint32_t)__shfl_xor((int)b, o));
+    c = max(c, (uint32_t)__shfl_xor((int)c, o));
   }
+  sum = __shfl(a, 0);
+  mn = (uint32_t)__shfl((int)b, 0);
+  mx = (uint32_t)__shfl((int)c, 0);
   __syncthreads();
-  (void)smem;
 }
 
 // Find the digit bucket holding the rem-th largest key among those counted in
 // hist[256] (called by one full wave).  Exactly one lane finds it and stores
-// the digit and the rank left inside that bucket.
-__device__ void pick_digit(const int* hist, int rem, int* sh_digit, int* sh_rem) {
+// the digit, the rank left inside that bucket and the bucket's population.
+__device__ void pick_digit(const int* hist, int rem, int* sh) {
   const int lane = threadIdx.x & 63;   // lane owns digits 4*lane .. 4*lane+3
-  int c[4], tot = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    c[e] = hist[4 * lane + e];
-    tot += c[e];
-  }
+  const int4 v = *reinterpret_cast<const int4*>(hist + 4 * lane);
+  const int c[4] = {v.x, v.y, v.z, v.w};
+  const int tot = c[0] + c[1] + c[2] + c[3];
   int x = tot;  // inclusive suffix sum over lanes (higher digits first)
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -101,24 +106,27 @@ __device__ void pick_digit(const int* hist, int rem, int* sh_digit, int* sh_rem)
 #pragma unroll
   for (int e = 3; e >= 0; --e) {
     if (above < rem && above + c[e] >= rem) {
-      *sh_digit = 4 * lane + e;
-      *sh_rem = rem - above;
+      sh[0] = 4 * lane + e;
+      sh[1] = rem - above;
+      sh[2] = c[e];
     }
     above += c[e];
   }
 }
 
-// Threshold T of the k-th largest key and the number `rem` of keys equal to T
-// that belong to the top k.  The radix passes cover only the bits in which
-// the keys differ (from the block-wide min and max of the valid keys), eight
-// at a time from the top, so the first digit already spreads the keys over
-// the histogram; a wave whose keys all share one digit adds it with a single
-// atomic.  Histograms are double-buffered so a pass needs two barriers.
+// Threshold T and count `rem` such that the top k keys are exactly the keys
+// above T plus the first `rem` keys equal to T (in the callers' order).  The
+// radix passes cover only the bits in which the valid keys differ (from their
+// min and max), eight at a time from the top, so the first digit already
+// spreads the keys over the histogram.  A pass whose boundary bucket is taken
+// whole ends the search: T becomes the value just below that bucket and rem
+// 0.  A wave whose keys all share one digit adds it with a single atomic.
+// Histograms are double-buffered so a pass needs two barriers.
 // for_each(f) calls f(key, valid) for each of this thread's slots, the same
-// number of times in every thread.  hist: [2][256]; sh: [2][2].
+// number of times in every thread.  hist: [2][256]; sh: [2][4].
 template <int NT, typename ForEach>
 __device__ void radix_threshold(ForEach for_each, int k, uint32_t kmin, uint32_t kmax,
-                                int (*hist)[256], int (*sh)[2], uint32_t* T_out, int* rem_out) {
+                                int (*hist)[256], int (*sh)[4], uint32_t* T_out, int* rem_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t diff = kmin ^ kmax;
   if (diff == 0u) {           // every valid key is equal
@@ -147,12 +155,18 @@ __device__ void radix_threshold(ForEach for_each, int k, uint32_t kmin, uint32_t
       }
     });
     __syncthreads();
-    if (wave == 0) pick_digit(hist[buf], rem, &sh[buf][0], &sh[buf][1]);
+    if (wave == 0) pick_digit(hist[buf], rem, sh[buf]);
     for (int i = tid; i < 256; i += NT) hist[buf ^ 1][i] = 0;   // next pass's buffer
     __syncthreads();
     prefix |= (uint32_t)sh[buf][0] << lo;
     pmask |= dmask << lo;
     rem = sh[buf][1];
+    if (lo > 0 && sh[buf][2] == rem) {
+      // the whole boundary bucket is taken: threshold just below it
+      *T_out = prefix == 0u ? 0u : prefix - 1u;
+      *rem_out = 0;
+      return;
+    }
     buf ^= 1;
   }
   *T_out = prefix;
@@ -189,13 +203,61 @@ __global__ __launch_bounds__(kSelThreads) void lse_partials_kernel(
 struct SelParams {
   const float* page_lse;
   const int32_t* seq_lens;
-  const float2* partials;
+  const float* head_l2;      // [b][hq] base-2 log of each head's total estimated mass
   uint32_t* cand_key;
   int32_t* cand_idx;
   int32_t* sel;
   int32_t* sel_count;
-  int32_t max_pages, hq, hkv, budget, n_partials, n_chunks, slots;
+  int32_t max_pages, hq, hkv, budget, n_chunks, slots;
 };
+
+// L_h (base 2) of every (sequence, query head) from the scorer's partials.
+constexpr int kHeadThreads = 256;
+constexpr int kHeadLoads = 16;
+
+__global__ __launch_bounds__(kHeadThreads) void head_lse_kernel(const float2* partials,
+                                                                int32_t n_partials, float* head_l2) {
+  const size_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float2* pp = partials + row * n_partials;
+  float m = -INFINITY, s = 0.f;
+  for (int c0 = tid; c0 < n_partials; c0 += kHeadLoads * kHeadThreads) {
+    float2 v[kHeadLoads];
+#pragma unroll
+    for (int u = 0; u < kHeadLoads; ++u) {
+      const int c = c0 + kHeadThreads * u;
+      v[u] = (c < n_partials) ? pp[c] : make_float2(-INFINITY, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kHeadLoads; ++u) lse2_merge(m, s, v[u].x, v[u].y);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+    lse2_merge(m, s, m2, s2);
+  }
+  __shared__ float2 red[kHeadThreads / 64];
+  if (lane == 0) red[wave] = make_float2(m, s);
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kHeadThreads / 64; ++w) lse2_merge(m, s, red[w].x, red[w].y);
+    head_l2[row] = (s > 0.f) ? m + fast_log2(s) : -INFINITY;
+  }
+}
+
+// Ordered compaction of the winners of one workgroup.  A key wins if it is
+// above T, or equal to T and among the first `rem` such keys in candidate
+// order; both counts come out of one scan of (above << 16 | equal), which is
+// exact while a workgroup holds fewer than 2^16 keys (2048 in stage 1, at
+// most 32768 in the register-resident stage 2).  Returns the numbers of
+// above-T and equal-to-T keys before this thread's first one.
+__device__ __forceinline__ void winner_scan(int n_gt, int n_eq, int* pos_gt, int* pos_eq,
+                                            int* scan_smem) {
+  int tot;
+  const int pre = block_exclusive_scan<kSelThreads>((n_gt << 16) | n_eq, &tot, scan_smem);
+  *pos_gt = pre >> 16;
+  *pos_eq = pre & 0xFFFF;
+}
 
 // Stage 2 over candidates held in registers: thread t owns the contiguous
 // run [t*per, t*per + per) of the page-ordered candidate list (per <= RUN), so
@@ -205,12 +267,13 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(SelParams p) 
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   __shared__ int hist[2][256];
-  __shared__ int sh[2][2];
-  __shared__ int scan_smem[kSelThreads / 64 + 1];
+  __shared__ int sh[2][4];
+  __shared__ uint32_t red_smem[3 * (kSelThreads / 64)];
+  __shared__ int scan_smem[kSelThreads / 64];
   const int n_cand = p.n_chunks * p.slots;
-  const size_t gbase = ((size_t)b * p.hkv + kvh) * (size_t)n_cand;
-  const uint32_t* gk = p.cand_key + gbase;
-  const int32_t* gi = p.cand_idx + gbase;
+  const size_t grp = (size_t)b * p.hkv + kvh;
+  const uint32_t* gk = p.cand_key + grp * (size_t)n_cand;
+  const int32_t* gi = p.cand_idx + grp * (size_t)n_cand;
   const int per = (n_cand + kSelThreads - 1) / kSelThreads;
   const int c0 = tid * per;
   uint32_t key[RUN];
@@ -222,15 +285,15 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(SelParams p) 
   int nv = 0;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-  for (int i = 0; i < RUN; ++i)
+  for (int i = 0; i < RUN; ++i) {
     if (key[i] != 0u) {
       ++nv;
       kmin = min(kmin, key[i]);
       kmax = max(kmax, key[i]);
     }
-  int total_valid;
-  (void)block_exclusive_scan<kSelThreads>(nv, &total_valid, scan_smem);
-  block_minmax<kSelThreads>(kmin, kmax, scan_smem);
+  }
+  int total_valid = nv;
+  block_sum_minmax<kSelThreads>(total_valid, kmin, kmax, red_smem);
   const int k = min(p.budget, total_valid);
   const bool all = (k >= total_valid);
   uint32_t T = 0u;
@@ -242,39 +305,36 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(SelParams p) 
           for (int i = 0; i < RUN; ++i) f(key[i], key[i] != 0u);
         },
         k, kmin, kmax, hist, sh, &T, &rem);
-  int neq = 0;
-#pragma unroll
-  for (int i = 0; i < RUN; ++i) neq += (!all && key[i] != 0u && key[i] == T);
-  int tot_eq;
-  const int eq_before = block_exclusive_scan<kSelThreads>(neq, &tot_eq, scan_smem);
-  uint32_t take = 0u;   // bit i: slot i is a winner
-  int ntake = 0;
-  {
-    int eqr = eq_before;
-#pragma unroll
-    for (int i = 0; i < RUN; ++i) {
-      bool tk = false;
-      if (key[i] != 0u && k > 0) {
-        if (all || key[i] > T) tk = true;
-        else if (key[i] == T) tk = (eqr++ < rem);
-      }
-      take |= (tk ? 1u : 0u) << i;
-      ntake += tk;
-    }
-  }
-  int tot_take;
-  int pos = block_exclusive_scan<kSelThreads>(ntake, &tot_take, scan_smem);
-  int32_t* out = p.sel + ((size_t)b * p.hkv + kvh) * p.budget;
+  int n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int i = 0; i < RUN; ++i) {
-    if ((take >> i) & 1u) {
-      if (pos < p.budget) out[pos] = gi[c0 + i];
-      ++pos;
-    }
+    n_gt += (key[i] != 0u && key[i] > T);
+    n_eq += (key[i] != 0u && key[i] == T);
   }
-  const int written = min(tot_take, p.budget);
-  for (int s2 = written + tid; s2 < p.budget; s2 += kSelThreads) out[s2] = -1;
-  if (tid == 0) p.sel_count[(size_t)b * p.hkv + kvh] = written;
+  int pos_gt, pos_eq;
+  winner_scan(n_gt, n_eq, &pos_gt, &pos_eq, scan_smem);
+  int32_t* out = p.sel + grp * p.budget;
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) {
+    if (key[i] == 0u || k == 0) continue;
+    bool tk;
+    int at;
+    if (key[i] > T) {
+      tk = true;
+      at = pos_gt + min(pos_eq, rem);
+      ++pos_gt;
+    } else if (key[i] == T) {
+      tk = pos_eq < rem;
+      at = pos_gt + pos_eq;
+      ++pos_eq;
+    } else {
+      tk = false;
+      at = 0;
+    }
+    if (tk && at < p.budget) out[at] = gi[c0 + i];
+  }
+  for (int s2 = k + tid; s2 < p.budget; s2 += kSelThreads) out[s2] = -1;
+  if (tid == 0) p.sel_count[grp] = k;
 }
 
 // Stage 2 for candidate lists longer than kSelThreads * 32: the same steps with the
@@ -283,27 +343,28 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_big_kernel(SelParams
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   __shared__ int hist[2][256];
-  __shared__ int sh[2][2];
-  __shared__ int scan_smem[kSelThreads / 64 + 1];
+  __shared__ int sh[2][4];
+  __shared__ uint32_t red_smem[3 * (kSelThreads / 64)];
+  __shared__ int scan_smem[kSelThreads / 64];
   const int n_cand = p.n_chunks * p.slots;
-  const size_t gbase = ((size_t)b * p.hkv + kvh) * (size_t)n_cand;
-  const uint32_t* gk = p.cand_key + gbase;
-  const int32_t* gi = p.cand_idx + gbase;
+  const size_t grp = (size_t)b * p.hkv + kvh;
+  const uint32_t* gk = p.cand_key + grp * (size_t)n_cand;
+  const int32_t* gi = p.cand_idx + grp * (size_t)n_cand;
   const int per = (n_cand + kSelThreads - 1) / kSelThreads;
   const int c0 = min(n_cand, tid * per), c1 = min(n_cand, c0 + per);
+  auto kread = [&](int c) -> uint32_t { return gk[c]; };
   int nv = 0;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   for (int c = c0; c < c1; ++c) {
-    const uint32_t kk = gk[c];
+    const uint32_t kk = kread(c);
     if (kk != 0u) {
       ++nv;
       kmin = min(kmin, kk);
       kmax = max(kmax, kk);
     }
   }
-  int total_valid;
-  (void)block_exclusive_scan<kSelThreads>(nv, &total_valid, scan_smem);
-  block_minmax<kSelThreads>(kmin, kmax, scan_smem);
+  int total_valid = nv;
+  block_sum_minmax<kSelThreads>(total_valid, kmin, kmax, red_smem);
   const int k = min(p.budget, total_valid);
   const bool all = (k >= total_valid);
   uint32_t T = 0u;
@@ -313,61 +374,55 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_big_kernel(SelParams
         [&](auto f) {
           for (int i = 0; i < per; ++i) {
             const int c = c0 + i;
-            const uint32_t kk = (c < c1) ? gk[c] : 0u;
+            const uint32_t kk = (c < c1) ? kread(c) : 0u;
             f(kk, kk != 0u);
           }
         },
         k, kmin, kmax, hist, sh, &T, &rem);
-  int neq = 0;
+  int n_gt = 0, n_eq = 0;
   for (int c = c0; c < c1; ++c) {
-    const uint32_t kk = gk[c];
-    neq += (!all && kk != 0u && kk == T);
+    const uint32_t kk = kread(c);
+    n_gt += (kk != 0u && kk > T);
+    n_eq += (kk != 0u && kk == T);
   }
-  int tot_eq;
-  const int eq_before = block_exclusive_scan<kSelThreads>(neq, &tot_eq, scan_smem);
-  auto winner = [&](uint32_t kk, int& eqr) -> bool {
-    if (kk == 0u || k == 0) return false;
-    if (all || kk > T) return true;
-    if (kk == T) return eqr++ < rem;
-    return false;
-  };
-  int ntake = 0;
-  {
-    int eqr = eq_before;
-    for (int c = c0; c < c1; ++c) ntake += winner(gk[c], eqr);
-  }
-  int tot_take;
-  int pos = block_exclusive_scan<kSelThreads>(ntake, &tot_take, scan_smem);
-  int32_t* out = p.sel + ((size_t)b * p.hkv + kvh) * p.budget;
-  {
-    int eqr = eq_before;
-    for (int c = c0; c < c1; ++c)
-      if (winner(gk[c], eqr)) {
-        if (pos < p.budget) out[pos] = gi[c];
-        ++pos;
+  // candidate lists here may exceed 2^16 entries: two separate scans
+  int tot;
+  int pos_gt = block_exclusive_scan<kSelThreads>(n_gt, &tot, scan_smem);
+  int pos_eq = block_exclusive_scan<kSelThreads>(n_eq, &tot, scan_smem);
+  int32_t* out = p.sel + grp * p.budget;
+  if (k > 0)
+    for (int c = c0; c < c1; ++c) {
+      const uint32_t kk = kread(c);
+      if (kk == 0u) continue;
+      if (kk > T) {
+        const int at = pos_gt + min(pos_eq, rem);
+        if (at < p.budget) out[at] = gi[c];
+        ++pos_gt;
+      } else if (kk == T) {
+        if (pos_eq < rem && pos_gt + pos_eq < p.budget) out[pos_gt + pos_eq] = gi[c];
+        ++pos_eq;
       }
-  }
-  const int written = min(tot_take, p.budget);
-  for (int s2 = written + tid; s2 < p.budget; s2 += kSelThreads) out[s2] = -1;
-  if (tid == 0) p.sel_count[(size_t)b * p.hkv + kvh] = written;
+    }
+  for (int s2 = k + tid; s2 < p.budget; s2 += kSelThreads) out[s2] = -1;
+  if (tid == 0) p.sel_count[grp] = k;
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) {
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
   const int n_fin = seq / kB;
 
-  __shared__ float L2[kG];
-  __shared__ float2 wpart[kSelThreads / 64];
   __shared__ int hist[2][256];
-  __shared__ int sh[2][2];
-  __shared__ int scan_smem[kSelThreads / 64 + 1];
+  __shared__ int sh[2][4];
+  __shared__ uint32_t red_smem[3 * (kSelThreads / 64)];
+  __shared__ int scan_smem[kSelThreads / 64];
 
-  // scores of this thread's pages: 4 x kPerThread loads (clamped in-bounds
-  // index), issued before the normalizer so that both are in flight together
+  // scores of this thread's pages (clamped in-bounds index) and the group's
+  // per-head normalizers
   const int jbase = chunk * kSelChunk + kPerThread * tid;
   float sv[kG][kPerThread];
+  float l2[kG];
   {
     const int jmax = max(n_fin - 1, 0);
 #pragma unroll
@@ -375,59 +430,23 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
       const float* s = p.page_lse + ((size_t)b * p.hq + kvh * kG + hh) * p.max_pages;
 #pragma unroll
       for (int t = 0; t < kPerThread; ++t) sv[hh][t] = s[min(jbase + t, jmax)];
+      l2[hh] = p.head_l2[(size_t)b * p.hq + kvh * kG + hh];
     }
   }
 
-  // per-head normalizer from the scoring partials: waves 4h..4h+3 merge head
-  // h's partials, 16 independent loads per lane per round
-  {
-    constexpr int kWavesPerHead = kSelThreads / 64 / kG;
-    constexpr int kU = 16;
-    const int hh = wave / kWavesPerHead, part = wave % kWavesPerHead;
-    const float2* pp = p.partials + ((size_t)b * p.hq + kvh * kG + hh) * p.n_partials;
-    float m = -INFINITY, s = 0.f;
-    for (int c0 = part * 64 + lane; c0 < p.n_partials; c0 += kU * kWavesPerHead * 64) {
-      float2 v[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int c = c0 + kWavesPerHead * 64 * u;
-        v[u] = (c < p.n_partials) ? pp[c] : make_float2(-INFINITY, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) lse2_merge(m, s, v[u].x, v[u].y);
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-      lse2_merge(m, s, m2, s2);
-    }
-    if (lane == 0) wpart[wave] = make_float2(m, s);
-    __syncthreads();
-    if (tid < kG) {
-      float mm = -INFINITY, ss = 0.f;
-#pragma unroll
-      for (int i = 0; i < kWavesPerHead; ++i) {
-        const float2 v = wpart[tid * kWavesPerHead + i];
-        lse2_merge(mm, ss, v.x, v.y);
-      }
-      L2[tid] = (ss > 0.f) ? mm + fast_log2(ss) : -INFINITY;
-    }
-    __syncthreads();
-  }
-
-  // keys of this thread's consecutive pages
+  // keys of this thread's consecutive pages: log2 sum_h 2^(s_hj log2 e - L_h)
   uint32_t key[kPerThread];
   int nvalid = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   {
     float lm[kPerThread];
 #pragma unroll
     for (int t = 0; t < kPerThread; ++t) lm[t] = -INFINITY;
 #pragma unroll
     for (int hh = 0; hh < kG; ++hh) {
-      const float l2 = L2[hh];
 #pragma unroll
       for (int t = 0; t < kPerThread; ++t) {
-        const float a = sv[hh][t] * kLog2e - l2;
+        const float a = sv[hh][t] * kLog2e - l2[hh];
         // log2(2^lm + 2^a) without overflow
         const float hi = fmaxf(lm[t], a), lo = fminf(lm[t], a);
         lm[t] = (hi == -INFINITY) ? -INFINITY : hi + fast_log2(1.f + fast_exp2(lo - hi));
@@ -438,21 +457,17 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
       const bool ok = (jbase + t < n_fin) && (lm[t] > -INFINITY) && (lm[t] < INFINITY);
       key[t] = ok ? float_key(lm[t]) : 0u;   // 0 = absent (no finite float maps to 0)
       nvalid += ok;
+      if (ok) {
+        kmin = min(kmin, key[t]);
+        kmax = max(kmax, key[t]);
+      }
     }
   }
-  int total_valid;
-  (void)block_exclusive_scan<kSelThreads>(nvalid, &total_valid, scan_smem);
+  int total_valid = nvalid;
+  block_sum_minmax<kSelThreads>(total_valid, kmin, kmax, red_smem);
   const int kc = min(p.budget, total_valid);
 
   // radix select of the kc-th largest key
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-  for (int t = 0; t < kPerThread; ++t)
-    if (key[t] != 0u) {
-      kmin = min(kmin, key[t]);
-      kmax = max(kmax, key[t]);
-    }
-  block_minmax<kSelThreads>(kmin, kmax, scan_smem);
   uint32_t T = 0u;
   int rem = kc;
   if (kc > 0 && kc < total_valid) {
@@ -463,43 +478,38 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
         },
         kc, kmin, kmax, hist, sh, &T, &rem);
   }
-  // winners: key > T, or key == T among the first `rem` in page order
-  const bool all = (kc >= total_valid);
-  int neq = 0;
-#pragma unroll
-  for (int t = 0; t < kPerThread; ++t) neq += (!all && key[t] != 0u && key[t] == T);
-  int tot_eq;
-  int eq_before = block_exclusive_scan<kSelThreads>(neq, &tot_eq, scan_smem);
-  bool take[kPerThread];
-  int ntake = 0;
+  // winners: key > T, or key == T among the first `rem` in page order (T = 0
+  // when every valid key is kept)
+  int n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int t = 0; t < kPerThread; ++t) {
-    bool tk;
-    if (key[t] == 0u) tk = false;
-    else if (all || kc == 0) tk = all;
-    else if (key[t] > T) tk = true;
-    else if (key[t] == T) tk = (eq_before++ < rem);
-    else tk = false;
-    take[t] = tk;
-    ntake += tk;
+    n_gt += (key[t] != 0u && key[t] > T);
+    n_eq += (key[t] != 0u && key[t] == T);
   }
-  int tot_take;
-  int pos = block_exclusive_scan<kSelThreads>(ntake, &tot_take, scan_smem);
-  const size_t gbase = ((size_t)b * p.hkv + kvh) * (size_t)p.n_chunks * p.slots;
-  const size_t cbase = gbase + (size_t)chunk * p.slots;
+  int pos_gt, pos_eq;
+  winner_scan(n_gt, n_eq, &pos_gt, &pos_eq, scan_smem);
+  const size_t grp = (size_t)b * p.hkv + kvh;
+  const size_t cbase = (grp * (size_t)p.n_chunks + chunk) * p.slots;
 #pragma unroll
   for (int t = 0; t < kPerThread; ++t) {
-    if (take[t]) {
-      p.cand_key[cbase + pos] = key[t];
-      p.cand_idx[cbase + pos] = jbase + t;
-      ++pos;
+    if (key[t] == 0u || kc == 0) continue;
+    int at = -1;
+    if (key[t] > T) {
+      at = pos_gt + min(pos_eq, rem);
+      ++pos_gt;
+    } else if (key[t] == T) {
+      if (pos_eq < rem) at = pos_gt + pos_eq;
+      ++pos_eq;
+    }
+    if (at >= 0) {
+      p.cand_key[cbase + at] = key[t];
+      p.cand_idx[cbase + at] = jbase + t;
     }
   }
-  for (int s = tot_take + tid; s < p.slots; s += kSelThreads) {
+  for (int s = kc + tid; s < p.slots; s += kSelThreads) {
     p.cand_key[cbase + s] = 0u;
     p.cand_idx[cbase + s] = -1;
   }
-
 }
 
 }  // namespace
@@ -522,14 +532,18 @@ hipError_t launch_lse_partials(const float* page_lse, int32_t max_pages, const i
 
 hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
                          int32_t batch, int32_t hq, int32_t hkv, int32_t budget_pages,
-                         const float2* partials, int32_t n_partials, uint32_t* cand_key,
-                         int32_t* cand_idx, const SelectPlan& plan, int32_t* sel,
-                         int32_t* sel_count, hipStream_t stream) {
-  SelParams p{page_lse, seq_lens, partials, cand_key, cand_idx, sel, sel_count,
-              max_pages, hq, hkv, budget_pages, n_partials, plan.n_chunks, plan.slots};
+                         const float2* partials, int32_t n_partials, float* head_l2,
+                         uint32_t* cand_key, int32_t* cand_idx, const SelectPlan& plan, int32_t* sel, int32_t* sel_count,
+                         hipStream_t stream) {
+  hipLaunchKernelGGL(head_lse_kernel, dim3(batch * hq), dim3(kHeadThreads), 0, stream, partials,
+                     n_partials, head_l2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SelParams p{page_lse, seq_lens, head_l2, cand_key, cand_idx, sel, sel_count,
+              max_pages, hq, hkv, budget_pages, plan.n_chunks, plan.slots};
   hipLaunchKernelGGL(select_chunk_kernel, dim3(plan.n_chunks, hkv, batch), dim3(kSelThreads), 0,
                      stream, p);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int per = (plan.n_chunks * plan.slots + kSelThreads - 1) / kSelThreads;
   if (per <= 8)

@@ -259,8 +259,10 @@ def test_repeated_pages_exact_ties():
         assert list(got) == list(want), (budget, got[:10], want[:10])
 
 
-@pytest.mark.parametrize("ctx,budget", [(16 * 8192, 600), (16 * 12000 + 7, 2000)])
+@pytest.mark.parametrize("ctx,budget", [(16 * 8192, 600), (16 * 12000 + 7, 2000),
+                                        (16 * 40000 + 3, 2048)])
 def test_long_candidate_lists(ctx, budget):
-    """Selection merge paths with ~10 and >32 candidates per thread."""
+    """Selection merge paths with about 5, 12 and 40 candidates per thread
+    (the last one re-reads its candidates from memory in every pass)."""
     x = gen("tiny-4k", ctx=ctx, carriers=8)
     run_and_check(x, budget=budget, gpu_records=True)
