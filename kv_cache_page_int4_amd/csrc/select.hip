@@ -277,10 +277,13 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(SelParams p) 
   const int per = (n_cand + kSelThreads - 1) / kSelThreads;
   const int c0 = tid * per;
   uint32_t key[RUN];
+  int32_t idx[RUN];   // page ids, loaded with the keys (the output needs them last)
 #pragma unroll
   for (int i = 0; i < RUN; ++i) {
     const int c = c0 + i;
-    key[i] = (i < per && c < n_cand) ? gk[c] : 0u;
+    const bool in = i < per && c < n_cand;
+    key[i] = in ? gk[c] : 0u;
+    idx[i] = in ? gi[c] : -1;
   }
   int nv = 0;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(SelParams p) 
       tk = false;
       at = 0;
     }
-    if (tk && at < p.budget) out[at] = gi[c0 + i];
+    if (tk && at < p.budget) out[at] = idx[i];
   }
   for (int s2 = k + tid; s2 < p.budget; s2 += kSelThreads) out[s2] = -1;
   if (tid == 0) p.sel_count[grp] = k;
