@@ -30,6 +30,7 @@ METRIC = "LOCKS decode-step µs/layer + achieved HBM GB/s (% of peak), 32K–1M 
 PEAK_HBM_GBS = 8000.0                 # MI355X HBM3E
 SCORE_BYTES_PER_PAGE_HEAD = 832 + 16  # record read + 4 fp32 page LSEs written
 ATTEND_BYTES_PER_PAGE_HEAD = 8192     # 16 tokens x 128 dims x bf16, K and V
+EXACT_BYTES_PER_PAGE_HEAD = 4096 + 16 # keys of a page-head read + 4 fp32 page LSEs written
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_llama8b-1m_traffic.json")
 SCORE_SRC = os.path.join(ROOT, "kv_cache_page_int4_amd", "csrc", "score.hip")
 
@@ -50,6 +51,10 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-small", action="store_true")
     ap.add_argument("--no-build", action="store_true", help="skip the summary-build timing")
+    ap.add_argument("--no-quality", action="store_true",
+                    help="skip the read-every-key comparator and the quality report")
+    ap.add_argument("--quality-layers", type=int, default=4,
+                    help="layers sampled for the quality report")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run a plain 1 GiB copy kernel (byte-counter calibration)")
     ap.add_argument("--kernel-reps", type=int, default=3,
@@ -160,6 +165,77 @@ def cpu_baseline(w, inp, summ, budget):
                        f"{(t_sel + t_att):.2f} s, scaled x{groups} (sequences x KV heads) to one layer")}
 
 
+def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps):
+    """The read-every-key comparator and the selection quality of LOCKS
+    against it: exact page LSE from the true keys (locks_exact_page_lse),
+    the exact top-k from it (locks_select_pages), recall of the LOCKS page
+    sets, retention of the planted carrier pages by both selectors, and the
+    key-deviation energy captured by the rank-r bases (GPU builder's
+    unquantized output on sampled page-heads)."""
+    import torch
+    from kv_cache_page_int4_amd import locks as L
+
+    P = inp.block_table.shape[1]
+    lse = torch.empty((w.batch, w.hq, P), dtype=torch.float32, device="cuda")
+
+    def exact_all_layers():
+        for layer in range(w.layers):
+            L.exact_page_lse(d, inp.q[layer], inp.k[layer], inp.block_table, inp.seq_lens, lse)
+
+    exact_ms = timed(exact_all_layers, kernel_reps) / w.layers
+    page_heads = w.batch * w.hkv * w.pages
+    exact_gbs = page_heads * EXACT_BYTES_PER_PAGE_HEAD / (exact_ms * 1e-3) / 1e9
+
+    ws = torch.empty(L.score_workspace_bytes(d, w.batch, P, budget), dtype=torch.uint8,
+                     device="cuda")
+    sel_x = torch.empty((w.batch, w.hkv, budget), dtype=torch.int32, device="cuda")
+    cnt_x = torch.empty((w.batch, w.hkv), dtype=torch.int32, device="cuda")
+    layers = sorted(set(int(round(i * (w.layers - 1) / max(1, n_layers - 1)))
+                        for i in range(min(n_layers, w.layers))))
+    inter = tot = 0
+    car_locks = car_exact = car_n = 0
+    for layer in layers:
+        L.exact_page_lse(d, inp.q[layer], inp.k[layer], inp.block_table, inp.seq_lens, lse)
+        L.select_pages(d, lse, inp.seq_lens, budget, sel_x, cnt_x, ws)
+        sl = step.sel[layer].cpu().numpy()
+        cl = step.cnt[layer].cpu().numpy()
+        sx = sel_x.cpu().numpy()
+        cx = cnt_x.cpu().numpy()
+        for b in range(w.batch):
+            for g in range(w.hkv):
+                a = set(sl[b, g, :cl[b, g]].tolist())
+                e = set(sx[b, g, :cx[b, g]].tolist())
+                inter += len(a & e)
+                tot += len(e)
+        for (lay, b, g, page, _slot, _head) in inp.carriers:
+            if lay != layer:
+                continue
+            car_n += 1
+            car_locks += int(page in set(sl[b, g, :cl[b, g]].tolist()))
+            car_exact += int(page in set(sx[b, g, :cx[b, g]].tolist()))
+    # energy captured on sampled page-heads of layer 0
+    n_smp = min(w.num_blocks, 2048)
+    blocks = torch.randperm(w.num_blocks, device="cuda")[:n_smp].to(torch.int32)
+    raw = torch.empty((n_smp, w.hkv, 1280), dtype=torch.float32, device="cuda")
+    tmp = torch.empty((w.hkv, w.num_blocks, L.summary_bytes(d)), dtype=torch.uint8, device="cuda")
+    L.build_summaries(d, inp.k[0], blocks, tmp, raw_debug=raw)
+    K = inp.k[0].index_select(0, blocks.long()).float()              # [n, hkv, 16, 128]
+    X = K - raw[:, :, None, :128]
+    C = raw[:, :, 1152:].reshape(n_smp, w.hkv, 16, 8)
+    energy = float(((C * C).sum(dim=(2, 3)) / (X * X).sum(dim=(2, 3)).clamp_min(1e-30)).mean())
+    del tmp, raw, K, X
+    return {"exact_us_per_layer": round(exact_ms * 1e3, 3),
+            "exact_scorer_gbs": round(exact_gbs, 1),
+            "exact_scorer_frac": round(exact_gbs / PEAK_HBM_GBS, 4),
+            "recall_vs_exact": inter / max(tot, 1),
+            "carrier_retention_locks": car_locks / max(car_n, 1),
+            "carrier_retention_exact": car_exact / max(car_n, 1),
+            "carriers": car_n, "layers_sampled": layers,
+            "energy_captured_rank8": round(energy, 4),
+            "note": ("exact = top-k from the true-key page LSE (reads every key); recall = "
+                     "fraction of the exact page set LOCKS also selects")}
+
+
 def traffic_if_current():
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -257,6 +333,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    quality = None
+    if not args.no_quality:
+        quality = quality_report(w, d, inp, summ, step, budget, args.quality_layers,
+                                 args.kernel_reps)
+        log(f"[{w.name}] read-every-key scorer {quality['exact_us_per_layer']:.1f} us/layer = "
+            f"{quality['exact_scorer_gbs']:.0f} GB/s; recall vs exact "
+            f"{quality['recall_vs_exact']:.4f}; carriers kept: LOCKS "
+            f"{quality['carrier_retention_locks']:.3f}, exact {quality['carrier_retention_exact']:.3f}; "
+            f"energy captured {quality['energy_captured_rank8']:.3f}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, inp, summ, budget)
@@ -303,6 +389,7 @@ def main():
         "pages_scored_per_s": page_heads / (score_ms * 1e-3),
         "build_page_heads_per_s": w.layers * w.num_blocks * w.hkv / (build_ms * 1e-3),
         "cpu_baseline": cpu,
+        "quality": quality,
     }
     result.update(extra)
     if also:

@@ -164,6 +164,24 @@ locks_status locks_sparse_attend(const locks_dims* dims, const void* q, const vo
                                  float softmax_scale, void* out, float* out_lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Exact page scores from the true keys, the "read every key" comparator the
+ * pages measure LOCKS against (sec. 3 contributions: selection quality
+ * against exact page attention mass):
+ *   page_lse[b][h][j] = LSE_i ( q_h . k_ij * softmax_scale ),
+ * natural log, over the 16 tokens of each finalized logical page j.  The
+ * output has the layout of locks_score_pages', so locks_select_pages turns it
+ * into the exact top-k page set.  Reads every key of every finalized page.
+ *   k_cache       : bf16 key cache of this layer, strides `layout`.
+ *   softmax_scale : logit scale, normally 1/sqrt(d).
+ *   page_lse      : fp32 [batch][Hq][max_pages]; pages that are not finalized
+ *                   (or whose block id is out of range) get -inf.
+ * Needs no workspace. */
+locks_status locks_exact_page_lse(const locks_dims* dims, const void* q, const void* k_cache,
+                                  locks_kv_layout layout, int32_t num_blocks,
+                                  const int32_t* block_table, int32_t max_pages,
+                                  const int32_t* seq_lens, int32_t batch, float softmax_scale,
+                                  float* page_lse, void* stream);
+
 /* Human-readable name of a status code (static string, host). */
 const char* locks_status_str(locks_status status);
 

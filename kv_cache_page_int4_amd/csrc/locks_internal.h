@@ -53,6 +53,13 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k_cache, const uint1
                          float scale, float* part_o, float2* part_ml, const AttendPlan& plan,
                          uint16_t* out, float* out_lse, hipStream_t stream);
 
+// ---- exact page LSE (read-every-key comparator) ---------------------------------
+hipError_t launch_exact_lse(const uint16_t* q, const uint16_t* k_cache, int64_t block_stride,
+                            int64_t head_stride, int64_t token_stride, int32_t num_blocks,
+                            const int32_t* block_table, int32_t max_pages,
+                            const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
+                            float scale, float* page_lse, hipStream_t stream);
+
 // ---- summary build -----------------------------------------------------------
 hipError_t launch_build(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
                         int64_t token_stride, const int32_t* block_ids, int32_t n_blocks,

@@ -53,6 +53,8 @@ _SIGS = {
                                   _SZ, _P]),
     "locks_sparse_attend": (_I32, [_DP, _P, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32, _P, _P,
                                    _I32, ctypes.c_float, _P, _P, _P, _SZ, _P]),
+    "locks_exact_page_lse": (_I32, [_DP, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32,
+                                    ctypes.c_float, _P, _P]),
     "locks_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -204,3 +206,21 @@ def sparse_attend(d: Dims, q, k_cache, v_cache, block_table, seq_lens, sel, sel_
                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream))
     _check("locks_sparse_attend", st)
+
+
+def exact_page_lse(d: Dims, q, k_cache, block_table, seq_lens, page_lse, softmax_scale=None,
+                   stream=None):
+    """Exact page LSE from the keys (the read-every-key comparator); page_lse:
+    fp32 [batch, Hq, max_pages], the layout of score_pages' output."""
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(block_table, "block_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(page_lse, "page_lse", torch.float32)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / (d.head_dim ** 0.5)
+    st = lib().locks_exact_page_lse(ctypes.byref(d), _ptr(q), _ptr(k_cache), kv_layout(k_cache),
+                                    k_cache.shape[0], _ptr(block_table), block_table.shape[1],
+                                    _ptr(seq_lens), block_table.shape[0], float(softmax_scale),
+                                    _ptr(page_lse), _stream(stream))
+    _check("locks_exact_page_lse", st)

@@ -127,3 +127,30 @@ def test_status_strings():
     for st in (L.OK, L.ERR_NULL, L.ERR_SHAPE, L.ERR_UNSUPPORTED, L.ERR_WORKSPACE, L.ERR_LAUNCH):
         assert len(L.status_str(st)) > 0
     assert L.status_str(-99) == "unknown status"
+
+
+def test_exact_page_lse_validation():
+    """Bad arguments of the exact scorer are refused on the host (nothing is
+    launched, so these run without a GPU)."""
+    lib = _lib_or_skip()
+    d = L.dims(32, 8)
+    P = ctypes.c_void_p
+    lay = L.KVLayout(16384, 2048, 128)
+    ok = dict(q=P(256), k=P(256), lay=lay, nb=4, bt=P(256), mp=4, seq=P(256), batch=1,
+              scale=0.1, lse=P(256))
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.locks_exact_page_lse(ctypes.byref(a.pop("d", d)), a["q"], a["k"], a["lay"],
+                                        a["nb"], a["bt"], a["mp"], a["seq"], a["batch"],
+                                        a["scale"], a["lse"], None)
+
+    assert call(q=None) == L.ERR_NULL
+    assert call(lse=None) == L.ERR_NULL
+    assert call(batch=0) == L.ERR_SHAPE
+    assert call(nb=0) == L.ERR_SHAPE
+    assert call(scale=-1.0) == L.ERR_SHAPE
+    assert call(scale=float("nan")) == L.ERR_SHAPE
+    assert call(lay=L.KVLayout(16384, 2048, 64)) == L.ERR_SHAPE
+    assert call(k=P(264)) == L.ERR_SHAPE
+    assert call(d=L.dims(32, 8, rank=4)) == L.ERR_UNSUPPORTED
