@@ -103,6 +103,24 @@ locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
                                    int32_t n_blocks, int32_t num_blocks, void* summaries,
                                    float* raw_debug, void* stream);
 
+/* Incremental finalization inside the decode step (sec. 2 implementation:
+ * a page is summarized once, when it is finalized, off the critical path).
+ * For every sequence b whose length seq_lens[b] is a positive multiple of 16
+ * -- the newest token has just completed its page -- the summary of logical
+ * page seq_lens[b]/16 - 1 is (re)built for every KV head, exactly as
+ * locks_build_summaries would build it.  The decision is taken on the
+ * device, so the call can sit in a captured graph and be replayed every
+ * step; sequences whose tail page is partial are left untouched.
+ *   k_cache     : bf16 key cache of this layer, strides `layout`.
+ *   block_table : [batch][max_pages]; a block id outside [0, num_blocks)
+ *                 is skipped.
+ *   summaries   : this layer's records, [Hkv][num_blocks][832]. */
+locks_status locks_finalize_pages(const locks_dims* dims, const void* k_cache,
+                                  locks_kv_layout layout, int32_t num_blocks,
+                                  const int32_t* block_table, int32_t max_pages,
+                                  const int32_t* seq_lens, int32_t batch, void* summaries,
+                                  void* stream);
+
 /* Score every finalized page of every sequence from its summary alone
  * (sec. 2 reconstruction and selection, the equation for s_hat_j(q)):
  *   s_hat[b][h][j] = LSE_i ( (q_h.mu_j + (V_j^T q_h).c_i) / sqrt(d) ),

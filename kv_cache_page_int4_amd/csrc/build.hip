@@ -93,16 +93,35 @@ struct BuildSmem {
   uint32_t rec[kRec / 4];
 };
 
+// Which block a workgroup summarizes: entry blockIdx.x of a list, or (for
+// incremental finalization) the last full page of sequence blockIdx.x when
+// that sequence's length is a positive multiple of the page size -- the page
+// that the newest token just completed.
+struct BlockSource {
+  const int32_t* block_ids;    // list mode
+  const int32_t* seq_lens;     // finalize mode: [batch]
+  const int32_t* block_table;  // finalize mode: [batch][max_pages]
+  int32_t max_pages;
+  bool from_seq;
+};
+
 __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ kc, int64_t bs,
-                                                   int64_t hs, int64_t ts,
-                                                   const int32_t* __restrict__ block_ids,
+                                                   int64_t hs, int64_t ts, BlockSource src,
                                                    int32_t n_blocks, int32_t num_blocks,
                                                    int32_t hkv, uint8_t* __restrict__ summ,
                                                    float* __restrict__ raw) {
   __shared__ BuildSmem sm;
   const int lane = threadIdx.x;
   const int bi = blockIdx.x, kvh = blockIdx.y;
-  const int blk = block_ids[bi];
+  int blk;
+  if (src.from_seq) {
+    const int seq = src.seq_lens[bi];
+    const int j = seq / kB - 1;
+    blk = (seq > 0 && seq % kB == 0 && j < src.max_pages)
+              ? src.block_table[(size_t)bi * src.max_pages + j] : -1;
+  } else {
+    blk = src.block_ids[bi];
+  }
   if ((unsigned)blk >= (unsigned)num_blocks) return;   // whole workgroup, uniform
   const int t = lane & 15, g = lane >> 4;
 
@@ -343,9 +362,21 @@ hipError_t launch_build(const uint16_t* k_cache, int64_t block_stride, int64_t h
                         int32_t num_blocks, int32_t hkv, uint8_t* summaries, float* raw_debug,
                         hipStream_t stream) {
   if (n_blocks == 0) return hipSuccess;
+  BlockSource src{block_ids, nullptr, nullptr, 0, false};
   hipLaunchKernelGGL(build_kernel, dim3(n_blocks, hkv), dim3(64), 0, stream, k_cache,
-                     block_stride, head_stride, token_stride, block_ids, n_blocks, num_blocks,
+                     block_stride, head_stride, token_stride, src, n_blocks, num_blocks,
                      hkv, summaries, raw_debug);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
+                           int64_t token_stride, const int32_t* block_table, int32_t max_pages,
+                           const int32_t* seq_lens, int32_t batch, int32_t num_blocks,
+                           int32_t hkv, uint8_t* summaries, hipStream_t stream) {
+  BlockSource src{nullptr, seq_lens, block_table, max_pages, true};
+  hipLaunchKernelGGL(build_kernel, dim3(batch, hkv), dim3(64), 0, stream, k_cache, block_stride,
+                     head_stride, token_stride, src, batch, num_blocks, hkv, summaries,
+                     (float*)nullptr);
   return hipGetLastError();
 }
 

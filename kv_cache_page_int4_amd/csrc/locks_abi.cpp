@@ -194,6 +194,28 @@ locks_status locks_score_select(const locks_dims* dims, const void* q, const voi
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
 }
 
+locks_status locks_finalize_pages(const locks_dims* dims, const void* k_cache,
+                                  locks_kv_layout layout, int32_t num_blocks,
+                                  const int32_t* block_table, int32_t max_pages,
+                                  const int32_t* seq_lens, int32_t batch, void* summaries,
+                                  void* stream) {
+  locks_status st = check_dims(dims);
+  if (st != LOCKS_OK) return st;
+  if (!k_cache || !block_table || !seq_lens || !summaries) return LOCKS_ERR_NULL;
+  if (batch <= 0 || batch > 65535 || max_pages <= 0 || max_pages > kMaxPages || num_blocks <= 0)
+    return LOCKS_ERR_SHAPE;
+  if (layout.token_stride < 128 || layout.block_stride <= 0 || layout.head_stride <= 0 ||
+      (layout.token_stride % 8) || (layout.head_stride % 8) || (layout.block_stride % 8))
+    return LOCKS_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(k_cache) & 15) return LOCKS_ERR_SHAPE;
+  hipError_t e = launch_finalize(static_cast<const uint16_t*>(k_cache), layout.block_stride,
+                                 layout.head_stride, layout.token_stride, block_table, max_pages,
+                                 seq_lens, batch, num_blocks, dims->num_kv_heads,
+                                 static_cast<uint8_t*>(summaries),
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
+}
+
 locks_status locks_exact_page_lse(const locks_dims* dims, const void* q, const void* k_cache,
                                   locks_kv_layout layout, int32_t num_blocks,
                                   const int32_t* block_table, int32_t max_pages,

@@ -66,4 +66,11 @@ hipError_t launch_build(const uint16_t* k_cache, int64_t block_stride, int64_t h
                         int32_t num_blocks, int32_t hkv, uint8_t* summaries, float* raw_debug,
                         hipStream_t stream);
 
+// Incremental finalization: summarize, for every sequence whose length is a
+// positive multiple of the page size, its last full page (decided on the device).
+hipError_t launch_finalize(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
+                           int64_t token_stride, const int32_t* block_table, int32_t max_pages,
+                           const int32_t* seq_lens, int32_t batch, int32_t num_blocks,
+                           int32_t hkv, uint8_t* summaries, hipStream_t stream);
+
 }  // namespace locks

@@ -53,6 +53,7 @@ _SIGS = {
                                   _SZ, _P]),
     "locks_sparse_attend": (_I32, [_DP, _P, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32, _P, _P,
                                    _I32, ctypes.c_float, _P, _P, _P, _SZ, _P]),
+    "locks_finalize_pages": (_I32, [_DP, _P, KVLayout, _I32, _P, _I32, _P, _I32, _P, _P]),
     "locks_exact_page_lse": (_I32, [_DP, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32,
                                     ctypes.c_float, _P, _P]),
     "locks_status_str": (ctypes.c_char_p, [_I32]),
@@ -224,3 +225,17 @@ def exact_page_lse(d: Dims, q, k_cache, block_table, seq_lens, page_lse, softmax
                                     _ptr(seq_lens), block_table.shape[0], float(softmax_scale),
                                     _ptr(page_lse), _stream(stream))
     _check("locks_exact_page_lse", st)
+
+
+def finalize_pages(d: Dims, k_cache, block_table, seq_lens, summaries, stream=None):
+    """Summarize each sequence's last page when its length is a positive
+    multiple of 16 (decided on the device; graph-capturable)."""
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(block_table, "block_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(summaries, "summaries", torch.uint8)
+    st = lib().locks_finalize_pages(ctypes.byref(d), _ptr(k_cache), kv_layout(k_cache),
+                                    k_cache.shape[0], _ptr(block_table), block_table.shape[1],
+                                    _ptr(seq_lens), block_table.shape[0], _ptr(summaries),
+                                    _stream(stream))
+    _check("locks_finalize_pages", st)
