@@ -296,6 +296,14 @@ def main():
                             step.out[layer], step.ws_att)
 
     attend_ms = timed(attend_all_layers, args.kernel_reps) / w.layers
+
+    # incremental finalization as it sits at the head of a decode step: every
+    # sequence's length is a multiple of 16 here, so one launch rebuilds one
+    # page per (layer, sequence, KV head)
+    def finalize_all_layers():
+        L.finalize_pages(d, inp.k, inp.block_table, inp.seq_lens, summ)
+
+    finalize_ms = timed(finalize_all_layers, args.kernel_reps)
     att_units = int(step.cnt.sum().item()) / w.layers
     attend_gbs = att_units * ATTEND_BYTES_PER_PAGE_HEAD / (attend_ms * 1e-3) / 1e9
     log(f"[{w.name}] scorer {score_ms * 1e3:.2f} us/launch = {score_gbs:.0f} GB/s; "
@@ -385,6 +393,7 @@ def main():
         "attention": {"achieved": round(attend_gbs, 1), "unit": "GB/s",
                       "frac": round(attend_gbs / PEAK_HBM_GBS, 4),
                       "kernel_us": round(attend_ms * 1e3, 3)},
+        "finalize_us_per_step": round(finalize_ms * 1e3, 3),
         "stream_read_gbs": round(stream_read_gbs, 1),
         "pages_scored_per_s": page_heads / (score_ms * 1e-3),
         "build_page_heads_per_s": w.layers * w.num_blocks * w.hkv / (build_ms * 1e-3),

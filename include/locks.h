@@ -103,6 +103,29 @@ locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
                                    int32_t n_blocks, int32_t num_blocks, void* summaries,
                                    float* raw_debug, void* stream);
 
+/* One layer of the decode step in one call: locks_score_select followed by
+ * locks_sparse_attend (sec. 2 implementation: scoring, selection and sparse
+ * attention run back to back inside the step's graph), with outputs
+ * identical to those two calls.  The last selection stage runs inside the
+ * attention kernel when budget_pages <= 1024 and the chunk candidates number
+ * at most 8192 (contexts up to 2M tokens at budget 2048 tokens); otherwise
+ * the stages run as in the two calls.
+ *   summaries, k_cache, v_cache share the physical block numbering
+ *   (num_blocks) and the block table.
+ *   sel, sel_count : written as by locks_select_pages.
+ *   out, out_lse   : as written by locks_sparse_attend.
+ *   score_ws       : >= locks_score_workspace_bytes(dims, batch, max_pages,
+ *                    budget_pages).
+ *   attend_ws      : >= locks_attend_workspace_bytes(dims, batch,
+ *                    budget_pages + 1). */
+locks_status locks_decode_layer(const locks_dims* dims, const void* q, const void* summaries,
+                                const void* k_cache, const void* v_cache, locks_kv_layout layout,
+                                int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t batch, int32_t budget_pages,
+                                float softmax_scale, int32_t* sel, int32_t* sel_count, void* out,
+                                float* out_lse, void* score_ws, size_t score_ws_bytes,
+                                void* attend_ws, size_t attend_ws_bytes, void* stream);
+
 /* Incremental finalization inside the decode step (sec. 2 implementation:
  * a page is summarized once, when it is finalized, off the critical path).
  * For every sequence b whose length seq_lens[b] is a positive multiple of 16
@@ -110,16 +133,21 @@ locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
  * page seq_lens[b]/16 - 1 is (re)built for every KV head, exactly as
  * locks_build_summaries would build it.  The decision is taken on the
  * device, so the call can sit in a captured graph and be replayed every
- * step; sequences whose tail page is partial are left untouched.
- *   k_cache     : bf16 key cache of this layer, strides `layout`.
+ * step; sequences whose tail page is partial are left untouched.  One call
+ * serves n_layers layers at once (all their pages are built in parallel).
+ *   k_cache     : bf16 key cache of layer 0, strides `layout`; layer l
+ *                 starts k_layer_stride bf16 elements further on.
  *   block_table : [batch][max_pages]; a block id outside [0, num_blocks)
  *                 is skipped.
- *   summaries   : this layer's records, [Hkv][num_blocks][832]. */
+ *   summaries   : layer 0's records, [Hkv][num_blocks][832]; layer l starts
+ *                 summ_layer_stride bytes further on.
+ *   n_layers    : >= 1 (the strides are ignored when it is 1). */
 locks_status locks_finalize_pages(const locks_dims* dims, const void* k_cache,
                                   locks_kv_layout layout, int32_t num_blocks,
                                   const int32_t* block_table, int32_t max_pages,
                                   const int32_t* seq_lens, int32_t batch, void* summaries,
-                                  void* stream);
+                                  int32_t n_layers, int64_t k_layer_stride,
+                                  int64_t summ_layer_stride, void* stream);
 
 /* Score every finalized page of every sequence from its summary alone
  * (sec. 2 reconstruction and selection, the equation for s_hat_j(q)):

@@ -15,6 +15,7 @@
 // A second kernel merges the splits by log-sum-exp into bf16 output.
 #include "locks_device.h"
 #include "locks_internal.h"
+#include "select_common.h"
 
 namespace locks {
 
@@ -39,24 +40,19 @@ struct AttendParams {
   int32_t num_blocks, max_pages, budget, hq, hkv, pages_per_split, n_splits;
 };
 
-__global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
+// One wave's split of the attended page list of (sequence b, KV head kvh):
+// the first `count` entries of `selrow` (logical pages, ascending; nullptr
+// means pages 0..count-1) and then the partial tail page.  `selrow` may point
+// to global memory or to LDS.
+__device__ __forceinline__ void attend_wave(const AttendParams& p, int split, int kvh, int b,
+                                            int count, const int32_t* selrow) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int split = blockIdx.x * kWaves + wave;
-  const int kvh = blockIdx.y, b = blockIdx.z;
   const int row = lane >> 4, col = lane & 15, h = lane & 3;
   const int qhead0 = kvh * kG;
-
-  if (split < p.n_splits) {
+  {
     int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
     const int n_fin = seq / kB;
     const int tail = seq - n_fin * kB;
-    int count = n_fin;
-    const int32_t* selrow = nullptr;
-    if (p.sel) {
-      count = max(0, min(p.sel_count[(size_t)b * p.hkv + kvh], p.budget));
-      selrow = p.sel + ((size_t)b * p.hkv + kvh) * p.budget;
-    }
     const int n_att = count + (tail > 0 ? 1 : 0);
     const int e0 = split * p.pages_per_split;
     const int e1 = min(e0 + p.pages_per_split, n_att);
@@ -216,6 +212,116 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   }
 }
 
+__global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
+  const int split = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  if (split >= p.n_splits) return;
+  int count;
+  const int32_t* selrow = nullptr;
+  if (p.sel) {
+    count = max(0, min(p.sel_count[(size_t)b * p.hkv + kvh], p.budget));
+    selrow = p.sel + ((size_t)b * p.hkv + kvh) * p.budget;
+  } else {
+    count = max(0, min(p.seq_lens[b], p.max_pages * kB)) / kB;
+  }
+  attend_wave(p, split, kvh, b, count, selrow);
+}
+
+// ---- final selection fused with the attention --------------------------------
+// Every workgroup of a (sequence, KV head) runs the last selection stage
+// itself (the top k of that group's chunk candidates, 256 threads), keeps the
+// ascending page list in LDS and attends its splits from there: no kernel
+// boundary and no global round trip between choosing the pages and reading
+// them.  The selection is the same computation as the stand-alone stage, on
+// the same candidates in the same order, so its result is identical;
+// workgroup 0 also writes it out.
+struct FusedSel {
+  const uint32_t* cand_key;
+  const int32_t* cand_idx;
+  int32_t* sel;
+  int32_t* sel_count;
+  int32_t n_chunks, slots;
+};
+
+constexpr int kFusedThreads = 256;
+
+template <int RUN>
+__global__ __launch_bounds__(kFusedThreads) void select_attend_kernel(AttendParams p, FusedSel f) {
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  __shared__ int hist[2][256];
+  __shared__ int sh[2][4];
+  __shared__ uint32_t red_smem[3 * (kFusedThreads / 64)];
+  __shared__ int scan_smem[kFusedThreads / 64];
+  __shared__ int32_t sel_lds[kFusedMaxBudget];
+
+  const int n_cand = f.n_chunks * f.slots;
+  const size_t grp = (size_t)b * p.hkv + kvh;
+  const uint32_t* gk = f.cand_key + grp * (size_t)n_cand;
+  const int32_t* gi = f.cand_idx + grp * (size_t)n_cand;
+  const int per = (n_cand + kFusedThreads - 1) / kFusedThreads;
+  const int c0 = tid * per;
+  uint32_t key[RUN];
+  int32_t idx[RUN];
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) {
+    const int c = c0 + i;
+    const bool in = i < per && c < n_cand;
+    key[i] = in ? gk[c] : 0u;
+    idx[i] = in ? gi[c] : -1;
+  }
+  int total_valid = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < RUN; ++i)
+    if (key[i] != 0u) {
+      ++total_valid;
+      kmin = min(kmin, key[i]);
+      kmax = max(kmax, key[i]);
+    }
+  sel::block_sum_minmax<kFusedThreads>(total_valid, kmin, kmax, red_smem);
+  const int k = min(p.budget, total_valid);
+  const bool all = (k >= total_valid);
+  uint32_t T = 0u;
+  int rem = k;
+  if (k > 0 && !all)
+    sel::radix_threshold<kFusedThreads>(
+        [&](auto fn) {
+#pragma unroll
+          for (int i = 0; i < RUN; ++i) fn(key[i], key[i] != 0u);
+        },
+        k, kmin, kmax, hist, sh, &T, &rem);
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) {
+    n_gt += (key[i] != 0u && key[i] > T);
+    n_eq += (key[i] != 0u && key[i] == T);
+  }
+  int pos_gt, pos_eq;
+  sel::winner_scan<kFusedThreads>(n_gt, n_eq, &pos_gt, &pos_eq, scan_smem);
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) {
+    if (key[i] == 0u || k == 0) continue;
+    int at = -1;
+    if (key[i] > T) {
+      at = pos_gt + min(pos_eq, rem);
+      ++pos_gt;
+    } else if (key[i] == T) {
+      if (pos_eq < rem) at = pos_gt + pos_eq;
+      ++pos_eq;
+    }
+    if (at >= 0 && at < p.budget) sel_lds[at] = idx[i];
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    int32_t* out = f.sel + grp * p.budget;
+    for (int s = tid; s < p.budget; s += kFusedThreads) out[s] = (s < k) ? sel_lds[s] : -1;
+    if (tid == 0) f.sel_count[grp] = k;
+  }
+  const int split = blockIdx.x * kWaves + (tid >> 6);
+  if (split < p.n_splits) attend_wave(p, split, kvh, b, k, sel_lds);
+}
+
 // One workgroup per (sequence, query head): log-sum-exp weights of the
 // splits, then out[d] = sum_s w_s o_s[d] / sum_s w_s l_s with independent,
 // coalesced loads of the split partials.
@@ -273,6 +379,40 @@ __global__ __launch_bounds__(128) void attend_merge_kernel(AttendParams p) {
 }
 
 }  // namespace
+
+bool fused_select_attend_fits(int32_t n_cand, int32_t budget_pages) {
+  return budget_pages <= kFusedMaxBudget && n_cand <= 32 * kFusedThreads;
+}
+
+hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
+                                const uint16_t* v_cache, int64_t block_stride,
+                                int64_t head_stride, int64_t token_stride, int32_t num_blocks,
+                                const int32_t* block_table, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
+                                const uint32_t* cand_key, const int32_t* cand_idx,
+                                const SelectPlan& sp, int32_t* sel, int32_t* sel_count,
+                                int32_t budget_pages, float scale, float* part_o,
+                                float2* part_ml, const AttendPlan& plan, uint16_t* out,
+                                float* out_lse, hipStream_t stream) {
+  AttendParams p{q, k_cache, v_cache, block_stride, head_stride, token_stride, block_table,
+                 seq_lens, sel, sel_count, part_o, part_ml, out, out_lse,
+                 scale * kLog2e, num_blocks, max_pages, budget_pages, hq, hkv,
+                 plan.pages_per_split, plan.n_splits};
+  FusedSel f{cand_key, cand_idx, sel, sel_count, sp.n_chunks, sp.slots};
+  const int32_t n_cand = sp.n_chunks * sp.slots;
+  const int per = (n_cand + kFusedThreads - 1) / kFusedThreads;
+  dim3 grid((plan.n_splits + kWaves - 1) / kWaves, hkv, batch);
+  if (per <= 4)
+    hipLaunchKernelGGL(select_attend_kernel<4>, grid, dim3(kFusedThreads), 0, stream, p, f);
+  else if (per <= 16)
+    hipLaunchKernelGGL(select_attend_kernel<16>, grid, dim3(kFusedThreads), 0, stream, p, f);
+  else
+    hipLaunchKernelGGL(select_attend_kernel<32>, grid, dim3(kFusedThreads), 0, stream, p, f);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attend_merge_kernel, dim3(hq, batch), dim3(128), 0, stream, p);
+  return hipGetLastError();
+}
 
 AttendPlan plan_attend(int32_t batch, int32_t hkv, int32_t max_attended) {
   AttendPlan pl;

@@ -9,7 +9,8 @@
 //  2. Gram matrix X X^T (16x16) on the matrix cores (fp32 16x16x4);
 //  3. cyclic Jacobi on the Gram matrix in LDS: pairs (i, i^m) for m = 1..15
 //     form 8 disjoint rotations per step; each lane owns one 2x2 block of the
-//     matrix and one row-pair of the eigenvector matrix;
+//     matrix and one row-pair of the eigenvector matrix; sweeps stop once the
+//     off-diagonal mass is below 1e-12 of the total (at most 10);
 //  4. the top-8 eigenpairs (descending, ties to the lower index) give the
 //     basis v_k = X^T u_k normalized to unit length (the dual of the d x d
 //     scatter's eigenproblem), zeroed when lambda_k <= 1e-5 lambda_1 or when
@@ -103,6 +104,8 @@ struct BlockSource {
   const int32_t* block_table;  // finalize mode: [batch][max_pages]
   int32_t max_pages;
   bool from_seq;
+  int64_t k_layer_stride;      // finalize mode: layer blockIdx.z of the caches
+  int64_t summ_layer_stride;
 };
 
 __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ kc, int64_t bs,
@@ -113,6 +116,8 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
   __shared__ BuildSmem sm;
   const int lane = threadIdx.x;
   const int bi = blockIdx.x, kvh = blockIdx.y;
+  kc += (size_t)blockIdx.z * src.k_layer_stride;
+  summ += (size_t)blockIdx.z * src.summ_layer_stride;
   int blk;
   if (src.from_seq) {
     const int seq = src.seq_lens[bi];
@@ -211,6 +216,19 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
       }
       __syncthreads();
     }
+    // converged when the off-diagonal mass is below 1e-12 of the total
+    // (off-norm 1e-6 relative: far below what the codes and fp16 scales resolve)
+    float off = 0.f, tot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * lane + e, a = i >> 4, b = i & 15;
+      const float v = sm.G[a][b];
+      tot = fmaf(v, v, tot);
+      if (a != b) off = fmaf(v, v, off);
+    }
+    off = wave_sum(off);
+    tot = wave_sum(tot);
+    if (!(off > 1e-12f * tot)) break;
   }
 
   // ---- 4. order eigenpairs: descending eigenvalue, ties to the lower index ----
@@ -362,7 +380,7 @@ hipError_t launch_build(const uint16_t* k_cache, int64_t block_stride, int64_t h
                         int32_t num_blocks, int32_t hkv, uint8_t* summaries, float* raw_debug,
                         hipStream_t stream) {
   if (n_blocks == 0) return hipSuccess;
-  BlockSource src{block_ids, nullptr, nullptr, 0, false};
+  BlockSource src{block_ids, nullptr, nullptr, 0, false, 0, 0};
   hipLaunchKernelGGL(build_kernel, dim3(n_blocks, hkv), dim3(64), 0, stream, k_cache,
                      block_stride, head_stride, token_stride, src, n_blocks, num_blocks,
                      hkv, summaries, raw_debug);
@@ -372,9 +390,12 @@ hipError_t launch_build(const uint16_t* k_cache, int64_t block_stride, int64_t h
 hipError_t launch_finalize(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
                            int64_t token_stride, const int32_t* block_table, int32_t max_pages,
                            const int32_t* seq_lens, int32_t batch, int32_t num_blocks,
-                           int32_t hkv, uint8_t* summaries, hipStream_t stream) {
-  BlockSource src{nullptr, seq_lens, block_table, max_pages, true};
-  hipLaunchKernelGGL(build_kernel, dim3(batch, hkv), dim3(64), 0, stream, k_cache, block_stride,
+                           int32_t hkv, uint8_t* summaries, int32_t n_layers,
+                           int64_t k_layer_stride, int64_t summ_layer_stride,
+                           hipStream_t stream) {
+  BlockSource src{nullptr, seq_lens, block_table, max_pages, true, k_layer_stride,
+                  summ_layer_stride};
+  hipLaunchKernelGGL(build_kernel, dim3(batch, hkv, n_layers), dim3(64), 0, stream, k_cache, block_stride,
                      head_stride, token_stride, src, batch, num_blocks, hkv, summaries,
                      (float*)nullptr);
   return hipGetLastError();

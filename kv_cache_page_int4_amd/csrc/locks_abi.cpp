@@ -194,11 +194,70 @@ locks_status locks_score_select(const locks_dims* dims, const void* q, const voi
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
 }
 
+locks_status locks_decode_layer(const locks_dims* dims, const void* q, const void* summaries,
+                                const void* k_cache, const void* v_cache, locks_kv_layout layout,
+                                int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t batch, int32_t budget_pages,
+                                float softmax_scale, int32_t* sel, int32_t* sel_count, void* out,
+                                float* out_lse, void* score_ws, size_t score_ws_bytes,
+                                void* attend_ws, size_t attend_ws_bytes, void* stream) {
+  locks_status st = score_checks(dims, q, summaries, num_blocks, block_table, max_pages, seq_lens, batch);
+  if (st != LOCKS_OK) return st;
+  if (!k_cache || !v_cache || !sel || !sel_count || !out) return LOCKS_ERR_NULL;
+  if (budget_pages <= 0) return LOCKS_ERR_SHAPE;
+  if (layout.token_stride < 128 || layout.block_stride <= 0 || layout.head_stride <= 0 ||
+      (layout.token_stride % 8) || (layout.head_stride % 8) || (layout.block_stride % 8))
+    return LOCKS_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(k_cache) & 15) || (reinterpret_cast<uintptr_t>(v_cache) & 15))
+    return LOCKS_ERR_SHAPE;
+  if (!(softmax_scale > 0.f) || softmax_scale != softmax_scale) return LOCKS_ERR_SHAPE;
+  const ScoreWs w = score_ws_layout(dims, batch, max_pages, budget_pages, true);
+  if (!score_ws || score_ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  const AttendWs a = attend_ws_layout(dims, batch, budget_pages + 1);
+  if (!attend_ws || attend_ws_bytes < a.total) return LOCKS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* lse = reinterpret_cast<float*>(ws_at(score_ws, w.lse_off));
+  float2* part = reinterpret_cast<float2*>(ws_at(score_ws, w.part_off));
+  float* l2 = reinterpret_cast<float*>(ws_at(score_ws, w.l2_off));
+  uint32_t* ck = reinterpret_cast<uint32_t*>(ws_at(score_ws, w.key_off));
+  int32_t* ci = reinterpret_cast<int32_t*>(ws_at(score_ws, w.idx_off));
+  float* po = reinterpret_cast<float*>(ws_at(attend_ws, a.o_off));
+  float2* pml = reinterpret_cast<float2*>(ws_at(attend_ws, a.ml_off));
+  const int hq = dims->num_q_heads, hkv = dims->num_kv_heads;
+  hipError_t e = launch_score(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
+                              num_blocks, block_table, max_pages, seq_lens, batch, hq, hkv, lse,
+                              part, w.sp, s);
+  if (e != hipSuccess) return LOCKS_ERR_LAUNCH;
+  const int32_t n_cand = w.sel.n_chunks * w.sel.slots;
+  if (fused_select_attend_fits(n_cand, budget_pages)) {
+    e = launch_select_stage1(lse, max_pages, seq_lens, batch, hq, hkv, budget_pages, part,
+                             w.sp.n_chunks, l2, ck, ci, w.sel, s);
+    if (e == hipSuccess)
+      e = launch_select_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+                               static_cast<const uint16_t*>(v_cache), layout.block_stride,
+                               layout.head_stride, layout.token_stride, num_blocks, block_table,
+                               max_pages, seq_lens, batch, hq, hkv, ck, ci, w.sel, sel, sel_count,
+                               budget_pages, softmax_scale, po, pml, a.ap,
+                               static_cast<uint16_t*>(out), out_lse, s);
+  } else {
+    e = launch_select(lse, max_pages, seq_lens, batch, hq, hkv, budget_pages, part, w.sp.n_chunks,
+                      l2, ck, ci, w.sel, sel, sel_count, s);
+    if (e == hipSuccess)
+      e = launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+                        static_cast<const uint16_t*>(v_cache), layout.block_stride,
+                        layout.head_stride, layout.token_stride, num_blocks, block_table,
+                        max_pages, seq_lens, batch, hq, hkv, sel, sel_count, budget_pages,
+                        softmax_scale, po, pml, a.ap, static_cast<uint16_t*>(out), out_lse, s);
+  }
+  return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
+}
+
 locks_status locks_finalize_pages(const locks_dims* dims, const void* k_cache,
                                   locks_kv_layout layout, int32_t num_blocks,
                                   const int32_t* block_table, int32_t max_pages,
                                   const int32_t* seq_lens, int32_t batch, void* summaries,
-                                  void* stream) {
+                                  int32_t n_layers, int64_t k_layer_stride,
+                                  int64_t summ_layer_stride, void* stream) {
   locks_status st = check_dims(dims);
   if (st != LOCKS_OK) return st;
   if (!k_cache || !block_table || !seq_lens || !summaries) return LOCKS_ERR_NULL;
@@ -208,11 +267,14 @@ locks_status locks_finalize_pages(const locks_dims* dims, const void* k_cache,
       (layout.token_stride % 8) || (layout.head_stride % 8) || (layout.block_stride % 8))
     return LOCKS_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(k_cache) & 15) return LOCKS_ERR_SHAPE;
+  if (n_layers <= 0 || n_layers > 65535 || (n_layers > 1 && (k_layer_stride <= 0 ||
+      summ_layer_stride <= 0 || (k_layer_stride % 8) || (summ_layer_stride % 16))))
+    return LOCKS_ERR_SHAPE;
   hipError_t e = launch_finalize(static_cast<const uint16_t*>(k_cache), layout.block_stride,
                                  layout.head_stride, layout.token_stride, block_table, max_pages,
                                  seq_lens, batch, num_blocks, dims->num_kv_heads,
-                                 static_cast<uint8_t*>(summaries),
-                                 static_cast<hipStream_t>(stream));
+                                 static_cast<uint8_t*>(summaries), n_layers, k_layer_stride,
+                                 summ_layer_stride, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
 }
 

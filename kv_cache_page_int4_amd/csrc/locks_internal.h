@@ -32,6 +32,13 @@ hipError_t launch_lse_partials(const float* page_lse, int32_t max_pages, const i
                                int32_t batch, int32_t hq, float2* partials, int32_t n_chunks,
                                int32_t pages_per_chunk, hipStream_t stream);
 
+// Stage 1 only: per-head normalizers and every chunk's candidates (page order).
+hipError_t launch_select_stage1(const float* page_lse, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
+                                int32_t budget_pages, const float2* partials,
+                                int32_t n_partials, float* head_l2, uint32_t* cand_key,
+                                int32_t* cand_idx, const SelectPlan& plan, hipStream_t stream);
+
 hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
                          int32_t batch, int32_t hq, int32_t hkv, int32_t budget_pages,
                          const float2* partials, int32_t n_partials, float* head_l2,
@@ -53,6 +60,20 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k_cache, const uint1
                          float scale, float* part_o, float2* part_ml, const AttendPlan& plan,
                          uint16_t* out, float* out_lse, hipStream_t stream);
 
+// Final selection stage fused with the attention (candidates from stage 1).
+constexpr int32_t kFusedMaxBudget = 1024;
+bool fused_select_attend_fits(int32_t n_cand, int32_t budget_pages);
+hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
+                                const uint16_t* v_cache, int64_t block_stride,
+                                int64_t head_stride, int64_t token_stride, int32_t num_blocks,
+                                const int32_t* block_table, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
+                                const uint32_t* cand_key, const int32_t* cand_idx,
+                                const SelectPlan& sp, int32_t* sel, int32_t* sel_count,
+                                int32_t budget_pages, float scale, float* part_o,
+                                float2* part_ml, const AttendPlan& plan, uint16_t* out,
+                                float* out_lse, hipStream_t stream);
+
 // ---- exact page LSE (read-every-key comparator) ---------------------------------
 hipError_t launch_exact_lse(const uint16_t* q, const uint16_t* k_cache, int64_t block_stride,
                             int64_t head_stride, int64_t token_stride, int32_t num_blocks,
@@ -71,6 +92,8 @@ hipError_t launch_build(const uint16_t* k_cache, int64_t block_stride, int64_t h
 hipError_t launch_finalize(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
                            int64_t token_stride, const int32_t* block_table, int32_t max_pages,
                            const int32_t* seq_lens, int32_t batch, int32_t num_blocks,
-                           int32_t hkv, uint8_t* summaries, hipStream_t stream);
+                           int32_t hkv, uint8_t* summaries, int32_t n_layers,
+                           int64_t k_layer_stride, int64_t summ_layer_stride,
+                           hipStream_t stream);
 
 }  // namespace locks

@@ -53,7 +53,10 @@ _SIGS = {
                                   _SZ, _P]),
     "locks_sparse_attend": (_I32, [_DP, _P, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32, _P, _P,
                                    _I32, ctypes.c_float, _P, _P, _P, _SZ, _P]),
-    "locks_finalize_pages": (_I32, [_DP, _P, KVLayout, _I32, _P, _I32, _P, _I32, _P, _P]),
+    "locks_decode_layer": (_I32, [_DP, _P, _P, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32, _I32,
+                                  ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
+    "locks_finalize_pages": (_I32, [_DP, _P, KVLayout, _I32, _P, _I32, _P, _I32, _P, _I32,
+                                    ctypes.c_int64, ctypes.c_int64, _P]),
     "locks_exact_page_lse": (_I32, [_DP, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32,
                                     ctypes.c_float, _P, _P]),
     "locks_status_str": (ctypes.c_char_p, [_I32]),
@@ -229,13 +232,54 @@ def exact_page_lse(d: Dims, q, k_cache, block_table, seq_lens, page_lse, softmax
 
 def finalize_pages(d: Dims, k_cache, block_table, seq_lens, summaries, stream=None):
     """Summarize each sequence's last page when its length is a positive
-    multiple of 16 (decided on the device; graph-capturable)."""
+    multiple of 16 (decided on the device; graph-capturable).  k_cache:
+    [blocks, Hkv, 16, 128] for one layer or [layers, blocks, Hkv, 16, 128] for
+    all layers at once; summaries: [Hkv, blocks, 832] or [layers, Hkv,
+    blocks, 832] to match."""
     _need(k_cache, "k_cache", torch.bfloat16)
     _need(block_table, "block_table", torch.int32)
     _need(seq_lens, "seq_lens", torch.int32)
     _need(summaries, "summaries", torch.uint8)
-    st = lib().locks_finalize_pages(ctypes.byref(d), _ptr(k_cache), kv_layout(k_cache),
-                                    k_cache.shape[0], _ptr(block_table), block_table.shape[1],
-                                    _ptr(seq_lens), block_table.shape[0], _ptr(summaries),
+    if k_cache.dim() == 5:
+        if summaries.dim() != 4 or summaries.shape[0] != k_cache.shape[0]:
+            raise ValueError("summaries must be [layers, Hkv, blocks, 832] for a 5-d k_cache")
+        n_layers, ks, ss = k_cache.shape[0], k_cache.stride(0), summaries.stride(0)
+        k0, s0 = k_cache[0], summaries[0]
+    else:
+        n_layers, ks, ss, k0, s0 = 1, 0, 0, k_cache, summaries
+    st = lib().locks_finalize_pages(ctypes.byref(d), _ptr(k0), kv_layout(k0), k0.shape[0],
+                                    _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                    block_table.shape[0], _ptr(s0), n_layers, ks, ss,
                                     _stream(stream))
     _check("locks_finalize_pages", st)
+
+
+def decode_layer(d: Dims, q, summaries, k_cache, v_cache, block_table, seq_lens, budget_pages,
+                 sel, sel_count, out, score_ws, attend_ws, out_lse=None, softmax_scale=None,
+                 stream=None):
+    """score_select followed by sparse_attend in one call (identical outputs)."""
+    _need(q, "q", torch.bfloat16)
+    _need(summaries, "summaries", torch.uint8)
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(v_cache, "v_cache", torch.bfloat16)
+    _need(block_table, "block_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(sel, "sel", torch.int32)
+    _need(sel_count, "sel_count", torch.int32)
+    _need(out, "out", torch.bfloat16)
+    _need(out_lse, "out_lse", torch.float32)
+    lay = kv_layout(k_cache)
+    lv = kv_layout(v_cache)
+    if (lay.block_stride, lay.head_stride, lay.token_stride) != (
+            lv.block_stride, lv.head_stride, lv.token_stride):
+        raise ValueError("k_cache and v_cache must share one layout")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / (d.head_dim ** 0.5)
+    st = lib().locks_decode_layer(ctypes.byref(d), _ptr(q), _ptr(summaries), _ptr(k_cache),
+                                  _ptr(v_cache), lay, k_cache.shape[0], _ptr(block_table),
+                                  block_table.shape[1], _ptr(seq_lens), block_table.shape[0],
+                                  budget_pages, float(softmax_scale), _ptr(sel), _ptr(sel_count),
+                                  _ptr(out), _ptr(out_lse), _ptr(score_ws),
+                                  score_ws.numel() * score_ws.element_size(), _ptr(attend_ws),
+                                  attend_ws.numel() * attend_ws.element_size(), _stream(stream))
+    _check("locks_decode_layer", st)

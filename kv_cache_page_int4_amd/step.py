@@ -2,10 +2,11 @@
 
 The decode step (technical summary sec. 2, implementation paragraph: scoring,
 selection and sparse attention run inside one full graph with no Python
-dispatch) is, per layer, locks_score_select followed by locks_sparse_attend;
-with finalize=True each layer first calls locks_finalize_pages, which builds
-the summary of any page that the newest token completed (decided on the
-device, so the same graph serves every step).
+dispatch) is, per layer, locks_decode_layer (locks_score_select followed by
+locks_sparse_attend, with the last selection stage inside the attention);
+with finalize=True the step first calls locks_finalize_pages once for all
+layers, which builds the summary of any page that the newest token completed
+(decided on the device, so the same graph serves every step).
 This module only allocates the per-layer outputs and the workspaces, issues
 the library calls in order on the current stream and records them into a
 torch.cuda.CUDAGraph (a hipGraph on ROCm).  Layers run in sequence because in
@@ -22,13 +23,17 @@ class DecodeStep:
     [layers, hkv, blocks, 832]; q: bf16 [layers, batch, hq, 128];
     block_table: int32 [batch, max_pages]; seq_lens: int32 [batch].
     dense=True attends every finalized page instead (no scoring/selection);
-    finalize=True summarizes pages completed by the newest token first."""
+    finalize=True summarizes pages completed by the newest token first;
+    fused=True issues each layer as one locks_decode_layer call (the last
+    selection stage runs inside the attention kernel), fused=False as
+    locks_score_select + locks_sparse_attend."""
 
     def __init__(self, d, k, v, summaries, q, block_table, seq_lens, budget_pages, dense=False,
-                 finalize=False):
+                 finalize=False, fused=True):
         self.d, self.k, self.v, self.summ, self.q = d, k, v, summaries, q
         self.bt, self.seq, self.budget, self.dense = block_table, seq_lens, budget_pages, dense
         self.finalize = finalize
+        self.fused = fused
         n_layers, batch = q.shape[0], q.shape[1]
         P = block_table.shape[1]
         dev = q.device
@@ -48,8 +53,12 @@ class DecodeStep:
 
     def run_layer(self, layer, stream=None):
         d = self.d
-        if self.finalize:
-            L.finalize_pages(d, self.k[layer], self.bt, self.seq, self.summ[layer], stream=stream)
+        if not self.dense and self.fused:
+            L.decode_layer(d, self.q[layer], self.summ[layer], self.k[layer], self.v[layer],
+                           self.bt, self.seq, self.budget, self.sel[layer], self.cnt[layer],
+                           self.out[layer], self.ws_score, self.ws_att,
+                           out_lse=self.out_lse[layer], stream=stream)
+            return
         if not self.dense:
             L.score_select(d, self.q[layer], self.summ[layer], self.num_blocks, self.bt, self.seq,
                            self.budget, self.sel[layer], self.cnt[layer], self.ws_score,
@@ -60,6 +69,8 @@ class DecodeStep:
                         self.ws_att, out_lse=self.out_lse[layer], stream=stream)
 
     def run(self):
+        if self.finalize:   # every layer's completed pages, in one launch
+            L.finalize_pages(self.d, self.k, self.bt, self.seq, self.summ)
         for layer in range(self.layers):
             self.run_layer(layer)
 

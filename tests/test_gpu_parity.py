@@ -266,3 +266,43 @@ def test_long_candidate_lists(ctx, budget):
     (the last one re-reads its candidates from memory in every pass)."""
     x = gen("tiny-4k", ctx=ctx, carriers=8)
     run_and_check(x, budget=budget, gpu_records=True)
+
+
+# ---------------------------------------------------------------------------
+# one-call layer step: identical to score_select + sparse_attend
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,kw,budget", [
+    ("tiny-4k", {}, 32),
+    ("tiny-4k", {}, 1),
+    ("tiny-4k", {"batch": 3, "shuffled_blocks": True,
+                 "seq_lens": [4096 - 5, 16 * 37 + 9, 7]}, 32),
+    ("llama8b-32k", {}, 128),
+    ("tiny-4k", {"ctx": 16 * 8192, "carriers": 8}, 128),     # 4 chunks x 128 candidates
+    ("tiny-4k", {"ctx": 16 * 8192, "carriers": 8}, 1000),    # budget near the fused limit
+    ("tiny-4k", {"ctx": 16 * 12000 + 7, "carriers": 8}, 2000),   # budget above it: two calls
+    ("tiny-4k", {"ctx": 16 * 40000 + 3, "carriers": 8}, 512),    # 40960 candidates: two calls
+])
+def test_decode_layer_equals_two_calls(name, kw, budget):
+    from kv_cache_page_int4_amd import locks as L
+    x = gen(name, **kw)
+    w = x.w
+    lay = Layer(x, 0)
+    lay.gpu_build()
+    sel_a, cnt_a, _ = lay.score_select(budget, with_lse=False)
+    out_a, olse_a = lay.attend(sel_a, cnt_a, budget)
+    P = lay.bt.shape[1]
+    sel_b = torch.full_like(sel_a, -7)
+    cnt_b = torch.full_like(cnt_a, -7)
+    out_b = torch.empty_like(out_a)
+    olse_b = torch.empty_like(olse_a)
+    ws = torch.empty(L.score_workspace_bytes(lay.d, w.batch, P, budget), dtype=torch.uint8,
+                     device="cuda")
+    wa = L.attend_workspace(lay.d, w.batch, budget + 1)
+    L.decode_layer(lay.d, lay.q, lay.summ, lay.k, lay.v, lay.bt, lay.seq, budget, sel_b, cnt_b,
+                   out_b, ws, wa, out_lse=olse_b)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_a, sel_b) and torch.equal(cnt_a, cnt_b), "selection differs"
+    assert torch.equal(out_a, out_b), "attention output differs"
+    assert torch.equal(olse_a, olse_b), "attention LSE differs"
+    log(f"[decode_layer {name} b={w.batch} budget={budget}] identical to the two calls")
