@@ -4,24 +4,21 @@
 //
 // Split-K: the attended page list of a (sequence, KV head) -- the selected
 // pages in ascending order, then the partial tail page -- is cut into splits
-// of `pages_per_split` pages, one wave each.  The 4 query heads of the group
-// share every K/V load.
-//  * QK^T on the matrix cores: rows = the 16 tokens of a page, K = head dim,
-//    columns = the 4 heads repeated 4 times; lane l gets the logits of tokens
-//    4*(l/16) + r (r = 0..3) for head l%4.
-//  * softmax in base 2 with an online maximum per 4-page group.
-//  * P.V on the vector units: lane l keeps the same 4 tokens and 8 of the
-//    128 dims; the 4 heads' probabilities come from its quad by DPP broadcast.
-// A second kernel merges the splits by log-sum-exp into bf16 output.
+// of `pages_per_split` pages, one wave each, streamed page by page through
+// LDS (see attend_wave).  The 4 query heads of the group share every K/V
+// load.  A second kernel merges the splits by log-sum-exp into bf16 output.
 #include "locks_device.h"
 #include "locks_internal.h"
 #include "select_common.h"
+
+#include <algorithm>
 
 namespace locks {
 
 namespace {
 
 constexpr int kWaves = 4;
+constexpr long long kAttendWaves = 2048;   // target waves per launch
 
 struct AttendParams {
   const uint16_t* q;
@@ -40,137 +37,174 @@ struct AttendParams {
   int32_t num_blocks, max_pages, budget, hq, hkv, pages_per_split, n_splits;
 };
 
+// Global -> LDS copy of 16 bytes per lane: lane l writes LDS bytes
+// [lds + 16 l, +16) from sbase + voff.  M0 carries the LDS address; the
+// compiler treats M0 as reserved and these kernels have no other user of it.
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(sbase), "s"(lds)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+constexpr int kPageBytes = 2 * kB * kD * 2;   // K then V of one page-head, bf16
+constexpr int kAttRing = 2;                    // LDS page slots per wave: 1 in flight
+constexpr int kRingBytes = kAttRing * kPageBytes;
+
 // One wave's split of the attended page list of (sequence b, KV head kvh):
 // the first `count` entries of `selrow` (logical pages, ascending; nullptr
 // means pages 0..count-1) and then the partial tail page.  `selrow` may point
-// to global memory or to LDS.
+// to global memory or to LDS.  `ring` is this wave's LDS (kRingBytes).
+//
+// The split's block ids and token counts are resolved 64 pages at a time, one
+// page per lane.  Each page-head's keys and values (8 KB) are then copied straight from
+// HBM into an LDS slot with global->LDS DMA (8 instructions of 64 x 16 B),
+// one page ahead of the one being computed (the ring depth less one).  The compiler does not
+// track these copies: every page issues exactly 8, they complete in order,
+// and a wait for "at most 8n outstanding" with n younger pages issued means
+// this page has landed.  Any other memory instruction only makes it stricter.
+//  * QK^T on the matrix cores: rows = the 16 tokens, K = head dim, columns =
+//    the 4 query heads repeated 4 times; lane l gets tokens 4*(l/16)+r
+//    (r = 0..3) of head l%4.
+//  * online softmax in base 2 per page.
+//  * P.V on the vector units: lane l keeps the same 4 tokens and dims
+//    8*(l%16)..+8; the 4 heads' probabilities come from its quad by DPP.
 __device__ __forceinline__ void attend_wave(const AttendParams& p, int split, int kvh, int b,
-                                            int count, const int32_t* selrow) {
+                                            int count, const int32_t* selrow, uint8_t* ring) {
   const int lane = threadIdx.x & 63;
   const int row = lane >> 4, col = lane & 15, h = lane & 3;
   const int qhead0 = kvh * kG;
-  {
-    int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
-    const int n_fin = seq / kB;
-    const int tail = seq - n_fin * kB;
-    const int n_att = count + (tail > 0 ? 1 : 0);
-    const int e0 = split * p.pages_per_split;
-    const int e1 = min(e0 + p.pages_per_split, n_att);
+  int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
+  const int n_fin = seq / kB;
+  const int tail = seq - n_fin * kB;
+  const int n_att = count + (tail > 0 ? 1 : 0);
+  const int e0 = split * p.pages_per_split;
+  const int n = max(0, min(e0 + p.pages_per_split, n_att) - e0);
 
+  float M = -INFINITY, lsum = 0.f;
+  float acc[4][8];
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+
+  if (n > 0) {
     const uint16_t* qrow = p.q + ((size_t)b * p.hq + qhead0 + h) * kD + 32 * row;
+    uint4 qv[4];
     bf16x8 bq[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 8 * s));
-
-    const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
-    // page-group bookkeeping: base offset of each page-head and its valid tokens
-    auto locate = [&](int eg, size_t off[4], int ntok[4]) {
+    for (int s = 0; s < 4; ++s) {
+      qv[s] = *reinterpret_cast<const uint4*>(qrow + 8 * s);
+      bq[s] = as_bf16x8(qv[s]);
+    }
+    // unit u = 64 i + lane of a 4 KB half lands at LDS token u / 16, 16-byte
+    // part u % 16.  Keys are stored XOR-swizzled (part c of token t holds the
+    // key's part c ^ t), so that the 16 lanes reading one part of 16 tokens
+    // hit 16 different banks; values are stored as they are.
+    uint32_t voffk[4], voffv[4];
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int e = eg + pp;
-        int nt = 0, j = -1;
-        if (e < e1) {
-          if (e < count) {
-            j = selrow ? selrow[e] : e;
-            nt = (j >= 0 && j < n_fin) ? kB : 0;
-          } else {
-            j = n_fin;
-            nt = tail;
-          }
+    for (int i = 0; i < 4; ++i) {
+      const int u = 64 * i + lane, t = u >> 4, c = u & 15;
+      voffk[i] = (uint32_t)(t * p.ts * 2 + (c ^ t) * 16);
+      voffv[i] = (uint32_t)(t * p.ts * 2 + c * 16);
+    }
+    const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
+    const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
+    // chunks of up to 64 pages: block id and valid tokens of page
+    // e0 + c0 + lane in lane `lane`
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const int nc = min(64, n - c0);
+      int mbid = 0, mnt = 0;
+      if (lane < nc) {
+        const int e = e0 + c0 + lane;
+        int j, nt;
+        if (e < count) {
+          j = selrow ? selrow[e] : e;
+          nt = (j >= 0 && j < n_fin) ? kB : 0;
+        } else {
+          j = n_fin;
+          nt = tail;
         }
         int bid = (nt > 0) ? bt[j] : 0;
         if ((unsigned)bid >= (unsigned)p.num_blocks) {
           bid = 0;
           nt = 0;
         }
-        off[pp] = (size_t)bid * p.bs + (size_t)kvh * p.hs;
-        ntok[pp] = nt;
+        mbid = bid;
+        mnt = nt;
       }
-    };
-    auto load_k = [&](const size_t off[4], uint4 kr[4][4]) {
+      // consume the loads above here, so that the compiler's waits for them
+      // come before the first page copies are issued
+      asm volatile("" ::"v"(mbid), "v"(mnt), "v"(qv[0].x), "v"(qv[1].x), "v"(qv[2].x),
+                   "v"(qv[3].x));
+      auto issue = [&](int k) {
+        const int bid = __builtin_amdgcn_readlane(mbid, k);
+        const uint16_t* kb = p.kc + (size_t)bid * p.bs + (size_t)kvh * p.hs;
+        const uint16_t* vb = p.vc + (size_t)bid * p.bs + (size_t)kvh * p.hs;
+        const uint32_t slot = ring0 + (uint32_t)((k % kAttRing) * kPageBytes);
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const uint16_t* kp = p.kc + off[pp] + (size_t)col * p.ts + 32 * row;
+        for (int i = 0; i < 4; ++i) dma16(voffk[i], kb, __builtin_amdgcn_readfirstlane(slot + 1024 * i));
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kr[pp][s] = *reinterpret_cast<const uint4*>(kp + 8 * s);
-      }
-    };
-    auto load_v = [&](const size_t off[4], uint4 vr[4][4]) {
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vr[pp][r] = *reinterpret_cast<const uint4*>(p.vc + off[pp] + (size_t)(4 * row + r) * p.ts + 8 * col);
-    };
+        for (int i = 0; i < 4; ++i)
+          dma16(voffv[i], vb, __builtin_amdgcn_readfirstlane(slot + 4096 + 1024 * i));
+      };
 
-    float M = -INFINITY, lsum = 0.f;
-    float acc[4][8];
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
-
-    size_t off[4];
-    int ntok[4];
-    uint4 kr[4][4], vr[4][4];
-    if (e0 < e1) {
-      locate(e0, off, ntok);
-      load_k(off, kr);
-      load_v(off, vr);
-    }
-    for (int eg = e0; eg < e1; eg += 4) {
-      float S[4][4];
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
+      wait_lgkm0();   // the previous chunk's last LDS reads
+      for (int k = 0; k < kAttRing - 1 && k < nc; ++k) issue(k);
+      for (int k = 0; k < nc; ++k) {
+        // every LDS read of page k-1 has returned: its slot may be refilled
+        wait_lgkm0();
+        if (k + kAttRing - 1 < nc) issue(k + kAttRing - 1);
+        const int ahead = min(kAttRing - 1, nc - 1 - k);   // younger pages in flight
+        static_assert(kAttRing <= 4, "wait counts below cover at most 3 pages ahead");
+        if (ahead >= 3) wait_vm<24>();
+        else if (ahead == 2) wait_vm<16>();
+        else if (ahead == 1) wait_vm<8>();
+        else wait_vm<0>();
+        const uint8_t* S = ring + (k % kAttRing) * kPageBytes;
+        const int ntok = __builtin_amdgcn_readlane(mnt, k);
+        // ---- logits of tokens 4 row + r for head col % 4 ----
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) a = mfma16x16x32(as_bf16x8(kr[pp][s]), bq[s], a);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[pp][r] = (4 * row + r < ntok[pp]) ? a[r] * p.scale2 : -INFINITY;
-      }
-      // keys of the next group are fetched while this group finishes
-      size_t off_n[4];
-      int ntok_n[4];
-      const bool more = eg + 4 < e1;
-      if (more) {
-        locate(eg + 4, off_n, ntok_n);
-        load_k(off_n, kr);
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[pp][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float Mn = fmaxf(M, mx);
-      const float alpha = (Mn == -INFINITY) ? 1.f : fast_exp2(M - Mn);
-      float P[4][4];
-      float ps = 0.f;
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          P[pp][r] = (S[pp][r] == -INFINITY) ? 0.f : fast_exp2(S[pp][r] - Mn);
-          ps += P[pp][r];
+        for (int s = 0; s < 4; ++s) {
+          const uint4 kv = *reinterpret_cast<const uint4*>(S + col * 256 + 16 * ((4 * row + s) ^ col));
+          a = mfma16x16x32(as_bf16x8(kv), bq[s], a);
         }
-      lsum = lsum * alpha + ps;
-      M = Mn;
-      const float al[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha),
-                           quad_bcast<3>(alpha)};
+        float x[4];
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] *= al[hh];
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
+        for (int r = 0; r < 4; ++r) x[r] = (4 * row + r < ntok) ? a[r] * p.scale2 : -INFINITY;
+        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float Mn = fmaxf(M, mx);
+        const float alpha = (Mn == -INFINITY) ? 1.f : fast_exp2(M - Mn);
+        float P[4];
+        float ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint4 v = vr[pp][r];
+          P[r] = (x[r] == -INFINITY) ? 0.f : fast_exp2(x[r] - Mn);
+          ps += P[r];
+        }
+        lsum = lsum * alpha + ps;
+        M = Mn;
+        const float al[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha),
+                             quad_bcast<3>(alpha)};
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[hh][e] *= al[hh];
+        // ---- P.V: tokens 4 row + r, dims 8 col .. 8 col + 7, all 4 heads ----
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint4 v = *reinterpret_cast<const uint4*>(S + 4096 + (4 * row + r) * 256 + 16 * col);
           const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-          const float p0 = quad_bcast<0>(P[pp][r]), p1 = quad_bcast<1>(P[pp][r]);
-          const float p2 = quad_bcast<2>(P[pp][r]), p3 = quad_bcast<3>(P[pp][r]);
+          const float p0 = quad_bcast<0>(P[r]), p1 = quad_bcast<1>(P[r]);
+          const float p2 = quad_bcast<2>(P[r]), p3 = quad_bcast<3>(P[r]);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             acc[0][e] = fmaf(p0, vf[e], acc[0][e]);
@@ -180,40 +214,35 @@ __device__ __forceinline__ void attend_wave(const AttendParams& p, int split, in
           }
         }
       }
-      if (more) {
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          off[pp] = off_n[pp];
-          ntok[pp] = ntok_n[pp];
-        }
-        load_v(off, vr);
-      }
     }
-    // each row of lanes holds a quarter of the tokens: sum the rows
+  }
+  // each row of lanes holds a quarter of the tokens: sum the rows
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh)
+  for (int hh = 0; hh < 4; ++hh)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        acc[hh][e] += __shfl_xor(acc[hh][e], 16);
-        acc[hh][e] += __shfl_xor(acc[hh][e], 32);
-      }
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    if (row == 0) {
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        float* o = p.part_o + (((size_t)b * p.hq + qhead0 + hh) * p.n_splits + split) * kD + 8 * col;
-        *reinterpret_cast<float4*>(o) = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
-        *reinterpret_cast<float4*>(o + 4) = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
-      }
-      if (col < 4)
-        p.part_ml[((size_t)b * p.hq + qhead0 + col) * p.n_splits + split] = make_float2(M, lsum);
+    for (int e = 0; e < 8; ++e) {
+      acc[hh][e] += __shfl_xor(acc[hh][e], 16);
+      acc[hh][e] += __shfl_xor(acc[hh][e], 32);
     }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (row == 0) {
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      float* o = p.part_o + (((size_t)b * p.hq + qhead0 + hh) * p.n_splits + split) * kD + 8 * col;
+      *reinterpret_cast<float4*>(o) = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
+    }
+    if (col < 4)
+      p.part_ml[((size_t)b * p.hq + qhead0 + col) * p.n_splits + split] = make_float2(M, lsum);
   }
 }
 
-__global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
-  const int split = blockIdx.x * kWaves + (threadIdx.x >> 6);
+// One wave per workgroup: 16 KB of LDS each, so up to ten waves share a CU.
+__global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[1][kRingBytes];
+  const int wave = 0;
+  const int split = blockIdx.x;
   const int kvh = blockIdx.y, b = blockIdx.z;
   if (split >= p.n_splits) return;
   int count;
@@ -224,7 +253,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   } else {
     count = max(0, min(p.seq_lens[b], p.max_pages * kB)) / kB;
   }
-  attend_wave(p, split, kvh, b, count, selrow);
+  attend_wave(p, split, kvh, b, count, selrow, &ring[wave][0]);
 }
 
 // ---- final selection fused with the attention --------------------------------
@@ -254,6 +283,7 @@ __global__ __launch_bounds__(kFusedThreads) void select_attend_kernel(AttendPara
   __shared__ uint32_t red_smem[3 * (kFusedThreads / 64)];
   __shared__ int scan_smem[kFusedThreads / 64];
   __shared__ int32_t sel_lds[kFusedMaxBudget];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kRingBytes];
 
   const int n_cand = f.n_chunks * f.slots;
   const size_t grp = (size_t)b * p.hkv + kvh;
@@ -318,64 +348,87 @@ __global__ __launch_bounds__(kFusedThreads) void select_attend_kernel(AttendPara
     for (int s = tid; s < p.budget; s += kFusedThreads) out[s] = (s < k) ? sel_lds[s] : -1;
     if (tid == 0) f.sel_count[grp] = k;
   }
-  const int split = blockIdx.x * kWaves + (tid >> 6);
-  if (split < p.n_splits) attend_wave(p, split, kvh, b, k, sel_lds);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int split = blockIdx.x * kWaves + wave;
+  if (split < p.n_splits) attend_wave(p, split, kvh, b, k, sel_lds, &ring[wave][0]);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp weights of the
-// splits, then out[d] = sum_s w_s o_s[d] / sum_s w_s l_s with independent,
-// coalesced loads of the split partials.
+// splits, then out[d] = sum_s w_s o_s[d] / sum_s w_s l_s.  Wave v takes the
+// splits s = v (mod 4) with lane l owning dims 2l, 2l+1 (one 512 B row per
+// split per wave), eight rows in flight per wave; the four wave sums meet in
+// LDS.
 constexpr int kMergeW = 4096;
+constexpr int kMergeThreads = 256;
+constexpr int kMergeWaves = kMergeThreads / 64;
 
-__global__ __launch_bounds__(128) void attend_merge_kernel(AttendParams p) {
+__global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(AttendParams p) {
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const size_t row = (size_t)b * p.hq + h;
   const int n = p.n_splits;
   const float2* ml = p.part_ml + row * n;
   __shared__ float wsh[kMergeW];
-  __shared__ float red[2];
+  __shared__ float red[kMergeWaves];
+  __shared__ float2 accsh[kMergeWaves][64];
   float M = -INFINITY;
-  for (int s = t; s < n; s += 128) M = fmaxf(M, ml[s].x);
+  for (int s = t; s < n; s += kMergeThreads) M = fmaxf(M, ml[s].x);
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
   if (lane == 0) red[wave] = M;
   __syncthreads();
-  M = fmaxf(red[0], red[1]);
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
+  auto weight = [&](float m) { return (m == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(m - M); };
   float L = 0.f;
-  for (int s = t; s < n; s += 128) {
+  for (int s = t; s < n; s += kMergeThreads) {
     const float2 v = ml[s];
-    const float w = (v.x == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(v.x - M);
+    const float w = weight(v.x);
     if (s < kMergeW) wsh[s] = w;
     L += w * v.y;
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
   if (lane == 0) red[wave] = L;
-  __syncthreads();
-  L = red[0] + red[1];
-  const float* po = p.part_o + row * n * kD + t;
-  float acc = 0.f;
-  int s = 0;
-  for (; s + 8 <= n; s += 8) {
-    float v[8];
+  __syncthreads();   // also publishes wsh
+  L = red[0] + red[1] + red[2] + red[3];
+
+  const float2* po = reinterpret_cast<const float2*>(p.part_o + row * n * kD) + lane;
+  float2 acc = make_float2(0.f, 0.f);
+  int s = wave;
+  for (; s + 7 * kMergeWaves < n; s += 8 * kMergeWaves) {
+    float2 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = po[(size_t)(s + u) * kD];
+    for (int u = 0; u < 8; ++u) v[u] = po[(size_t)(s + u * kMergeWaves) * (kD / 2)];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int ss = s + u;
-      const float w = (ss < kMergeW) ? wsh[ss]
-                    : ((ml[ss].x == -INFINITY) ? 0.f : fast_exp2(ml[ss].x - M));
-      acc = fmaf(w, v[u], acc);
+      const int ss = s + u * kMergeWaves;
+      const float w = (ss < kMergeW) ? wsh[ss] : weight(ml[ss].x);
+      acc.x = fmaf(w, v[u].x, acc.x);
+      acc.y = fmaf(w, v[u].y, acc.y);
     }
   }
-  for (; s < n; ++s) {
-    const float w = (s < kMergeW) ? wsh[s] : ((ml[s].x == -INFINITY) ? 0.f : fast_exp2(ml[s].x - M));
-    acc = fmaf(w, po[(size_t)s * kD], acc);
+  for (; s < n; s += kMergeWaves) {
+    const float w = (s < kMergeW) ? wsh[s] : weight(ml[s].x);
+    const float2 v = po[(size_t)s * (kD / 2)];
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
   }
-  p.out[row * kD + t] = (uint16_t)f32_to_bf16((L > 0.f) ? acc / L : 0.f);
-  if (p.out_lse && t == 0) p.out_lse[row] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+  accsh[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    float2 r = accsh[0][lane];
+#pragma unroll
+    for (int v = 1; v < kMergeWaves; ++v) {
+      r.x += accsh[v][lane].x;
+      r.y += accsh[v][lane].y;
+    }
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+    const uint32_t lo = f32_to_bf16(r.x * inv), hi = f32_to_bf16(r.y * inv);
+    reinterpret_cast<uint32_t*>(p.out + row * kD)[lane] = lo | (hi << 16);
+    if (p.out_lse && lane == 0) p.out_lse[row] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+  }
 }
 
 }  // namespace
@@ -410,18 +463,19 @@ hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
     hipLaunchKernelGGL(select_attend_kernel<32>, grid, dim3(kFusedThreads), 0, stream, p, f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3(hq, batch), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL(attend_merge_kernel, dim3(hq, batch), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 AttendPlan plan_attend(int32_t batch, int32_t hkv, int32_t max_attended) {
+  // about kAttendWaves waves over all (sequence, KV head) groups (eight per
+  // CU, fewer than the ten that fit, so that no wave waits for a second
+  // round), 2 to 1024 pages each
   AttendPlan pl;
   const long long groups = (long long)batch * hkv;
-  long long per = 2048 / (groups > 0 ? groups : 1);
-  if (per < 1) per = 1;
-  long long pages = (max_attended + per - 1) / per;
-  pages = ((pages + 3) / 4) * 4;
-  if (pages < 4) pages = 4;
+  const long long total = groups * (long long)max_attended;
+  long long pages = (total + kAttendWaves - 1) / kAttendWaves;
+  pages = std::max(2LL, std::min(1024LL, pages));
   pl.pages_per_split = (int32_t)pages;
   pl.n_splits = (int32_t)((max_attended + pages - 1) / pages);
   if (pl.n_splits < 1) pl.n_splits = 1;
@@ -439,11 +493,11 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k_cache, const uint1
                  seq_lens, sel, sel_count, part_o, part_ml, out, out_lse,
                  scale * kLog2e, num_blocks, max_pages, budget_pages, hq, hkv,
                  plan.pages_per_split, plan.n_splits};
-  dim3 grid((plan.n_splits + kWaves - 1) / kWaves, hkv, batch);
-  hipLaunchKernelGGL(attend_kernel, grid, dim3(256), 0, stream, p);
+  dim3 grid(plan.n_splits, hkv, batch);
+  hipLaunchKernelGGL(attend_kernel, grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3(hq, batch), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL(attend_merge_kernel, dim3(hq, batch), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -47,7 +47,7 @@ hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t
 
 // ---- sparse attention ---------------------------------------------------------
 struct AttendPlan {
-  int32_t pages_per_split;  // multiple of 4
+  int32_t pages_per_split;  // 2 .. 64
   int32_t n_splits;         // splits per (sequence, KV head)
 };
 AttendPlan plan_attend(int32_t batch, int32_t hkv, int32_t max_attended);

@@ -119,6 +119,26 @@ def test_dense_attention_matches_oracle():
     assert np.abs(olse[0].cpu().numpy() - l_ref).max() <= 1e-3
 
 
+def test_dense_attention_long_splits():
+    """A block table wide enough that a split spans more than 64 pages (the
+    page list is walked in chunks of 64): dense attention over a short
+    sequence in such a table still matches the oracle."""
+    x = gen("tiny-4k", seq_lens=[16 * 150 + 5])
+    lay = Layer(x, 0)
+    wide = np.full((1, 2560 * 68), -1, dtype=np.int32)
+    wide[0, :x.block_table.shape[1]] = x.block_table[0]
+    lay.bt = torch.from_numpy(wide).cuda()
+    out, olse = lay.attend(None, None, 0, dense=True)
+    torch.cuda.synchronize()
+    q = O.bf16_to_f64(x.q[0, 0])
+    o_ref, l_ref = O.sparse_attention(q, x.k_cache[0], x.v_cache[0], x.block_table[0], 0,
+                                      list(range(150)), 16 * 150 + 5)
+    e = np.abs(out[0].float().cpu().numpy() - o_ref).max()
+    log(f"[dense, 2560 x 68 table] max|dOut|={e:.2e}")
+    assert e <= OUT_TOL
+    assert np.abs(olse[0].cpu().numpy() - l_ref).max() <= 1e-3
+
+
 def test_full_budget_equals_dense_on_gpu():
     x = gen("tiny-4k")
     lay = Layer(x, 0)
