@@ -2,11 +2,12 @@
 // (LOCKS explainer, technical summary sec. 2, reconstruction and selection).
 //
 // Work split.  The pages of one (sequence, KV head) are cut into 4-page
-// steps; a launch has a fixed number W of one-wave workgroups per
-// (sequence, KV head), and workgroup w takes steps w, w + W, w + 2W, ...
-// so that at any moment the workgroups sweep neighbouring parts of the
-// summary array.  Waves are short (a few steps): many dispatch rounds keep
-// the end-of-launch tail small.
+// steps; one-wave workgroup w of a (sequence, KV head) takes the kScoreSteps
+// consecutive steps from w * kScoreSteps on.  Waves are short: many dispatch
+// rounds keep the end-of-launch tail small.  A workgroup collects its page
+// LSEs in LDS and writes each head's run of 4 * kScoreSteps pages at the end
+// as whole 64-byte pieces (one 16-byte piece per step and head, written as it
+// came, costs partial-line write-backs).
 //
 // Data movement.  The four 832-byte records of a step are copied straight
 // from HBM into a ring of LDS slots with global->LDS DMA (one 816-byte
@@ -104,6 +105,7 @@ __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_c
 
 __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kStepBytes];
+  __shared__ __attribute__((aligned(16))) float outl[kG][4 * kScoreSteps];
 
   const int lane = threadIdx.x;
   const int w = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -117,7 +119,8 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
   seq = max(0, min(seq, p.max_pages * kB));
   const int n_fin = seq / kB;
   const int nsteps = (n_fin + 3) / 4;
-  const int n = w < nsteps ? (nsteps - 1 - w) / W + 1 : 0;
+  const int s0 = w * kScoreSteps;                          // first step of this workgroup
+  const int n = max(0, min(kScoreSteps, nsteps - s0));    // its steps
 
   const uint8_t* __restrict__ summ_h = p.summ + (size_t)kvh * p.num_blocks * kRec;
   const int32_t* __restrict__ bt = p.block_table + (size_t)b * p.max_pages;
@@ -164,7 +167,7 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
     const __attribute__((address_space(4))) int32_t* btc =
         (const __attribute__((address_space(4))) int32_t*)bt;
     auto step_bids = [&](int k) -> int4 {
-      const int j0 = 4 * (w + k * W);
+      const int j0 = 4 * (s0 + k);
       const unsigned nbk = (unsigned)p.num_blocks;
       int4 v;
       if (j0 + 4 <= n_fin) {
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
 
       const uint8_t* S = &ring[k & 1][0];
       const uint8_t* Sr = S + kSlotRec * row;          // record of this lane's page
-      const int jpg = 4 * (w + k * W) + row;           // this lane's page
+      const int jpg = 4 * (s0 + k) + row;              // this lane's page
       const int bid_row = (row == 0) ? bcur.x : (row == 1) ? bcur.y : (row == 2) ? bcur.z : bcur.w;
       const bool okp = bid_row >= 0;
 
@@ -292,8 +295,26 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
       }
       const float s2 = qmu2 + lse2;
       if (tok < 4 && jpg < n_fin) {
-        lse_out[(size_t)h * p.max_pages + jpg] = okp ? s2 * kLn2 : -INFINITY;
+        outl[h][4 * k + row] = okp ? s2 * kLn2 : -INFINITY;
         if (okp) lse2_merge(pm, ps, s2, 1.f);
+      }
+    }
+  }
+
+  // ---- this workgroup's finalized pages: 4 lanes per head, 4 pages each ----
+  __syncthreads();
+  {
+    const int nval = min(4 * n, n_fin - 4 * s0);
+    const int hh = lane >> 2, part = lane & 3;
+    float* dst = lse_out + (size_t)hh * p.max_pages + 4 * s0 + 4 * part;
+    const bool vec = (p.max_pages & 3) == 0 && ((uintptr_t)p.page_lse & 15) == 0;
+    if (lane < 16 && 4 * part < nval) {
+      const float4 v = *reinterpret_cast<const float4*>(&outl[hh][4 * part]);
+      if (vec && 4 * part + 4 <= nval) {
+        *reinterpret_cast<float4*>(dst) = v;
+      } else {
+        const float e[4] = {v.x, v.y, v.z, v.w};
+        for (int i = 0; i < 4 && 4 * part + i < nval; ++i) dst[i] = e[i];
       }
     }
   }
