@@ -6,9 +6,11 @@
 // kernels turn it into the exact top-k page set.
 //
 // Work split: one-wave workgroups, W per (sequence, KV head); workgroup w
-// takes pages w, w + W, w + 2W, ...  A page-head (16 x 128 bf16 = 4 KB) is
-// read by the 64 lanes as 64 contiguous bytes each (token lane%16, dims
-// 32*(lane/16)..+32), two pages ahead of the one being computed.
+// takes the kExactPages consecutive pages from w * kExactPages on, and writes
+// each head's run of page LSEs at the end as whole 64-byte pieces.  A
+// page-head (16 x 128 bf16 = 4 KB) is read by the 64 lanes as 64 contiguous
+// bytes each (token lane%16, dims 32*(lane/16)..+32), two pages ahead of the
+// one being computed.
 //  * QK^T on the matrix cores: rows = the 16 tokens, K = head dim, columns =
 //    the 4 query heads repeated 4 times; lane l gets tokens 4*(l/16)+r
 //    (r = 0..3) of head l%4.
@@ -22,6 +24,8 @@
 namespace locks {
 
 namespace {
+
+constexpr int kExactPages = 16;   // pages per workgroup
 
 struct ExactParams {
   const uint16_t* q;
@@ -44,14 +48,16 @@ __global__ __launch_bounds__(64) void exact_lse_kernel(ExactParams p) {
   int seq = p.seq_lens[b];
   seq = max(0, min(seq, p.max_pages * kB));
   const int n_fin = seq / kB;
-  const int n = w < n_fin ? (n_fin - 1 - w) / W + 1 : 0;
+  const int j0 = w * kExactPages;                          // first page of this workgroup
+  const int n = max(0, min(kExactPages, n_fin - j0));     // its pages
+  __shared__ __attribute__((aligned(16))) float outl[kG][kExactPages];
   float* __restrict__ lse_out = p.page_lse + ((size_t)b * p.hq + qhead0) * p.max_pages;
 
   // pages that are not finalized score -inf
   for (int j = n_fin + 64 * w + lane; j < p.max_pages; j += 64 * W)
 #pragma unroll
     for (int hh = 0; hh < kG; ++hh) lse_out[(size_t)hh * p.max_pages + j] = -INFINITY;
-  if (n == 0) return;
+  if (n == 0) return;   // uniform: the whole (one-wave) workgroup leaves
 
   const uint16_t* qrow = p.q + ((size_t)b * p.hq + qhead0 + h) * kD + 32 * row;
   bf16x8 bq[4];
@@ -64,7 +70,7 @@ __global__ __launch_bounds__(64) void exact_lse_kernel(ExactParams p) {
   // score dropped)
   auto bid_of = [&](int k) -> int {
     if (k >= n) return -1;
-    const int x = bt[w + k * W];
+    const int x = bt[j0 + k];
     return ((unsigned)x < (unsigned)p.num_blocks) ? x : -1;
   };
   auto load = [&](int bid, uint4 kr[4]) {
@@ -104,9 +110,20 @@ __global__ __launch_bounds__(64) void exact_lse_kernel(ExactParams p) {
               fast_exp2(x[3] - m);
     e += __shfl_xor(e, 16);
     e += __shfl_xor(e, 32);
-    if (lane < kG) {
-      const int j = w + k * W;
-      lse_out[(size_t)h * p.max_pages + j] = (bcur >= 0) ? (m + fast_log2(e)) * kLn2 : -INFINITY;
+    if (lane < kG) outl[h][k] = (bcur >= 0) ? (m + fast_log2(e)) * kLn2 : -INFINITY;
+  }
+  // 4 lanes per head, 4 pages each
+  __syncthreads();
+  const int hh = lane >> 2, part = lane & 3;
+  float* dst = lse_out + (size_t)hh * p.max_pages + j0 + 4 * part;
+  const bool vec = (p.max_pages & 3) == 0 && ((uintptr_t)p.page_lse & 15) == 0;
+  if (lane < 16 && 4 * part < n) {
+    const float4 v = *reinterpret_cast<const float4*>(&outl[hh][4 * part]);
+    if (vec && 4 * part + 4 <= n) {
+      *reinterpret_cast<float4*>(dst) = v;
+    } else {
+      const float e[4] = {v.x, v.y, v.z, v.w};
+      for (int i = 0; i < 4 && 4 * part + i < n; ++i) dst[i] = e[i];
     }
   }
 }
@@ -118,8 +135,8 @@ hipError_t launch_exact_lse(const uint16_t* q, const uint16_t* k_cache, int64_t 
                             const int32_t* block_table, int32_t max_pages,
                             const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
                             float scale, float* page_lse, hipStream_t stream) {
-  // about 16 pages per wave: many short waves keep the end-of-launch tail small
-  const int32_t W = std::max(1, (max_pages + 15) / 16);
+  // kExactPages pages per wave: many short waves keep the end-of-launch tail small
+  const int32_t W = std::max(1, (max_pages + kExactPages - 1) / kExactPages);
   ExactParams p{q, k_cache, block_stride, head_stride, token_stride, block_table, seq_lens,
                 page_lse, scale * kLog2e, num_blocks, max_pages, hq, hkv, W};
   hipLaunchKernelGGL(exact_lse_kernel, dim3(W, hkv, batch), dim3(64), 0, stream, p);
