@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the layer-wide selection-table variant")
     ap.add_argument("--no-small", action="store_true")
     ap.add_argument("--no-build", action="store_true", help="skip the summary-build timing")
     ap.add_argument("--no-quality", action="store_true",
@@ -323,6 +325,34 @@ def main():
         log(f"[{w.name}] dense {extra['dense_us_per_layer']:.2f} us/layer, "
             f"speedup {extra['speedup_vs_dense']:.2f}x")
         del dense
+
+    # variant: one selection table for the whole layer (all query heads share
+    # one page set) -- its step time and how much of each KV head's own page
+    # set it keeps
+    if not args.no_variants:
+        wide = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, inp.seq_lens, budget,
+                          n_tables=1)
+        wide_ms = time_step(wide, max(2, args.steps // 2), 1)
+        keep = []
+        for layer in range(w.layers):
+            for b in range(w.batch):
+                c1 = int(wide.cnt[layer, b, 0])
+                s1 = set(wide.sel[layer, b, 0, :c1].tolist())
+                for g in range(w.hkv):
+                    c = int(step.cnt[layer, b, g])
+                    own = set(step.sel[layer, b, g, :c].tolist())
+                    keep.append(len(own & s1) / max(len(own), 1))
+        extra["variants"] = {"layer_wide_table": {
+            "us_per_layer": round(wide_ms * 1e3 / w.layers, 3),
+            "own_pages_kept": round(sum(keep) / len(keep), 4),
+            "note": ("one table per layer over all query heads (the wider reading of the "
+                     "group-shared table); "
+                     "own_pages_kept = mean fraction of a KV head's own top-k pages that the "
+                     "layer-wide table also selects")}}
+        log(f"[{w.name}] layer-wide table {wide_ms * 1e3 / w.layers:.2f} us/layer; keeps "
+            f"{extra['variants']['layer_wide_table']['own_pages_kept']:.3f} of each KV head's "
+            f"own pages")
+        del wide
 
     # achievable streaming-read bandwidth (context for the roofline)
     from synth.device import device_read

@@ -210,6 +210,52 @@ locks_status locks_sparse_attend(const locks_dims* dims, const void* q, const vo
                                  float softmax_scale, void* out, float* out_lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Selection-table scope.  The pages average the mass shares of the query
+ * heads that share a selection table, so that they all attend the same pages
+ * (sec. 2 group-shared selection); the calls above take that table to be one
+ * per (sequence, KV head), over its G query heads.  The *_tables variants let
+ * one table serve several KV heads: n_tables tables per sequence, table t
+ * covering KV heads [t*Hkv/n_tables, (t+1)*Hkv/n_tables) and all their query
+ * heads.  n_tables = Hkv gives the calls above exactly; n_tables = 1 gives one
+ * table for the whole layer (the other reading of the shared table).
+ *   n_tables      : >= 1 and a divisor of Hkv; otherwise LOCKS_ERR_SHAPE.
+ *   sel           : int32 [batch][n_tables][budget_pages], ascending, -1 padded.
+ *   sel_count     : int32 [batch][n_tables].
+ * Every other argument, buffer size and workspace is as for the call without
+ * the suffix (the workspaces sized for Hkv tables serve any n_tables). */
+locks_status locks_select_pages_tables(const locks_dims* dims, const float* page_lse,
+                                       int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                                       int32_t budget_pages, int32_t n_tables, int32_t* sel,
+                                       int32_t* sel_count, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* Attention of every KV head's query heads over its table's selection
+ * (table kvh / (Hkv / n_tables)); sel == NULL means dense attention, as for
+ * locks_sparse_attend, whose rules apply otherwise too. */
+locks_status locks_sparse_attend_tables(const locks_dims* dims, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        locks_kv_layout layout, int32_t num_blocks,
+                                        const int32_t* block_table, int32_t max_pages,
+                                        const int32_t* seq_lens, int32_t batch,
+                                        const int32_t* sel, const int32_t* sel_count,
+                                        int32_t budget_pages, int32_t n_tables,
+                                        float softmax_scale, void* out, float* out_lse,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* locks_decode_layer with n_tables selection tables per sequence; outputs
+ * identical to locks_score_pages, locks_select_pages_tables and
+ * locks_sparse_attend_tables in a row. */
+locks_status locks_decode_layer_tables(const locks_dims* dims, const void* q,
+                                       const void* summaries, const void* k_cache,
+                                       const void* v_cache, locks_kv_layout layout,
+                                       int32_t num_blocks, const int32_t* block_table,
+                                       int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                                       int32_t budget_pages, int32_t n_tables,
+                                       float softmax_scale, int32_t* sel, int32_t* sel_count,
+                                       void* out, float* out_lse, void* score_ws,
+                                       size_t score_ws_bytes, void* attend_ws,
+                                       size_t attend_ws_bytes, void* stream);
+
 /* Exact page scores from the true keys, the "read every key" comparator the
  * pages measure LOCKS against (sec. 3 contributions: selection quality
  * against exact page attention mass):

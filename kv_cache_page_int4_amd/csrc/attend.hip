@@ -35,6 +35,7 @@ struct AttendParams {
   float* out_lse;
   float scale2;
   int32_t num_blocks, max_pages, budget, hq, hkv, pages_per_split, n_splits;
+  int32_t ntab;   // selection tables per sequence; KV head kvh reads table kvh / (hkv / ntab)
 };
 
 // Global -> LDS copy of 16 bytes per lane: lane l writes LDS bytes
@@ -248,8 +249,9 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   int count;
   const int32_t* selrow = nullptr;
   if (p.sel) {
-    count = max(0, min(p.sel_count[(size_t)b * p.hkv + kvh], p.budget));
-    selrow = p.sel + ((size_t)b * p.hkv + kvh) * p.budget;
+    const size_t tab = (size_t)b * p.ntab + kvh / (p.hkv / p.ntab);
+    count = max(0, min(p.sel_count[tab], p.budget));
+    selrow = p.sel + tab * p.budget;
   } else {
     count = max(0, min(p.seq_lens[b], p.max_pages * kB)) / kB;
   }
@@ -257,13 +259,13 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
 }
 
 // ---- final selection fused with the attention --------------------------------
-// Every workgroup of a (sequence, KV head) runs the last selection stage
-// itself (the top k of that group's chunk candidates, 256 threads), keeps the
-// ascending page list in LDS and attends its splits from there: no kernel
-// boundary and no global round trip between choosing the pages and reading
-// them.  The selection is the same computation as the stand-alone stage, on
-// the same candidates in the same order, so its result is identical;
-// workgroup 0 also writes it out.
+// Every workgroup of a (sequence, KV head) runs the last selection stage of
+// its table itself (the top k of that table's chunk candidates, 256 threads),
+// keeps the ascending page list in LDS and attends its splits from there: no
+// kernel boundary and no global round trip between choosing the pages and
+// reading them.  The selection is the same computation as the stand-alone
+// stage, on the same candidates in the same order, so its result is
+// identical; workgroup 0 of the table's first KV head also writes it out.
 struct FusedSel {
   const uint32_t* cand_key;
   const int32_t* cand_idx;
@@ -286,7 +288,8 @@ __global__ __launch_bounds__(kFusedThreads) void select_attend_kernel(AttendPara
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kRingBytes];
 
   const int n_cand = f.n_chunks * f.slots;
-  const size_t grp = (size_t)b * p.hkv + kvh;
+  const int kv_per_tab = p.hkv / p.ntab;
+  const size_t grp = (size_t)b * p.ntab + kvh / kv_per_tab;   // this KV head's table
   const uint32_t* gk = f.cand_key + grp * (size_t)n_cand;
   const int32_t* gi = f.cand_idx + grp * (size_t)n_cand;
   const int per = (n_cand + kFusedThreads - 1) / kFusedThreads;
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(kFusedThreads) void select_attend_kernel(AttendPara
     if (at >= 0 && at < p.budget) sel_lds[at] = idx[i];
   }
   __syncthreads();
-  if (blockIdx.x == 0) {
+  if (blockIdx.x == 0 && kvh % kv_per_tab == 0) {   // one writer per table
     int32_t* out = f.sel + grp * p.budget;
     for (int s = tid; s < p.budget; s += kFusedThreads) out[s] = (s < k) ? sel_lds[s] : -1;
     if (tid == 0) f.sel_count[grp] = k;
@@ -442,7 +445,7 @@ hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
                                 int64_t head_stride, int64_t token_stride, int32_t num_blocks,
                                 const int32_t* block_table, int32_t max_pages,
                                 const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
-                                const uint32_t* cand_key, const int32_t* cand_idx,
+                                int32_t ntab, const uint32_t* cand_key, const int32_t* cand_idx,
                                 const SelectPlan& sp, int32_t* sel, int32_t* sel_count,
                                 int32_t budget_pages, float scale, float* part_o,
                                 float2* part_ml, const AttendPlan& plan, uint16_t* out,
@@ -450,7 +453,7 @@ hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
   AttendParams p{q, k_cache, v_cache, block_stride, head_stride, token_stride, block_table,
                  seq_lens, sel, sel_count, part_o, part_ml, out, out_lse,
                  scale * kLog2e, num_blocks, max_pages, budget_pages, hq, hkv,
-                 plan.pages_per_split, plan.n_splits};
+                 plan.pages_per_split, plan.n_splits, ntab};
   FusedSel f{cand_key, cand_idx, sel, sel_count, sp.n_chunks, sp.slots};
   const int32_t n_cand = sp.n_chunks * sp.slots;
   const int per = (n_cand + kFusedThreads - 1) / kFusedThreads;
@@ -486,13 +489,13 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k_cache, const uint1
                          int64_t block_stride, int64_t head_stride, int64_t token_stride,
                          int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
                          const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
-                         const int32_t* sel, const int32_t* sel_count, int32_t budget_pages,
+                         int32_t ntab, const int32_t* sel, const int32_t* sel_count, int32_t budget_pages,
                          float scale, float* part_o, float2* part_ml, const AttendPlan& plan,
                          uint16_t* out, float* out_lse, hipStream_t stream) {
   AttendParams p{q, k_cache, v_cache, block_stride, head_stride, token_stride, block_table,
                  seq_lens, sel, sel_count, part_o, part_ml, out, out_lse,
                  scale * kLog2e, num_blocks, max_pages, budget_pages, hq, hkv,
-                 plan.pages_per_split, plan.n_splits};
+                 plan.pages_per_split, plan.n_splits, ntab};
   dim3 grid(plan.n_splits, hkv, batch);
   hipLaunchKernelGGL(attend_kernel, grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();

@@ -142,12 +142,14 @@ locks_status locks_score_pages(const locks_dims* dims, const void* q, const void
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
 }
 
-locks_status locks_select_pages(const locks_dims* dims, const float* page_lse, int32_t max_pages,
-                                const int32_t* seq_lens, int32_t batch, int32_t budget_pages,
-                                int32_t* sel, int32_t* sel_count, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+static locks_status select_pages_impl(const locks_dims* dims, const float* page_lse,
+                                      int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                                      int32_t budget_pages, int32_t n_tables, int32_t* sel,
+                                      int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
   locks_status st = check_dims(dims);
   if (st != LOCKS_OK) return st;
+  if (n_tables <= 0 || dims->num_kv_heads % n_tables) return LOCKS_ERR_SHAPE;
   if (!page_lse || !seq_lens || !sel || !sel_count) return LOCKS_ERR_NULL;
   if (batch <= 0 || max_pages <= 0 || max_pages > kMaxPages || budget_pages <= 0)
     return LOCKS_ERR_SHAPE;
@@ -158,13 +160,31 @@ locks_status locks_select_pages(const locks_dims* dims, const float* page_lse, i
   hipError_t e = launch_lse_partials(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, part,
                                      w.sel.n_chunks, kSelChunk, s);
   if (e == hipSuccess)
-    e = launch_select(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, dims->num_kv_heads,
+    e = launch_select(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, n_tables,
                       budget_pages, part, w.sel.n_chunks,
                       reinterpret_cast<float*>(ws_at(workspace, w.l2_off)),
                       reinterpret_cast<uint32_t*>(ws_at(workspace, w.key_off)),
                       reinterpret_cast<int32_t*>(ws_at(workspace, w.idx_off)), w.sel, sel,
                       sel_count, s);
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
+}
+
+locks_status locks_select_pages(const locks_dims* dims, const float* page_lse, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t batch, int32_t budget_pages,
+                                int32_t* sel, int32_t* sel_count, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return select_pages_impl(dims, page_lse, max_pages, seq_lens, batch, budget_pages,
+                           dims ? dims->num_kv_heads : 0, sel, sel_count, workspace,
+                           workspace_bytes, stream);
+}
+
+locks_status locks_select_pages_tables(const locks_dims* dims, const float* page_lse,
+                                       int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                                       int32_t budget_pages, int32_t n_tables, int32_t* sel,
+                                       int32_t* sel_count, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return select_pages_impl(dims, page_lse, max_pages, seq_lens, batch, budget_pages, n_tables,
+                           sel, sel_count, workspace, workspace_bytes, stream);
 }
 
 locks_status locks_score_select(const locks_dims* dims, const void* q, const void* summaries,
@@ -194,15 +214,18 @@ locks_status locks_score_select(const locks_dims* dims, const void* q, const voi
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
 }
 
-locks_status locks_decode_layer(const locks_dims* dims, const void* q, const void* summaries,
-                                const void* k_cache, const void* v_cache, locks_kv_layout layout,
-                                int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
-                                const int32_t* seq_lens, int32_t batch, int32_t budget_pages,
-                                float softmax_scale, int32_t* sel, int32_t* sel_count, void* out,
-                                float* out_lse, void* score_ws, size_t score_ws_bytes,
-                                void* attend_ws, size_t attend_ws_bytes, void* stream) {
+static locks_status decode_layer_impl(const locks_dims* dims, const void* q,
+                                      const void* summaries, const void* k_cache,
+                                      const void* v_cache, locks_kv_layout layout,
+                                      int32_t num_blocks, const int32_t* block_table,
+                                      int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                                      int32_t budget_pages, int32_t n_tables, float softmax_scale,
+                                      int32_t* sel, int32_t* sel_count, void* out, float* out_lse,
+                                      void* score_ws, size_t score_ws_bytes, void* attend_ws,
+                                      size_t attend_ws_bytes, void* stream) {
   locks_status st = score_checks(dims, q, summaries, num_blocks, block_table, max_pages, seq_lens, batch);
   if (st != LOCKS_OK) return st;
+  if (n_tables <= 0 || dims->num_kv_heads % n_tables) return LOCKS_ERR_SHAPE;
   if (!k_cache || !v_cache || !sel || !sel_count || !out) return LOCKS_ERR_NULL;
   if (budget_pages <= 0) return LOCKS_ERR_SHAPE;
   if (layout.token_stride < 128 || layout.block_stride <= 0 || layout.head_stride <= 0 ||
@@ -230,26 +253,56 @@ locks_status locks_decode_layer(const locks_dims* dims, const void* q, const voi
   if (e != hipSuccess) return LOCKS_ERR_LAUNCH;
   const int32_t n_cand = w.sel.n_chunks * w.sel.slots;
   if (fused_select_attend_fits(n_cand, budget_pages)) {
-    e = launch_select_stage1(lse, max_pages, seq_lens, batch, hq, hkv, budget_pages, part,
+    e = launch_select_stage1(lse, max_pages, seq_lens, batch, hq, n_tables, budget_pages, part,
                              w.sp.n_chunks, l2, ck, ci, w.sel, s);
     if (e == hipSuccess)
       e = launch_select_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                                static_cast<const uint16_t*>(v_cache), layout.block_stride,
                                layout.head_stride, layout.token_stride, num_blocks, block_table,
-                               max_pages, seq_lens, batch, hq, hkv, ck, ci, w.sel, sel, sel_count,
+                               max_pages, seq_lens, batch, hq, hkv, n_tables, ck, ci, w.sel, sel,
+                               sel_count,
                                budget_pages, softmax_scale, po, pml, a.ap,
                                static_cast<uint16_t*>(out), out_lse, s);
   } else {
-    e = launch_select(lse, max_pages, seq_lens, batch, hq, hkv, budget_pages, part, w.sp.n_chunks,
-                      l2, ck, ci, w.sel, sel, sel_count, s);
+    e = launch_select(lse, max_pages, seq_lens, batch, hq, n_tables, budget_pages, part,
+                      w.sp.n_chunks, l2, ck, ci, w.sel, sel, sel_count, s);
     if (e == hipSuccess)
       e = launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                         static_cast<const uint16_t*>(v_cache), layout.block_stride,
                         layout.head_stride, layout.token_stride, num_blocks, block_table,
-                        max_pages, seq_lens, batch, hq, hkv, sel, sel_count, budget_pages,
+                        max_pages, seq_lens, batch, hq, hkv, n_tables, sel, sel_count, budget_pages,
                         softmax_scale, po, pml, a.ap, static_cast<uint16_t*>(out), out_lse, s);
   }
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
+}
+
+locks_status locks_decode_layer(const locks_dims* dims, const void* q, const void* summaries,
+                                const void* k_cache, const void* v_cache, locks_kv_layout layout,
+                                int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t batch, int32_t budget_pages,
+                                float softmax_scale, int32_t* sel, int32_t* sel_count, void* out,
+                                float* out_lse, void* score_ws, size_t score_ws_bytes,
+                                void* attend_ws, size_t attend_ws_bytes, void* stream) {
+  return decode_layer_impl(dims, q, summaries, k_cache, v_cache, layout, num_blocks, block_table,
+                           max_pages, seq_lens, batch, budget_pages, dims ? dims->num_kv_heads : 0,
+                           softmax_scale, sel, sel_count, out, out_lse, score_ws, score_ws_bytes,
+                           attend_ws, attend_ws_bytes, stream);
+}
+
+locks_status locks_decode_layer_tables(const locks_dims* dims, const void* q,
+                                       const void* summaries, const void* k_cache,
+                                       const void* v_cache, locks_kv_layout layout,
+                                       int32_t num_blocks, const int32_t* block_table,
+                                       int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                                       int32_t budget_pages, int32_t n_tables,
+                                       float softmax_scale, int32_t* sel, int32_t* sel_count,
+                                       void* out, float* out_lse, void* score_ws,
+                                       size_t score_ws_bytes, void* attend_ws,
+                                       size_t attend_ws_bytes, void* stream) {
+  return decode_layer_impl(dims, q, summaries, k_cache, v_cache, layout, num_blocks, block_table,
+                           max_pages, seq_lens, batch, budget_pages, n_tables, softmax_scale, sel,
+                           sel_count, out, out_lse, score_ws, score_ws_bytes, attend_ws,
+                           attend_ws_bytes, stream);
 }
 
 locks_status locks_finalize_pages(const locks_dims* dims, const void* k_cache,
@@ -303,15 +356,18 @@ locks_status locks_exact_page_lse(const locks_dims* dims, const void* q, const v
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
 }
 
-locks_status locks_sparse_attend(const locks_dims* dims, const void* q, const void* k_cache,
-                                 const void* v_cache, locks_kv_layout layout, int32_t num_blocks,
-                                 const int32_t* block_table, int32_t max_pages,
-                                 const int32_t* seq_lens, int32_t batch, const int32_t* sel,
-                                 const int32_t* sel_count, int32_t budget_pages,
-                                 float softmax_scale, void* out, float* out_lse,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+static locks_status sparse_attend_impl(const locks_dims* dims, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       locks_kv_layout layout, int32_t num_blocks,
+                                       const int32_t* block_table, int32_t max_pages,
+                                       const int32_t* seq_lens, int32_t batch, const int32_t* sel,
+                                       const int32_t* sel_count, int32_t budget_pages,
+                                       int32_t n_tables, float softmax_scale, void* out,
+                                       float* out_lse, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
   locks_status st = check_dims(dims);
   if (st != LOCKS_OK) return st;
+  if (n_tables <= 0 || dims->num_kv_heads % n_tables) return LOCKS_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return LOCKS_ERR_NULL;
   if (sel && !sel_count) return LOCKS_ERR_NULL;
   if (batch <= 0 || batch > 65535 || max_pages <= 0 || max_pages > kMaxPages || num_blocks <= 0)
@@ -331,11 +387,38 @@ locks_status locks_sparse_attend(const locks_dims* dims, const void* q, const vo
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
       static_cast<const uint16_t*>(v_cache), layout.block_stride, layout.head_stride,
       layout.token_stride, num_blocks, block_table, max_pages, seq_lens, batch, dims->num_q_heads,
-      dims->num_kv_heads, sel, sel_count, budget_pages, softmax_scale,
+      dims->num_kv_heads, n_tables, sel, sel_count, budget_pages, softmax_scale,
       reinterpret_cast<float*>(ws_at(workspace, w.o_off)),
       reinterpret_cast<float2*>(ws_at(workspace, w.ml_off)), w.ap, static_cast<uint16_t*>(out),
       out_lse, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
+}
+
+locks_status locks_sparse_attend(const locks_dims* dims, const void* q, const void* k_cache,
+                                 const void* v_cache, locks_kv_layout layout, int32_t num_blocks,
+                                 const int32_t* block_table, int32_t max_pages,
+                                 const int32_t* seq_lens, int32_t batch, const int32_t* sel,
+                                 const int32_t* sel_count, int32_t budget_pages,
+                                 float softmax_scale, void* out, float* out_lse,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_attend_impl(dims, q, k_cache, v_cache, layout, num_blocks, block_table, max_pages,
+                            seq_lens, batch, sel, sel_count, budget_pages,
+                            dims ? dims->num_kv_heads : 0, softmax_scale, out, out_lse, workspace,
+                            workspace_bytes, stream);
+}
+
+locks_status locks_sparse_attend_tables(const locks_dims* dims, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        locks_kv_layout layout, int32_t num_blocks,
+                                        const int32_t* block_table, int32_t max_pages,
+                                        const int32_t* seq_lens, int32_t batch,
+                                        const int32_t* sel, const int32_t* sel_count,
+                                        int32_t budget_pages, int32_t n_tables,
+                                        float softmax_scale, void* out, float* out_lse,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_attend_impl(dims, q, k_cache, v_cache, layout, num_blocks, block_table, max_pages,
+                            seq_lens, batch, sel, sel_count, budget_pages, n_tables,
+                            softmax_scale, out, out_lse, workspace, workspace_bytes, stream);
 }
 
 const char* locks_status_str(locks_status status) {

@@ -32,22 +32,25 @@ hipError_t launch_lse_partials(const float* page_lse, int32_t max_pages, const i
                                int32_t batch, int32_t hq, float2* partials, int32_t n_chunks,
                                int32_t pages_per_chunk, hipStream_t stream);
 
+// Selection runs per (sequence, table): `ntab` tables per sequence, each over
+// hq / ntab query heads (ntab = hkv: one table per KV head).
+//
 // Stage 1 only: per-head normalizers and every chunk's candidates (page order).
 hipError_t launch_select_stage1(const float* page_lse, int32_t max_pages,
-                                const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
+                                const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t ntab,
                                 int32_t budget_pages, const float2* partials,
                                 int32_t n_partials, float* head_l2, uint32_t* cand_key,
                                 int32_t* cand_idx, const SelectPlan& plan, hipStream_t stream);
 
 hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
-                         int32_t batch, int32_t hq, int32_t hkv, int32_t budget_pages,
+                         int32_t batch, int32_t hq, int32_t ntab, int32_t budget_pages,
                          const float2* partials, int32_t n_partials, float* head_l2,
                          uint32_t* cand_key, int32_t* cand_idx, const SelectPlan& plan, int32_t* sel, int32_t* sel_count,
                          hipStream_t stream);
 
 // ---- sparse attention ---------------------------------------------------------
 struct AttendPlan {
-  int32_t pages_per_split;  // 2 .. 64
+  int32_t pages_per_split;  // 2 .. 1024
   int32_t n_splits;         // splits per (sequence, KV head)
 };
 AttendPlan plan_attend(int32_t batch, int32_t hkv, int32_t max_attended);
@@ -56,7 +59,8 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k_cache, const uint1
                          int64_t block_stride, int64_t head_stride, int64_t token_stride,
                          int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
                          const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
-                         const int32_t* sel, const int32_t* sel_count, int32_t budget_pages,
+                         int32_t ntab, const int32_t* sel, const int32_t* sel_count,
+                         int32_t budget_pages,
                          float scale, float* part_o, float2* part_ml, const AttendPlan& plan,
                          uint16_t* out, float* out_lse, hipStream_t stream);
 
@@ -68,7 +72,7 @@ hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
                                 int64_t head_stride, int64_t token_stride, int32_t num_blocks,
                                 const int32_t* block_table, int32_t max_pages,
                                 const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
-                                const uint32_t* cand_key, const int32_t* cand_idx,
+                                int32_t ntab, const uint32_t* cand_key, const int32_t* cand_idx,
                                 const SelectPlan& sp, int32_t* sel, int32_t* sel_count,
                                 int32_t budget_pages, float scale, float* part_o,
                                 float2* part_ml, const AttendPlan& plan, uint16_t* out,

@@ -1,7 +1,10 @@
 // Group-shared page selection (LOCKS explainer, technical summary sec. 2:
 // group-shared selection; reconstruction and selection).
 //
-// For a (sequence, KV head) with query heads h of the group:
+// For a (sequence, selection table) with query heads h of the table -- the
+// query heads of one KV head by default, or of several KV heads (one table for
+// the whole layer at the widest), the other reading of the group-shared
+// table:
 //   L_h   = LSE_j s_hat_hj                        (base-2 partials merged)
 //   log m_j = log( mean_h exp(s_hat_hj - L_h) )   (kept in the log domain so
 //                                                  tiny shares never tie at 0)
@@ -67,7 +70,8 @@ struct SelParams {
   int32_t* cand_idx;
   int32_t* sel;
   int32_t* sel_count;
-  int32_t max_pages, hq, hkv, budget, n_chunks, slots;
+  // ntab: selection tables per sequence; a table holds hq / ntab query heads
+  int32_t max_pages, hq, ntab, budget, n_chunks, slots;
 };
 
 // L_h (base 2) of every (sequence, query head) from the scorer's partials.
@@ -109,14 +113,14 @@ __global__ __launch_bounds__(kHeadThreads) void head_lse_kernel(const float2* pa
 // runs are in page order and the ordered compaction is one exclusive scan.
 template <int RUN>
 __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(SelParams p) {
-  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int tab = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   __shared__ int hist[2][256];
   __shared__ int sh[2][4];
   __shared__ uint32_t red_smem[3 * (kSelThreads / 64)];
   __shared__ int scan_smem[kSelThreads / 64];
   const int n_cand = p.n_chunks * p.slots;
-  const size_t grp = (size_t)b * p.hkv + kvh;
+  const size_t grp = (size_t)b * p.ntab + tab;
   const uint32_t* gk = p.cand_key + grp * (size_t)n_cand;
   const int32_t* gi = p.cand_idx + grp * (size_t)n_cand;
   const int per = (n_cand + kSelThreads - 1) / kSelThreads;
@@ -188,14 +192,14 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(SelParams p) 
 // Stage 2 for candidate lists longer than kSelThreads * 32: the same steps with the
 // candidates re-read from memory in every pass (correct, slower).
 __global__ __launch_bounds__(kSelThreads) void select_merge_big_kernel(SelParams p) {
-  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int tab = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   __shared__ int hist[2][256];
   __shared__ int sh[2][4];
   __shared__ uint32_t red_smem[3 * (kSelThreads / 64)];
   __shared__ int scan_smem[kSelThreads / 64];
   const int n_cand = p.n_chunks * p.slots;
-  const size_t grp = (size_t)b * p.hkv + kvh;
+  const size_t grp = (size_t)b * p.ntab + tab;
   const uint32_t* gk = p.cand_key + grp * (size_t)n_cand;
   const int32_t* gi = p.cand_idx + grp * (size_t)n_cand;
   const int per = (n_cand + kSelThreads - 1) / kSelThreads;
@@ -256,8 +260,9 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_big_kernel(SelParams
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) {
-  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int chunk = blockIdx.x, tab = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
+  const int hpt = p.hq / p.ntab;   // query heads of this table (a multiple of 4)
   int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
   const int n_fin = seq / kB;
 
@@ -266,38 +271,36 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
   __shared__ uint32_t red_smem[3 * (kSelThreads / 64)];
   __shared__ int scan_smem[kSelThreads / 64];
 
-  // scores of this thread's pages (clamped in-bounds index) and the group's
-  // per-head normalizers
-  const int jbase = chunk * kSelChunk + kPerThread * tid;
-  float sv[kG][kPerThread];
-  float l2[kG];
-  {
-    const int jmax = max(n_fin - 1, 0);
-#pragma unroll
-    for (int hh = 0; hh < kG; ++hh) {
-      const float* s = p.page_lse + ((size_t)b * p.hq + kvh * kG + hh) * p.max_pages;
-#pragma unroll
-      for (int t = 0; t < kPerThread; ++t) sv[hh][t] = s[min(jbase + t, jmax)];
-      l2[hh] = p.head_l2[(size_t)b * p.hq + kvh * kG + hh];
-    }
-  }
-
   // keys of this thread's consecutive pages: log2 sum_h 2^(s_hj log2 e - L_h)
+  // over the table's heads, four heads' scores and normalizers loaded at a time
+  const int jbase = chunk * kSelChunk + kPerThread * tid;
   uint32_t key[kPerThread];
   int nvalid = 0;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   {
+    const int jmax = max(n_fin - 1, 0);
     float lm[kPerThread];
 #pragma unroll
     for (int t = 0; t < kPerThread; ++t) lm[t] = -INFINITY;
+    for (int h0 = tab * hpt; h0 < (tab + 1) * hpt; h0 += kG) {
+      float sv[kG][kPerThread];
+      float l2[kG];
 #pragma unroll
-    for (int hh = 0; hh < kG; ++hh) {
+      for (int hh = 0; hh < kG; ++hh) {
+        const float* s = p.page_lse + ((size_t)b * p.hq + h0 + hh) * p.max_pages;
 #pragma unroll
-      for (int t = 0; t < kPerThread; ++t) {
-        const float a = sv[hh][t] * kLog2e - l2[hh];
-        // log2(2^lm + 2^a) without overflow
-        const float hi = fmaxf(lm[t], a), lo = fminf(lm[t], a);
-        lm[t] = (hi == -INFINITY) ? -INFINITY : hi + fast_log2(1.f + fast_exp2(lo - hi));
+        for (int t = 0; t < kPerThread; ++t) sv[hh][t] = s[min(jbase + t, jmax)];
+        l2[hh] = p.head_l2[(size_t)b * p.hq + h0 + hh];
+      }
+#pragma unroll
+      for (int hh = 0; hh < kG; ++hh) {
+#pragma unroll
+        for (int t = 0; t < kPerThread; ++t) {
+          const float a = sv[hh][t] * kLog2e - l2[hh];
+          // log2(2^lm + 2^a) without overflow
+          const float hi = fmaxf(lm[t], a), lo = fminf(lm[t], a);
+          lm[t] = (hi == -INFINITY) ? -INFINITY : hi + fast_log2(1.f + fast_exp2(lo - hi));
+        }
       }
     }
 #pragma unroll
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
   }
   int pos_gt, pos_eq;
   sel::winner_scan<kSelThreads>(n_gt, n_eq, &pos_gt, &pos_eq, scan_smem);
-  const size_t grp = (size_t)b * p.hkv + kvh;
+  const size_t grp = (size_t)b * p.ntab + tab;
   const size_t cbase = (grp * (size_t)p.n_chunks + chunk) * p.slots;
 #pragma unroll
   for (int t = 0; t < kPerThread; ++t) {
@@ -379,7 +382,7 @@ hipError_t launch_lse_partials(const float* page_lse, int32_t max_pages, const i
 }
 
 hipError_t launch_select_stage1(const float* page_lse, int32_t max_pages,
-                                const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
+                                const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t ntab,
                                 int32_t budget_pages, const float2* partials,
                                 int32_t n_partials, float* head_l2, uint32_t* cand_key,
                                 int32_t* cand_idx, const SelectPlan& plan, hipStream_t stream) {
@@ -388,30 +391,30 @@ hipError_t launch_select_stage1(const float* page_lse, int32_t max_pages,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SelParams p{page_lse, seq_lens, head_l2, cand_key, cand_idx, nullptr, nullptr,
-              max_pages, hq, hkv, budget_pages, plan.n_chunks, plan.slots};
-  hipLaunchKernelGGL(select_chunk_kernel, dim3(plan.n_chunks, hkv, batch), dim3(kSelThreads), 0,
+              max_pages, hq, ntab, budget_pages, plan.n_chunks, plan.slots};
+  hipLaunchKernelGGL(select_chunk_kernel, dim3(plan.n_chunks, ntab, batch), dim3(kSelThreads), 0,
                      stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
-                         int32_t batch, int32_t hq, int32_t hkv, int32_t budget_pages,
+                         int32_t batch, int32_t hq, int32_t ntab, int32_t budget_pages,
                          const float2* partials, int32_t n_partials, float* head_l2,
                          uint32_t* cand_key, int32_t* cand_idx, const SelectPlan& plan,
                          int32_t* sel, int32_t* sel_count, hipStream_t stream) {
-  hipError_t e = launch_select_stage1(page_lse, max_pages, seq_lens, batch, hq, hkv, budget_pages,
+  hipError_t e = launch_select_stage1(page_lse, max_pages, seq_lens, batch, hq, ntab, budget_pages,
                                       partials, n_partials, head_l2, cand_key, cand_idx, plan,
                                       stream);
   if (e != hipSuccess) return e;
   SelParams p{page_lse, seq_lens, head_l2, cand_key, cand_idx, sel, sel_count,
-              max_pages, hq, hkv, budget_pages, plan.n_chunks, plan.slots};
+              max_pages, hq, ntab, budget_pages, plan.n_chunks, plan.slots};
   const int per = (plan.n_chunks * plan.slots + kSelThreads - 1) / kSelThreads;
   if (per <= 8)
-    hipLaunchKernelGGL(select_merge_kernel<8>, dim3(hkv, batch), dim3(kSelThreads), 0, stream, p);
+    hipLaunchKernelGGL(select_merge_kernel<8>, dim3(ntab, batch), dim3(kSelThreads), 0, stream, p);
   else if (per <= 32)
-    hipLaunchKernelGGL(select_merge_kernel<32>, dim3(hkv, batch), dim3(kSelThreads), 0, stream, p);
+    hipLaunchKernelGGL(select_merge_kernel<32>, dim3(ntab, batch), dim3(kSelThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(select_merge_big_kernel, dim3(hkv, batch), dim3(kSelThreads), 0, stream, p);
+    hipLaunchKernelGGL(select_merge_big_kernel, dim3(ntab, batch), dim3(kSelThreads), 0, stream, p);
   return hipGetLastError();
 }
 

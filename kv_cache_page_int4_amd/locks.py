@@ -59,6 +59,13 @@ _SIGS = {
                                     ctypes.c_int64, ctypes.c_int64, _P]),
     "locks_exact_page_lse": (_I32, [_DP, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32,
                                     ctypes.c_float, _P, _P]),
+    "locks_select_pages_tables": (_I32, [_DP, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _SZ,
+                                         _P]),
+    "locks_sparse_attend_tables": (_I32, [_DP, _P, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32, _P,
+                                          _P, _I32, _I32, ctypes.c_float, _P, _P, _P, _SZ, _P]),
+    "locks_decode_layer_tables": (_I32, [_DP, _P, _P, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32,
+                                         _I32, _I32, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P,
+                                         _SZ, _P]),
     "locks_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -161,15 +168,22 @@ def score_pages(d: Dims, q, summaries, num_blocks, block_table, seq_lens, page_l
     _check("locks_score_pages", st)
 
 
-def select_pages(d: Dims, page_lse, seq_lens, budget_pages, sel, sel_count, workspace, stream=None):
+def select_pages(d: Dims, page_lse, seq_lens, budget_pages, sel, sel_count, workspace, stream=None,
+                 n_tables=None):
+    """n_tables=None: one table per KV head (sel [batch, Hkv, budget]); else
+    n_tables tables per sequence (sel [batch, n_tables, budget])."""
     _need(page_lse, "page_lse", torch.float32)
     _need(sel, "sel", torch.int32)
     _need(sel_count, "sel_count", torch.int32)
-    st = lib().locks_select_pages(ctypes.byref(d), _ptr(page_lse), page_lse.shape[-1],
-                                  _ptr(seq_lens), page_lse.shape[0], budget_pages, _ptr(sel),
-                                  _ptr(sel_count), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(stream))
-    _check("locks_select_pages", st)
+    args = [ctypes.byref(d), _ptr(page_lse), page_lse.shape[-1], _ptr(seq_lens),
+            page_lse.shape[0], budget_pages]
+    rest = [_ptr(sel), _ptr(sel_count), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream)]
+    if n_tables is None:
+        _check("locks_select_pages", lib().locks_select_pages(*args, *rest))
+    else:
+        _check("locks_select_pages_tables",
+               lib().locks_select_pages_tables(*args, int(n_tables), *rest))
 
 
 def score_select(d: Dims, q, summaries, num_blocks, block_table, seq_lens, budget_pages, sel,
@@ -188,8 +202,10 @@ def score_select(d: Dims, q, summaries, num_blocks, block_table, seq_lens, budge
 
 
 def sparse_attend(d: Dims, q, k_cache, v_cache, block_table, seq_lens, sel, sel_count,
-                  budget_pages, out, workspace, out_lse=None, softmax_scale=None, stream=None):
-    """sel=None attends every finalized page (dense attention)."""
+                  budget_pages, out, workspace, out_lse=None, softmax_scale=None, stream=None,
+                  n_tables=None):
+    """sel=None attends every finalized page (dense attention); n_tables as
+    for select_pages."""
     _need(q, "q", torch.bfloat16)
     _need(k_cache, "k_cache", torch.bfloat16)
     _need(v_cache, "v_cache", torch.bfloat16)
@@ -202,14 +218,16 @@ def sparse_attend(d: Dims, q, k_cache, v_cache, block_table, seq_lens, sel, sel_
         raise ValueError("k_cache and v_cache must share one layout")
     if softmax_scale is None:
         softmax_scale = 1.0 / (d.head_dim ** 0.5)
-    st = lib().locks_sparse_attend(ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), lay,
-                                   k_cache.shape[0], _ptr(block_table), block_table.shape[1],
-                                   _ptr(seq_lens), block_table.shape[0], _ptr(sel),
-                                   _ptr(sel_count), budget_pages if sel is not None else 0,
-                                   float(softmax_scale), _ptr(out), _ptr(out_lse),
-                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                   _stream(stream))
-    _check("locks_sparse_attend", st)
+    head = [ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), lay, k_cache.shape[0],
+            _ptr(block_table), block_table.shape[1], _ptr(seq_lens), block_table.shape[0],
+            _ptr(sel), _ptr(sel_count), budget_pages if sel is not None else 0]
+    tail = [float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream)]
+    if n_tables is None:
+        _check("locks_sparse_attend", lib().locks_sparse_attend(*head, *tail))
+    else:
+        _check("locks_sparse_attend_tables",
+               lib().locks_sparse_attend_tables(*head, int(n_tables), *tail))
 
 
 def exact_page_lse(d: Dims, q, k_cache, block_table, seq_lens, page_lse, softmax_scale=None,
@@ -256,8 +274,9 @@ def finalize_pages(d: Dims, k_cache, block_table, seq_lens, summaries, stream=No
 
 def decode_layer(d: Dims, q, summaries, k_cache, v_cache, block_table, seq_lens, budget_pages,
                  sel, sel_count, out, score_ws, attend_ws, out_lse=None, softmax_scale=None,
-                 stream=None):
-    """score_select followed by sparse_attend in one call (identical outputs)."""
+                 stream=None, n_tables=None):
+    """score_select followed by sparse_attend in one call (identical outputs);
+    n_tables as for select_pages."""
     _need(q, "q", torch.bfloat16)
     _need(summaries, "summaries", torch.uint8)
     _need(k_cache, "k_cache", torch.bfloat16)
@@ -275,11 +294,14 @@ def decode_layer(d: Dims, q, summaries, k_cache, v_cache, block_table, seq_lens,
         raise ValueError("k_cache and v_cache must share one layout")
     if softmax_scale is None:
         softmax_scale = 1.0 / (d.head_dim ** 0.5)
-    st = lib().locks_decode_layer(ctypes.byref(d), _ptr(q), _ptr(summaries), _ptr(k_cache),
-                                  _ptr(v_cache), lay, k_cache.shape[0], _ptr(block_table),
-                                  block_table.shape[1], _ptr(seq_lens), block_table.shape[0],
-                                  budget_pages, float(softmax_scale), _ptr(sel), _ptr(sel_count),
-                                  _ptr(out), _ptr(out_lse), _ptr(score_ws),
-                                  score_ws.numel() * score_ws.element_size(), _ptr(attend_ws),
-                                  attend_ws.numel() * attend_ws.element_size(), _stream(stream))
-    _check("locks_decode_layer", st)
+    head = [ctypes.byref(d), _ptr(q), _ptr(summaries), _ptr(k_cache), _ptr(v_cache), lay,
+            k_cache.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+            block_table.shape[0], budget_pages]
+    tail = [float(softmax_scale), _ptr(sel), _ptr(sel_count), _ptr(out), _ptr(out_lse),
+            _ptr(score_ws), score_ws.numel() * score_ws.element_size(), _ptr(attend_ws),
+            attend_ws.numel() * attend_ws.element_size(), _stream(stream)]
+    if n_tables is None:
+        _check("locks_decode_layer", lib().locks_decode_layer(*head, *tail))
+    else:
+        _check("locks_decode_layer_tables",
+               lib().locks_decode_layer_tables(*head, int(n_tables), *tail))

@@ -26,22 +26,26 @@ class DecodeStep:
     finalize=True summarizes pages completed by the newest token first;
     fused=True issues each layer as one locks_decode_layer call (the last
     selection stage runs inside the attention kernel), fused=False as
-    locks_score_select + locks_sparse_attend."""
+    locks_score_select + locks_sparse_attend.  n_tables sets the number of
+    selection tables per sequence (default: one per KV head; 1: one table for
+    the whole layer); sel and cnt then hold n_tables rows per sequence."""
 
     def __init__(self, d, k, v, summaries, q, block_table, seq_lens, budget_pages, dense=False,
-                 finalize=False, fused=True):
+                 finalize=False, fused=True, n_tables=None):
         self.d, self.k, self.v, self.summ, self.q = d, k, v, summaries, q
         self.bt, self.seq, self.budget, self.dense = block_table, seq_lens, budget_pages, dense
         self.finalize = finalize
         self.fused = fused
+        self.n_tables = n_tables
+        ntab = d.num_kv_heads if n_tables is None else n_tables
         n_layers, batch = q.shape[0], q.shape[1]
         P = block_table.shape[1]
         dev = q.device
         self.layers = n_layers
         self.num_blocks = k.shape[1]
-        self.sel = torch.full((n_layers, batch, d.num_kv_heads, budget_pages), -1,
-                              dtype=torch.int32, device=dev)
-        self.cnt = torch.zeros((n_layers, batch, d.num_kv_heads), dtype=torch.int32, device=dev)
+        self.sel = torch.full((n_layers, batch, ntab, budget_pages), -1, dtype=torch.int32,
+                              device=dev)
+        self.cnt = torch.zeros((n_layers, batch, ntab), dtype=torch.int32, device=dev)
         self.out = torch.zeros((n_layers, batch, d.num_q_heads, d.head_dim), dtype=torch.bfloat16,
                                device=dev)
         self.out_lse = torch.zeros((n_layers, batch, d.num_q_heads), dtype=torch.float32, device=dev)
@@ -49,6 +53,9 @@ class DecodeStep:
                                     dtype=torch.uint8, device=dev)
         n_att = (P if dense else budget_pages) + 1
         self.ws_att = L.attend_workspace(d, batch, n_att, device=dev)
+        # page scores for the three-call path with several KV heads per table
+        self.lse = (torch.empty((batch, d.num_q_heads, P), dtype=torch.float32, device=dev)
+                    if n_tables is not None and not fused and not dense else None)
         self.graph = None
 
     def run_layer(self, layer, stream=None):
@@ -57,16 +64,22 @@ class DecodeStep:
             L.decode_layer(d, self.q[layer], self.summ[layer], self.k[layer], self.v[layer],
                            self.bt, self.seq, self.budget, self.sel[layer], self.cnt[layer],
                            self.out[layer], self.ws_score, self.ws_att,
-                           out_lse=self.out_lse[layer], stream=stream)
+                           out_lse=self.out_lse[layer], stream=stream, n_tables=self.n_tables)
             return
-        if not self.dense:
+        if not self.dense and self.n_tables is None:
             L.score_select(d, self.q[layer], self.summ[layer], self.num_blocks, self.bt, self.seq,
                            self.budget, self.sel[layer], self.cnt[layer], self.ws_score,
                            stream=stream)
+        elif not self.dense:
+            L.score_pages(d, self.q[layer], self.summ[layer], self.num_blocks, self.bt, self.seq,
+                          self.lse, self.ws_score, stream=stream)
+            L.select_pages(d, self.lse, self.seq, self.budget, self.sel[layer], self.cnt[layer],
+                           self.ws_score, stream=stream, n_tables=self.n_tables)
         L.sparse_attend(d, self.q[layer], self.k[layer], self.v[layer], self.bt, self.seq,
                         None if self.dense else self.sel[layer],
                         None if self.dense else self.cnt[layer], self.budget, self.out[layer],
-                        self.ws_att, out_lse=self.out_lse[layer], stream=stream)
+                        self.ws_att, out_lse=self.out_lse[layer], stream=stream,
+                        n_tables=self.n_tables)
 
     def run(self):
         if self.finalize:   # every layer's completed pages, in one launch

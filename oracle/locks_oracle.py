@@ -343,6 +343,29 @@ def select_top_pages(mass, budget_pages):
     return np.array(sorted(order[:k]), dtype=np.int64)
 
 
+def table_selection(s_hat, n_tables, budget_pages):
+    """Selection with n_tables tables per sequence.  [P1] sec. 2, group-shared
+    selection: the heads that share a table average their mass shares and all
+    attend the table's pages.  The default reading gives each KV head its own
+    table (n_tables = Hkv); n_tables = 1 is the wider reading, one table for
+    the whole layer.
+
+    s_hat [Hq, N]: every query head of one sequence, query head h belonging to
+    KV head h // (Hq / Hkv).  Table t averages the query heads
+    [t*Hq/n_tables, (t+1)*Hq/n_tables).  Returns a list over tables of
+    (log_m [N], selected pages ascending)."""
+    s = np.asarray(s_hat, dtype=np.float64)
+    hq = s.shape[0]
+    if n_tables < 1 or hq % n_tables:
+        raise ValueError("n_tables must divide the number of query heads")
+    hpt = hq // n_tables
+    out = []
+    for t in range(n_tables):
+        _, log_m, _ = group_mass(s[t * hpt:(t + 1) * hpt])
+        out.append((log_m, select_top_pages(log_m, budget_pages)))
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Sparse attention  [P2] abstract (attend only the top pages); [P1] sec. 2
 # ---------------------------------------------------------------------------

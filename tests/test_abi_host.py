@@ -154,3 +154,30 @@ def test_exact_page_lse_validation():
     assert call(lay=L.KVLayout(16384, 2048, 64)) == L.ERR_SHAPE
     assert call(k=P(264)) == L.ERR_SHAPE
     assert call(d=L.dims(32, 8, rank=4)) == L.ERR_UNSUPPORTED
+
+
+def test_table_count_validation():
+    """n_tables must be a positive divisor of the KV-head count; the check
+    comes before anything is launched."""
+    lib = _lib_or_skip()
+    d = L.dims(32, 8)
+    P = ctypes.c_void_p
+    lay = L.KVLayout(32768, 4096, 128)
+    for bad in (0, -1, 3, 16):
+        st = lib.locks_select_pages_tables(ctypes.byref(d), P(256), 16, P(256), 1, 4, bad, P(256),
+                                           P(256), P(256), 1 << 40, None)
+        assert st == L.ERR_SHAPE, bad
+        st = lib.locks_sparse_attend_tables(ctypes.byref(d), P(256), P(256), P(256), lay, 4,
+                                            P(256), 4, P(256), 1, P(256), P(256), 4, bad, 0.1,
+                                            P(256), None, P(256), 1 << 40, None)
+        assert st == L.ERR_SHAPE, bad
+        st = lib.locks_decode_layer_tables(ctypes.byref(d), P(256), P(256), P(256), P(256), lay, 4,
+                                           P(256), 4, P(256), 1, 4, bad, 0.1, P(256), P(256),
+                                           P(256), None, P(256), 1 << 40, P(256), 1 << 40, None)
+        assert st == L.ERR_SHAPE, bad
+    # a valid count still meets the other checks (workspace too small here)
+    st = lib.locks_select_pages_tables(ctypes.byref(d), P(256), 16, P(256), 1, 4, 2, P(256),
+                                       P(256), P(256), 8, None)
+    assert st == L.ERR_WORKSPACE
+    assert lib.locks_select_pages_tables(None, P(256), 16, P(256), 1, 4, 1, P(256), P(256),
+                                         P(256), 1 << 40, None) == L.ERR_NULL

@@ -66,6 +66,15 @@ def _gather_no_tail(cache_layer, block_row, kvh, pages, seq_len, page=O.PAGE):
     return np.concatenate(parts, axis=0) if parts else np.zeros((0, cache_layer.shape[-1]))
 
 
+def _tables_strided(s_hat, n_tables, budget_pages):
+    s = np.asarray(s_hat, np.float64)
+    out = []
+    for t in range(n_tables):                                 # mistake: heads t, t + n_tables, ...
+        _, log_m, _ = OL.group_mass(s[t::n_tables])
+        out.append((log_m, OL.select_top_pages(log_m, budget_pages)))
+    return out
+
+
 def _scale_no_fp16(x):
     return np.asarray(x, np.float64)                          # mistake: scale not rounded to fp16
 
@@ -79,6 +88,7 @@ MUTANTS = [
     ("select_top_pages", _select_high_ties, P.test_topk_against_counting_bruteforce),
     ("select_top_pages", _select_high_ties, P.test_share_hand_worked_cases),
     ("group_mass", _group_mass_unnormalized, P.test_share_hand_worked_cases),
+    ("table_selection", _tables_strided, P.test_table_selection_layer_wide_differs_from_per_kv_head),
     ("gather_pages", _gather_no_tail, lambda: P.test_full_budget_equals_dense(4096 - 5)),
     ("fp16_round", _scale_no_fp16, P.test_quantization_codes_and_scales),
 ]

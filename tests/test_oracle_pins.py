@@ -271,6 +271,58 @@ def test_topk_against_counting_bruteforce():
         assert list(O.select_top_pages(vals, k)) == sorted(sel)
 
 
+def test_table_selection_bruteforce():
+    """Tables over several KV heads: shares from explicit loops (each head's
+    softmax over pages, averaged over the table's heads) and the top-k by
+    counting, for 1, 2 and 4 tables over 8 query heads."""
+    rng = np.random.default_rng(47)
+    for trial in range(12):
+        hq, n = 8, int(rng.integers(1, 25))
+        s = rng.standard_normal((hq, n)) * 3
+        s[:, rng.integers(0, n)] += 4          # a shared heavy page now and then
+        for n_tables in (1, 2, 4):
+            k = int(rng.integers(1, n + 2))
+            got = O.table_selection(s, n_tables, k)
+            assert len(got) == n_tables
+            hpt = hq // n_tables
+            for t, (log_m, sel) in enumerate(got):
+                heads = range(t * hpt, (t + 1) * hpt)
+                m = []
+                for j in range(n):
+                    acc = 0.0
+                    for h in heads:
+                        z = sum(math.exp(s[h, i]) for i in range(n))
+                        acc += math.exp(s[h, j]) / z
+                    m.append(acc / hpt)
+                np.testing.assert_allclose(np.exp(log_m), m, rtol=1e-12)
+                want = sorted(j for j in range(n)
+                              if sum(1 for i in range(n)
+                                     if m[i] > m[j] or (m[i] == m[j] and i < j)) < k)
+                assert list(sel) == want
+
+
+def test_table_selection_layer_wide_differs_from_per_kv_head():
+    """Two KV heads of 2 query heads each, 3 pages, k = 1, shares written out.
+    Case 1: KV head 0's heads give pages (0.45, 0.40, 0.15), KV head 1's
+    (0.15, 0.40, 0.45).  Per KV head: pages {0} and {2}.  One table for the
+    layer averages to (0.30, 0.40, 0.30) and keeps page 1, which neither
+    per-KV-head table keeps.  Case 2: (0.65, 0.30, 0.05) and (0.05, 0.30,
+    0.65) average to (0.35, 0.30, 0.35); the tie goes to the lower index, so
+    the layer-wide table keeps page 0 and KV head 1 loses its top page."""
+    def logits(shares):
+        return np.log(np.array(shares))
+    s = np.stack([logits([0.45, 0.40, 0.15])] * 2 + [logits([0.15, 0.40, 0.45])] * 2)
+    assert [list(sel) for _, sel in O.table_selection(s, 2, 1)] == [[0], [2]]
+    (log_m, sel), = O.table_selection(s, 1, 1)
+    np.testing.assert_allclose(np.exp(log_m), [0.30, 0.40, 0.30], atol=1e-12)
+    assert list(sel) == [1]
+    s2 = np.stack([logits([0.65, 0.30, 0.05])] * 2 + [logits([0.05, 0.30, 0.65])] * 2)
+    assert [list(sel) for _, sel in O.table_selection(s2, 2, 1)] == [[0], [2]]
+    (log_m2, sel2), = O.table_selection(s2, 1, 1)
+    np.testing.assert_allclose(np.exp(log_m2), [0.35, 0.30, 0.35], atol=1e-12)
+    assert list(sel2) == [0]
+
+
 def test_shift_invariance_of_shares():
     rng = np.random.default_rng(43)
     s = rng.standard_normal((4, 30))
