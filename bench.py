@@ -194,20 +194,46 @@ def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps):
     cnt_x = torch.empty((w.batch, w.hkv), dtype=torch.int32, device="cuda")
     layers = sorted(set(int(round(i * (w.layers - 1) / max(1, n_layers - 1)))
                         for i in range(min(n_layers, w.layers))))
-    inter = tot = 0
+    inter = tot = inter_sh = 0
     car_locks = car_exact = car_n = 0
+    # the shared-basis selector: one pooled basis per (layer, KV head) over
+    # every finalized page, summaries in it, then the same scorer and selection
+    fin = torch.cat([inp.block_table[b, :int(inp.seq_lens[b]) // w.page]
+                     for b in range(w.batch)]).unique().to(torch.int32)
+    basis = torch.empty((w.hkv, 8, 128), dtype=torch.float32, device="cuda")
+    eig = torch.empty((w.hkv, 128), dtype=torch.float32, device="cuda")
+    summ_sh = torch.empty((w.hkv, w.num_blocks, L.summary_bytes(d)), dtype=torch.uint8,
+                          device="cuda")
+    sel_sh = torch.empty_like(sel_x)
+    cnt_sh = torch.empty_like(cnt_x)
+    energy_sh = []
+    shared_ms = []
     for layer in layers:
         L.exact_page_lse(d, inp.q[layer], inp.k[layer], inp.block_table, inp.seq_lens, lse)
         L.select_pages(d, lse, inp.seq_lens, budget, sel_x, cnt_x, ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        L.shared_basis(d, inp.k[layer], fin, basis, eigvals=eig)
+        torch.cuda.synchronize()
+        shared_ms.append((time.perf_counter() - t0) * 1e3)
+        L.build_summaries_basis(d, inp.k[layer], fin, basis, summ_sh)
+        L.score_select(d, inp.q[layer], summ_sh, w.num_blocks, inp.block_table, inp.seq_lens,
+                       budget, sel_sh, cnt_sh, ws)
+        ev = eig.double()
+        energy_sh.append(float((ev[:, :8].sum(dim=1) / ev.clamp_min(0).sum(dim=1)).mean()))
         sl = step.sel[layer].cpu().numpy()
         cl = step.cnt[layer].cpu().numpy()
         sx = sel_x.cpu().numpy()
         cx = cnt_x.cpu().numpy()
+        ss = sel_sh.cpu().numpy()
+        cs = cnt_sh.cpu().numpy()
         for b in range(w.batch):
             for g in range(w.hkv):
                 a = set(sl[b, g, :cl[b, g]].tolist())
                 e = set(sx[b, g, :cx[b, g]].tolist())
+                sh = set(ss[b, g, :cs[b, g]].tolist())
                 inter += len(a & e)
+                inter_sh += len(sh & e)
                 tot += len(e)
         for (lay, b, g, page, _slot, _head) in inp.carriers:
             if lay != layer:
@@ -225,7 +251,7 @@ def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps):
     X = K - raw[:, :, None, :128]
     C = raw[:, :, 1152:].reshape(n_smp, w.hkv, 16, 8)
     energy = float(((C * C).sum(dim=(2, 3)) / (X * X).sum(dim=(2, 3)).clamp_min(1e-30)).mean())
-    del tmp, raw, K, X
+    del tmp, raw, K, X, summ_sh
     return {"exact_us_per_layer": round(exact_ms * 1e3, 3),
             "exact_scorer_gbs": round(exact_gbs, 1),
             "exact_scorer_frac": round(exact_gbs / PEAK_HBM_GBS, 4),
@@ -234,6 +260,11 @@ def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps):
             "carrier_retention_exact": car_exact / max(car_n, 1),
             "carriers": car_n, "layers_sampled": layers,
             "energy_captured_rank8": round(energy, 4),
+            "shared_basis": {"recall_vs_exact": inter_sh / max(tot, 1),
+                             "energy_captured_rank8": round(sum(energy_sh) / len(energy_sh), 4),
+                             "basis_ms_per_layer": round(sum(shared_ms) / len(shared_ms), 2),
+                             "note": ("one rank-8 basis per (layer, KV head) from the pooled page "
+                                      "deviations, same record size, scorer and selection")},
             "note": ("exact = top-k from the true-key page LSE (reads every key); recall = "
                      "fraction of the exact page set LOCKS also selects")}
 
@@ -379,7 +410,9 @@ def main():
             f"{quality['exact_scorer_gbs']:.0f} GB/s; recall vs exact "
             f"{quality['recall_vs_exact']:.4f}; carriers kept: LOCKS "
             f"{quality['carrier_retention_locks']:.3f}, exact {quality['carrier_retention_exact']:.3f}; "
-            f"energy captured {quality['energy_captured_rank8']:.3f}")
+            f"energy captured {quality['energy_captured_rank8']:.3f}; shared basis: recall "
+            f"{quality['shared_basis']['recall_vs_exact']:.4f}, energy "
+            f"{quality['shared_basis']['energy_captured_rank8']:.3f}")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -256,6 +256,41 @@ locks_status locks_decode_layer_tables(const locks_dims* dims, const void* q,
                                        size_t score_ws_bytes, void* attend_ws,
                                        size_t attend_ws_bytes, void* stream);
 
+/* The shared low-rank basis the pages contrast LOCKS with (sec. 1 and sec. 3,
+ * Proposition 1: one query-independent rank-r projection for every page is
+ * blind to in-page directions outside it).  For each KV head: the pooled
+ * scatter S = sum_j X_j^T X_j of the listed pages' deviations from their own
+ * centroids, and its top-8 eigenvectors.
+ *   block_ids : [n_blocks] physical blocks pooled (ids outside
+ *               [0, num_blocks) add nothing); n_blocks >= 1.
+ *   basis     : fp32 [Hkv][8][128], row k = the k-th eigenvector (descending
+ *               eigenvalue, ties to the lower index), unit length, largest-
+ *               |entry| component positive (lowest index on ties).
+ *   eigvals   : nullable fp32 [Hkv][128], all eigenvalues of S, descending.
+ *   workspace : >= locks_shared_basis_workspace_bytes(dims, n_blocks) bytes,
+ *               16-byte aligned.
+ * Eigenvectors of (near-)equal eigenvalues are any orthonormal basis of their
+ * span.  Off the decode path; a few milliseconds per call. */
+size_t locks_shared_basis_workspace_bytes(const locks_dims* dims, int32_t n_blocks);
+locks_status locks_shared_basis(const locks_dims* dims, const void* k_cache,
+                                locks_kv_layout layout, const int32_t* block_ids,
+                                int32_t n_blocks, int32_t num_blocks, float* basis,
+                                float* eigvals, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Summaries in a given basis instead of each page's own eigenbasis: the
+ * shared-basis selector at the same state size.  Each record keeps its
+ * page's centroid and coefficients c_i = V^T x_i in the given basis, stored
+ * and quantized exactly as locks_build_summaries stores its own (the record
+ * layout above), so locks_score_pages and the rest read them unchanged.
+ *   basis : fp32 [Hkv][8][128] (rows = basis vectors), e.g. from
+ *           locks_shared_basis.
+ * Other arguments and errors as for locks_build_summaries. */
+locks_status locks_build_summaries_basis(const locks_dims* dims, const void* k_cache,
+                                         locks_kv_layout layout, const int32_t* block_ids,
+                                         int32_t n_blocks, int32_t num_blocks,
+                                         const float* basis, void* summaries, void* stream);
+
 /* Exact page scores from the true keys, the "read every key" comparator the
  * pages measure LOCKS against (sec. 3 contributions: selection quality
  * against exact page attention mass):

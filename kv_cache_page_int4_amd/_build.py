@@ -8,7 +8,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblocks.so")
-SOURCES = ["locks_abi.cpp", "score.hip", "select.hip", "attend.hip", "build.hip", "exact.hip"]
+SOURCES = ["locks_abi.cpp", "score.hip", "select.hip", "attend.hip", "build.hip", "exact.hip",
+           "shared.hip"]
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     # never emit packed fp32 VALU ops

@@ -21,6 +21,9 @@
 //  6. symmetric quantization with fp16 scales (max|x|/7 for the basis,
 //     max|x|/127 for coefficients and centroid, round half to even) and
 //     packing into the 832-byte record.
+// With a given basis (the shared-basis selector the pages contrast LOCKS
+// with), steps 2-5 are replaced by that basis: the record keeps the page's own
+// centroid and coefficients c_i = V^T x_i in the given basis.
 #include "locks_device.h"
 #include "locks_internal.h"
 
@@ -112,7 +115,8 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
                                                    int64_t hs, int64_t ts, BlockSource src,
                                                    int32_t n_blocks, int32_t num_blocks,
                                                    int32_t hkv, uint8_t* __restrict__ summ,
-                                                   float* __restrict__ raw) {
+                                                   float* __restrict__ raw,
+                                                   const float* __restrict__ basis) {
   __shared__ BuildSmem sm;
   const int lane = threadIdx.x;
   const int bi = blockIdx.x, kvh = blockIdx.y;
@@ -155,142 +159,152 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 #pragma unroll
   for (int e = 0; e < 32; ++e) sm.X[t][32 * g + e] = x[e];
 
-  // ---- 2. Gram matrix on the matrix cores: K index (step s, group g) = dim 32g+s ----
-  f32x4v gacc = {0.f, 0.f, 0.f, 0.f};
+  const int d0 = 2 * lane;   // basis dims owned by this lane: d0, d0 + 1
+  if (basis) {
+    const float* bk = basis + (size_t)kvh * kR * kD;
 #pragma unroll
-  for (int s = 0; s < 32; ++s) gacc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], x[s], gacc, 0, 0, 0);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) sm.G[4 * g + r][t] = gacc[r];
-  for (int i = lane; i < kB * kB; i += 64) sm.U[i >> 4][i & 15] = ((i >> 4) == (i & 15)) ? 1.f : 0.f;
-  __syncthreads();
-  // symmetrize (the product is symmetric up to rounding order)
-  for (int i = lane; i < kB * kB; i += 64) {
-    const int a = i >> 4, b = i & 15;
-    if (a < b) {
-      const float v = 0.5f * (sm.G[a][b] + sm.G[b][a]);
-      sm.G[a][b] = v;
-      sm.G[b][a] = v;
+    for (int k = 0; k < kR; ++k) {
+      sm.V[k][d0] = bk[k * kD + d0];
+      sm.V[k][d0 + 1] = bk[k * kD + d0 + 1];
     }
-  }
-  __syncthreads();
+    __syncthreads();
+  } else {
+    // ---- 2. Gram matrix on the matrix cores: K index (step s, group g) = dim 32g+s ----
+    f32x4v gacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) gacc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], x[s], gacc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.G[4 * g + r][t] = gacc[r];
+    for (int i = lane; i < kB * kB; i += 64) sm.U[i >> 4][i & 15] = ((i >> 4) == (i & 15)) ? 1.f : 0.f;
+    __syncthreads();
+    // symmetrize (the product is symmetric up to rounding order)
+    for (int i = lane; i < kB * kB; i += 64) {
+      const int a = i >> 4, b = i & 15;
+      if (a < b) {
+        const float v = 0.5f * (sm.G[a][b] + sm.G[b][a]);
+        sm.G[a][b] = v;
+        sm.G[b][a] = v;
+      }
+    }
+    __syncthreads();
 
-  // ---- 3. cyclic Jacobi ----
-  const int ia = lane >> 3, ib = lane & 7;   // row pair, column pair of this lane's block
-  const int urow = lane & 15, upair0 = 2 * (lane >> 4);
-  for (int sweep = 0; sweep < kSweeps; ++sweep) {
-    for (int m = 1; m < 16; ++m) {
-      const int hb = 31 - __clz(m);
-      auto pair_p = [&](int pi) { return ((pi >> hb) << (hb + 1)) | (pi & ((1 << hb) - 1)); };
-      const int a0 = pair_p(ia), a1 = a0 ^ m, b0 = pair_p(ib), b1 = b0 ^ m;
-      const float g00 = sm.G[a0][b0], g01 = sm.G[a0][b1], g10 = sm.G[a1][b0], g11 = sm.G[a1][b1];
-      if (ia == ib) {
-        float c, s;
-        jacobi_rot(g00, 0.5f * (g01 + g10), g11, c, s);
-        sm.cs[ia][0] = c;
-        sm.cs[ia][1] = s;
-      }
-      __syncthreads();
-      const float ca = sm.cs[ia][0], sa = sm.cs[ia][1], cb = sm.cs[ib][0], sb = sm.cs[ib][1];
-      // T = G J (columns b0, b1), then G' = J^T T (rows a0, a1)
-      const float t00 = g00 * cb - g01 * sb, t01 = g00 * sb + g01 * cb;
-      const float t10 = g10 * cb - g11 * sb, t11 = g10 * sb + g11 * cb;
-      float n00 = ca * t00 - sa * t10, n01 = ca * t01 - sa * t11;
-      float n10 = sa * t00 + ca * t10, n11 = sa * t01 + ca * t11;
-      if (ia == ib) {
-        n01 = 0.f;
-        n10 = 0.f;
-      }
-      sm.G[a0][b0] = n00;
-      sm.G[a0][b1] = n01;
-      sm.G[a1][b0] = n10;
-      sm.G[a1][b1] = n11;
-      // U' = U J for row urow and pairs upair0, upair0 + 1
+    // ---- 3. cyclic Jacobi ----
+    const int ia = lane >> 3, ib = lane & 7;   // row pair, column pair of this lane's block
+    const int urow = lane & 15, upair0 = 2 * (lane >> 4);
+    for (int sweep = 0; sweep < kSweeps; ++sweep) {
+      for (int m = 1; m < 16; ++m) {
+        const int hb = 31 - __clz(m);
+        auto pair_p = [&](int pi) { return ((pi >> hb) << (hb + 1)) | (pi & ((1 << hb) - 1)); };
+        const int a0 = pair_p(ia), a1 = a0 ^ m, b0 = pair_p(ib), b1 = b0 ^ m;
+        const float g00 = sm.G[a0][b0], g01 = sm.G[a0][b1], g10 = sm.G[a1][b0], g11 = sm.G[a1][b1];
+        if (ia == ib) {
+          float c, s;
+          jacobi_rot(g00, 0.5f * (g01 + g10), g11, c, s);
+          sm.cs[ia][0] = c;
+          sm.cs[ia][1] = s;
+        }
+        __syncthreads();
+        const float ca = sm.cs[ia][0], sa = sm.cs[ia][1], cb = sm.cs[ib][0], sb = sm.cs[ib][1];
+        // T = G J (columns b0, b1), then G' = J^T T (rows a0, a1)
+        const float t00 = g00 * cb - g01 * sb, t01 = g00 * sb + g01 * cb;
+        const float t10 = g10 * cb - g11 * sb, t11 = g10 * sb + g11 * cb;
+        float n00 = ca * t00 - sa * t10, n01 = ca * t01 - sa * t11;
+        float n10 = sa * t00 + ca * t10, n11 = sa * t01 + ca * t11;
+        if (ia == ib) {
+          n01 = 0.f;
+          n10 = 0.f;
+        }
+        sm.G[a0][b0] = n00;
+        sm.G[a0][b1] = n01;
+        sm.G[a1][b0] = n10;
+        sm.G[a1][b1] = n11;
+        // U' = U J for row urow and pairs upair0, upair0 + 1
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int pi = upair0 + u;
-        const int p0 = pair_p(pi), p1 = p0 ^ m;
-        const float c = sm.cs[pi][0], s = sm.cs[pi][1];
-        const float up = sm.U[urow][p0], uq = sm.U[urow][p1];
-        sm.U[urow][p0] = c * up - s * uq;
-        sm.U[urow][p1] = s * up + c * uq;
+        for (int u = 0; u < 2; ++u) {
+          const int pi = upair0 + u;
+          const int p0 = pair_p(pi), p1 = p0 ^ m;
+          const float c = sm.cs[pi][0], s = sm.cs[pi][1];
+          const float up = sm.U[urow][p0], uq = sm.U[urow][p1];
+          sm.U[urow][p0] = c * up - s * uq;
+          sm.U[urow][p1] = s * up + c * uq;
+        }
+        __syncthreads();
       }
-      __syncthreads();
-    }
-    // converged when the off-diagonal mass is below 1e-12 of the total
-    // (off-norm 1e-6 relative: far below what the codes and fp16 scales resolve)
-    float off = 0.f, tot = 0.f;
+      // converged when the off-diagonal mass is below 1e-12 of the total
+      // (off-norm 1e-6 relative: far below what the codes and fp16 scales resolve)
+      float off = 0.f, tot = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * lane + e, a = i >> 4, b = i & 15;
-      const float v = sm.G[a][b];
-      tot = fmaf(v, v, tot);
-      if (a != b) off = fmaf(v, v, off);
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * lane + e, a = i >> 4, b = i & 15;
+        const float v = sm.G[a][b];
+        tot = fmaf(v, v, tot);
+        if (a != b) off = fmaf(v, v, off);
+      }
+      off = wave_sum(off);
+      tot = wave_sum(tot);
+      if (!(off > 1e-12f * tot)) break;
     }
-    off = wave_sum(off);
-    tot = wave_sum(tot);
-    if (!(off > 1e-12f * tot)) break;
-  }
 
-  // ---- 4. order eigenpairs: descending eigenvalue, ties to the lower index ----
-  if (lane < 16) {
-    const float lj = sm.G[lane][lane];
-    int rank = 0;
-    for (int i = 0; i < 16; ++i) {
-      const float li = sm.G[i][i];
-      rank += (li > lj) || (li == lj && i < lane);
-    }
-    sm.order[rank] = lane;
-  }
-  __syncthreads();
-  const float lam1 = sm.G[sm.order[0]][sm.order[0]];
-  const bool page_has_basis = lam1 > kEpsConst * ksq;
-
-  // basis v_k = X^T u_k / |X^T u_k|; lane owns dims 2*lane, 2*lane+1
-  const int d0 = 2 * lane;
-#pragma unroll
-  for (int k = 0; k < kR; ++k) {
-    const int j = sm.order[k];
-    const float lk = sm.G[j][j];
-    const bool keep = page_has_basis && (lk > kTau * lam1);
-    float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < kB; ++tt) {
-      const float u = sm.U[tt][j];
-      v0 = fmaf(sm.X[tt][d0], u, v0);
-      v1 = fmaf(sm.X[tt][d0 + 1], u, v1);
-    }
-    const float nrm2 = wave_sum(v0 * v0 + v1 * v1);
-    const float inv = (keep && nrm2 > 0.f) ? 1.f / sqrtf(nrm2) : 0.f;
-    v0 *= inv;
-    v1 *= inv;
-    // sign: largest |v| (lowest dim on ties) positive
-    float best = fabsf(v0);
-    int bidx = d0;
-    float bval = v0;
-    if (fabsf(v1) > best) {
-      best = fabsf(v1);
-      bidx = d0 + 1;
-      bval = v1;
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float ob = __shfl_xor(best, o);
-      const int oi = __shfl_xor(bidx, o);
-      const float ov = __shfl_xor(bval, o);
-      if (ob > best || (ob == best && oi < bidx)) {
-        best = ob;
-        bidx = oi;
-        bval = ov;
+    // ---- 4. order eigenpairs: descending eigenvalue, ties to the lower index ----
+    if (lane < 16) {
+      const float lj = sm.G[lane][lane];
+      int rank = 0;
+      for (int i = 0; i < 16; ++i) {
+        const float li = sm.G[i][i];
+        rank += (li > lj) || (li == lj && i < lane);
       }
+      sm.order[rank] = lane;
     }
-    if (bval < 0.f) {
-      v0 = -v0;
-      v1 = -v1;
+    __syncthreads();
+    const float lam1 = sm.G[sm.order[0]][sm.order[0]];
+    const bool page_has_basis = lam1 > kEpsConst * ksq;
+
+    // basis v_k = X^T u_k / |X^T u_k|; lane owns dims 2*lane, 2*lane+1
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const int j = sm.order[k];
+      const float lk = sm.G[j][j];
+      const bool keep = page_has_basis && (lk > kTau * lam1);
+      float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < kB; ++tt) {
+        const float u = sm.U[tt][j];
+        v0 = fmaf(sm.X[tt][d0], u, v0);
+        v1 = fmaf(sm.X[tt][d0 + 1], u, v1);
+      }
+      const float nrm2 = wave_sum(v0 * v0 + v1 * v1);
+      const float inv = (keep && nrm2 > 0.f) ? 1.f / sqrtf(nrm2) : 0.f;
+      v0 *= inv;
+      v1 *= inv;
+      // sign: largest |v| (lowest dim on ties) positive
+      float best = fabsf(v0);
+      int bidx = d0;
+      float bval = v0;
+      if (fabsf(v1) > best) {
+        best = fabsf(v1);
+        bidx = d0 + 1;
+        bval = v1;
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float ob = __shfl_xor(best, o);
+        const int oi = __shfl_xor(bidx, o);
+        const float ov = __shfl_xor(bval, o);
+        if (ob > best || (ob == best && oi < bidx)) {
+          best = ob;
+          bidx = oi;
+          bval = ov;
+        }
+      }
+      if (bval < 0.f) {
+        v0 = -v0;
+        v1 = -v1;
+      }
+      sm.V[k][d0] = v0;
+      sm.V[k][d0 + 1] = v1;
     }
-    sm.V[k][d0] = v0;
-    sm.V[k][d0 + 1] = v1;
+    __syncthreads();
   }
-  __syncthreads();
 
   // coefficients c_ik = v_k . x_i : lane -> token t, columns 2*(lane>>4) .. +1
   {
@@ -383,7 +397,19 @@ hipError_t launch_build(const uint16_t* k_cache, int64_t block_stride, int64_t h
   BlockSource src{block_ids, nullptr, nullptr, 0, false, 0, 0};
   hipLaunchKernelGGL(build_kernel, dim3(n_blocks, hkv), dim3(64), 0, stream, k_cache,
                      block_stride, head_stride, token_stride, src, n_blocks, num_blocks,
-                     hkv, summaries, raw_debug);
+                     hkv, summaries, raw_debug, (const float*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_basis(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
+                              int64_t token_stride, const int32_t* block_ids, int32_t n_blocks,
+                              int32_t num_blocks, int32_t hkv, const float* basis,
+                              uint8_t* summaries, hipStream_t stream) {
+  if (n_blocks == 0) return hipSuccess;
+  BlockSource src{block_ids, nullptr, nullptr, 0, false, 0, 0};
+  hipLaunchKernelGGL(build_kernel, dim3(n_blocks, hkv), dim3(64), 0, stream, k_cache,
+                     block_stride, head_stride, token_stride, src, n_blocks, num_blocks,
+                     hkv, summaries, (float*)nullptr, basis);
   return hipGetLastError();
 }
 
@@ -397,7 +423,7 @@ hipError_t launch_finalize(const uint16_t* k_cache, int64_t block_stride, int64_
                   summ_layer_stride};
   hipLaunchKernelGGL(build_kernel, dim3(batch, hkv, n_layers), dim3(64), 0, stream, k_cache, block_stride,
                      head_stride, token_stride, src, batch, num_blocks, hkv, summaries,
-                     (float*)nullptr);
+                     (float*)nullptr, (const float*)nullptr);
   return hipGetLastError();
 }
 

@@ -421,6 +421,66 @@ locks_status locks_sparse_attend_tables(const locks_dims* dims, const void* q,
                             softmax_scale, out, out_lse, workspace, workspace_bytes, stream);
 }
 
+size_t locks_shared_basis_workspace_bytes(const locks_dims* dims, int32_t n_blocks) {
+  if (check_dims(dims) != LOCKS_OK || n_blocks <= 0) return 0;
+  const SharedPlan pl = plan_shared(n_blocks);
+  return align_up((size_t)dims->num_kv_heads * pl.n_chunks * 128 * 128 * sizeof(float));
+}
+
+static locks_status kv_layout_checks(const void* k_cache, locks_kv_layout layout) {
+  if (layout.token_stride < 128 || layout.block_stride <= 0 || layout.head_stride <= 0 ||
+      (layout.token_stride % 8) || (layout.head_stride % 8) || (layout.block_stride % 8))
+    return LOCKS_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(k_cache) & 15) return LOCKS_ERR_SHAPE;
+  return LOCKS_OK;
+}
+
+locks_status locks_shared_basis(const locks_dims* dims, const void* k_cache,
+                                locks_kv_layout layout, const int32_t* block_ids,
+                                int32_t n_blocks, int32_t num_blocks, float* basis,
+                                float* eigvals, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  locks_status st = check_dims(dims);
+  if (st != LOCKS_OK) return st;
+  if (!k_cache || !block_ids || !basis) return LOCKS_ERR_NULL;
+  if (n_blocks <= 0 || num_blocks <= 0 || dims->num_kv_heads > 65535) return LOCKS_ERR_SHAPE;
+  st = kv_layout_checks(k_cache, layout);
+  if (st != LOCKS_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(basis) & 3) || (reinterpret_cast<uintptr_t>(eigvals) & 3))
+    return LOCKS_ERR_SHAPE;
+  const SharedPlan pl = plan_shared(n_blocks);
+  const size_t need = locks_shared_basis_workspace_bytes(dims, n_blocks);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15))
+    return LOCKS_ERR_WORKSPACE;
+  hipError_t e = launch_shared_basis(static_cast<const uint16_t*>(k_cache), layout.block_stride,
+                                     layout.head_stride, layout.token_stride, block_ids, n_blocks,
+                                     num_blocks, dims->num_kv_heads,
+                                     static_cast<float*>(workspace), pl, basis, eigvals,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
+}
+
+locks_status locks_build_summaries_basis(const locks_dims* dims, const void* k_cache,
+                                         locks_kv_layout layout, const int32_t* block_ids,
+                                         int32_t n_blocks, int32_t num_blocks,
+                                         const float* basis, void* summaries, void* stream) {
+  locks_status st = check_dims(dims);
+  if (st != LOCKS_OK) return st;
+  if (n_blocks < 0 || num_blocks <= 0 || dims->num_kv_heads > 65535) return LOCKS_ERR_SHAPE;
+  if (n_blocks == 0) return LOCKS_OK;
+  if (!k_cache || !block_ids || !basis || !summaries) return LOCKS_ERR_NULL;
+  st = kv_layout_checks(k_cache, layout);
+  if (st != LOCKS_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(summaries) & 15) || (reinterpret_cast<uintptr_t>(basis) & 3))
+    return LOCKS_ERR_SHAPE;
+  hipError_t e = launch_build_basis(static_cast<const uint16_t*>(k_cache), layout.block_stride,
+                                    layout.head_stride, layout.token_stride, block_ids, n_blocks,
+                                    num_blocks, dims->num_kv_heads, basis,
+                                    static_cast<uint8_t*>(summaries),
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
+}
+
 const char* locks_status_str(locks_status status) {
   switch (status) {
     case LOCKS_OK: return "ok";

@@ -78,6 +78,26 @@ hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
                                 float2* part_ml, const AttendPlan& plan, uint16_t* out,
                                 float* out_lse, hipStream_t stream);
 
+// ---- shared basis (the rejected baseline, for comparison) ------------------------
+constexpr int32_t kSharedMaxChunks = 64;   // partial 128x128 sums per KV head
+struct SharedPlan {
+  int32_t n_chunks;    // partial sums per KV head
+  int32_t per_chunk;   // pages per partial
+};
+SharedPlan plan_shared(int32_t n_blocks);
+// partials: float [hkv][n_chunks][128][128]; basis: float [hkv][8][128];
+// eigvals: nullable float [hkv][128], descending.
+hipError_t launch_shared_basis(const uint16_t* k_cache, int64_t block_stride,
+                               int64_t head_stride, int64_t token_stride,
+                               const int32_t* block_ids, int32_t n_blocks, int32_t num_blocks,
+                               int32_t hkv, float* partials, const SharedPlan& plan,
+                               float* basis, float* eigvals, hipStream_t stream);
+// Summaries in a given basis (float [hkv][8][128], rows = basis vectors).
+hipError_t launch_build_basis(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
+                              int64_t token_stride, const int32_t* block_ids, int32_t n_blocks,
+                              int32_t num_blocks, int32_t hkv, const float* basis,
+                              uint8_t* summaries, hipStream_t stream);
+
 // ---- exact page LSE (read-every-key comparator) ---------------------------------
 hipError_t launch_exact_lse(const uint16_t* q, const uint16_t* k_cache, int64_t block_stride,
                             int64_t head_stride, int64_t token_stride, int32_t num_blocks,

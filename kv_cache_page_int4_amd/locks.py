@@ -66,6 +66,9 @@ _SIGS = {
     "locks_decode_layer_tables": (_I32, [_DP, _P, _P, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32,
                                          _I32, _I32, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P,
                                          _SZ, _P]),
+    "locks_shared_basis_workspace_bytes": (_SZ, [_DP, _I32]),
+    "locks_shared_basis": (_I32, [_DP, _P, KVLayout, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "locks_build_summaries_basis": (_I32, [_DP, _P, KVLayout, _P, _I32, _I32, _P, _P, _P]),
     "locks_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -305,3 +308,33 @@ def decode_layer(d: Dims, q, summaries, k_cache, v_cache, block_table, seq_lens,
     else:
         _check("locks_decode_layer_tables",
                lib().locks_decode_layer_tables(*head, int(n_tables), *tail))
+
+
+def shared_basis(d: Dims, k_cache, block_ids, basis, eigvals=None, workspace=None, stream=None):
+    """Top-8 eigenvectors of the pooled page deviations per KV head.
+    basis: fp32 [Hkv, 8, 128]; eigvals: optional fp32 [Hkv, 128]."""
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(block_ids, "block_ids", torch.int32)
+    _need(basis, "basis", torch.float32)
+    _need(eigvals, "eigvals", torch.float32)
+    n = block_ids.numel()
+    if workspace is None:
+        workspace = torch.empty(max(1, lib().locks_shared_basis_workspace_bytes(ctypes.byref(d), n)),
+                                dtype=torch.uint8, device=k_cache.device)
+    st = lib().locks_shared_basis(ctypes.byref(d), _ptr(k_cache), kv_layout(k_cache),
+                                  _ptr(block_ids), n, k_cache.shape[0], _ptr(basis),
+                                  _ptr(eigvals), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("locks_shared_basis", st)
+
+
+def build_summaries_basis(d: Dims, k_cache, block_ids, basis, summaries, stream=None):
+    """Summaries of the listed blocks in a given basis (fp32 [Hkv, 8, 128])."""
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(block_ids, "block_ids", torch.int32)
+    _need(basis, "basis", torch.float32)
+    _need(summaries, "summaries", torch.uint8)
+    st = lib().locks_build_summaries_basis(ctypes.byref(d), _ptr(k_cache), kv_layout(k_cache),
+                                           _ptr(block_ids), block_ids.numel(), k_cache.shape[0],
+                                           _ptr(basis), _ptr(summaries), _stream(stream))
+    _check("locks_build_summaries_basis", st)

@@ -125,6 +125,29 @@ def shared_basis(K_pages, rho=RANK):
     return W[:rho].T.copy()
 
 
+def pooled_scatter(K_pages):
+    """Sum over pages of X_j^T X_j with X_j = K_j - mu_j, the deviations of
+    each page from its own centroid, pooled: the matrix whose top eigenvectors
+    are the shared basis above.  K [n, B, d] -> [d, d]."""
+    K = np.asarray(K_pages, dtype=np.float64)
+    X = (K - K.mean(axis=-2, keepdims=True)).reshape(-1, K.shape[-1])
+    return X.T @ X
+
+
+def shared_summary(K_pages, Vb):
+    """Summaries of pages K [n, B, d] in one given basis Vb [d, r] (columns):
+    each page keeps its own centroid, its coefficients are C = X Vb, and every
+    record carries Vb -- the shared-basis selector the pages contrast LOCKS
+    with ([P1] sec. 3, Proposition 1), at the same state size.  Returns
+    (mu [n, d], V [n, d, r], C [n, B, r])."""
+    K = np.asarray(K_pages, dtype=np.float64)
+    Vb = np.asarray(Vb, dtype=np.float64)
+    mu = K.mean(axis=-2)
+    X = K - mu[..., None, :]
+    V = np.broadcast_to(Vb, K.shape[:-2] + Vb.shape).copy()
+    return mu, V, X @ Vb
+
+
 # ---------------------------------------------------------------------------
 # Quantization  [P1] sec. 2: int4 basis, int8 coefficients and centroid
 # ---------------------------------------------------------------------------
@@ -264,6 +287,14 @@ def build_records(K_pages):
     mu, V, C, lam = page_summary(K_pages)
     qz = quantize_summary(mu, V, C)
     return pack_records(qz), qz, lam
+
+
+def build_records_with_basis(K_pages, Vb):
+    """Records of pages K [n, B, d] summarized in the given basis Vb [d, r]
+    (quantized and packed as LOCKS records) -> (records [n, 832], qz)."""
+    mu, V, C = shared_summary(K_pages, Vb)
+    qz = quantize_summary(mu, V, C)
+    return pack_records(qz), qz
 
 
 # ---------------------------------------------------------------------------

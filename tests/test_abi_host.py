@@ -181,3 +181,31 @@ def test_table_count_validation():
     assert st == L.ERR_WORKSPACE
     assert lib.locks_select_pages_tables(None, P(256), 16, P(256), 1, 4, 1, P(256), P(256),
                                          P(256), 1 << 40, None) == L.ERR_NULL
+
+
+def test_shared_basis_validation():
+    lib = _lib_or_skip()
+    d = L.dims(32, 8)
+    P = ctypes.c_void_p
+    lay = L.KVLayout(32768, 4096, 128)
+    need = lib.locks_shared_basis_workspace_bytes(ctypes.byref(d), 1000)
+    assert need > 0 and lib.locks_shared_basis_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert lib.locks_shared_basis_workspace_bytes(ctypes.byref(L.dims(32, 8, rank=4)), 10) == 0
+    call = lambda **kw: lib.locks_shared_basis(
+        ctypes.byref(kw.get("d", d)), kw.get("k", P(256)), kw.get("lay", lay), kw.get("ids", P(256)),
+        kw.get("n", 1000), 4096, kw.get("basis", P(256)), None, kw.get("ws", P(256)),
+        kw.get("wsb", need), None)
+    assert call(n=0) == L.ERR_SHAPE
+    assert call(basis=None) == L.ERR_NULL
+    assert call(k=None) == L.ERR_NULL
+    assert call(wsb=need - 1) == L.ERR_WORKSPACE
+    assert call(ws=None) == L.ERR_WORKSPACE
+    assert call(lay=L.KVLayout(32768, 4096, 64)) == L.ERR_SHAPE
+    assert call(d=L.dims(32, 8, head_dim=64)) == L.ERR_UNSUPPORTED
+    b = lambda n, basis=P(256), summ=P(256): lib.locks_build_summaries_basis(
+        ctypes.byref(d), P(256), lay, P(256), n, 4096, basis, summ, None)
+    assert b(0) == L.OK
+    assert b(-1) == L.ERR_SHAPE
+    assert b(3, basis=None) == L.ERR_NULL
+    assert b(3, summ=None) == L.ERR_NULL
+    assert b(3, summ=P(264)) == L.ERR_SHAPE

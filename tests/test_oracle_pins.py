@@ -191,6 +191,42 @@ def test_proposition1_shared_projection_content_blind():
     np.testing.assert_allclose(sA, O.page_lse_exact(q[None], KA[None])[0, 0], atol=1e-10)
 
 
+def test_pooled_scatter_trace_and_subspace():
+    """The pooled scatter's trace is the pages' total deviation energy (the
+    sum of every page's eigenvalues, from per-page SVDs), and its top
+    eigenvectors span the same subspace as the shared basis (an SVD of the
+    stacked deviations, another routine on another matrix)."""
+    rng = np.random.default_rng(53)
+    K = rng.standard_normal((30, 16, 128)) * np.linspace(0.2, 3.0, 128)
+    S = O.pooled_scatter(K)
+    lam = O.page_spectrum(K)[2]
+    np.testing.assert_allclose(np.trace(S), lam.sum(), rtol=1e-12)
+    np.testing.assert_allclose(S, S.T, atol=1e-9)
+    ev, W = np.linalg.eigh(S)
+    top = W[:, ::-1][:, :8]
+    Wsh = O.shared_basis(K)
+    np.testing.assert_allclose(np.abs(np.linalg.svd(top.T @ Wsh)[1]), 1.0, atol=1e-8)
+
+
+def test_records_with_own_basis_equal_locks_records():
+    """Summarizing a page in its own eigenbasis reproduces the LOCKS record
+    bit for bit; a page whose deviations lie in a given orthonormal basis is
+    scored exactly by the shared summary (unquantized)."""
+    rng = np.random.default_rng(59)
+    K = rng.standard_normal((6, 16, 128)) + rng.standard_normal((6, 1, 128)) * 3
+    recs, _, _ = O.build_records(K)
+    mu, V, _, _ = O.page_summary(K)
+    for p in range(6):
+        r2, _ = O.build_records_with_basis(K[p:p + 1], V[p])
+        assert np.array_equal(r2[0], recs[p])
+    Wb = _orthonormal(rng, 128, 8)
+    a = rng.standard_normal((3, 16, 8)) * 4
+    Kin = rng.standard_normal((3, 1, 128)) + a @ Wb.T
+    m2, V2, C2 = O.shared_summary(Kin, Wb)
+    q = rng.standard_normal((4, 128))
+    np.testing.assert_allclose(O.page_lse(q, m2, V2, C2), O.page_lse_exact(q, Kin), atol=1e-9)
+
+
 # --- quantization and packing ------------------------------------------------
 
 def test_quantization_codes_and_scales():
