@@ -42,8 +42,29 @@ V_QMAX = 7            # int4 basis codes lie in [-7, 7]
 CM_QMAX = 127         # int8 coefficient / centroid codes lie in [-127, 127]
 FP16_MAX = 65504.0
 
-# byte offsets inside one record
+# byte offsets inside one record (rank 8)
 OFF_V, OFF_C, OFF_MU, OFF_SV, OFF_SC, OFF_SMU, OFF_END = 0, 512, 640, 768, 784, 800, 802
+RANKS = (4, 8, 16)    # ranks with a record layout
+
+
+def record_layout(r=RANK):
+    """Byte offsets of a rank-r record, the rank-8 layout with every field
+    sized by r: basis codes at 0 (64 bytes per column), coefficient codes at
+    64r ([16 tokens][r]), centroid codes at 80r, s_V at 80r + 128, s_c at
+    82r + 128, s_mu at 84r + 128; zero padding up to a multiple of 64 bytes
+    (512, 832 and 1536 bytes for r = 4, 8, 16)."""
+    off_c = 64 * r
+    off_mu = off_c + PAGE * r
+    off_sv = off_mu + D_HEAD
+    off_sc = off_sv + 2 * r
+    off_smu = off_sc + 2 * r
+    end = off_smu + 2
+    return dict(v=0, c=off_c, mu=off_mu, sv=off_sv, sc=off_sc, smu=off_smu, end=end,
+                bytes=-(-end // 64) * 64)
+
+
+def record_bytes(r=RANK):
+    return record_layout(r)["bytes"]
 
 
 # ---------------------------------------------------------------------------
@@ -204,45 +225,49 @@ def _v_byte_index(k, d):
 
 
 def pack_record(qz) -> np.ndarray:
-    """Pack one quantized summary into its 832-byte record."""
-    rec = np.zeros(RECORD_BYTES, dtype=np.uint8)
+    """Pack one quantized summary into its record (832 bytes at rank 8)."""
     v = np.asarray(qz["v_q"], dtype=np.int64)      # [d, r]
     d, r = v.shape
+    lay = record_layout(r)
+    rec = np.zeros(lay["bytes"], dtype=np.uint8)
     for k in range(r):
         for t in range(d):
             bi, hi = _v_byte_index(k, t)
             nib = int(v[t, k]) & 0xF
             rec[bi] |= (nib << 4) if hi else nib
     c = np.asarray(qz["c_q"], dtype=np.int8)       # [B, r]
-    rec[OFF_C:OFF_C + c.size] = c.reshape(-1).view(np.uint8)
+    rec[lay["c"]:lay["c"] + c.size] = c.reshape(-1).view(np.uint8)
     m = np.asarray(qz["mu_q"], dtype=np.int8)
-    rec[OFF_MU:OFF_MU + m.size] = m.view(np.uint8)
-    rec[OFF_SV:OFF_SV + 2 * r] = np.asarray(qz["s_v"], dtype=np.float16).view(np.uint8)
-    rec[OFF_SC:OFF_SC + 2 * r] = np.asarray(qz["s_c"], dtype=np.float16).view(np.uint8)
-    rec[OFF_SMU:OFF_SMU + 2] = np.asarray([qz["s_mu"]], dtype=np.float16).view(np.uint8)
+    rec[lay["mu"]:lay["mu"] + m.size] = m.view(np.uint8)
+    rec[lay["sv"]:lay["sv"] + 2 * r] = np.asarray(qz["s_v"], dtype=np.float16).view(np.uint8)
+    rec[lay["sc"]:lay["sc"] + 2 * r] = np.asarray(qz["s_c"], dtype=np.float16).view(np.uint8)
+    rec[lay["smu"]:lay["smu"] + 2] = np.asarray([qz["s_mu"]], dtype=np.float16).view(np.uint8)
     return rec
 
 
 def unpack_record(rec, d=D_HEAD, B=PAGE, r=RANK):
-    """Inverse of pack_record for one record (uint8[832])."""
+    """Inverse of pack_record for one record (uint8[record_bytes(r)])."""
     rec = np.asarray(rec, dtype=np.uint8)
+    lay = record_layout(r)
     v = np.zeros((d, r), dtype=np.int8)
     for k in range(r):
         for t in range(d):
             bi, hi = _v_byte_index(k, t)
             nib = (int(rec[bi]) >> 4) if hi else (int(rec[bi]) & 0xF)
             v[t, k] = nib - 16 if nib >= 8 else nib
-    c = rec[OFF_C:OFF_C + B * r].view(np.int8).reshape(B, r).copy()
-    mu = rec[OFF_MU:OFF_MU + d].view(np.int8).copy()
-    s_v = rec[OFF_SV:OFF_SV + 2 * r].view(np.float16).astype(np.float64)
-    s_c = rec[OFF_SC:OFF_SC + 2 * r].view(np.float16).astype(np.float64)
-    s_mu = float(rec[OFF_SMU:OFF_SMU + 2].view(np.float16)[0])
+    c = rec[lay["c"]:lay["c"] + B * r].view(np.int8).reshape(B, r).copy()
+    mu = rec[lay["mu"]:lay["mu"] + d].view(np.int8).copy()
+    s_v = rec[lay["sv"]:lay["sv"] + 2 * r].view(np.float16).astype(np.float64)
+    s_c = rec[lay["sc"]:lay["sc"] + 2 * r].view(np.float16).astype(np.float64)
+    s_mu = float(rec[lay["smu"]:lay["smu"] + 2].view(np.float16)[0])
     return dict(mu_q=mu, s_mu=s_mu, v_q=v, s_v=s_v, c_q=c, s_c=s_c)
 
 
 def unpack_records(recs, d=D_HEAD, B=PAGE, r=RANK):
-    """Vectorized unpack of records [..., 832] into a dict of stacked arrays."""
+    """Vectorized unpack of records [..., record_bytes(r)] into a dict of
+    stacked arrays."""
     recs = np.asarray(recs, dtype=np.uint8)
+    lay = record_layout(r)
     lead = recs.shape[:-1]
     kk, tt = np.meshgrid(np.arange(r), np.arange(d), indexing="ij")   # [r, d]
     w, e = tt // 8, tt % 8
@@ -251,11 +276,11 @@ def unpack_records(recs, d=D_HEAD, B=PAGE, r=RANK):
     nib = np.where(e >= 4, byte >> 4, byte & 0xF)
     v = np.where(nib >= 8, nib - 16, nib).astype(np.int8)
     v = np.swapaxes(v, -1, -2)                                          # [..., d, r]
-    c = recs[..., OFF_C:OFF_C + B * r].copy().view(np.int8).reshape(*lead, B, r)
-    mu = recs[..., OFF_MU:OFF_MU + d].copy().view(np.int8)
-    s_v = recs[..., OFF_SV:OFF_SV + 2 * r].copy().view(np.float16).astype(np.float64)
-    s_c = recs[..., OFF_SC:OFF_SC + 2 * r].copy().view(np.float16).astype(np.float64)
-    s_mu = recs[..., OFF_SMU:OFF_SMU + 2].copy().view(np.float16).astype(np.float64)[..., 0]
+    c = recs[..., lay["c"]:lay["c"] + B * r].copy().view(np.int8).reshape(*lead, B, r)
+    mu = recs[..., lay["mu"]:lay["mu"] + d].copy().view(np.int8)
+    s_v = recs[..., lay["sv"]:lay["sv"] + 2 * r].copy().view(np.float16).astype(np.float64)
+    s_c = recs[..., lay["sc"]:lay["sc"] + 2 * r].copy().view(np.float16).astype(np.float64)
+    s_mu = recs[..., lay["smu"]:lay["smu"] + 2].copy().view(np.float16).astype(np.float64)[..., 0]
     return dict(mu_q=mu, s_mu=s_mu, v_q=v, s_v=s_v, c_q=c, s_c=s_c)
 
 
@@ -263,28 +288,32 @@ def pack_records(qz) -> np.ndarray:
     """Vectorized pack_record over a batch: qz arrays with a leading axis n."""
     v = np.asarray(qz["v_q"], dtype=np.int64)                  # [n, d, r]
     n, d, r = v.shape
-    recs = np.zeros((n, RECORD_BYTES), dtype=np.uint8)
+    lay = record_layout(r)
+    nbytes = lay["bytes"]
+    recs = np.zeros((n, nbytes), dtype=np.uint8)
     kk, tt = np.meshgrid(np.arange(r), np.arange(d), indexing="ij")
     w, e = tt // 8, tt % 8
     bi = (OFF_V + 64 * kk + 4 * w + (e % 4)).reshape(-1)
     sh = np.where(e >= 4, 4, 0).reshape(-1)
     nib = (np.swapaxes(v, 1, 2).reshape(n, -1) & 0xF) << sh       # [n, r*d]
-    acc = np.zeros((n, RECORD_BYTES), dtype=np.int64)
+    acc = np.zeros((n, nbytes), dtype=np.int64)
     np.add.at(acc, (slice(None), bi), nib)
-    recs[:, :OFF_C] = acc[:, :OFF_C].astype(np.uint8)
+    oc, om, osv, osc, osm = lay["c"], lay["mu"], lay["sv"], lay["sc"], lay["smu"]
+    recs[:, :oc] = acc[:, :oc].astype(np.uint8)
     c = np.asarray(qz["c_q"], dtype=np.int8).reshape(n, -1)
-    recs[:, OFF_C:OFF_C + c.shape[1]] = c.view(np.uint8)
+    recs[:, oc:oc + c.shape[1]] = c.view(np.uint8)
     m = np.asarray(qz["mu_q"], dtype=np.int8).reshape(n, -1)
-    recs[:, OFF_MU:OFF_MU + m.shape[1]] = m.view(np.uint8)
-    recs[:, OFF_SV:OFF_SV + 2 * r] = np.asarray(qz["s_v"], np.float16).reshape(n, r).view(np.uint8)
-    recs[:, OFF_SC:OFF_SC + 2 * r] = np.asarray(qz["s_c"], np.float16).reshape(n, r).view(np.uint8)
-    recs[:, OFF_SMU:OFF_SMU + 2] = np.asarray(qz["s_mu"], np.float16).reshape(n, 1).view(np.uint8)
+    recs[:, om:om + m.shape[1]] = m.view(np.uint8)
+    recs[:, osv:osv + 2 * r] = np.asarray(qz["s_v"], np.float16).reshape(n, r).view(np.uint8)
+    recs[:, osc:osc + 2 * r] = np.asarray(qz["s_c"], np.float16).reshape(n, r).view(np.uint8)
+    recs[:, osm:osm + 2] = np.asarray(qz["s_mu"], np.float16).reshape(n, 1).view(np.uint8)
     return recs
 
 
-def build_records(K_pages):
-    """Summaries of pages K [n, B, d] (float64) -> (records [n, 832], qz, lam)."""
-    mu, V, C, lam = page_summary(K_pages)
+def build_records(K_pages, r=RANK):
+    """Summaries of pages K [n, B, d] (float64) at rank r -> (records
+    [n, record_bytes(r)], qz, lam)."""
+    mu, V, C, lam = page_summary(K_pages, r)
     qz = quantize_summary(mu, V, C)
     return pack_records(qz), qz, lam
 
@@ -338,9 +367,10 @@ def page_lse_exact(q, K, scale=None):
     return logsumexp(np.einsum("...gd,...id->...gi", q, K) * scale, axis=-1)
 
 
-def score_records(q, records, scale=None):
-    """s_hat for G query heads q [G, d] against records [n, 832] -> [G, n]."""
-    qz = unpack_records(records)
+def score_records(q, records, scale=None, r=RANK):
+    """s_hat for G query heads q [G, d] against rank-r records
+    [n, record_bytes(r)] -> [G, n]."""
+    qz = unpack_records(records, r=r)
     mu, V, C = dequantize_summary(qz)
     s = page_lse(np.asarray(q, np.float64)[None], mu, V, C, scale)     # [n, G]
     return s.T.copy()

@@ -62,6 +62,73 @@ def test_estimate_exact_when_rank_le_r(rho):
     np.testing.assert_allclose(mu[:, None, :] + C @ np.swapaxes(V, 1, 2), K, atol=1e-10)
 
 
+@pytest.mark.parametrize("r,rho", [(4, 2), (4, 4), (16, 11), (16, 15)])
+def test_estimate_exact_when_rank_le_r_other_ranks(r, rho):
+    """The rank-4 and rank-16 summaries follow the same rule: a page of
+    centered rank rho <= r is reconstructed exactly (16 centered tokens have
+    rank <= 15, so rank 16 is exact on every page)."""
+    rng = np.random.default_rng(100 + 10 * r + rho)
+    K = _low_rank_pages(rng, 5, rho)
+    mu, V, C, lam = O.page_summary(K, r)
+    assert V.shape == (5, 128, r) and C.shape == (5, 16, r)
+    q = rng.standard_normal((4, 128)) * 2.0
+    np.testing.assert_allclose(O.page_lse(q[None], mu, V, C), O.page_lse_exact(q[None], K),
+                               rtol=0, atol=1e-10)
+    if r == 16:
+        K2 = rng.standard_normal((3, 16, 128))
+        m2, V2, C2, lam2 = O.page_summary(K2, 16)
+        np.testing.assert_allclose(O.energy_captured(lam2, 16), 1.0, atol=1e-12)
+        np.testing.assert_allclose(O.page_lse(q[None], m2, V2, C2),
+                                   O.page_lse_exact(q[None], K2), atol=1e-10)
+
+
+def test_record_layout_other_ranks():
+    """Rank-r records: 84r + 130 bytes of fields padded to a multiple of 64
+    (512 / 832 / 1536 bytes, 6.25% / 10.2% / 18.75% of a page-head's 8 KB of
+    K and V); rank 8 is the layout above.  Each field sits where the layout
+    says: a single nonzero code or scale lands in the byte it names, and a
+    pack/unpack round trip is exact."""
+    assert [O.record_bytes(r) for r in (4, 8, 16)] == [512, 832, 1536]
+    lay8 = O.record_layout(8)
+    assert (lay8["c"], lay8["mu"], lay8["sv"], lay8["sc"], lay8["smu"], lay8["end"]) == (
+        O.OFF_C, O.OFF_MU, O.OFF_SV, O.OFF_SC, O.OFF_SMU, O.OFF_END)
+    rng = np.random.default_rng(61)
+    for r in (4, 16):
+        lay = O.record_layout(r)
+        z = dict(v_q=np.zeros((128, r), np.int8), c_q=np.zeros((16, r), np.int8),
+                 mu_q=np.zeros(128, np.int8), s_v=np.zeros(r), s_c=np.zeros(r), s_mu=0.0)
+        t, k = 5, r - 1
+        one = dict(z, c_q=z["c_q"].copy())
+        one["c_q"][t, k] = 3
+        rec = O.pack_record(one)
+        assert rec.shape == (lay["bytes"],) and np.flatnonzero(rec).tolist() == [64 * r + r * t + k]
+        one = dict(z, mu_q=z["mu_q"].copy())
+        one["mu_q"][7] = -2
+        assert np.flatnonzero(O.pack_record(one)).tolist() == [80 * r + 7]
+        one = dict(z, s_c=np.eye(r)[k] * 1.0)      # fp16 1.0 = 0x3C00: high byte only
+        assert np.flatnonzero(O.pack_record(one)).tolist() == [82 * r + 128 + 2 * k + 1]
+        one = dict(z, s_mu=1.0)
+        assert np.flatnonzero(O.pack_record(one)).tolist() == [84 * r + 128 + 1]
+        # round trip, single and batched
+        K = rng.standard_normal((7, 16, 128)) * 2
+        recs, qz, _ = O.build_records(K, r)
+        assert recs.shape == (7, lay["bytes"]) and np.all(recs[:, lay["end"]:] == 0)
+        for p in range(7):
+            assert np.array_equal(O.pack_record({key: np.asarray(qz[key])[p] for key in qz}),
+                                  recs[p])
+            u = O.unpack_record(recs[p], r=r)
+            for key in qz:
+                np.testing.assert_array_equal(u[key], np.asarray(qz[key])[p])
+        ub = O.unpack_records(recs, r=r)
+        for key in qz:
+            np.testing.assert_array_equal(ub[key], qz[key])
+        # scoring the records is scoring the quantized summary they carry
+        q = rng.standard_normal((4, 128))
+        mh, Vh, Ch = O.dequantize_summary(qz)
+        np.testing.assert_allclose(O.score_records(q, recs, r=r),
+                                   O.page_lse(q[None], mh, Vh, Ch).T, atol=1e-12)
+
+
 def test_estimate_exact_on_bf16_axis_aligned_pages():
     """bf16 pages whose keys differ only in <= 8 coordinates keep rank <= 8
     after rounding, so the unquantized estimate is exact on the stored bytes."""
