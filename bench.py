@@ -385,6 +385,49 @@ def main():
             f"own pages")
         del wide
 
+    # variant: summary ranks 4 and 16 (the same step at other state sizes) on
+    # the first layers: step time per layer and recall against exact selection
+    if not args.no_variants:
+        nl = min(w.layers, 4)
+        P = inp.block_table.shape[1]
+        lse_x = torch.empty((w.batch, w.hq, P), dtype=torch.float32, device="cuda")
+        ws_x = torch.empty(L.score_workspace_bytes(d, w.batch, P, budget), dtype=torch.uint8,
+                           device="cuda")
+        sel_x = torch.empty((nl, w.batch, w.hkv, budget), dtype=torch.int32, device="cuda")
+        cnt_x = torch.empty((nl, w.batch, w.hkv), dtype=torch.int32, device="cuda")
+        for layer in range(nl):
+            L.exact_page_lse(d, inp.q[layer], inp.k[layer], inp.block_table, inp.seq_lens, lse_x)
+            L.select_pages(d, lse_x, inp.seq_lens, budget, sel_x[layer], cnt_x[layer], ws_x)
+        ranks = {}
+        for r in (4, 16):
+            dr = L.dims(w.hq, w.hkv, rank=r)
+            summ_r = torch.empty((nl, w.hkv, w.num_blocks, L.summary_bytes(dr)),
+                                 dtype=torch.uint8, device="cuda")
+            blocks = torch.arange(w.num_blocks, dtype=torch.int32, device="cuda")
+            for layer in range(nl):
+                L.build_summaries(dr, inp.k[layer], blocks, summ_r[layer])
+            st_r = DecodeStep(dr, inp.k[:nl], inp.v[:nl], summ_r, inp.q[:nl], inp.block_table,
+                              inp.seq_lens, budget)
+            ms_r = time_step(st_r, max(4, args.steps), 2)
+            inter = tot = 0
+            for layer in range(nl):
+                for b in range(w.batch):
+                    for g in range(w.hkv):
+                        c = int(st_r.cnt[layer, b, g])
+                        cx = int(cnt_x[layer, b, g])
+                        a = set(st_r.sel[layer, b, g, :c].tolist())
+                        e = set(sel_x[layer, b, g, :cx].tolist())
+                        inter += len(a & e)
+                        tot += len(e)
+            ranks[f"rank{r}"] = {"us_per_layer": round(ms_r * 1e3 / nl, 3),
+                                 "record_bytes": L.summary_bytes(dr),
+                                 "recall_vs_exact": inter / max(tot, 1), "layers": nl}
+            log(f"[{w.name}] rank {r}: {ms_r * 1e3 / nl:.2f} us/layer, recall vs exact "
+                f"{inter / max(tot, 1):.4f} ({L.summary_bytes(dr)} B records)")
+            del st_r, summ_r
+        extra.setdefault("variants", {}).update(ranks)
+        del lse_x, ws_x
+
     # achievable streaming-read bandwidth (context for the roofline)
     from synth.device import device_read
     rbuf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")

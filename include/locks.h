@@ -18,7 +18,8 @@
  *    failure a negative status is returned and nothing is launched.  A launch
  *    error returns LOCKS_ERR_LAUNCH.  Faults inside kernels surface at the
  *    caller's next synchronization.
- *  - Supported shape: head_dim 128, page_size 16, rank 8, and
+ *  - Supported shape: head_dim 128, page_size 16, rank 4, 8 or 16 (8 is the
+ *    pages' setting; 4 and 16 are the same method at other state sizes), and
  *    num_q_heads = 4 * num_kv_heads (GQA group of 4); anything else returns
  *    LOCKS_ERR_UNSUPPORTED.
  *  - bf16 tensors are raw bfloat16 bit patterns (uint16).
@@ -50,7 +51,7 @@ typedef struct {
   int32_t num_kv_heads; /* Hkv; Hq / Hkv is the GQA group size G   */
   int32_t head_dim;     /* d (128)                                 */
   int32_t page_size;    /* B, tokens per KV page (16)              */
-  int32_t rank;         /* r, basis vectors per page summary (8)   */
+  int32_t rank;         /* r, basis vectors per page summary (4, 8 or 16) */
 } locks_dims;
 
 /* Element strides (bf16 elements) of one layer's paged K or V cache:
@@ -62,10 +63,10 @@ typedef struct {
   int64_t token_stride;
 } locks_kv_layout;
 
-/* Bytes of one summary record per (page, KV head): 832 at d=128, B=16, r=8
- * (codes 768 B + 17 fp16 scales + padding to 64-byte lines; about 10% of
- * the page-head's 8192 K+V bytes, sec. 2 quantization paragraph).
- * Returns 0 for unsupported dims. */
+/* Bytes of one summary record per (page, KV head): 84r + 130 bytes of fields
+ * padded to a multiple of 64: 832 at r=8 (codes 768 B + 17 fp16 scales; about
+ * 10% of the page-head's 8192 K+V bytes, sec. 2 quantization paragraph), 512
+ * at r=4, 1536 at r=16.  Returns 0 for unsupported dims. */
 size_t locks_summary_bytes(const locks_dims* dims);
 
 /* Workspace sizes (bytes).  max_pages is the block-table row length; the
@@ -85,17 +86,19 @@ size_t locks_attend_workspace_bytes(const locks_dims* dims, int32_t batch,
  *   num_blocks : physical blocks in the layer (record array extent).
  *   summaries  : [Hkv][num_blocks][locks_summary_bytes] records, written for
  *                the listed blocks only.
- *   raw_debug  : nullable; fp32 [n_blocks][Hkv][1280] unquantized summary
- *                (mu[128], V as [r][128], C as [16][r]) for testing.
- * Record layout (little-endian):
- *   [0,512)   basis codes, int4 two's complement in [-7,7]: column k owns
- *             bytes [64k, 64k+64); 32-bit word w covers dims [8w, 8w+8);
- *             byte m of the word holds dim 8w+m in its low nibble and dim
- *             8w+4+m in its high nibble.
- *   [512,640) coefficient codes int8 [16 tokens][8 columns].
- *   [640,768) centroid codes int8 [128].
- *   [768,784) fp16 basis scales s_V[8]; [784,800) fp16 coefficient scales
- *             s_c[8]; [800,802) fp16 centroid scale; [802,832) zero.
+ *   raw_debug  : nullable; fp32 [n_blocks][Hkv][128 + 144 r] unquantized
+ *                summary (mu[128], V as [r][128], C as [16][r]) for testing
+ *                (1280 floats at r=8).
+ * Record layout (little-endian), offsets for rank r (r=8 in brackets):
+ *   [0, 64r)          [0,512) basis codes, int4 two's complement in [-7,7]:
+ *                     column k owns bytes [64k, 64k+64); 32-bit word w covers
+ *                     dims [8w, 8w+8); byte m of the word holds dim 8w+m in its
+ *                     low nibble and dim 8w+4+m in its high nibble.
+ *   [64r, 80r)        [512,640) coefficient codes int8 [16 tokens][r columns].
+ *   [80r, 80r+128)    [640,768) centroid codes int8 [128].
+ *   [80r+128, 82r+128) [768,784) fp16 basis scales s_V[r];
+ *   [82r+128, 84r+128) [784,800) fp16 coefficient scales s_c[r];
+ *   [84r+128, +2)     [800,802) fp16 centroid scale; zero to the record end.
  *   Dequantized: mu = s_mu*mu_q, v_k = s_V[k]*V_q[:,k], c_ik = s_c[k]*C_q[i,k].
  */
 locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
@@ -139,8 +142,8 @@ locks_status locks_decode_layer(const locks_dims* dims, const void* q, const voi
  *                 starts k_layer_stride bf16 elements further on.
  *   block_table : [batch][max_pages]; a block id outside [0, num_blocks)
  *                 is skipped.
- *   summaries   : layer 0's records, [Hkv][num_blocks][832]; layer l starts
- *                 summ_layer_stride bytes further on.
+ *   summaries   : layer 0's records, [Hkv][num_blocks][locks_summary_bytes];
+ *                 layer l starts summ_layer_stride bytes further on.
  *   n_layers    : >= 1 (the strides are ignored when it is 1). */
 locks_status locks_finalize_pages(const locks_dims* dims, const void* k_cache,
                                   locks_kv_layout layout, int32_t num_blocks,
@@ -154,7 +157,7 @@ locks_status locks_finalize_pages(const locks_dims* dims, const void* k_cache,
  *   s_hat[b][h][j] = LSE_i ( (q_h.mu_j + (V_j^T q_h).c_i) / sqrt(d) ),
  * natural log, for query head h and logical page j < seq_lens[b] / 16.
  *   q           : bf16 [batch][Hq][d].
- *   summaries   : this layer's records, [Hkv][num_blocks][832].
+ *   summaries   : this layer's records, [Hkv][num_blocks][locks_summary_bytes].
  *   block_table : [batch][max_pages] physical block of each logical page.
  *   seq_lens    : [batch] tokens per sequence.
  *   page_lse    : fp32 [batch][Hq][max_pages]; entries for pages that are not
@@ -260,10 +263,10 @@ locks_status locks_decode_layer_tables(const locks_dims* dims, const void* q,
  * Proposition 1: one query-independent rank-r projection for every page is
  * blind to in-page directions outside it).  For each KV head: the pooled
  * scatter S = sum_j X_j^T X_j of the listed pages' deviations from their own
- * centroids, and its top-8 eigenvectors.
+ * centroids, and its top-r eigenvectors (r = dims->rank).
  *   block_ids : [n_blocks] physical blocks pooled (ids outside
  *               [0, num_blocks) add nothing); n_blocks >= 1.
- *   basis     : fp32 [Hkv][8][128], row k = the k-th eigenvector (descending
+ *   basis     : fp32 [Hkv][r][128], row k = the k-th eigenvector (descending
  *               eigenvalue, ties to the lower index), unit length, largest-
  *               |entry| component positive (lowest index on ties).
  *   eigvals   : nullable fp32 [Hkv][128], all eigenvalues of S, descending.
@@ -283,7 +286,7 @@ locks_status locks_shared_basis(const locks_dims* dims, const void* k_cache,
  * page's centroid and coefficients c_i = V^T x_i in the given basis, stored
  * and quantized exactly as locks_build_summaries stores its own (the record
  * layout above), so locks_score_pages and the rest read them unchanged.
- *   basis : fp32 [Hkv][8][128] (rows = basis vectors), e.g. from
+ *   basis : fp32 [Hkv][r][128] (rows = basis vectors), e.g. from
  *           locks_shared_basis.
  * Other arguments and errors as for locks_build_summaries. */
 locks_status locks_build_summaries_basis(const locks_dims* dims, const void* k_cache,

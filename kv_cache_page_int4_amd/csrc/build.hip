@@ -84,17 +84,30 @@ __device__ __forceinline__ void jacobi_rot(float app, float apq, float aqq, floa
   s = t * c;
 }
 
+// Record of rank R (R = 4, 8, 16): the rank-8 layout with every field sized
+// by R, in 32-bit words: basis codes [0, 16R), coefficient codes
+// [16R, 20R), centroid codes [20R, 20R + 32), s_V [20R + 32, +R/2), s_c the
+// next R/2 words, s_mu the low half of the word after, zero up to the record
+// size (the fields' 84R + 130 bytes rounded up to 64).
+template <int R>
+struct RecLayout {
+  static constexpr int kBytes = rec_bytes(R);
+  static constexpr int kWC = 16 * R, kWMu = 20 * R, kWSv = 20 * R + 32;
+  static constexpr int kWSc = kWSv + R / 2, kWSmu = kWSc + R / 2;
+};
+
+template <int R>
 struct BuildSmem {
   float X[kB][kD + 4];     // centered keys
   float G[kB][kB + 1];     // Gram matrix -> eigenvalues on the diagonal
   float U[kB][kB + 1];     // eigenvectors (columns)
   float cs[8][2];          // rotations of the current step
-  float V[kR][kD + 4];     // unquantized basis, [k][d]
-  float C[kB][kR];         // unquantized coefficients
+  float V[R][kD + 4];      // unquantized basis, [k][d]
+  float C[kB][R];          // unquantized coefficients
   float mu[kD];
   int order[kB];
-  int8_t vq[kR][kD];
-  uint32_t rec[kRec / 4];
+  int8_t vq[R][kD];
+  uint32_t rec[RecLayout<R>::kBytes / 4];
 };
 
 // Which block a workgroup summarizes: entry blockIdx.x of a list, or (for
@@ -111,13 +124,15 @@ struct BlockSource {
   int64_t summ_layer_stride;
 };
 
+template <int R>
 __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ kc, int64_t bs,
                                                    int64_t hs, int64_t ts, BlockSource src,
                                                    int32_t n_blocks, int32_t num_blocks,
                                                    int32_t hkv, uint8_t* __restrict__ summ,
                                                    float* __restrict__ raw,
                                                    const float* __restrict__ basis) {
-  __shared__ BuildSmem sm;
+  using RL = RecLayout<R>;
+  __shared__ BuildSmem<R> sm;
   const int lane = threadIdx.x;
   const int bi = blockIdx.x, kvh = blockIdx.y;
   kc += (size_t)blockIdx.z * src.k_layer_stride;
@@ -161,9 +176,9 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 
   const int d0 = 2 * lane;   // basis dims owned by this lane: d0, d0 + 1
   if (basis) {
-    const float* bk = basis + (size_t)kvh * kR * kD;
+    const float* bk = basis + (size_t)kvh * R * kD;
 #pragma unroll
-    for (int k = 0; k < kR; ++k) {
+    for (int k = 0; k < R; ++k) {
       sm.V[k][d0] = bk[k * kD + d0];
       sm.V[k][d0 + 1] = bk[k * kD + d0 + 1];
     }
@@ -261,7 +276,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 
     // basis v_k = X^T u_k / |X^T u_k|; lane owns dims 2*lane, 2*lane+1
 #pragma unroll
-    for (int k = 0; k < kR; ++k) {
+    for (int k = 0; k < R; ++k) {
       const int j = sm.order[k];
       const float lk = sm.G[j][j];
       const bool keep = page_has_basis && (lk > kTau * lam1);
@@ -306,17 +321,21 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     __syncthreads();
   }
 
-  // coefficients c_ik = v_k . x_i : lane -> token t, columns 2*(lane>>4) .. +1
+  // coefficients c_ik = v_k . x_i : lane -> token t, columns
+  // (R/4)*(lane>>4) .. +R/4
   {
-    const int tk = lane & 15, k0 = 2 * (lane >> 4);
-    float c0 = 0.f, c1 = 0.f;
+    constexpr int kPer = R / 4;
+    const int tk = lane & 15, k0 = kPer * (lane >> 4);
+    float cc[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) cc[j] = 0.f;
     for (int d = 0; d < kD; ++d) {
       const float xv = sm.X[tk][d];
-      c0 = fmaf(xv, sm.V[k0][d], c0);
-      c1 = fmaf(xv, sm.V[k0 + 1][d], c1);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) cc[j] = fmaf(xv, sm.V[k0 + j][d], cc[j]);
     }
-    sm.C[tk][k0] = c0;
-    sm.C[tk][k0 + 1] = c1;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) sm.C[tk][k0 + j] = cc[j];
   }
   __syncthreads();
 
@@ -326,28 +345,27 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
   const float s_mu = fp16_scale(wave_max(fmaxf(fabsf(mu0), fabsf(mu1))), 127.f);
   const int mq0 = quant(mu0, s_mu, 127), mq1 = quant(mu1, s_mu, 127);
   // basis scales and codes
-  float s_v[kR];
+  float s_v[R];
 #pragma unroll
-  for (int k = 0; k < kR; ++k) {
+  for (int k = 0; k < R; ++k) {
     const float a = sm.V[k][d0], b2 = sm.V[k][d0 + 1];
     s_v[k] = fp16_scale(wave_max(fmaxf(fabsf(a), fabsf(b2))), 7.f);
     sm.vq[k][d0] = (int8_t)quant(a, s_v[k], 7);
     sm.vq[k][d0 + 1] = (int8_t)quant(b2, s_v[k], 7);
   }
   // coefficient scales: column k max over the 16 tokens
-  float s_c[kR];
+  float s_c[R];
 #pragma unroll
-  for (int k = 0; k < kR; ++k) {
+  for (int k = 0; k < R; ++k) {
     const float a = (lane < 16) ? fabsf(sm.C[lane][k]) : 0.f;
     s_c[k] = fp16_scale(wave_max(a), 127.f);
   }
   __syncthreads();
-  // record words: [0,128) basis, [128,160) coefficients, [160,192) centroid,
-  // [192,196) s_V, [196,200) s_c, [200] s_mu, [201,208) zero
-  uint8_t* mub = reinterpret_cast<uint8_t*>(&sm.rec[160]);
+  // record words: basis, coefficients, centroid, s_V, s_c, s_mu, zero
+  uint8_t* mub = reinterpret_cast<uint8_t*>(&sm.rec[RL::kWMu]);
   mub[d0] = (uint8_t)(int8_t)mq0;
   mub[d0 + 1] = (uint8_t)(int8_t)mq1;
-  for (int wi = lane; wi < 128; wi += 64) {
+  for (int wi = lane; wi < 16 * R; wi += 64) {
     const int k = wi >> 4, w = wi & 15;
     uint32_t word = 0;
 #pragma unroll
@@ -358,73 +376,109 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     }
     sm.rec[wi] = word;
   }
-  if (lane < 32) {
-    const int tk = lane >> 1, kh = 4 * (lane & 1);
+  // coefficient words: token tk holds R/4 words of 4 codes each
+  if (lane < 4 * R) {
+    constexpr int kWpt = R / 4;
+    const int tk = lane / kWpt, kh = 4 * (lane % kWpt);
     uint32_t word = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      word |= ((uint32_t)(uint8_t)(int8_t)quant(sm.C[tk][kh + e], s_c[kh + e], 127)) << (8 * e);
-    sm.rec[128 + lane] = word;
+    for (int e = 0; e < 4; ++e) {
+      float sce = s_c[0];
+#pragma unroll
+      for (int k = 1; k < R; ++k) sce = (k == kh + e) ? s_c[k] : sce;
+      word |= ((uint32_t)(uint8_t)(int8_t)quant(sm.C[tk][kh + e], sce, 127)) << (8 * e);
+    }
+    sm.rec[RL::kWC + lane] = word;
   }
   if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sm.rec[192 + i] = fp16_bits(s_v[2 * i]) | (fp16_bits(s_v[2 * i + 1]) << 16);
-      sm.rec[196 + i] = fp16_bits(s_c[2 * i]) | (fp16_bits(s_c[2 * i + 1]) << 16);
+    for (int i = 0; i < R / 2; ++i) {
+      sm.rec[RL::kWSv + i] = fp16_bits(s_v[2 * i]) | (fp16_bits(s_v[2 * i + 1]) << 16);
+      sm.rec[RL::kWSc + i] = fp16_bits(s_c[2 * i]) | (fp16_bits(s_c[2 * i + 1]) << 16);
     }
-    sm.rec[200] = fp16_bits(s_mu);
-    for (int i = 201; i < kRec / 4; ++i) sm.rec[i] = 0u;
+    sm.rec[RL::kWSmu] = fp16_bits(s_mu);
+    for (int i = RL::kWSmu + 1; i < RL::kBytes / 4; ++i) sm.rec[i] = 0u;
   }
   __syncthreads();
-  uint32_t* dst = reinterpret_cast<uint32_t*>(summ + ((size_t)kvh * num_blocks + blk) * kRec);
-  for (int wi = lane; wi < kRec / 4; wi += 64) dst[wi] = sm.rec[wi];
+  uint32_t* dst =
+      reinterpret_cast<uint32_t*>(summ + ((size_t)kvh * num_blocks + blk) * RL::kBytes);
+  for (int wi = lane; wi < RL::kBytes / 4; wi += 64) dst[wi] = sm.rec[wi];
 
-  if (raw) {
-    float* r = raw + ((size_t)bi * hkv + kvh) * 1280;
+  if (raw) {   // [128 + 144 R] floats: mu, V [R][128], C [16][R]
+    float* r = raw + ((size_t)bi * hkv + kvh) * raw_floats(R);
     for (int i = lane; i < kD; i += 64) r[i] = sm.mu[i];
-    for (int i = lane; i < kR * kD; i += 64) r[kD + i] = sm.V[i >> 7][i & 127];
-    for (int i = lane; i < kB * kR; i += 64) r[kD + kR * kD + i] = sm.C[i >> 3][i & 7];
+    for (int i = lane; i < R * kD; i += 64) r[kD + i] = sm.V[i >> 7][i & 127];
+    for (int i = lane; i < kB * R; i += 64) r[kD + R * kD + i] = sm.C[i / R][i % R];
+  }
+}
+
+template <int R>
+hipError_t launch_build_r(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
+                          int64_t token_stride, const BlockSource& src, dim3 grid,
+                          int32_t n_blocks, int32_t num_blocks, int32_t hkv, uint8_t* summaries,
+                          float* raw_debug, const float* basis, hipStream_t stream) {
+  hipLaunchKernelGGL(build_kernel<R>, grid, dim3(64), 0, stream, k_cache, block_stride,
+                     head_stride, token_stride, src, n_blocks, num_blocks, hkv, summaries,
+                     raw_debug, basis);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_any(int32_t rank, const uint16_t* k_cache, int64_t block_stride,
+                            int64_t head_stride, int64_t token_stride, const BlockSource& src,
+                            dim3 grid, int32_t n_blocks, int32_t num_blocks, int32_t hkv,
+                            uint8_t* summaries, float* raw_debug, const float* basis,
+                            hipStream_t stream) {
+  switch (rank) {
+    case 4:
+      return launch_build_r<4>(k_cache, block_stride, head_stride, token_stride, src, grid,
+                               n_blocks, num_blocks, hkv, summaries, raw_debug, basis, stream);
+    case 8:
+      return launch_build_r<8>(k_cache, block_stride, head_stride, token_stride, src, grid,
+                               n_blocks, num_blocks, hkv, summaries, raw_debug, basis, stream);
+    case 16:
+      return launch_build_r<16>(k_cache, block_stride, head_stride, token_stride, src, grid,
+                                n_blocks, num_blocks, hkv, summaries, raw_debug, basis, stream);
+    default:
+      return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_build(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
-                        int64_t token_stride, const int32_t* block_ids, int32_t n_blocks,
-                        int32_t num_blocks, int32_t hkv, uint8_t* summaries, float* raw_debug,
-                        hipStream_t stream) {
+hipError_t launch_build(int32_t rank, const uint16_t* k_cache, int64_t block_stride,
+                        int64_t head_stride, int64_t token_stride, const int32_t* block_ids,
+                        int32_t n_blocks, int32_t num_blocks, int32_t hkv, uint8_t* summaries,
+                        float* raw_debug, hipStream_t stream) {
   if (n_blocks == 0) return hipSuccess;
   BlockSource src{block_ids, nullptr, nullptr, 0, false, 0, 0};
-  hipLaunchKernelGGL(build_kernel, dim3(n_blocks, hkv), dim3(64), 0, stream, k_cache,
-                     block_stride, head_stride, token_stride, src, n_blocks, num_blocks,
-                     hkv, summaries, raw_debug, (const float*)nullptr);
-  return hipGetLastError();
+  return launch_build_any(rank, k_cache, block_stride, head_stride, token_stride, src,
+                          dim3(n_blocks, hkv), n_blocks, num_blocks, hkv, summaries, raw_debug,
+                          nullptr, stream);
 }
 
-hipError_t launch_build_basis(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
-                              int64_t token_stride, const int32_t* block_ids, int32_t n_blocks,
-                              int32_t num_blocks, int32_t hkv, const float* basis,
-                              uint8_t* summaries, hipStream_t stream) {
+hipError_t launch_build_basis(int32_t rank, const uint16_t* k_cache, int64_t block_stride,
+                              int64_t head_stride, int64_t token_stride,
+                              const int32_t* block_ids, int32_t n_blocks, int32_t num_blocks,
+                              int32_t hkv, const float* basis, uint8_t* summaries,
+                              hipStream_t stream) {
   if (n_blocks == 0) return hipSuccess;
   BlockSource src{block_ids, nullptr, nullptr, 0, false, 0, 0};
-  hipLaunchKernelGGL(build_kernel, dim3(n_blocks, hkv), dim3(64), 0, stream, k_cache,
-                     block_stride, head_stride, token_stride, src, n_blocks, num_blocks,
-                     hkv, summaries, (float*)nullptr, basis);
-  return hipGetLastError();
+  return launch_build_any(rank, k_cache, block_stride, head_stride, token_stride, src,
+                          dim3(n_blocks, hkv), n_blocks, num_blocks, hkv, summaries, nullptr,
+                          basis, stream);
 }
 
-hipError_t launch_finalize(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
-                           int64_t token_stride, const int32_t* block_table, int32_t max_pages,
-                           const int32_t* seq_lens, int32_t batch, int32_t num_blocks,
-                           int32_t hkv, uint8_t* summaries, int32_t n_layers,
+hipError_t launch_finalize(int32_t rank, const uint16_t* k_cache, int64_t block_stride,
+                           int64_t head_stride, int64_t token_stride, const int32_t* block_table,
+                           int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                           int32_t num_blocks, int32_t hkv, uint8_t* summaries, int32_t n_layers,
                            int64_t k_layer_stride, int64_t summ_layer_stride,
                            hipStream_t stream) {
   BlockSource src{nullptr, seq_lens, block_table, max_pages, true, k_layer_stride,
                   summ_layer_stride};
-  hipLaunchKernelGGL(build_kernel, dim3(batch, hkv, n_layers), dim3(64), 0, stream, k_cache, block_stride,
-                     head_stride, token_stride, src, batch, num_blocks, hkv, summaries,
-                     (float*)nullptr, (const float*)nullptr);
-  return hipGetLastError();
+  return launch_build_any(rank, k_cache, block_stride, head_stride, token_stride, src,
+                          dim3(batch, hkv, n_layers), batch, num_blocks, hkv, summaries, nullptr,
+                          nullptr, stream);
 }
 
 }  // namespace locks

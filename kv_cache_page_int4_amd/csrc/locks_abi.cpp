@@ -15,7 +15,8 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 locks_status check_dims(const locks_dims* d) {
   if (!d) return LOCKS_ERR_NULL;
   if (d->num_q_heads <= 0 || d->num_kv_heads <= 0) return LOCKS_ERR_SHAPE;
-  if (d->head_dim != 128 || d->page_size != 16 || d->rank != 8) return LOCKS_ERR_UNSUPPORTED;
+  if (d->head_dim != 128 || d->page_size != 16 || !rank_supported(d->rank))
+    return LOCKS_ERR_UNSUPPORTED;
   if (d->num_q_heads != 4 * d->num_kv_heads) return LOCKS_ERR_UNSUPPORTED;
   return LOCKS_OK;
 }
@@ -74,7 +75,7 @@ inline char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; 
 extern "C" {
 
 size_t locks_summary_bytes(const locks_dims* dims) {
-  return check_dims(dims) == LOCKS_OK ? (size_t)832 : 0;
+  return check_dims(dims) == LOCKS_OK ? (size_t)rec_bytes(dims->rank) : 0;
 }
 
 size_t locks_score_workspace_bytes(const locks_dims* dims, int32_t batch, int32_t max_pages,
@@ -104,7 +105,7 @@ locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
     return LOCKS_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(k_cache) & 15) || (reinterpret_cast<uintptr_t>(summaries) & 15))
     return LOCKS_ERR_SHAPE;
-  hipError_t e = launch_build(static_cast<const uint16_t*>(k_cache), layout.block_stride,
+  hipError_t e = launch_build(dims->rank, static_cast<const uint16_t*>(k_cache), layout.block_stride,
                               layout.head_stride, layout.token_stride, block_ids, n_blocks,
                               num_blocks, dims->num_kv_heads, static_cast<uint8_t*>(summaries),
                               raw_debug, static_cast<hipStream_t>(stream));
@@ -134,7 +135,7 @@ locks_status locks_score_pages(const locks_dims* dims, const void* q, const void
   if (!page_lse) return LOCKS_ERR_NULL;
   const ScoreWs w = score_ws_layout(dims, batch, max_pages, 0, true);
   if (!workspace || workspace_bytes < w.total) return LOCKS_ERR_WORKSPACE;
-  hipError_t e = launch_score(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
+  hipError_t e = launch_score(dims->rank, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
                               num_blocks, block_table, max_pages, seq_lens, batch,
                               dims->num_q_heads, dims->num_kv_heads, page_lse,
                               reinterpret_cast<float2*>(ws_at(workspace, w.part_off)), w.sp,
@@ -201,7 +202,7 @@ locks_status locks_score_select(const locks_dims* dims, const void* q, const voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* lse = page_lse ? page_lse : reinterpret_cast<float*>(ws_at(workspace, w.lse_off));
   float2* part = reinterpret_cast<float2*>(ws_at(workspace, w.part_off));
-  hipError_t e = launch_score(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
+  hipError_t e = launch_score(dims->rank, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
                               num_blocks, block_table, max_pages, seq_lens, batch,
                               dims->num_q_heads, dims->num_kv_heads, lse, part, w.sp, s);
   if (e == hipSuccess)
@@ -247,7 +248,7 @@ static locks_status decode_layer_impl(const locks_dims* dims, const void* q,
   float* po = reinterpret_cast<float*>(ws_at(attend_ws, a.o_off));
   float2* pml = reinterpret_cast<float2*>(ws_at(attend_ws, a.ml_off));
   const int hq = dims->num_q_heads, hkv = dims->num_kv_heads;
-  hipError_t e = launch_score(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
+  hipError_t e = launch_score(dims->rank, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
                               num_blocks, block_table, max_pages, seq_lens, batch, hq, hkv, lse,
                               part, w.sp, s);
   if (e != hipSuccess) return LOCKS_ERR_LAUNCH;
@@ -323,7 +324,7 @@ locks_status locks_finalize_pages(const locks_dims* dims, const void* k_cache,
   if (n_layers <= 0 || n_layers > 65535 || (n_layers > 1 && (k_layer_stride <= 0 ||
       summ_layer_stride <= 0 || (k_layer_stride % 8) || (summ_layer_stride % 16))))
     return LOCKS_ERR_SHAPE;
-  hipError_t e = launch_finalize(static_cast<const uint16_t*>(k_cache), layout.block_stride,
+  hipError_t e = launch_finalize(dims->rank, static_cast<const uint16_t*>(k_cache), layout.block_stride,
                                  layout.head_stride, layout.token_stride, block_table, max_pages,
                                  seq_lens, batch, num_blocks, dims->num_kv_heads,
                                  static_cast<uint8_t*>(summaries), n_layers, k_layer_stride,
@@ -452,7 +453,8 @@ locks_status locks_shared_basis(const locks_dims* dims, const void* k_cache,
   const size_t need = locks_shared_basis_workspace_bytes(dims, n_blocks);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15))
     return LOCKS_ERR_WORKSPACE;
-  hipError_t e = launch_shared_basis(static_cast<const uint16_t*>(k_cache), layout.block_stride,
+  hipError_t e = launch_shared_basis(dims->rank, static_cast<const uint16_t*>(k_cache),
+                                     layout.block_stride,
                                      layout.head_stride, layout.token_stride, block_ids, n_blocks,
                                      num_blocks, dims->num_kv_heads,
                                      static_cast<float*>(workspace), pl, basis, eigvals,
@@ -473,7 +475,8 @@ locks_status locks_build_summaries_basis(const locks_dims* dims, const void* k_c
   if (st != LOCKS_OK) return st;
   if ((reinterpret_cast<uintptr_t>(summaries) & 15) || (reinterpret_cast<uintptr_t>(basis) & 3))
     return LOCKS_ERR_SHAPE;
-  hipError_t e = launch_build_basis(static_cast<const uint16_t*>(k_cache), layout.block_stride,
+  hipError_t e = launch_build_basis(dims->rank, static_cast<const uint16_t*>(k_cache),
+                                    layout.block_stride,
                                     layout.head_stride, layout.token_stride, block_ids, n_blocks,
                                     num_blocks, dims->num_kv_heads, basis,
                                     static_cast<uint8_t*>(summaries),

@@ -7,6 +7,14 @@
 
 namespace locks {
 
+// ---- summary records ----------------------------------------------------------
+// A rank-r record holds 84r + 130 bytes of fields (basis codes, coefficient
+// codes, centroid codes, fp16 scales), padded to a multiple of 64 bytes.
+constexpr int rec_bytes(int r) { return (84 * r + 130 + 63) / 64 * 64; }
+constexpr bool rank_supported(int r) { return r == 4 || r == 8 || r == 16; }
+// raw_debug floats per page-head: mu [128], V [r][128], C [16][r]
+constexpr int raw_floats(int r) { return 128 + 144 * r; }
+
 // ---- scoring ---------------------------------------------------------------
 constexpr int32_t kScoreSteps = 4;     // 4-page steps per scoring wave
 struct ScorePlan {
@@ -14,7 +22,7 @@ struct ScorePlan {
 };
 ScorePlan plan_score(int32_t batch, int32_t hkv, int32_t max_pages);
 
-hipError_t launch_score(const uint16_t* q, const uint8_t* summ, int32_t num_blocks,
+hipError_t launch_score(int32_t rank, const uint16_t* q, const uint8_t* summ, int32_t num_blocks,
                         const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
                         int32_t batch, int32_t hq, int32_t hkv, float* page_lse,
                         float2* partials, const ScorePlan& plan, hipStream_t stream);
@@ -87,16 +95,18 @@ struct SharedPlan {
 SharedPlan plan_shared(int32_t n_blocks);
 // partials: float [hkv][n_chunks][128][128]; basis: float [hkv][8][128];
 // eigvals: nullable float [hkv][128], descending.
-hipError_t launch_shared_basis(const uint16_t* k_cache, int64_t block_stride,
+// basis: float [hkv][rank][128] (the top-rank eigenvectors).
+hipError_t launch_shared_basis(int32_t rank, const uint16_t* k_cache, int64_t block_stride,
                                int64_t head_stride, int64_t token_stride,
                                const int32_t* block_ids, int32_t n_blocks, int32_t num_blocks,
                                int32_t hkv, float* partials, const SharedPlan& plan,
                                float* basis, float* eigvals, hipStream_t stream);
-// Summaries in a given basis (float [hkv][8][128], rows = basis vectors).
-hipError_t launch_build_basis(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
-                              int64_t token_stride, const int32_t* block_ids, int32_t n_blocks,
-                              int32_t num_blocks, int32_t hkv, const float* basis,
-                              uint8_t* summaries, hipStream_t stream);
+// Summaries in a given basis (float [hkv][rank][128], rows = basis vectors).
+hipError_t launch_build_basis(int32_t rank, const uint16_t* k_cache, int64_t block_stride,
+                              int64_t head_stride, int64_t token_stride,
+                              const int32_t* block_ids, int32_t n_blocks, int32_t num_blocks,
+                              int32_t hkv, const float* basis, uint8_t* summaries,
+                              hipStream_t stream);
 
 // ---- exact page LSE (read-every-key comparator) ---------------------------------
 hipError_t launch_exact_lse(const uint16_t* q, const uint16_t* k_cache, int64_t block_stride,
@@ -106,15 +116,16 @@ hipError_t launch_exact_lse(const uint16_t* q, const uint16_t* k_cache, int64_t 
                             float scale, float* page_lse, hipStream_t stream);
 
 // ---- summary build -----------------------------------------------------------
-hipError_t launch_build(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
-                        int64_t token_stride, const int32_t* block_ids, int32_t n_blocks,
-                        int32_t num_blocks, int32_t hkv, uint8_t* summaries, float* raw_debug,
-                        hipStream_t stream);
+hipError_t launch_build(int32_t rank, const uint16_t* k_cache, int64_t block_stride,
+                        int64_t head_stride, int64_t token_stride, const int32_t* block_ids,
+                        int32_t n_blocks, int32_t num_blocks, int32_t hkv, uint8_t* summaries,
+                        float* raw_debug, hipStream_t stream);
 
 // Incremental finalization: summarize, for every sequence whose length is a
 // positive multiple of the page size, its last full page (decided on the device).
-hipError_t launch_finalize(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
-                           int64_t token_stride, const int32_t* block_table, int32_t max_pages,
+hipError_t launch_finalize(int32_t rank, const uint16_t* k_cache, int64_t block_stride,
+                           int64_t head_stride, int64_t token_stride, const int32_t* block_table,
+                           int32_t max_pages,
                            const int32_t* seq_lens, int32_t batch, int32_t num_blocks,
                            int32_t hkv, uint8_t* summaries, int32_t n_layers,
                            int64_t k_layer_stride, int64_t summ_layer_stride,

@@ -72,9 +72,22 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16(uint2 v) {
 }
 
 constexpr int kRing = 2;           // LDS record slots (steps) per wave: 1 in flight
-constexpr int kUnits = 51;         // 16-byte units copied per record (bytes [0, 816))
-constexpr int kSlotRec = 16 * kUnits;
-constexpr int kStepBytes = 4 * kSlotRec;
+
+// Field offsets of a rank-R record (the rank-8 layout with every field sized
+// by R) and its LDS slot: the record's fields are copied in whole 16-byte
+// units, the trailing pad skipped (51 units at rank 8), one or two DMA
+// instructions per record.
+template <int R>
+struct ScoreLayout {
+  static constexpr int kRecB = rec_bytes(R);
+  static constexpr int kOffC = 64 * R, kOffMu = 80 * R, kOffSv = 80 * R + 128;
+  static constexpr int kOffSc = 82 * R + 128, kOffSmu = 84 * R + 128;
+  static constexpr int kUnits = (84 * R + 130 + 15) / 16;
+  static constexpr int kSlotRec = 16 * kUnits;
+  static constexpr int kStepBytes = 4 * kSlotRec;
+  static constexpr int kDmaPerRec = (kUnits + 63) / 64;
+  static constexpr int kDmaPerStep = 4 * kDmaPerRec;
+};
 
 struct ScoreParams {
   const uint16_t* q;
@@ -103,7 +116,12 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+template <int R>
 __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
+  using SL = ScoreLayout<R>;
+  constexpr int kSlotRec = SL::kSlotRec, kStepBytes = SL::kStepBytes;
+  constexpr int kOffC = SL::kOffC, kOffMu = SL::kOffMu, kOffSv = SL::kOffSv;
+  constexpr int kOffSc = SL::kOffSc, kOffSmu = SL::kOffSmu;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kStepBytes];
   __shared__ __attribute__((aligned(16))) float outl[kG][4 * kScoreSteps];
 
@@ -122,7 +140,7 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
   const int s0 = w * kScoreSteps;                          // first step of this workgroup
   const int n = max(0, min(kScoreSteps, nsteps - s0));    // its steps
 
-  const uint8_t* __restrict__ summ_h = p.summ + (size_t)kvh * p.num_blocks * kRec;
+  const uint8_t* __restrict__ summ_h = p.summ + (size_t)kvh * p.num_blocks * SL::kRecB;
   const int32_t* __restrict__ bt = p.block_table + (size_t)b * p.max_pages;
   float* __restrict__ lse_out = p.page_lse + ((size_t)b * p.hq + qhead0) * p.max_pages;
 
@@ -192,9 +210,12 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
       const int bi[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint8_t* base = summ_h + (size_t)max(bi[i], 0) * kRec;
-        if (lane < kUnits)
-          dma16(16u * lane, base, __builtin_amdgcn_readfirstlane(slot + kSlotRec * i));
+        const uint8_t* base = summ_h + (size_t)max(bi[i], 0) * SL::kRecB;
+#pragma unroll
+        for (int u = 0; u < SL::kDmaPerRec; ++u)
+          if (64 * u + lane < SL::kUnits)
+            dma16(16u * (64 * u + lane), base,
+                  __builtin_amdgcn_readfirstlane(slot + kSlotRec * i + 1024 * u));
       }
     };
 
@@ -212,7 +233,7 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
       if (more) issue(k + 1, b1);
       b0 = b1;
       b1 = (k + 2 < n) ? step_bids(k + 2) : none;
-      if (more) wait_vm<4>();
+      if (more) wait_vm<SL::kDmaPerStep>();
       else wait_vm<0>();
 
       const uint8_t* S = &ring[k & 1][0];
@@ -221,19 +242,23 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
       const int bid_row = (row == 0) ? bcur.x : (row == 1) ? bcur.y : (row == 2) ? bcur.z : bcur.w;
       const bool okp = bid_row >= 0;
 
-      // ---- V^T q: A rows (page tok/4, basis tok%4 [+4]), dims 32 row + 8s + e ----
+      // ---- V^T q: A rows (page tok/4, basis tok%4 + 4j), dims 32 row + 8s + e ----
+      constexpr int kAcc = R / 4;   // accumulators: basis columns 4j .. 4j+3
       const uint8_t* av = S + kSlotRec * (tok >> 2) + 64 * (lane & 3) + 16 * row;
-      const uint4 va = lds16(av), vb = lds16(av + 256);
-      f32x4 acc0 = {acc0_init, acc0_init, acc0_init, acc0_init};
-      f32x4 acc1 = acc0;
-      acc0 = mfma16x16x32(nib8_to_bf16(va.x), bq[0], acc0);
-      acc1 = mfma16x16x32(nib8_to_bf16(vb.x), bq[0], acc1);
-      acc0 = mfma16x16x32(nib8_to_bf16(va.y), bq[1], acc0);
-      acc1 = mfma16x16x32(nib8_to_bf16(vb.y), bq[1], acc1);
-      acc0 = mfma16x16x32(nib8_to_bf16(va.z), bq[2], acc0);
-      acc1 = mfma16x16x32(nib8_to_bf16(vb.z), bq[2], acc1);
-      acc0 = mfma16x16x32(nib8_to_bf16(va.w), bq[3], acc0);
-      acc1 = mfma16x16x32(nib8_to_bf16(vb.w), bq[3], acc1);
+      uint4 va[kAcc];
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) va[j] = lds16(av + 256 * j);
+      f32x4 acc[kAcc];
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) acc[j] = f32x4{acc0_init, acc0_init, acc0_init, acc0_init};
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].x), bq[0], acc[j]);
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].y), bq[1], acc[j]);
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].z), bq[2], acc[j]);
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].w), bq[3], acc[j]);
 
       // ---- q.mu: A row (page (lane/4)%4, dim group lane%4), K (lane group g, e) ----
       const uint2 mq = *reinterpret_cast<const uint2*>(S + kSlotRec * sq + kOffMu + 32 * row +
@@ -248,31 +273,43 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
       const float qmu2 = qmu * smu * c0;
 
       // ---- w[k] = (q_h.v_k) * s_V[k] * s_c[k] for this lane's page and head ----
-      const uint4 sv = lds16(Sr + kOffSv), sc = lds16(Sr + kOffSc);
-      const uint32_t svw[4] = {sv.x, sv.y, sv.z, sv.w};
-      const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
+      uint32_t svw[R / 2], scw[R / 2];
+#pragma unroll
+      for (int i = 0; i < R / 2; ++i) {
+        svw[i] = *reinterpret_cast<const uint32_t*>(Sr + kOffSv + 4 * i);
+        scw[i] = *reinterpret_cast<const uint32_t*>(Sr + kOffSc + 4 * i);
+      }
       // fp16 operand times fp32 with a +0 addend: one mixed-precision FMA each
       auto hmul = [](uint32_t pair, int hi, float x) {
         return __builtin_fmaf(hi ? half_hi(pair) : half_lo(pair), x, 0.0f);
       };
-      float wk[8];
+      float wk[R];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int k0 = r, k1 = r + 4;
-        wk[k0] = hmul(scw[k0 >> 1], k0 & 1, hmul(svw[k0 >> 1], k0 & 1, acc0[r]));
-        wk[k1] = hmul(scw[k1 >> 1], k1 & 1, hmul(svw[k1 >> 1], k1 & 1, acc1[r]));
-      }
+      for (int j = 0; j < kAcc; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kk = 4 * j + r;
+          wk[kk] = hmul(scw[kk >> 1], kk & 1, hmul(svw[kk >> 1], kk & 1, acc[j][r]));
+        }
       // ---- deviation logits (base 2, without q.mu) of tokens 4cg..4cg+3 ----
-      const uint8_t* cp = Sr + kOffC + 32 * (tok >> 2);
-      const uint4 cc0 = lds16(cp), cc1 = lds16(cp + 16);
-      const uint32_t cw[8] = {cc0.x, cc0.y, cc0.z, cc0.w, cc1.x, cc1.y, cc1.z, cc1.w};
+      // codes of token t: R bytes from kOffC + R t
+      const uint8_t* cp = Sr + kOffC + 4 * R * (tok >> 2);
+      uint32_t cw[R];
+#pragma unroll
+      for (int i = 0; i < R / 4; ++i) {
+        const uint4 c4 = lds16(cp + 16 * i);
+        cw[4 * i] = c4.x;
+        cw[4 * i + 1] = c4.y;
+        cw[4 * i + 2] = c4.z;
+        cw[4 * i + 3] = c4.w;
+      }
       float dl[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         float a = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-          a = fmaf(wk[kk], (float)(int8_t)(cw[2 * t + (kk >> 2)] >> (8 * (kk & 3))), a);
+        for (int kk = 0; kk < R; ++kk)
+          a = fmaf(wk[kk], (float)(int8_t)(cw[(R / 4) * t + (kk >> 2)] >> (8 * (kk & 3))), a);
         dl[t] = a * c0;
       }
       // page LSE over 16 tokens: 4 in this lane, the rest in the lanes 4 and 8
@@ -343,14 +380,19 @@ ScorePlan plan_score(int32_t batch, int32_t hkv, int32_t max_pages) {
   return pl;
 }
 
-hipError_t launch_score(const uint16_t* q, const uint8_t* summ, int32_t num_blocks,
+hipError_t launch_score(int32_t rank, const uint16_t* q, const uint8_t* summ, int32_t num_blocks,
                         const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
                         int32_t batch, int32_t hq, int32_t hkv, float* page_lse,
                         float2* partials, const ScorePlan& plan, hipStream_t stream) {
   ScoreParams p{q, summ, block_table, seq_lens, page_lse, partials, num_blocks, max_pages, hq,
                 hkv, plan.n_chunks};
   dim3 grid(plan.n_chunks, hkv, batch);
-  hipLaunchKernelGGL(score_kernel, grid, dim3(64), 0, stream, p);
+  switch (rank) {
+    case 4: hipLaunchKernelGGL(score_kernel<4>, grid, dim3(64), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(score_kernel<8>, grid, dim3(64), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL(score_kernel<16>, grid, dim3(64), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -18,9 +18,10 @@
 //    and runs cyclic Jacobi on the 128x128 matrix in LDS with round-robin
 //    ordering (64 disjoint rotations per round, 127 rounds per sweep; each
 //    round applies J^T A J and V <- V J), until the off-diagonal mass is below
-//    1e-10 of the total (at most 24 sweeps).  The top-r eigenvectors (descending eigenvalue, ties
-//    to the lower index) are normalized and signed like a page's basis
-//    (largest-|entry| component positive, lowest index on ties).
+//    1e-10 of the total (at most 24 sweeps).  The top-r eigenvectors
+//    (descending eigenvalue, ties to the lower index) are normalized and
+//    signed like a page's basis (largest-|entry| component positive, lowest
+//    index on ties).
 #include "locks_device.h"
 #include "locks_internal.h"
 
@@ -124,7 +125,7 @@ struct EigSmem {
 };
 
 __global__ __launch_bounds__(kEigThreads) void eigen_kernel(const float* __restrict__ part,
-                                                            int32_t n_chunks,
+                                                            int32_t n_chunks, int32_t rank,
                                                             float* __restrict__ basis,
                                                             float* __restrict__ eigvals) {
   __shared__ EigSmem sm;
@@ -215,9 +216,9 @@ __global__ __launch_bounds__(kEigThreads) void eigen_kernel(const float* __restr
     if (eigvals) eigvals[(size_t)kvh * kD + rank] = lj;
   }
   __syncthreads();
-  // wave k < r: basis vector k (lane owns entries lane and lane + 64)
+  // wave k < rank: basis vector k (lane owns entries lane and lane + 64)
   const int wave = tid >> 6, lane = tid & 63;
-  if (wave < kR) {
+  if (wave < rank) {
     const int col = sm.order[wave];
     float v0 = sm.V[lane][col], v1 = sm.V[lane + 64][col];
     float n2 = v0 * v0 + v1 * v1;
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(kEigThreads) void eigen_kernel(const float* __restr
       v0 = -v0;
       v1 = -v1;
     }
-    float* out = basis + ((size_t)kvh * kR + wave) * kD;
+    float* out = basis + ((size_t)kvh * rank + wave) * kD;
     out[lane] = v0;
     out[lane + 64] = v1;
   }
@@ -263,7 +264,7 @@ SharedPlan plan_shared(int32_t n_blocks) {
   return pl;
 }
 
-hipError_t launch_shared_basis(const uint16_t* k_cache, int64_t block_stride,
+hipError_t launch_shared_basis(int32_t rank, const uint16_t* k_cache, int64_t block_stride,
                                int64_t head_stride, int64_t token_stride,
                                const int32_t* block_ids, int32_t n_blocks, int32_t num_blocks,
                                int32_t hkv, float* partials, const SharedPlan& plan,
@@ -274,7 +275,7 @@ hipError_t launch_shared_basis(const uint16_t* k_cache, int64_t block_stride,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(eigen_kernel, dim3(hkv), dim3(kEigThreads), 0, stream, partials,
-                     plan.n_chunks, basis, eigvals);
+                     plan.n_chunks, rank, basis, eigvals);
   return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblocks.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4, -5
-SUMMARY_BYTES = 832
+SUMMARY_BYTES = 832   # record bytes at rank 8; summary_bytes(d) gives any rank
 
 
 class LocksError(RuntimeError):
@@ -146,7 +146,8 @@ def attend_workspace(d: Dims, batch, max_attended_pages, device="cuda") -> torch
 
 def build_summaries(d: Dims, k_cache, block_ids, summaries, raw_debug=None, stream=None):
     """k_cache: bf16 [num_blocks, Hkv, 16, 128] (one layer); block_ids: int32
-    [n]; summaries: uint8 [Hkv, num_blocks, 832]; raw_debug: fp32 [n, Hkv, 1280]."""
+    [n]; summaries: uint8 [Hkv, num_blocks, summary_bytes(d)]; raw_debug: fp32
+    [n, Hkv, 128 + 144 * rank] (1280 at rank 8)."""
     _need(k_cache, "k_cache", torch.bfloat16)
     _need(block_ids, "block_ids", torch.int32)
     _need(summaries, "summaries", torch.uint8)
@@ -255,15 +256,15 @@ def finalize_pages(d: Dims, k_cache, block_table, seq_lens, summaries, stream=No
     """Summarize each sequence's last page when its length is a positive
     multiple of 16 (decided on the device; graph-capturable).  k_cache:
     [blocks, Hkv, 16, 128] for one layer or [layers, blocks, Hkv, 16, 128] for
-    all layers at once; summaries: [Hkv, blocks, 832] or [layers, Hkv,
-    blocks, 832] to match."""
+    all layers at once; summaries: [Hkv, blocks, summary_bytes(d)] or
+    [layers, Hkv, blocks, summary_bytes(d)] to match."""
     _need(k_cache, "k_cache", torch.bfloat16)
     _need(block_table, "block_table", torch.int32)
     _need(seq_lens, "seq_lens", torch.int32)
     _need(summaries, "summaries", torch.uint8)
     if k_cache.dim() == 5:
         if summaries.dim() != 4 or summaries.shape[0] != k_cache.shape[0]:
-            raise ValueError("summaries must be [layers, Hkv, blocks, 832] for a 5-d k_cache")
+            raise ValueError("summaries must be [layers, Hkv, blocks, record] for a 5-d k_cache")
         n_layers, ks, ss = k_cache.shape[0], k_cache.stride(0), summaries.stride(0)
         k0, s0 = k_cache[0], summaries[0]
     else:
@@ -312,7 +313,7 @@ def decode_layer(d: Dims, q, summaries, k_cache, v_cache, block_table, seq_lens,
 
 def shared_basis(d: Dims, k_cache, block_ids, basis, eigvals=None, workspace=None, stream=None):
     """Top-8 eigenvectors of the pooled page deviations per KV head.
-    basis: fp32 [Hkv, 8, 128]; eigvals: optional fp32 [Hkv, 128]."""
+    basis: fp32 [Hkv, rank, 128]; eigvals: optional fp32 [Hkv, 128]."""
     _need(k_cache, "k_cache", torch.bfloat16)
     _need(block_ids, "block_ids", torch.int32)
     _need(basis, "basis", torch.float32)
@@ -329,7 +330,7 @@ def shared_basis(d: Dims, k_cache, block_ids, basis, eigvals=None, workspace=Non
 
 
 def build_summaries_basis(d: Dims, k_cache, block_ids, basis, summaries, stream=None):
-    """Summaries of the listed blocks in a given basis (fp32 [Hkv, 8, 128])."""
+    """Summaries of the listed blocks in a given basis (fp32 [Hkv, rank, 128])."""
     _need(k_cache, "k_cache", torch.bfloat16)
     _need(block_ids, "block_ids", torch.int32)
     _need(basis, "basis", torch.float32)

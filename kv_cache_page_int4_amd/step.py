@@ -20,7 +20,7 @@ from . import locks as L
 
 class DecodeStep:
     """k, v: bf16 [layers, blocks, hkv, 16, 128]; summaries: uint8
-    [layers, hkv, blocks, 832]; q: bf16 [layers, batch, hq, 128];
+    [layers, hkv, blocks, record bytes]; q: bf16 [layers, batch, hq, 128];
     block_table: int32 [batch, max_pages]; seq_lens: int32 [batch].
     dense=True attends every finalized page instead (no scoring/selection);
     finalize=True summarizes pages completed by the newest token first;

@@ -25,22 +25,23 @@ def from_dev_bf16(t: torch.Tensor) -> np.ndarray:
 class Layer:
     """Device copies of one layer of a generated workload."""
 
-    def __init__(self, x, layer=0):
+    def __init__(self, x, layer=0, rank=8):
         w = x.w
-        self.x, self.w, self.layer = x, w, layer
-        self.d = L.dims(w.hq, w.hkv)
+        self.x, self.w, self.layer, self.rank = x, w, layer, rank
+        self.d = L.dims(w.hq, w.hkv, rank=rank)
         self.k = to_dev_bf16(x.k_cache[layer])      # [nb, hkv, 16, 128]
         self.v = to_dev_bf16(x.v_cache[layer])
         self.q = to_dev_bf16(x.q[layer])            # [b, hq, 128]
         self.bt = torch.from_numpy(x.block_table).cuda()
         self.seq = torch.from_numpy(x.seq_lens).cuda()
         self.nb = w.num_blocks
-        self.summ = torch.zeros((w.hkv, self.nb, O.RECORD_BYTES), dtype=torch.uint8, device="cuda")
+        self.summ = torch.zeros((w.hkv, self.nb, O.record_bytes(self.d.rank)), dtype=torch.uint8,
+                                device="cuda")
 
     # -- oracle-built records (host), uploaded ---------------------------------
     def upload_oracle_records(self):
         x, w = self.x, self.w
-        recs = np.zeros((w.hkv, self.nb, O.RECORD_BYTES), dtype=np.uint8)
+        recs = np.zeros((w.hkv, self.nb, O.record_bytes(self.rank)), dtype=np.uint8)
         for b in range(w.batch):
             n = int(x.seq_lens[b]) // 16
             if n == 0:
@@ -48,14 +49,15 @@ class Layer:
             blk = x.block_table[b, :n]
             for g in range(w.hkv):
                 K = O.bf16_to_f64(x.k_cache[self.layer][blk, g])
-                r, _, _ = O.build_records(K)
+                r, _, _ = O.build_records(K, self.rank)
                 recs[g, blk] = r
         self.summ.copy_(torch.from_numpy(recs))
         return recs
 
     def gpu_build(self, raw=False):
         blocks = torch.arange(self.nb, dtype=torch.int32, device="cuda")
-        rd = torch.zeros((self.nb, self.w.hkv, 1280), dtype=torch.float32, device="cuda") if raw else None
+        rd = (torch.zeros((self.nb, self.w.hkv, 128 + 144 * self.rank), dtype=torch.float32,
+                          device="cuda") if raw else None)
         L.build_summaries(self.d, self.k, blocks, self.summ, raw_debug=rd)
         return rd
 
@@ -100,12 +102,12 @@ class Layer:
         return out, olse
 
 
-def oracle_scores(x, recs, layer, b, g):
+def oracle_scores(x, recs, layer, b, g, r=8):
     """fp64 page LSE of the group's heads from records (host array [hkv, nb, 832])."""
     n = int(x.seq_lens[b]) // 16
     G = x.w.group
     q = O.bf16_to_f64(x.q[layer, b, g * G:(g + 1) * G])
-    return O.score_records(q, recs[g, x.block_table[b, :n]])
+    return O.score_records(q, recs[g, x.block_table[b, :n]], r=r)
 
 
 def check_selection(gpu_sel, oracle_log_m, budget):
@@ -173,7 +175,8 @@ def exempt_columns(lam, V):
         gaps = []
         if k > 0:
             gaps.append(lam[k - 1] - lam[k])
-        gaps.append(lam[k] - lam[k + 1])
+        if k + 1 < len(lam):
+            gaps.append(lam[k] - lam[k + 1])
         if min(gaps) < 1e-3 * lam1:
             ex[k] = True
         a = np.sort(np.abs(V[:, k]))[::-1]
@@ -184,14 +187,14 @@ def exempt_columns(lam, V):
     return ex
 
 
-def compare_build_codes(K, recs_gpu, where=""):
-    """K: fp64 keys [n, 16, 128]; recs_gpu: the GPU's records [n, 832] for
+def compare_build_codes(K, recs_gpu, where="", r=8):
+    """K: fp64 keys [n, 16, 128]; recs_gpu: the GPU's rank-r records [n, bytes] for
     the same page-heads.  Codes within 1 LSB and scales within 1 fp16 ulp
     outside the exempt columns; exempt pages compared by reconstruction.
     Returns (columns, exempt columns, worst exempt-page reconstruction diff)."""
-    mu, V, C, lam = O.page_summary(K)
+    mu, V, C, lam = O.page_summary(K, r)
     qo = O.quantize_summary(mu, V, C)
-    qg = O.unpack_records(recs_gpu)
+    qg = O.unpack_records(recs_gpu, r=r)
     assert np.abs(qg["mu_q"].astype(int) - qo["mu_q"]).max() <= 1, where
     assert np.all(np.abs(qg["s_mu"] - qo["s_mu"]) <= fp16_ulp(qo["s_mu"])), where
     n_cols = n_ex = 0

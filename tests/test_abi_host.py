@@ -46,7 +46,10 @@ def test_summary_bytes_and_unsupported_dims():
     _lib_or_skip()
     assert L.summary_bytes(L.dims(32, 8)) == 832
     assert L.summary_bytes(L.dims(32, 8, head_dim=64)) == 0
-    assert L.summary_bytes(L.dims(32, 8, rank=4)) == 0
+    assert L.summary_bytes(L.dims(32, 8, rank=4)) == 512
+    assert L.summary_bytes(L.dims(32, 8, rank=16)) == 1536
+    assert L.summary_bytes(L.dims(32, 8, rank=5)) == 0
+    assert L.summary_bytes(L.dims(32, 8, rank=32)) == 0
     assert L.summary_bytes(L.dims(16, 8)) == 0       # group of 2 not supported
 
 
@@ -153,7 +156,7 @@ def test_exact_page_lse_validation():
     assert call(scale=float("nan")) == L.ERR_SHAPE
     assert call(lay=L.KVLayout(16384, 2048, 64)) == L.ERR_SHAPE
     assert call(k=P(264)) == L.ERR_SHAPE
-    assert call(d=L.dims(32, 8, rank=4)) == L.ERR_UNSUPPORTED
+    assert call(d=L.dims(32, 8, rank=6)) == L.ERR_UNSUPPORTED
 
 
 def test_table_count_validation():
@@ -190,7 +193,7 @@ def test_shared_basis_validation():
     lay = L.KVLayout(32768, 4096, 128)
     need = lib.locks_shared_basis_workspace_bytes(ctypes.byref(d), 1000)
     assert need > 0 and lib.locks_shared_basis_workspace_bytes(ctypes.byref(d), 0) == 0
-    assert lib.locks_shared_basis_workspace_bytes(ctypes.byref(L.dims(32, 8, rank=4)), 10) == 0
+    assert lib.locks_shared_basis_workspace_bytes(ctypes.byref(L.dims(32, 8, rank=12)), 10) == 0
     call = lambda **kw: lib.locks_shared_basis(
         ctypes.byref(kw.get("d", d)), kw.get("k", P(256)), kw.get("lay", lay), kw.get("ids", P(256)),
         kw.get("n", 1000), 4096, kw.get("basis", P(256)), None, kw.get("ws", P(256)),
