@@ -11,7 +11,7 @@ Sources (cited by page and section; no passage is quoted):
   [P2] The same paper's digest page (arXiv 2607.24555v1) and its English
        abstract.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
   * The eigendecomposition is of the page's centered keys X = K - 1 mu^T; its
     top-r eigenvectors are those of the scatter X^T X, obtained here as the
     right singular vectors of X.
