@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b-1m")
     ap.add_argument("--small-workload", default="llama8b-32k")
+    ap.add_argument("--large-workload", default="llama8b-256k-b16",
+                    help="large-batch configuration reported beside the main one")
+    ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -463,8 +466,47 @@ def main():
         log(f"[{w.name}] oracle {cpu['value']:.0f} us/layer on {cpu['cores']} core")
 
     also = {}
+    del step
+    if not args.no_large and args.large_workload:
+        # the large-batch configuration, after the main one's buffers are freed
+        del inp, summ, lse_buf
+        torch.cuda.empty_cache()
+        wl = get_workload(args.large_workload)
+        d3, inp3, summ3, _ = setup(wl)
+        st3 = DecodeStep(d3, inp3.k, inp3.v, summ3, inp3.q, inp3.block_table, inp3.seq_lens,
+                         wl.budget_pages)
+        ms3 = time_step(st3, max(5, args.steps // 2), 2)
+        P3 = inp3.block_table.shape[1]
+        lse3 = torch.empty((wl.batch, wl.hq, P3), dtype=torch.float32, device="cuda")
+
+        def score_large():
+            for layer in range(wl.layers):
+                L.score_pages(d3, inp3.q[layer], summ3[layer], wl.num_blocks, inp3.block_table,
+                              inp3.seq_lens, lse3, st3.ws_score)
+
+        sc3 = timed(score_large, args.kernel_reps) / wl.layers
+        ph3 = wl.batch * wl.hkv * wl.pages
+        entry = {"us_per_layer": round(ms3 * 1e3 / wl.layers, 3),
+                 "scorer_us": round(sc3 * 1e3, 3),
+                 "scorer_gbs": round(ph3 * SCORE_BYTES_PER_PAGE_HEAD / (sc3 * 1e-3) / 1e9, 1),
+                 "batch": wl.batch, "ctx": wl.ctx, "layers": wl.layers}
+        entry["scorer_frac"] = round(entry["scorer_gbs"] / PEAK_HBM_GBS, 4)
+        log(f"[{wl.name}] decode step {ms3 * 1e3 / wl.layers:.2f} us/layer; scorer "
+            f"{sc3 * 1e3:.2f} us = {entry['scorer_gbs']:.0f} GB/s")
+        del st3
+        if not args.no_dense:
+            dn3 = DecodeStep(d3, inp3.k, inp3.v, summ3, inp3.q, inp3.block_table, inp3.seq_lens,
+                             1, dense=True)
+            dms3 = time_step(dn3, 2, 1)
+            entry["dense_us_per_layer"] = round(dms3 * 1e3 / wl.layers, 3)
+            entry["speedup_vs_dense"] = round(dms3 / ms3, 3)
+            log(f"[{wl.name}] dense {dms3 * 1e3 / wl.layers:.2f} us/layer, "
+                f"speedup {dms3 / ms3:.2f}x")
+            del dn3
+        also[wl.name] = entry
+        del inp3, summ3, lse3
+        torch.cuda.empty_cache()
     if not args.no_small and args.small_workload:
-        del step
         ws = get_workload(args.small_workload)
         d2, inp2, summ2, _ = setup(ws)
         st2 = DecodeStep(d2, inp2.k, inp2.v, summ2, inp2.q, inp2.block_table, inp2.seq_lens,
