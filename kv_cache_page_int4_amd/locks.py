@@ -110,13 +110,36 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _need(t, name, dtype, cuda=True):
+def _need(t, name, dtype, numel=None):
+    """Type checks; with numel, also that the tensor is dense and holds at
+    least the numel elements the library will read or write through its
+    pointer (the C ABI itself cannot see buffer sizes)."""
     if t is None:
         return
-    if cuda and not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None:
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.numel() < numel:
+            raise ValueError(f"{name} holds {t.numel()} elements; the call needs {numel}")
+
+
+def _on_device(**tensors):
+    """Every given tensor lives on the GPU (checked after the size checks)."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+
+
+def _rec_bytes(d: Dims) -> int:
+    """Record bytes at rank d.rank (84 r + 130 bytes of fields, padded to 64)."""
+    return (84 * d.rank + 130 + 63) // 64 * 64
+
+
+def _kv_heads(d: Dims, cache, name):
+    if cache.dim() >= 3 and cache.shape[-3] != d.num_kv_heads:
+        raise ValueError(f"{name} has {cache.shape[-3]} KV heads, dims say {d.num_kv_heads}")
 
 
 def kv_layout(cache: torch.Tensor) -> KVLayout:
@@ -148,10 +171,13 @@ def build_summaries(d: Dims, k_cache, block_ids, summaries, raw_debug=None, stre
     """k_cache: bf16 [num_blocks, Hkv, 16, 128] (one layer); block_ids: int32
     [n]; summaries: uint8 [Hkv, num_blocks, summary_bytes(d)]; raw_debug: fp32
     [n, Hkv, 128 + 144 * rank] (1280 at rank 8)."""
+    nb, hkv, n = k_cache.shape[0], d.num_kv_heads, block_ids.numel()
     _need(k_cache, "k_cache", torch.bfloat16)
-    _need(block_ids, "block_ids", torch.int32)
-    _need(summaries, "summaries", torch.uint8)
-    _need(raw_debug, "raw_debug", torch.float32)
+    _kv_heads(d, k_cache, "k_cache")
+    _need(block_ids, "block_ids", torch.int32, numel=n)
+    _need(summaries, "summaries", torch.uint8, numel=hkv * nb * _rec_bytes(d))
+    _need(raw_debug, "raw_debug", torch.float32, numel=n * hkv * (128 + 144 * d.rank))
+    _on_device(k_cache=k_cache, block_ids=block_ids, summaries=summaries, raw_debug=raw_debug)
     st = lib().locks_build_summaries(ctypes.byref(d), _ptr(k_cache), kv_layout(k_cache),
                                      _ptr(block_ids), block_ids.numel(), k_cache.shape[0],
                                      _ptr(summaries), _ptr(raw_debug), _stream(stream))
@@ -160,11 +186,14 @@ def build_summaries(d: Dims, k_cache, block_ids, summaries, raw_debug=None, stre
 
 def score_pages(d: Dims, q, summaries, num_blocks, block_table, seq_lens, page_lse, workspace,
                 stream=None):
-    _need(q, "q", torch.bfloat16)
-    _need(summaries, "summaries", torch.uint8)
-    _need(block_table, "block_table", torch.int32)
-    _need(seq_lens, "seq_lens", torch.int32)
-    _need(page_lse, "page_lse", torch.float32)
+    B, P, hq = block_table.shape[0], block_table.shape[1], d.num_q_heads
+    _need(q, "q", torch.bfloat16, numel=B * hq * d.head_dim)
+    _need(summaries, "summaries", torch.uint8, numel=d.num_kv_heads * num_blocks * _rec_bytes(d))
+    _need(block_table, "block_table", torch.int32, numel=B * P)
+    _need(seq_lens, "seq_lens", torch.int32, numel=B)
+    _need(page_lse, "page_lse", torch.float32, numel=B * hq * P)
+    _on_device(q=q, summaries=summaries, block_table=block_table, seq_lens=seq_lens,
+               page_lse=page_lse)
     st = lib().locks_score_pages(ctypes.byref(d), _ptr(q), _ptr(summaries), num_blocks,
                                  _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
                                  block_table.shape[0], _ptr(page_lse), _ptr(workspace),
@@ -176,9 +205,13 @@ def select_pages(d: Dims, page_lse, seq_lens, budget_pages, sel, sel_count, work
                  n_tables=None):
     """n_tables=None: one table per KV head (sel [batch, Hkv, budget]); else
     n_tables tables per sequence (sel [batch, n_tables, budget])."""
-    _need(page_lse, "page_lse", torch.float32)
-    _need(sel, "sel", torch.int32)
-    _need(sel_count, "sel_count", torch.int32)
+    B, P = page_lse.shape[0], page_lse.shape[-1]
+    ntab = d.num_kv_heads if n_tables is None else int(n_tables)
+    _need(page_lse, "page_lse", torch.float32, numel=B * d.num_q_heads * P)
+    _need(seq_lens, "seq_lens", torch.int32, numel=B)
+    _need(sel, "sel", torch.int32, numel=B * ntab * budget_pages)
+    _need(sel_count, "sel_count", torch.int32, numel=B * ntab)
+    _on_device(page_lse=page_lse, seq_lens=seq_lens, sel=sel, sel_count=sel_count)
     args = [ctypes.byref(d), _ptr(page_lse), page_lse.shape[-1], _ptr(seq_lens),
             page_lse.shape[0], budget_pages]
     rest = [_ptr(sel), _ptr(sel_count), _ptr(workspace),
@@ -192,11 +225,16 @@ def select_pages(d: Dims, page_lse, seq_lens, budget_pages, sel, sel_count, work
 
 def score_select(d: Dims, q, summaries, num_blocks, block_table, seq_lens, budget_pages, sel,
                  sel_count, workspace, page_lse=None, stream=None):
-    _need(q, "q", torch.bfloat16)
-    _need(summaries, "summaries", torch.uint8)
-    _need(block_table, "block_table", torch.int32)
-    _need(sel, "sel", torch.int32)
-    _need(page_lse, "page_lse", torch.float32)
+    B, P, hq, hkv = block_table.shape[0], block_table.shape[1], d.num_q_heads, d.num_kv_heads
+    _need(q, "q", torch.bfloat16, numel=B * hq * d.head_dim)
+    _need(summaries, "summaries", torch.uint8, numel=hkv * num_blocks * _rec_bytes(d))
+    _need(block_table, "block_table", torch.int32, numel=B * P)
+    _need(seq_lens, "seq_lens", torch.int32, numel=B)
+    _need(sel, "sel", torch.int32, numel=B * hkv * budget_pages)
+    _need(sel_count, "sel_count", torch.int32, numel=B * hkv)
+    _need(page_lse, "page_lse", torch.float32, numel=B * hq * P)
+    _on_device(q=q, summaries=summaries, block_table=block_table, seq_lens=seq_lens, sel=sel,
+               sel_count=sel_count, page_lse=page_lse)
     st = lib().locks_score_select(ctypes.byref(d), _ptr(q), _ptr(summaries), num_blocks,
                                   _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
                                   block_table.shape[0], budget_pages, _ptr(sel), _ptr(sel_count),
@@ -210,11 +248,22 @@ def sparse_attend(d: Dims, q, k_cache, v_cache, block_table, seq_lens, sel, sel_
                   n_tables=None):
     """sel=None attends every finalized page (dense attention); n_tables as
     for select_pages."""
-    _need(q, "q", torch.bfloat16)
+    B, P, hq = block_table.shape[0], block_table.shape[1], d.num_q_heads
+    ntab = d.num_kv_heads if n_tables is None else int(n_tables)
+    _need(q, "q", torch.bfloat16, numel=B * hq * d.head_dim)
     _need(k_cache, "k_cache", torch.bfloat16)
     _need(v_cache, "v_cache", torch.bfloat16)
-    _need(out, "out", torch.bfloat16)
-    _need(out_lse, "out_lse", torch.float32)
+    _kv_heads(d, k_cache, "k_cache")
+    _kv_heads(d, v_cache, "v_cache")
+    _need(block_table, "block_table", torch.int32, numel=B * P)
+    _need(seq_lens, "seq_lens", torch.int32, numel=B)
+    if sel is not None:
+        _need(sel, "sel", torch.int32, numel=B * ntab * budget_pages)
+        _need(sel_count, "sel_count", torch.int32, numel=B * ntab)
+    _need(out, "out", torch.bfloat16, numel=B * hq * d.head_dim)
+    _need(out_lse, "out_lse", torch.float32, numel=B * hq)
+    _on_device(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, seq_lens=seq_lens,
+               sel=sel, sel_count=sel_count, out=out, out_lse=out_lse)
     lay = kv_layout(k_cache)
     lv = kv_layout(v_cache)
     if (lay.block_stride, lay.head_stride, lay.token_stride) != (
@@ -238,11 +287,14 @@ def exact_page_lse(d: Dims, q, k_cache, block_table, seq_lens, page_lse, softmax
                    stream=None):
     """Exact page LSE from the keys (the read-every-key comparator); page_lse:
     fp32 [batch, Hq, max_pages], the layout of score_pages' output."""
-    _need(q, "q", torch.bfloat16)
+    B, P, hq = block_table.shape[0], block_table.shape[1], d.num_q_heads
+    _need(q, "q", torch.bfloat16, numel=B * hq * d.head_dim)
     _need(k_cache, "k_cache", torch.bfloat16)
-    _need(block_table, "block_table", torch.int32)
-    _need(seq_lens, "seq_lens", torch.int32)
-    _need(page_lse, "page_lse", torch.float32)
+    _kv_heads(d, k_cache, "k_cache")
+    _need(block_table, "block_table", torch.int32, numel=B * P)
+    _need(seq_lens, "seq_lens", torch.int32, numel=B)
+    _need(page_lse, "page_lse", torch.float32, numel=B * hq * P)
+    _on_device(q=q, k_cache=k_cache, block_table=block_table, seq_lens=seq_lens, page_lse=page_lse)
     if softmax_scale is None:
         softmax_scale = 1.0 / (d.head_dim ** 0.5)
     st = lib().locks_exact_page_lse(ctypes.byref(d), _ptr(q), _ptr(k_cache), kv_layout(k_cache),
@@ -258,10 +310,12 @@ def finalize_pages(d: Dims, k_cache, block_table, seq_lens, summaries, stream=No
     [blocks, Hkv, 16, 128] for one layer or [layers, blocks, Hkv, 16, 128] for
     all layers at once; summaries: [Hkv, blocks, summary_bytes(d)] or
     [layers, Hkv, blocks, summary_bytes(d)] to match."""
+    B, P = block_table.shape[0], block_table.shape[1]
     _need(k_cache, "k_cache", torch.bfloat16)
-    _need(block_table, "block_table", torch.int32)
-    _need(seq_lens, "seq_lens", torch.int32)
-    _need(summaries, "summaries", torch.uint8)
+    _kv_heads(d, k_cache, "k_cache")
+    _need(block_table, "block_table", torch.int32, numel=B * P)
+    _need(seq_lens, "seq_lens", torch.int32, numel=B)
+    _on_device(k_cache=k_cache, block_table=block_table, seq_lens=seq_lens, summaries=summaries)
     if k_cache.dim() == 5:
         if summaries.dim() != 4 or summaries.shape[0] != k_cache.shape[0]:
             raise ValueError("summaries must be [layers, Hkv, blocks, record] for a 5-d k_cache")
@@ -269,6 +323,10 @@ def finalize_pages(d: Dims, k_cache, block_table, seq_lens, summaries, stream=No
         k0, s0 = k_cache[0], summaries[0]
     else:
         n_layers, ks, ss, k0, s0 = 1, 0, 0, k_cache, summaries
+    per_layer = d.num_kv_heads * k0.shape[0] * _rec_bytes(d)
+    _need(s0, "summaries (one layer)", torch.uint8, numel=per_layer)
+    if n_layers > 1 and ss < per_layer:
+        raise ValueError("summaries layers overlap")
     st = lib().locks_finalize_pages(ctypes.byref(d), _ptr(k0), kv_layout(k0), k0.shape[0],
                                     _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
                                     block_table.shape[0], _ptr(s0), n_layers, ks, ss,
@@ -281,16 +339,23 @@ def decode_layer(d: Dims, q, summaries, k_cache, v_cache, block_table, seq_lens,
                  stream=None, n_tables=None):
     """score_select followed by sparse_attend in one call (identical outputs);
     n_tables as for select_pages."""
-    _need(q, "q", torch.bfloat16)
-    _need(summaries, "summaries", torch.uint8)
+    B, P, hq = block_table.shape[0], block_table.shape[1], d.num_q_heads
+    ntab = d.num_kv_heads if n_tables is None else int(n_tables)
+    _need(q, "q", torch.bfloat16, numel=B * hq * d.head_dim)
+    _need(summaries, "summaries", torch.uint8,
+          numel=d.num_kv_heads * k_cache.shape[0] * _rec_bytes(d))
     _need(k_cache, "k_cache", torch.bfloat16)
     _need(v_cache, "v_cache", torch.bfloat16)
-    _need(block_table, "block_table", torch.int32)
-    _need(seq_lens, "seq_lens", torch.int32)
-    _need(sel, "sel", torch.int32)
-    _need(sel_count, "sel_count", torch.int32)
-    _need(out, "out", torch.bfloat16)
-    _need(out_lse, "out_lse", torch.float32)
+    _kv_heads(d, k_cache, "k_cache")
+    _kv_heads(d, v_cache, "v_cache")
+    _need(block_table, "block_table", torch.int32, numel=B * P)
+    _need(seq_lens, "seq_lens", torch.int32, numel=B)
+    _need(sel, "sel", torch.int32, numel=B * ntab * budget_pages)
+    _need(sel_count, "sel_count", torch.int32, numel=B * ntab)
+    _need(out, "out", torch.bfloat16, numel=B * hq * d.head_dim)
+    _need(out_lse, "out_lse", torch.float32, numel=B * hq)
+    _on_device(q=q, summaries=summaries, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+               seq_lens=seq_lens, sel=sel, sel_count=sel_count, out=out, out_lse=out_lse)
     lay = kv_layout(k_cache)
     lv = kv_layout(v_cache)
     if (lay.block_stride, lay.head_stride, lay.token_stride) != (
@@ -312,16 +377,18 @@ def decode_layer(d: Dims, q, summaries, k_cache, v_cache, block_table, seq_lens,
 
 
 def shared_basis(d: Dims, k_cache, block_ids, basis, eigvals=None, workspace=None, stream=None):
-    """Top-8 eigenvectors of the pooled page deviations per KV head.
+    """Top-rank eigenvectors of the pooled page deviations per KV head.
     basis: fp32 [Hkv, rank, 128]; eigvals: optional fp32 [Hkv, 128]."""
+    n, hkv = block_ids.numel(), d.num_kv_heads
     _need(k_cache, "k_cache", torch.bfloat16)
-    _need(block_ids, "block_ids", torch.int32)
-    _need(basis, "basis", torch.float32)
-    _need(eigvals, "eigvals", torch.float32)
-    n = block_ids.numel()
+    _kv_heads(d, k_cache, "k_cache")
+    _need(block_ids, "block_ids", torch.int32, numel=n)
+    _need(basis, "basis", torch.float32, numel=hkv * d.rank * d.head_dim)
+    _need(eigvals, "eigvals", torch.float32, numel=hkv * d.head_dim)
+    _on_device(k_cache=k_cache, block_ids=block_ids, basis=basis, eigvals=eigvals)
     if workspace is None:
-        workspace = torch.empty(max(1, lib().locks_shared_basis_workspace_bytes(ctypes.byref(d), n)),
-                                dtype=torch.uint8, device=k_cache.device)
+        nbytes = lib().locks_shared_basis_workspace_bytes(ctypes.byref(d), n)
+        workspace = torch.empty(max(1, nbytes), dtype=torch.uint8, device=k_cache.device)
     st = lib().locks_shared_basis(ctypes.byref(d), _ptr(k_cache), kv_layout(k_cache),
                                   _ptr(block_ids), n, k_cache.shape[0], _ptr(basis),
                                   _ptr(eigvals), _ptr(workspace),
@@ -331,10 +398,13 @@ def shared_basis(d: Dims, k_cache, block_ids, basis, eigvals=None, workspace=Non
 
 def build_summaries_basis(d: Dims, k_cache, block_ids, basis, summaries, stream=None):
     """Summaries of the listed blocks in a given basis (fp32 [Hkv, rank, 128])."""
+    hkv = d.num_kv_heads
     _need(k_cache, "k_cache", torch.bfloat16)
-    _need(block_ids, "block_ids", torch.int32)
-    _need(basis, "basis", torch.float32)
-    _need(summaries, "summaries", torch.uint8)
+    _kv_heads(d, k_cache, "k_cache")
+    _need(block_ids, "block_ids", torch.int32, numel=block_ids.numel())
+    _need(basis, "basis", torch.float32, numel=hkv * d.rank * d.head_dim)
+    _need(summaries, "summaries", torch.uint8, numel=hkv * k_cache.shape[0] * _rec_bytes(d))
+    _on_device(k_cache=k_cache, block_ids=block_ids, basis=basis, summaries=summaries)
     st = lib().locks_build_summaries_basis(ctypes.byref(d), _ptr(k_cache), kv_layout(k_cache),
                                            _ptr(block_ids), block_ids.numel(), k_cache.shape[0],
                                            _ptr(basis), _ptr(summaries), _stream(stream))
