@@ -272,13 +272,17 @@ def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps):
                      "fraction of the exact page set LOCKS also selects")}
 
 
-def traffic_if_current():
+def traffic_if_current(workload):
+    """Counter-measured HBM bytes per scorer launch, when the stored counters
+    were taken on this workload and on the current score.hip."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
         rec = json.load(open(TRAFFIC_FILE))
         sha = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
         if rec.get("score_hip_sha256") != sha:
+            return None
+        if str(rec.get("workload", "")).split(" ")[0] != workload:
             return None
         return rec.get("hbm_bytes_per_launch")
     except Exception:
@@ -535,7 +539,7 @@ def main():
                    "carriers_per_kv_head": w.carriers, "graph": "one hipGraph per step"},
         "roofline": {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(score_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_if_current(), "kernel": "score_kernel",
+                     "traffic": traffic_if_current(w.name), "kernel": "score_kernel",
                      "kernel_us": round(score_ms * 1e3, 3),
                      "bytes_per_launch": page_heads * SCORE_BYTES_PER_PAGE_HEAD},
         "attention": {"achieved": round(attend_gbs, 1), "unit": "GB/s",
