@@ -2,22 +2,28 @@
 // (LOCKS explainer, technical summary sec. 2, reconstruction and selection).
 //
 // Work split.  The pages of one (sequence, KV head) are cut into 4-page
-// steps; one-wave workgroup w of a (sequence, KV head) takes the kScoreSteps
-// consecutive steps from w * kScoreSteps on.  Waves are short: many dispatch
-// rounds keep the end-of-launch tail small.  A workgroup collects its page
-// LSEs in LDS and writes each head's run of 4 * kScoreSteps pages at the end
-// as whole 64-byte pieces (one 16-byte piece per step and head, written as it
-// came, costs partial-line write-backs).
+// steps.  Workgroup g of a (sequence, KV head) has kScoreWaves independent
+// waves; wave v takes the kScoreSteps consecutive steps from
+// (g * kScoreWaves + v) * kScoreSteps on, so the workgroup covers one
+// contiguous run of pages.  Waves are short: many dispatch rounds keep the
+// end-of-launch tail small.  The page LSEs of all waves are collected in LDS
+// and leave at the end as one contiguous run per head (256 bytes, two whole
+// lines), and the waves' (max, sum) partials are merged into one per head.
+// Stores are few on purpose: under a full HBM read stream every store
+// instruction, even a whole-line one, costs far more time than its bytes.
 //
 // Data movement.  The four 832-byte records of a step are copied straight
-// from HBM into a ring of LDS slots with global->LDS DMA (one 816-byte
-// instruction per record: 51 lanes x 16 B; the trailing pad is skipped).
-// The next step is in flight while one is computed, at no VGPR cost; with
-// 6.5 KB of LDS per wave, six waves share each SIMD.  The compiler does not track these copies, so the issue and the
-// waits are written out: every step issues exactly 4 copies, copies of one
-// wave complete in order, and waiting for "at most 4 outstanding" with one
-// younger step issued therefore means this step has landed.  Any other
-// memory instruction in flight only makes such a wait stricter.
+// from HBM into the wave's LDS slot with global->LDS DMA (one 816-byte
+// instruction per record: 51 lanes x 16 B; the trailing pad is skipped),
+// marked non-temporal: the records are read once, and streaming them past
+// the cache's normal allocation raises the read rate.  One slot per wave:
+// the step's LDS reads all complete (into registers) before the next step's
+// copies are issued into the same slot, and those copies are in flight while
+// the step computes.  The group's query heads sit in LDS too, so a wave holds
+// no q in VGPRs; with 4.3 KB of LDS and at most 72 VGPRs per wave, seven
+// waves share each SIMD.  The compiler does not track these copies, so the
+// issue and the waits are written out: a step is the only copy in flight when
+// it is waited for, so waiting for zero outstanding means it has landed.
 //
 // Per step one wave does:
 //  * V^T q on the matrix cores: rows = (page, basis) pairs, K = head dim,
@@ -30,9 +36,9 @@
 //    (dim group s', head h), K over the 4 dim quarters; the diagonal
 //    s'' = s' summed over s' is q_h.mu_p.  Lane l picks its diagonal entry
 //    and the 4 lanes 4 apart in the row add up the rest.
-//  * the coefficient term on the vector units: lane l keeps its own head
-//    h = l%4 and page l/16 and takes the 4 tokens 4*cg..4*cg+3 of that page
-//    (cg = (l%16)/4).
+//  * the coefficient term on the matrix cores, one 16-block 4x4x1 fp32
+//    MFMA per basis index: lane l keeps its own head h = l%4 and page l/16
+//    and gets the 4 tokens 4*cg..4*cg+3 of that page (cg = (l%16)/4).
 //  * the page LSE over 16 tokens: 4 exponentials in the lane, then the 4
 //    lanes of the same (page, head) -- 4 and 8 apart in the row -- are summed
 //    with two DPP row rotations.
@@ -46,6 +52,7 @@ namespace locks {
 namespace {
 
 constexpr uint32_t kMagic = 0x43434343u;  // bf16 high byte of 128.0
+constexpr int kScoreWaves = 4;            // independent waves per workgroup
 
 // 8 int4 codes (two's complement, layout of the record) -> 8 bf16 = 136 + code.
 __device__ __forceinline__ bf16x8 nib8_to_bf16(uint32_t x) {
@@ -71,7 +78,6 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16(uint2 v) {
   return r;
 }
 
-constexpr int kRing = 2;           // LDS record slots (steps) per wave: 1 in flight
 
 // Field offsets of a rank-R record (the rank-8 layout with every field sized
 // by R) and its LDS slot: the record's fields are copied in whole 16-byte
@@ -86,7 +92,6 @@ struct ScoreLayout {
   static constexpr int kSlotRec = 16 * kUnits;
   static constexpr int kStepBytes = 4 * kSlotRec;
   static constexpr int kDmaPerRec = (kUnits + 63) / 64;
-  static constexpr int kDmaPerStep = 4 * kDmaPerRec;
 };
 
 struct ScoreParams {
@@ -104,7 +109,7 @@ struct ScoreParams {
 // address; the compiler treats M0 as reserved and this kernel has no other
 // user of it.
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff),
                "s"(sbase), "s"(lds)
                : "memory");
 }
@@ -117,16 +122,24 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 template <int R>
-__global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
+__global__ __launch_bounds__(64 * kScoreWaves) __attribute__((amdgpu_waves_per_eu(7, 7))) void
+score_kernel(ScoreParams p) {
   using SL = ScoreLayout<R>;
   constexpr int kSlotRec = SL::kSlotRec, kStepBytes = SL::kStepBytes;
   constexpr int kOffC = SL::kOffC, kOffMu = SL::kOffMu, kOffSv = SL::kOffSv;
   constexpr int kOffSc = SL::kOffSc, kOffSmu = SL::kOffSmu;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kStepBytes];
-  __shared__ __attribute__((aligned(16))) float outl[kG][4 * kScoreSteps];
+  constexpr int kWavePages = 4 * kScoreSteps;             // pages of one wave
+  constexpr int kWgPages = kScoreWaves * kWavePages;       // pages of the workgroup
+  __shared__ __attribute__((aligned(16))) uint8_t ring_all[kScoreWaves][kStepBytes];
+  __shared__ __attribute__((aligned(16))) uint4 qs_all[kScoreWaves][kG * kD / 8];
+  __shared__ __attribute__((aligned(16))) float outl[kG][kWgPages];
+  __shared__ float2 red[kScoreWaves][kG];
 
-  const int lane = threadIdx.x;
-  const int w = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave in the workgroup
+  uint8_t* ring = ring_all[wv];          // this wave's record slot
+  uint4* qs = qs_all[wv];                // this wave's copy of the group's query heads
+  const int g = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int W = p.n_wg;
   const int qhead0 = kvh * kG;
   const int row = lane >> 4;   // page slot of this lane in a step
@@ -137,7 +150,7 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
   seq = max(0, min(seq, p.max_pages * kB));
   const int n_fin = seq / kB;
   const int nsteps = (n_fin + 3) / 4;
-  const int s0 = w * kScoreSteps;                          // first step of this workgroup
+  const int s0 = (g * kScoreWaves + wv) * kScoreSteps;    // first step of this wave
   const int n = max(0, min(kScoreSteps, nsteps - s0));    // its steps
 
   const uint8_t* __restrict__ summ_h = p.summ + (size_t)kvh * p.num_blocks * SL::kRecB;
@@ -145,21 +158,22 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
   float* __restrict__ lse_out = p.page_lse + ((size_t)b * p.hq + qhead0) * p.max_pages;
 
   // pages that are not finalized score -inf
-  for (int j = n_fin + 64 * w + lane; j < p.max_pages; j += 64 * W)
+  for (int j = n_fin + kWgPages * g + (int)threadIdx.x; j < p.max_pages; j += kWgPages * W)
 #pragma unroll
     for (int hh = 0; hh < kG; ++hh) lse_out[(size_t)hh * p.max_pages + j] = -INFINITY;
 
   float pm = -INFINITY, ps = 0.f;   // running base-2 (max, sum) of head h (lanes tok < 4)
   if (n > 0) {
-    // q as MFMA B operands for V^T q: column (lane%16) is head lane%4; K element
+    // The group's 4 query heads (1 KB of bf16) are staged in LDS once and
+    // each step reads its MFMA B operands from there, which keeps them out of
+    // VGPRs.  For V^T q, column (lane%16) is head lane%4 and K element
     // (step s, lane group g, e) is dim 32g + 8s + e.
-    const uint16_t* qh = p.q + ((size_t)b * p.hq + qhead0 + h) * kD;
-    bf16x8 bq[4];
+    qs[lane] = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.hq + qhead0) * kD + 8 * lane);
+    auto qpiece = [&](int s) -> uint4 { return qs[h * (kD / 8) + 4 * row + s]; };
     float qsum = 0.f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qh + 32 * row + 8 * s);
-      bq[s] = as_bf16x8(v);
+      const uint4 v = qpiece(s);
       qsum += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
               bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
     }
@@ -167,18 +181,13 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
     qsum += __shfl_xor(qsum, 32);
     // the codes enter the product as 136 + n: start the accumulator at -136 sum(q)
     const float acc0_init = -136.f * qsum;
-    // q as the B operand of q.mu: column (lane%16) = (dim group s' = (lane/4)%4,
-    // head lane%4), K element (lane group g, e) is dim 32g + 8s' + e
+    // for q.mu, column (lane%16) = (dim group s' = (lane/4)%4, head lane%4) and
+    // K element (lane group g, e) is dim 32g + 8s' + e
     const int sq = (lane >> 2) & 3;
-    const uint4 qm_raw = *reinterpret_cast<const uint4*>(qh + 32 * row + 8 * sq);
-    const bf16x8 bqm = as_bf16x8(qm_raw);
-    // consume the q loads here, so that the compiler's wait for them comes
-    // before the first record copies are issued rather than behind them
-    asm volatile("" ::"v"(qm_raw.x), "v"(qm_raw.y), "v"(qm_raw.z), "v"(qm_raw.w), "v"(acc0_init));
     const float c0 = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
 
     const uint32_t ring0 =
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&ring[0][0];
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&ring[0];
     // block ids of step k (scalar loads through the constant address space);
     // -1 marks a page past the finalized ones or with an out-of-range block id
     // (its record 0 is copied and its score dropped)
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
       return v;
     };
     auto issue = [&](int k, int4 bb) {
-      const uint32_t slot = ring0 + (uint32_t)((k & 1) * kStepBytes);
+      const uint32_t slot = ring0;
       const int bi[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -220,65 +229,84 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
     };
 
     // block ids of step k (b0) and k+1 (b1, the next one to issue)
-    static_assert(kRing == 2, "the block-id pipeline below holds two steps");
     const int4 none = make_int4(-1, -1, -1, -1);
     int4 b0 = step_bids(0);
     int4 b1 = (n > 1) ? step_bids(1) : none;
     issue(0, b0);
     for (int k = 0; k < n; ++k) {
-      // every LDS read of step k-1 has returned: its slot may be refilled
-      wait_lgkm0();
       const int4 bcur = b0;
       const bool more = k + 1 < n;
-      if (more) issue(k + 1, b1);
-      b0 = b1;
-      b1 = (k + 2 < n) ? step_bids(k + 2) : none;
-      if (more) wait_vm<SL::kDmaPerStep>();
-      else wait_vm<0>();
+      // step k is the only copy in flight
+      wait_vm<0>();
 
-      const uint8_t* S = &ring[k & 1][0];
+      const uint8_t* S = &ring[0];
       const uint8_t* Sr = S + kSlotRec * row;          // record of this lane's page
       const int jpg = 4 * (s0 + k) + row;              // this lane's page
       const int bid_row = (row == 0) ? bcur.x : (row == 1) ? bcur.y : (row == 2) ? bcur.z : bcur.w;
       const bool okp = bid_row >= 0;
 
-      // ---- V^T q: A rows (page tok/4, basis tok%4 + 4j), dims 32 row + 8s + e ----
-      constexpr int kAcc = R / 4;   // accumulators: basis columns 4j .. 4j+3
+      // ---- every LDS read of the step; then the slot takes step k+1 ----
+      constexpr int kAcc = R / 4;   // V^T q accumulators: basis columns 4j .. 4j+3
+      // basis codes: A rows (page tok/4, basis tok%4 + 4j), dims 32 row + 8s + e
       const uint8_t* av = S + kSlotRec * (tok >> 2) + 64 * (lane & 3) + 16 * row;
       uint4 va[kAcc];
 #pragma unroll
       for (int j = 0; j < kAcc; ++j) va[j] = lds16(av + 256 * j);
-      f32x4 acc[kAcc];
-#pragma unroll
-      for (int j = 0; j < kAcc; ++j) acc[j] = f32x4{acc0_init, acc0_init, acc0_init, acc0_init};
-#pragma unroll
-      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].x), bq[0], acc[j]);
-#pragma unroll
-      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].y), bq[1], acc[j]);
-#pragma unroll
-      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].z), bq[2], acc[j]);
-#pragma unroll
-      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].w), bq[3], acc[j]);
-
-      // ---- q.mu: A row (page (lane/4)%4, dim group lane%4), K (lane group g, e) ----
+      // centroid codes: A row (page (lane/4)%4, dim group lane%4), K (lane group g, e)
       const uint2 mq = *reinterpret_cast<const uint2*>(S + kSlotRec * sq + kOffMu + 32 * row +
                                                        8 * (lane & 3));
-      f32x4 dmu = {0.f, 0.f, 0.f, 0.f};
-      dmu = mfma16x16x32(i8x8_to_bf16(mq), bqm, dmu);
-      // lane (page row, s' = sq, head h) holds D[(row, r)][(sq, h)] in register r
-      float qmu = (sq == 0) ? dmu[0] : (sq == 1) ? dmu[1] : (sq == 2) ? dmu[2] : dmu[3];
-      qmu += dpp<kRowRor4>(qmu);
-      qmu += dpp<kRowRor8>(qmu);
-      const float smu = half_lo(*reinterpret_cast<const uint16_t*>(Sr + kOffSmu));
-      const float qmu2 = qmu * smu * c0;
-
-      // ---- w[k] = (q_h.v_k) * s_V[k] * s_c[k] for this lane's page and head ----
+      const uint16_t smu_raw = *reinterpret_cast<const uint16_t*>(Sr + kOffSmu);
       uint32_t svw[R / 2], scw[R / 2];
 #pragma unroll
       for (int i = 0; i < R / 2; ++i) {
         svw[i] = *reinterpret_cast<const uint32_t*>(Sr + kOffSv + 4 * i);
         scw[i] = *reinterpret_cast<const uint32_t*>(Sr + kOffSc + 4 * i);
       }
+      // coefficient codes of this lane's token
+      const uint8_t* cp = Sr + kOffC + R * tok;
+      uint32_t cw[R / 4];
+      if constexpr (R == 4) {
+        cw[0] = *reinterpret_cast<const uint32_t*>(cp);
+      } else if constexpr (R == 8) {
+        const uint2 c2 = *reinterpret_cast<const uint2*>(cp);
+        cw[0] = c2.x;
+        cw[1] = c2.y;
+      } else {
+        const uint4 c4 = lds16(cp);
+        cw[0] = c4.x;
+        cw[1] = c4.y;
+        cw[2] = c4.z;
+        cw[3] = c4.w;
+      }
+      wait_lgkm0();
+      if (more) issue(k + 1, b1);
+      b0 = b1;
+      b1 = (k + 2 < n) ? step_bids(k + 2) : none;
+
+      // ---- V^T q on the matrix cores ----
+      f32x4 acc[kAcc];
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) acc[j] = f32x4{acc0_init, acc0_init, acc0_init, acc0_init};
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].x), as_bf16x8(qpiece(0)), acc[j]);
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].y), as_bf16x8(qpiece(1)), acc[j]);
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].z), as_bf16x8(qpiece(2)), acc[j]);
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].w), as_bf16x8(qpiece(3)), acc[j]);
+
+      // ---- q.mu ----
+      f32x4 dmu = {0.f, 0.f, 0.f, 0.f};
+      dmu = mfma16x16x32(i8x8_to_bf16(mq), as_bf16x8(qpiece(sq)), dmu);
+      // lane (page row, s' = sq, head h) holds D[(row, r)][(sq, h)] in register r
+      float qmu = (sq == 0) ? dmu[0] : (sq == 1) ? dmu[1] : (sq == 2) ? dmu[2] : dmu[3];
+      qmu += dpp<kRowRor4>(qmu);
+      qmu += dpp<kRowRor8>(qmu);
+      const float smu = half_lo(smu_raw);
+      const float qmu2 = qmu * smu * c0;
+
+      // ---- w[k] = (q_h.v_k) * s_V[k] * s_c[k] for this lane's page and head ----
       // fp16 operand times fp32 with a +0 addend: one mixed-precision FMA each
       auto hmul = [](uint32_t pair, int hi, float x) {
         return __builtin_fmaf(hi ? half_hi(pair) : half_lo(pair), x, 0.0f);
@@ -292,26 +320,19 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
           wk[kk] = hmul(scw[kk >> 1], kk & 1, hmul(svw[kk >> 1], kk & 1, acc[j][r]));
         }
       // ---- deviation logits (base 2, without q.mu) of tokens 4cg..4cg+3 ----
-      // codes of token t: R bytes from kOffC + R t
-      const uint8_t* cp = Sr + kOffC + 4 * R * (tok >> 2);
-      uint32_t cw[R];
+      // One 16-block 4x4x1 MFMA per basis index k: block l/4 is (page, token
+      // quarter cg), its rows the 4 tokens, its columns the 4 heads.  Lane l
+      // gives A = c[token l%16][k] and B = w[k] of its own page and head; it
+      // gets back tokens 4cg..4cg+3 of head l%4.  Each code is converted once
+      // instead of once per head, and the products stay fp32.
+      f32x4 dv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < R / 4; ++i) {
-        const uint4 c4 = lds16(cp + 16 * i);
-        cw[4 * i] = c4.x;
-        cw[4 * i + 1] = c4.y;
-        cw[4 * i + 2] = c4.z;
-        cw[4 * i + 3] = c4.w;
-      }
+      for (int kk = 0; kk < R; ++kk)
+        dv = __builtin_amdgcn_mfma_f32_4x4x1f32((float)(int8_t)(cw[kk >> 2] >> (8 * (kk & 3))),
+                                                wk[kk], dv, 0, 0, 0);
       float dl[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        float a = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < R; ++kk)
-          a = fmaf(wk[kk], (float)(int8_t)(cw[(R / 4) * t + (kk >> 2)] >> (8 * (kk & 3))), a);
-        dl[t] = a * c0;
-      }
+      for (int t = 0; t < 4; ++t) dl[t] = dv[t] * c0;
       // page LSE over 16 tokens: 4 in this lane, the rest in the lanes 4 and 8
       // apart in this row (same page and head, other token quarters)
       float sm = fast_exp2(dl[0]) + fast_exp2(dl[1]) + fast_exp2(dl[2]) + fast_exp2(dl[3]);
@@ -332,20 +353,33 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
       }
       const float s2 = qmu2 + lse2;
       if (tok < 4 && jpg < n_fin) {
-        outl[h][4 * k + row] = okp ? s2 * kLn2 : -INFINITY;
+        outl[h][kWavePages * wv + 4 * k + row] = okp ? s2 * kLn2 : -INFINITY;
         if (okp) lse2_merge(pm, ps, s2, 1.f);
       }
     }
   }
 
-  // ---- this workgroup's finalized pages: 4 lanes per head, 4 pages each ----
+  // ---- this wave's (max, sum) of each head, for the page-mass normalization ----
+  float m2 = __shfl_xor(pm, 16), s2 = __shfl_xor(ps, 16);
+  lse2_merge(pm, ps, m2, s2);
+  m2 = __shfl_xor(pm, 32);
+  s2 = __shfl_xor(ps, 32);
+  lse2_merge(pm, ps, m2, s2);
+  if (lane < kG) red[wv][lane] = make_float2(pm, ps);
   __syncthreads();
+
+  // ---- the workgroup's finalized pages: one 4-page piece per thread, each
+  // head's kWgPages scores leave as one contiguous run ----
+  constexpr int kPieces = kWgPages / 4;   // per head
+  static_assert(kG * kPieces <= 64 * kScoreWaves, "one 4-page piece per thread");
   {
-    const int nval = min(4 * n, n_fin - 4 * s0);
-    const int hh = lane >> 2, part = lane & 3;
-    float* dst = lse_out + (size_t)hh * p.max_pages + 4 * s0 + 4 * part;
+    const int t = threadIdx.x;
+    const int p0 = kWgPages * g;
+    const int nval = min(kWgPages, n_fin - p0);
+    const int hh = t / kPieces, part = t % kPieces;
+    float* dst = lse_out + (size_t)hh * p.max_pages + p0 + 4 * part;
     const bool vec = (p.max_pages & 3) == 0 && ((uintptr_t)p.page_lse & 15) == 0;
-    if (lane < 16 && 4 * part < nval) {
+    if (t < kG * kPieces && 4 * part < nval) {
       const float4 v = *reinterpret_cast<const float4*>(&outl[hh][4 * part]);
       if (vec && 4 * part + 4 <= nval) {
         *reinterpret_cast<float4*>(dst) = v;
@@ -354,16 +388,14 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
         for (int i = 0; i < 4 && 4 * part + i < nval; ++i) dst[i] = e[i];
       }
     }
+    // one (max, sum) partial per workgroup and head
+    if (t < kG && p.partials) {
+      float pm2 = -INFINITY, ps2 = 0.f;
+#pragma unroll
+      for (int v2 = 0; v2 < kScoreWaves; ++v2) lse2_merge(pm2, ps2, red[v2][t].x, red[v2][t].y);
+      p.partials[((size_t)b * p.hq + qhead0 + t) * W + g] = make_float2(pm2, ps2);
+    }
   }
-
-  // ---- per-workgroup (max, sum) of each head, for the page-mass normalization ----
-  float m2 = __shfl_xor(pm, 16), s2 = __shfl_xor(ps, 16);
-  lse2_merge(pm, ps, m2, s2);
-  m2 = __shfl_xor(pm, 32);
-  s2 = __shfl_xor(ps, 32);
-  lse2_merge(pm, ps, m2, s2);
-  if (lane < 4 && p.partials)
-    p.partials[((size_t)b * p.hq + qhead0 + lane) * W + w] = make_float2(pm, ps);
 }
 
 }  // namespace
@@ -374,7 +406,7 @@ ScorePlan plan_score(int32_t batch, int32_t hkv, int32_t max_pages) {
   (void)batch;
   (void)hkv;
   ScorePlan pl;
-  const long long steps = kScoreSteps;
+  const long long steps = (long long)kScoreSteps * kScoreWaves;
   const long long nsteps = ((long long)max_pages + 3) / 4;
   pl.n_chunks = (int32_t)std::max(1LL, (nsteps + steps - 1) / steps);
   return pl;
@@ -388,9 +420,9 @@ hipError_t launch_score(int32_t rank, const uint16_t* q, const uint8_t* summ, in
                 hkv, plan.n_chunks};
   dim3 grid(plan.n_chunks, hkv, batch);
   switch (rank) {
-    case 4: hipLaunchKernelGGL(score_kernel<4>, grid, dim3(64), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(score_kernel<8>, grid, dim3(64), 0, stream, p); break;
-    case 16: hipLaunchKernelGGL(score_kernel<16>, grid, dim3(64), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(score_kernel<4>, grid, dim3(64 * kScoreWaves), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(score_kernel<8>, grid, dim3(64 * kScoreWaves), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL(score_kernel<16>, grid, dim3(64 * kScoreWaves), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
