@@ -41,8 +41,12 @@ struct AttendParams {
 // Global -> LDS copy of 16 bytes per lane: lane l writes LDS bytes
 // [lds + 16 l, +16) from sbase + voff.  M0 carries the LDS address; the
 // compiler treats M0 as reserved and these kernels have no other user of it.
+// The copy is non-temporal: each K/V page is read once per step, and
+// streaming it past the cache's normal allocation raises the read rate
+// (each instruction reads one contiguous kilobyte, so no line is split
+// between instructions).
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff),
                "s"(sbase), "s"(lds)
                : "memory");
 }
