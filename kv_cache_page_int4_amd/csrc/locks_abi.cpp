@@ -25,7 +25,7 @@ locks_status check_dims(const locks_dims* d) {
 constexpr int64_t kMaxPages = (int64_t)1 << 26;
 
 struct ScoreWs {
-  size_t lse_off, part_off, l2_off, key_off, idx_off, total;
+  size_t lse_off, part_off, key_off, idx_off, total;
   ScorePlan sp;
   SelectPlan sel;
 };
@@ -42,8 +42,6 @@ ScoreWs score_ws_layout(const locks_dims* d, int32_t batch, int32_t max_pages, i
   // partials serve the scorer's chunking and the standalone-select chunking
   const int32_t n_part = w.sp.n_chunks > w.sel.n_chunks ? w.sp.n_chunks : w.sel.n_chunks;
   off += align_up((size_t)batch * d->num_q_heads * n_part * sizeof(float2));
-  w.l2_off = off;
-  off += align_up((size_t)batch * d->num_q_heads * sizeof(float));
   const size_t ncand = (size_t)batch * d->num_kv_heads * w.sel.n_chunks * w.sel.slots;
   w.key_off = off;
   off += align_up(ncand * sizeof(uint32_t));
@@ -163,7 +161,6 @@ static locks_status select_pages_impl(const locks_dims* dims, const float* page_
   if (e == hipSuccess)
     e = launch_select(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, n_tables,
                       budget_pages, part, w.sel.n_chunks,
-                      reinterpret_cast<float*>(ws_at(workspace, w.l2_off)),
                       reinterpret_cast<uint32_t*>(ws_at(workspace, w.key_off)),
                       reinterpret_cast<int32_t*>(ws_at(workspace, w.idx_off)), w.sel, sel,
                       sel_count, s);
@@ -208,7 +205,6 @@ locks_status locks_score_select(const locks_dims* dims, const void* q, const voi
   if (e == hipSuccess)
     e = launch_select(lse, max_pages, seq_lens, batch, dims->num_q_heads, dims->num_kv_heads,
                       budget_pages, part, w.sp.n_chunks,
-                      reinterpret_cast<float*>(ws_at(workspace, w.l2_off)),
                       reinterpret_cast<uint32_t*>(ws_at(workspace, w.key_off)),
                       reinterpret_cast<int32_t*>(ws_at(workspace, w.idx_off)), w.sel, sel,
                       sel_count, s);
@@ -242,7 +238,6 @@ static locks_status decode_layer_impl(const locks_dims* dims, const void* q,
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* lse = reinterpret_cast<float*>(ws_at(score_ws, w.lse_off));
   float2* part = reinterpret_cast<float2*>(ws_at(score_ws, w.part_off));
-  float* l2 = reinterpret_cast<float*>(ws_at(score_ws, w.l2_off));
   uint32_t* ck = reinterpret_cast<uint32_t*>(ws_at(score_ws, w.key_off));
   int32_t* ci = reinterpret_cast<int32_t*>(ws_at(score_ws, w.idx_off));
   float* po = reinterpret_cast<float*>(ws_at(attend_ws, a.o_off));
@@ -255,7 +250,7 @@ static locks_status decode_layer_impl(const locks_dims* dims, const void* q,
   const int32_t n_cand = w.sel.n_chunks * w.sel.slots;
   if (fused_select_attend_fits(n_cand, budget_pages)) {
     e = launch_select_stage1(lse, max_pages, seq_lens, batch, hq, n_tables, budget_pages, part,
-                             w.sp.n_chunks, l2, ck, ci, w.sel, s);
+                             w.sp.n_chunks, ck, ci, w.sel, s);
     if (e == hipSuccess)
       e = launch_select_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                                static_cast<const uint16_t*>(v_cache), layout.block_stride,
@@ -266,7 +261,7 @@ static locks_status decode_layer_impl(const locks_dims* dims, const void* q,
                                static_cast<uint16_t*>(out), out_lse, s);
   } else {
     e = launch_select(lse, max_pages, seq_lens, batch, hq, n_tables, budget_pages, part,
-                      w.sp.n_chunks, l2, ck, ci, w.sel, sel, sel_count, s);
+                      w.sp.n_chunks, ck, ci, w.sel, sel, sel_count, s);
     if (e == hipSuccess)
       e = launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                         static_cast<const uint16_t*>(v_cache), layout.block_stride,

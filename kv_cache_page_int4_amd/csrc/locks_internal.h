@@ -43,18 +43,19 @@ hipError_t launch_lse_partials(const float* page_lse, int32_t max_pages, const i
 // Selection runs per (sequence, table): `ntab` tables per sequence, each over
 // hq / ntab query heads (ntab = hkv: one table per KV head).
 //
-// Stage 1 only: per-head normalizers and every chunk's candidates (page order).
+// Stage 1 only: every chunk's candidates (page order); each chunk workgroup
+// merges the per-head (max, sum) partials into the normalizers it needs.
 hipError_t launch_select_stage1(const float* page_lse, int32_t max_pages,
                                 const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t ntab,
                                 int32_t budget_pages, const float2* partials,
-                                int32_t n_partials, float* head_l2, uint32_t* cand_key,
+                                int32_t n_partials, uint32_t* cand_key,
                                 int32_t* cand_idx, const SelectPlan& plan, hipStream_t stream);
 
 hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
                          int32_t batch, int32_t hq, int32_t ntab, int32_t budget_pages,
-                         const float2* partials, int32_t n_partials, float* head_l2,
-                         uint32_t* cand_key, int32_t* cand_idx, const SelectPlan& plan, int32_t* sel, int32_t* sel_count,
-                         hipStream_t stream);
+                         const float2* partials, int32_t n_partials, uint32_t* cand_key,
+                         int32_t* cand_idx, const SelectPlan& plan, int32_t* sel,
+                         int32_t* sel_count, hipStream_t stream);
 
 // ---- sparse attention ---------------------------------------------------------
 struct AttendPlan {

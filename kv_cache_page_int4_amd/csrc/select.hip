@@ -11,9 +11,11 @@
 // and the k = min(budget, valid pages) largest m_j are kept, ties to the lower
 // page index, listed in ascending page order.
 //
-// Three kernels.  First L_h per query head from the scorer's (max, sum)
-// partials.  Stage 1: one workgroup per 2048-page chunk turns scores into
-// order-preserving 32-bit keys and radix-selects the chunk's top min(k, 2048)
+// Two kernels.  Stage 1: one workgroup per 2048-page chunk first merges the
+// (max, sum) partials of its table's query heads into L_h (one head per
+// wave; a few kilobytes per head, cheaper than a kernel boundary), then turns
+// scores into order-preserving 32-bit keys and radix-selects the chunk's top
+// min(k, 2048)
 // (8-bit digits, LDS histograms); survivors are written in page
 // order.  Stage 2: one workgroup per (sequence, KV head) radix-selects the
 // global top k over all candidates.  Because each chunk emits its survivors in
@@ -65,7 +67,8 @@ __global__ __launch_bounds__(kSelThreads) void lse_partials_kernel(
 struct SelParams {
   const float* page_lse;
   const int32_t* seq_lens;
-  const float* head_l2;      // [b][hq] base-2 log of each head's total estimated mass
+  const float2* partials;    // [b][hq][n_partials] base-2 (max, sum) pieces of each head's mass
+  int32_t n_partials;
   uint32_t* cand_key;
   int32_t* cand_idx;
   int32_t* sel;
@@ -73,40 +76,6 @@ struct SelParams {
   // ntab: selection tables per sequence; a table holds hq / ntab query heads
   int32_t max_pages, hq, ntab, budget, n_chunks, slots;
 };
-
-// L_h (base 2) of every (sequence, query head) from the scorer's partials.
-constexpr int kHeadThreads = 256;
-constexpr int kHeadLoads = 16;
-
-__global__ __launch_bounds__(kHeadThreads) void head_lse_kernel(const float2* partials,
-                                                                int32_t n_partials, float* head_l2) {
-  const size_t row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float2* pp = partials + row * n_partials;
-  float m = -INFINITY, s = 0.f;
-  for (int c0 = tid; c0 < n_partials; c0 += kHeadLoads * kHeadThreads) {
-    float2 v[kHeadLoads];
-#pragma unroll
-    for (int u = 0; u < kHeadLoads; ++u) {
-      const int c = c0 + kHeadThreads * u;
-      v[u] = (c < n_partials) ? pp[c] : make_float2(-INFINITY, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < kHeadLoads; ++u) lse2_merge(m, s, v[u].x, v[u].y);
-  }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-    lse2_merge(m, s, m2, s2);
-  }
-  __shared__ float2 red[kHeadThreads / 64];
-  if (lane == 0) red[wave] = make_float2(m, s);
-  __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < kHeadThreads / 64; ++w) lse2_merge(m, s, red[w].x, red[w].y);
-    head_l2[row] = (s > 0.f) ? m + fast_log2(s) : -INFINITY;
-  }
-}
 
 // Stage 2 over candidates held in registers: thread t owns the contiguous
 // run [t*per, t*per + per) of the page-ordered candidate list (per <= RUN), so
@@ -272,7 +241,11 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
   __shared__ int scan_smem[kSelThreads / 64];
 
   // keys of this thread's consecutive pages: log2 sum_h 2^(s_hj log2 e - L_h)
-  // over the table's heads, four heads' scores and normalizers loaded at a time
+  // over the table's heads.  The heads go in batches of one per wave: each
+  // wave first merges its head's (max, sum) partials into L_h (base 2), then
+  // every thread adds the batch's heads to its keys, four heads at a time.
+  __shared__ float l2s[kSelThreads / 64];
+  const int lane = tid & 63, wave = tid >> 6;
   const int jbase = chunk * kSelChunk + kPerThread * tid;
   uint32_t key[kPerThread];
   int nvalid = 0;
@@ -282,7 +255,32 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
     float lm[kPerThread];
 #pragma unroll
     for (int t = 0; t < kPerThread; ++t) lm[t] = -INFINITY;
-    for (int h0 = tab * hpt; h0 < (tab + 1) * hpt; h0 += kG) {
+    const int h_end = (tab + 1) * hpt;
+    for (int hb = tab * hpt; hb < h_end; hb += kSelThreads / 64) {
+      const int nb = min(kSelThreads / 64, h_end - hb);
+      __syncthreads();   // the previous batch's normalizers have been read
+      if (wave < nb) {
+        const float2* pp = p.partials + ((size_t)b * p.hq + hb + wave) * p.n_partials;
+        float m = -INFINITY, sm = 0.f;
+        for (int c0 = lane; c0 < p.n_partials; c0 += 8 * 64) {
+          float2 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int c = c0 + 64 * u;
+            v[u] = (c < p.n_partials) ? pp[c] : make_float2(-INFINITY, 0.f);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) lse2_merge(m, sm, v[u].x, v[u].y);
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sm, o);
+          lse2_merge(m, sm, m2, s2);
+        }
+        if (lane == 0) l2s[wave] = (sm > 0.f) ? m + fast_log2(sm) : -INFINITY;
+      }
+      __syncthreads();
+      for (int h0 = hb; h0 < hb + nb; h0 += kG) {
       float sv[kG][kPerThread];
       float l2[kG];
 #pragma unroll
@@ -290,7 +288,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
         const float* s = p.page_lse + ((size_t)b * p.hq + h0 + hh) * p.max_pages;
 #pragma unroll
         for (int t = 0; t < kPerThread; ++t) sv[hh][t] = s[min(jbase + t, jmax)];
-        l2[hh] = p.head_l2[(size_t)b * p.hq + h0 + hh];
+        l2[hh] = l2s[h0 - hb + hh];
       }
 #pragma unroll
       for (int hh = 0; hh < kG; ++hh) {
@@ -301,6 +299,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
           const float hi = fmaxf(lm[t], a), lo = fminf(lm[t], a);
           lm[t] = (hi == -INFINITY) ? -INFINITY : hi + fast_log2(1.f + fast_exp2(lo - hi));
         }
+      }
       }
     }
 #pragma unroll
@@ -384,13 +383,9 @@ hipError_t launch_lse_partials(const float* page_lse, int32_t max_pages, const i
 hipError_t launch_select_stage1(const float* page_lse, int32_t max_pages,
                                 const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t ntab,
                                 int32_t budget_pages, const float2* partials,
-                                int32_t n_partials, float* head_l2, uint32_t* cand_key,
+                                int32_t n_partials, uint32_t* cand_key,
                                 int32_t* cand_idx, const SelectPlan& plan, hipStream_t stream) {
-  hipLaunchKernelGGL(head_lse_kernel, dim3(batch * hq), dim3(kHeadThreads), 0, stream, partials,
-                     n_partials, head_l2);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  SelParams p{page_lse, seq_lens, head_l2, cand_key, cand_idx, nullptr, nullptr,
+  SelParams p{page_lse, seq_lens, partials, n_partials, cand_key, cand_idx, nullptr, nullptr,
               max_pages, hq, ntab, budget_pages, plan.n_chunks, plan.slots};
   hipLaunchKernelGGL(select_chunk_kernel, dim3(plan.n_chunks, ntab, batch), dim3(kSelThreads), 0,
                      stream, p);
@@ -399,14 +394,13 @@ hipError_t launch_select_stage1(const float* page_lse, int32_t max_pages,
 
 hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
                          int32_t batch, int32_t hq, int32_t ntab, int32_t budget_pages,
-                         const float2* partials, int32_t n_partials, float* head_l2,
-                         uint32_t* cand_key, int32_t* cand_idx, const SelectPlan& plan,
-                         int32_t* sel, int32_t* sel_count, hipStream_t stream) {
+                         const float2* partials, int32_t n_partials, uint32_t* cand_key,
+                         int32_t* cand_idx, const SelectPlan& plan, int32_t* sel,
+                         int32_t* sel_count, hipStream_t stream) {
   hipError_t e = launch_select_stage1(page_lse, max_pages, seq_lens, batch, hq, ntab, budget_pages,
-                                      partials, n_partials, head_l2, cand_key, cand_idx, plan,
-                                      stream);
+                                      partials, n_partials, cand_key, cand_idx, plan, stream);
   if (e != hipSuccess) return e;
-  SelParams p{page_lse, seq_lens, head_l2, cand_key, cand_idx, sel, sel_count,
+  SelParams p{page_lse, seq_lens, partials, n_partials, cand_key, cand_idx, sel, sel_count,
               max_pages, hq, ntab, budget_pages, plan.n_chunks, plan.slots};
   const int per = (plan.n_chunks * plan.slots + kSelThreads - 1) / kSelThreads;
   if (per <= 8)
