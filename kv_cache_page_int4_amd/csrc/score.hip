@@ -157,8 +157,10 @@ score_kernel(ScoreParams p) {
   const int32_t* __restrict__ bt = p.block_table + (size_t)b * p.max_pages;
   float* __restrict__ lse_out = p.page_lse + ((size_t)b * p.hq + qhead0) * p.max_pages;
 
-  // pages that are not finalized score -inf
-  for (int j = n_fin + kWgPages * g + (int)threadIdx.x; j < p.max_pages; j += kWgPages * W)
+  // pages that are not finalized score -inf (each written once: a grid-stride
+  // loop over all threads of the (sequence, KV head)'s workgroups)
+  constexpr int kThreads = 64 * kScoreWaves;
+  for (int j = n_fin + kThreads * g + (int)threadIdx.x; j < p.max_pages; j += kThreads * W)
 #pragma unroll
     for (int hh = 0; hh < kG; ++hh) lse_out[(size_t)hh * p.max_pages + j] = -INFINITY;
 
