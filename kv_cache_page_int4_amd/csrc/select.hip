@@ -281,25 +281,25 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
       }
       __syncthreads();
       for (int h0 = hb; h0 < hb + nb; h0 += kG) {
-      float sv[kG][kPerThread];
-      float l2[kG];
+        float sv[kG][kPerThread];
+        float l2[kG];
 #pragma unroll
-      for (int hh = 0; hh < kG; ++hh) {
-        const float* s = p.page_lse + ((size_t)b * p.hq + h0 + hh) * p.max_pages;
+        for (int hh = 0; hh < kG; ++hh) {
+          const float* s = p.page_lse + ((size_t)b * p.hq + h0 + hh) * p.max_pages;
 #pragma unroll
-        for (int t = 0; t < kPerThread; ++t) sv[hh][t] = s[min(jbase + t, jmax)];
-        l2[hh] = l2s[h0 - hb + hh];
-      }
-#pragma unroll
-      for (int hh = 0; hh < kG; ++hh) {
-#pragma unroll
-        for (int t = 0; t < kPerThread; ++t) {
-          const float a = sv[hh][t] * kLog2e - l2[hh];
-          // log2(2^lm + 2^a) without overflow
-          const float hi = fmaxf(lm[t], a), lo = fminf(lm[t], a);
-          lm[t] = (hi == -INFINITY) ? -INFINITY : hi + fast_log2(1.f + fast_exp2(lo - hi));
+          for (int t = 0; t < kPerThread; ++t) sv[hh][t] = s[min(jbase + t, jmax)];
+          l2[hh] = l2s[h0 - hb + hh];
         }
-      }
+#pragma unroll
+        for (int hh = 0; hh < kG; ++hh) {
+#pragma unroll
+          for (int t = 0; t < kPerThread; ++t) {
+            const float a = sv[hh][t] * kLog2e - l2[hh];
+            // log2(2^lm + 2^a) without overflow
+            const float hi = fmaxf(lm[t], a), lo = fminf(lm[t], a);
+            lm[t] = (hi == -INFINITY) ? -INFINITY : hi + fast_log2(1.f + fast_exp2(lo - hi));
+          }
+        }
       }
     }
 #pragma unroll

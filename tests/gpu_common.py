@@ -64,7 +64,8 @@ class Layer:
     def score(self):
         w = self.w
         P = self.bt.shape[1]
-        lse = torch.empty((w.batch, w.hq, P), dtype=torch.float32, device="cuda")
+        # NaN-filled, so that a page the scorer skips cannot pass as -inf
+        lse = torch.full((w.batch, w.hq, P), float("nan"), dtype=torch.float32, device="cuda")
         ws = torch.empty(L.score_workspace_bytes(self.d, w.batch, P, 0), dtype=torch.uint8, device="cuda")
         L.score_pages(self.d, self.q, self.summ, self.nb, self.bt, self.seq, lse, ws)
         return lse
@@ -74,7 +75,8 @@ class Layer:
         P = self.bt.shape[1]
         sel = torch.full((w.batch, w.hkv, budget), -7, dtype=torch.int32, device="cuda")
         cnt = torch.full((w.batch, w.hkv), -7, dtype=torch.int32, device="cuda")
-        lse = torch.empty((w.batch, w.hq, P), dtype=torch.float32, device="cuda") if with_lse else None
+        lse = (torch.full((w.batch, w.hq, P), float("nan"), dtype=torch.float32, device="cuda")
+               if with_lse else None)
         ws = torch.empty(L.score_workspace_bytes(self.d, w.batch, P, budget), dtype=torch.uint8,
                          device="cuda")
         L.score_select(self.d, self.q, self.summ, self.nb, self.bt, self.seq, budget, sel, cnt, ws,
