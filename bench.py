@@ -489,14 +489,28 @@ def main():
                               inp3.seq_lens, lse3, st3.ws_score)
 
         sc3 = timed(score_large, args.kernel_reps) / wl.layers
+
+        def attend_large():
+            for layer in range(wl.layers):
+                L.sparse_attend(d3, inp3.q[layer], inp3.k[layer], inp3.v[layer],
+                                inp3.block_table, inp3.seq_lens, st3.sel[layer], st3.cnt[layer],
+                                wl.budget_pages, st3.out[layer], st3.ws_att)
+
+        at3 = timed(attend_large, args.kernel_reps) / wl.layers
+        att3_units = int(st3.cnt.sum().item()) / wl.layers
         ph3 = wl.batch * wl.hkv * wl.pages
         entry = {"us_per_layer": round(ms3 * 1e3 / wl.layers, 3),
                  "scorer_us": round(sc3 * 1e3, 3),
                  "scorer_gbs": round(ph3 * SCORE_BYTES_PER_PAGE_HEAD / (sc3 * 1e-3) / 1e9, 1),
+                 "attention_us": round(at3 * 1e3, 3),
+                 "attention_gbs": round(att3_units * ATTEND_BYTES_PER_PAGE_HEAD
+                                        / (at3 * 1e-3) / 1e9, 1),
                  "batch": wl.batch, "ctx": wl.ctx, "layers": wl.layers}
         entry["scorer_frac"] = round(entry["scorer_gbs"] / PEAK_HBM_GBS, 4)
+        entry["attention_frac"] = round(entry["attention_gbs"] / PEAK_HBM_GBS, 4)
         log(f"[{wl.name}] decode step {ms3 * 1e3 / wl.layers:.2f} us/layer; scorer "
-            f"{sc3 * 1e3:.2f} us = {entry['scorer_gbs']:.0f} GB/s")
+            f"{sc3 * 1e3:.2f} us = {entry['scorer_gbs']:.0f} GB/s; attention "
+            f"{at3 * 1e3:.2f} us = {entry['attention_gbs']:.0f} GB/s")
         del st3
         if not args.no_dense:
             dn3 = DecodeStep(d3, inp3.k, inp3.v, summ3, inp3.q, inp3.block_table, inp3.seq_lens,
@@ -544,7 +558,11 @@ def main():
                      "bytes_per_launch": page_heads * SCORE_BYTES_PER_PAGE_HEAD},
         "attention": {"achieved": round(attend_gbs, 1), "unit": "GB/s",
                       "frac": round(attend_gbs / PEAK_HBM_GBS, 4),
-                      "kernel_us": round(attend_ms * 1e3, 3)},
+                      "kernel_us": round(attend_ms * 1e3, 3),
+                      "note": ("attention + split merge, selected K/V bytes only; "
+                               f"{att_units * ATTEND_BYTES_PER_PAGE_HEAD / 2**20:.1f} MiB per "
+                               "layer is latency-bound, see also.*.attention_gbs for the "
+                               "large-batch rate")},
         "finalize_us_per_step": round(finalize_ms * 1e3, 3),
         "stream_read_gbs": round(stream_read_gbs, 1),
         "pages_scored_per_s": page_heads / (score_ms * 1e-3),
