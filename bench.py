@@ -533,6 +533,15 @@ def main():
         also[ws.name] = {"us_per_layer": ms2 * 1e3 / ws.layers,
                          "note": "working set fits the 256 MB Infinity Cache; latency-bound"}
         log(f"[{ws.name}] decode step {ms2 * 1e3:.2f} us/layer")
+        if not args.no_dense:
+            dn2 = DecodeStep(d2, inp2.k, inp2.v, summ2, inp2.q, inp2.block_table, inp2.seq_lens,
+                             1, dense=True)
+            dms2 = time_step(dn2, max(args.steps, 50), args.warmup)
+            also[ws.name]["dense_us_per_layer"] = round(dms2 * 1e3 / ws.layers, 3)
+            also[ws.name]["speedup_vs_dense"] = round(dms2 / ms2, 3)
+            log(f"[{ws.name}] dense {dms2 * 1e3 / ws.layers:.2f} us/layer, speedup "
+                f"{dms2 / ms2:.2f}x")
+            del dn2
 
     result = {
         "metric": METRIC,
