@@ -93,6 +93,19 @@ def timed(fn, reps, warm=1):
     return e0.elapsed_time(e1) / reps
 
 
+def replay_times(step, n):
+    """ms of each of n graph replays, each bracketed by its own pair of events."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        step.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
 def setup(w, build=True):
     import torch
     from kv_cache_page_int4_amd import locks as L
@@ -315,6 +328,14 @@ def main():
     ms_step = time_step(step, args.steps, args.warmup)
     us_layer = ms_step * 1e3 / w.layers
     log(f"[{w.name}] decode step {ms_step:.3f} ms = {us_layer:.2f} us/layer")
+    # spread of single replays, each between its own pair of events (after the
+    # timed region, so that the value above is untouched by the extra events)
+    import numpy as np
+    per_replay = replay_times(step, args.steps)
+    pct = np.percentile(np.array(per_replay) * 1e3 / w.layers, [10, 50, 90])
+    step_spread = {"p10": round(float(pct[0]), 3), "p50": round(float(pct[1]), 3),
+                   "p90": round(float(pct[2]), 3), "replays": len(per_replay)}
+    log(f"[{w.name}] single replays: p10 {pct[0]:.2f}, median {pct[1]:.2f}, p90 {pct[2]:.2f} us/layer")
 
     # --- dominant kernel: the scorer, timed in isolation on the launch stream ---
     P = inp.block_table.shape[1]
@@ -551,6 +572,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "us_per_layer_single_replays": step_spread,
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
