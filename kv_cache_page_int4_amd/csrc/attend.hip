@@ -183,8 +183,7 @@ __device__ __forceinline__ void attend_wave(const AttendParams& p, int split, in
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = (4 * row + r < ntok) ? a[r] * p.scale2 : -INFINITY;
         float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = cross_rows_max(mx);
         const float Mn = fmaxf(M, mx);
         const float alpha = (Mn == -INFINITY) ? 1.f : fast_exp2(M - Mn);
         float P[4];
@@ -226,11 +225,9 @@ __device__ __forceinline__ void attend_wave(const AttendParams& p, int split, in
   for (int hh = 0; hh < 4; ++hh)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      acc[hh][e] += __shfl_xor(acc[hh][e], 16);
-      acc[hh][e] += __shfl_xor(acc[hh][e], 32);
+      acc[hh][e] = cross_rows_sum(acc[hh][e]);
     }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = cross_rows_sum(lsum);
   if (row == 0) {
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
@@ -381,8 +378,7 @@ __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(AttendParam
   __shared__ float2 accsh[kMergeWaves][64];
   float M = -INFINITY;
   for (int s = t; s < n; s += kMergeThreads) M = fmaxf(M, ml[s].x);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+  M = wave_max_f(M);
   if (lane == 0) red[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -395,8 +391,7 @@ __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(AttendParam
     if (s < kMergeW) wsh[s] = w;
     L += w * v.y;
   }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
+  L = wave_sum_f(L);
   if (lane == 0) red[wave] = L;
   __syncthreads();   // also publishes wsh
   L = red[0] + red[1] + red[2] + red[3];

@@ -104,12 +104,10 @@ __global__ __launch_bounds__(64) void exact_lse_kernel(ExactParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = a[r] * p.scale2;
     float m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = cross_rows_max(m);
     float e = fast_exp2(x[0] - m) + fast_exp2(x[1] - m) + fast_exp2(x[2] - m) +
               fast_exp2(x[3] - m);
-    e += __shfl_xor(e, 16);
-    e += __shfl_xor(e, 32);
+    e = cross_rows_sum(e);
     if (lane < kG) outl[h][k] = (bcur >= 0) ? (m + fast_log2(e)) * kLn2 : -INFINITY;
   }
   // 4 lanes per head, 4 pages each

@@ -50,11 +50,7 @@ __global__ __launch_bounds__(kSelThreads) void lse_partials_kernel(
     const float v = s[j] * kLog2e;
     if (v > -INFINITY) lse2_merge(m, sm, v, 1.f);
   }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sm, o);
-    lse2_merge(m, sm, m2, s2);
-  }
+  wave_lse2(m, sm);
   __shared__ float2 red[kSelThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(m, sm);
   __syncthreads();
@@ -272,11 +268,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
 #pragma unroll
           for (int u = 0; u < 8; ++u) lse2_merge(m, sm, v[u].x, v[u].y);
         }
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sm, o);
-          lse2_merge(m, sm, m2, s2);
-        }
+        wave_lse2(m, sm);
         if (lane == 0) l2s[wave] = (sm > 0.f) ? m + fast_log2(sm) : -INFINITY;
       }
       __syncthreads();

@@ -14,24 +14,16 @@ namespace sel {
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* smem) {
   constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int x = wave_incl_scan(v);
   if (lane == 63) smem[wave] = x;
   __syncthreads();
   const int t = (lane < NW) ? smem[lane] : 0;
-  int u = t;
-#pragma unroll
-  for (int o = 1; o < NW; o <<= 1) {
-    const int y = __shfl_up(u, o);
-    if (lane >= o) u += y;
-  }
-  const int before = __shfl(u, wave) - __shfl(t, wave);   // totals of the waves below
-  *total = __shfl(u, NW - 1);
+  const int u = wave_incl_scan(t);
+  // totals of the waves below
+  const int before = __builtin_amdgcn_readlane(u, wave) - __builtin_amdgcn_readlane(t, wave);
+  *total = __builtin_amdgcn_readlane(u, NW - 1);
   __syncthreads();   // smem is reused by the next call
   return before + x - v;
 }
@@ -42,30 +34,21 @@ template <int NT>
 __device__ __forceinline__ void block_sum_minmax(int& sum, uint32_t& mn, uint32_t& mx, uint32_t* smem) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    sum += __shfl_xor(sum, o);
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-  }
+  sum = (int)wave_sum_u((uint32_t)sum);
+  mn = wave_min_u(mn);
+  mx = wave_max_u(mx);
   if (lane == 0) {
     smem[wave] = (uint32_t)sum;
     smem[NW + wave] = mn;
     smem[2 * NW + wave] = mx;
   }
   __syncthreads();
-  int a = (lane < NW) ? (int)smem[lane] : 0;
-  uint32_t b = (lane < NW) ? smem[NW + lane] : 0xFFFFFFFFu;
-  uint32_t c = (lane < NW) ? smem[2 * NW + lane] : 0u;
-#pragma unroll
-  for (int o = 1; o < NW; o <<= 1) {
-    a += __shfl_xor(a, o);
-    b = min(b, (uint32_t)__shfl_xor((int)b, o));
-    c = max(c, (uint32_t)__shfl_xor((int)c, o));
-  }
-  sum = __shfl(a, 0);
-  mn = (uint32_t)__shfl((int)b, 0);
-  mx = (uint32_t)__shfl((int)c, 0);
+  const uint32_t a = (lane < NW) ? smem[lane] : 0u;
+  const uint32_t b = (lane < NW) ? smem[NW + lane] : 0xFFFFFFFFu;
+  const uint32_t c = (lane < NW) ? smem[2 * NW + lane] : 0u;
+  sum = (int)wave_sum_u(a);
+  mn = wave_min_u(b);
+  mx = wave_max_u(c);
   __syncthreads();
 }
 
@@ -77,13 +60,8 @@ __device__ __forceinline__ void pick_digit(const int* hist, int rem, int* sh) {
   const int4 v = *reinterpret_cast<const int4*>(hist + 4 * lane);
   const int c[4] = {v.x, v.y, v.z, v.w};
   const int tot = c[0] + c[1] + c[2] + c[3];
-  int x = tot;  // inclusive suffix sum over lanes (higher digits first)
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_down(x, o);
-    if (lane + o < 64) x += y;
-  }
-  int above = x - tot;  // keys whose digit exceeds 4*lane+3
+  const int pre = wave_incl_scan(tot);   // digits up to 4*lane+3
+  int above = __builtin_amdgcn_readlane(pre, 63) - pre;  // keys whose digit exceeds 4*lane+3
 #pragma unroll
   for (int e = 3; e >= 0; --e) {
     if (above < rem && above + c[e] >= rem) {
