@@ -179,8 +179,7 @@ score_kernel(ScoreParams p) {
       qsum += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
               bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
     }
-    qsum += __shfl_xor(qsum, 16);
-    qsum += __shfl_xor(qsum, 32);
+    qsum = cross_rows_sum(qsum);
     // the codes enter the product as 136 + n: start the accumulator at -136 sum(q)
     const float acc0_init = -136.f * qsum;
     // for q.mu, column (lane%16) = (dim group s' = (lane/4)%4, head lane%4) and
@@ -362,11 +361,21 @@ score_kernel(ScoreParams p) {
   }
 
   // ---- this wave's (max, sum) of each head, for the page-mass normalization ----
-  float m2 = __shfl_xor(pm, 16), s2 = __shfl_xor(ps, 16);
-  lse2_merge(pm, ps, m2, s2);
-  m2 = __shfl_xor(pm, 32);
-  s2 = __shfl_xor(ps, 32);
-  lse2_merge(pm, ps, m2, s2);
+  // over the lanes 16 and 32 apart, by row swaps (lse2_merge gives the same
+  // bits with its operands exchanged, so both lanes of a pair agree)
+  {
+    float ma, mb, sa, sb;
+    swap16(pm, ma, mb);
+    swap16(ps, sa, sb);
+    pm = ma;
+    ps = sa;
+    lse2_merge(pm, ps, mb, sb);
+    swap32(pm, ma, mb);
+    swap32(ps, sa, sb);
+    pm = ma;
+    ps = sa;
+    lse2_merge(pm, ps, mb, sb);
+  }
   if (lane < kG) red[wv][lane] = make_float2(pm, ps);
   __syncthreads();
 
