@@ -37,16 +37,9 @@ constexpr float kEpsConst = 1e-12f;
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
-  return x;
-}
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
+// whole-wave sum and max on DPP and the row swaps (no LDS round trips)
+__device__ __forceinline__ float wave_sum(float x) { return wave_sum_f(x); }
+__device__ __forceinline__ float wave_max(float x) { return wave_max_f(x); }
 
 // fp16 scale of a max-magnitude: round to nearest even, saturate at 65504.
 __device__ __forceinline__ float fp16_scale(float m, float qmax) {
