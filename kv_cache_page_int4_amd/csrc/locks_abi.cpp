@@ -34,7 +34,7 @@ ScoreWs score_ws_layout(const locks_dims* d, int32_t batch, int32_t max_pages, i
                         bool need_lse) {
   ScoreWs w{};
   w.sp = plan_score(batch, d->num_kv_heads, max_pages);
-  w.sel = plan_select(max_pages, budget > 0 ? budget : 1);
+  w.sel = plan_select(max_pages, budget > 0 ? budget : 1, (int64_t)batch * d->num_kv_heads);
   size_t off = 0;
   w.lse_off = off;
   if (need_lse) off += align_up((size_t)batch * d->num_q_heads * max_pages * sizeof(float));
@@ -157,7 +157,7 @@ static locks_status select_pages_impl(const locks_dims* dims, const float* page_
   hipStream_t s = static_cast<hipStream_t>(stream);
   float2* part = reinterpret_cast<float2*>(ws_at(workspace, w.part_off));
   hipError_t e = launch_lse_partials(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, part,
-                                     w.sel.n_chunks, kSelChunk, s);
+                                     w.sel.n_chunks, w.sel.chunk_pages, s);
   if (e == hipSuccess)
     e = launch_select(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, n_tables,
                       budget_pages, part, w.sel.n_chunks,

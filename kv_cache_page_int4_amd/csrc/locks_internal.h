@@ -28,12 +28,14 @@ hipError_t launch_score(int32_t rank, const uint16_t* q, const uint8_t* summ, in
                         float2* partials, const ScorePlan& plan, hipStream_t stream);
 
 // ---- selection -------------------------------------------------------------
-constexpr int32_t kSelChunk = 2048;   // pages per first-stage select workgroup
+constexpr int32_t kSelChunk = 2048;   // pages per first-stage select workgroup (at least)
 struct SelectPlan {
-  int32_t n_chunks;     // first-stage chunks per (sequence, KV head)
-  int32_t slots;        // candidates kept per chunk = min(budget, kSelChunk)
+  int32_t chunk_pages;  // kSelChunk, or twice it when the grid is large
+  int32_t n_chunks;     // first-stage chunks per (sequence, table)
+  int32_t slots;        // candidates kept per chunk = min(budget, chunk_pages)
 };
-SelectPlan plan_select(int32_t max_pages, int32_t budget_pages);
+// groups: the most (sequence, table) pairs a call may select for (batch * Hkv)
+SelectPlan plan_select(int32_t max_pages, int32_t budget_pages, int64_t groups);
 
 // Per-head (max, sum) base-2 partials straight from page scores.
 hipError_t launch_lse_partials(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,

@@ -35,7 +35,8 @@ using sel::block_sum_minmax;
 using sel::radix_threshold;
 
 constexpr int kSelThreads = 1024;   // 16 waves: 4 per SIMD hide the latency chains
-constexpr int kPerThread = kSelChunk / kSelThreads;  // 2
+// stage-1 workgroups that two per CU run in one round
+constexpr long long kSelOneRound = 512;
 
 __global__ __launch_bounds__(kSelThreads) void lse_partials_kernel(
     const float* page_lse, int32_t max_pages, const int32_t* seq_lens, int32_t hq,
@@ -224,7 +225,13 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_big_kernel(SelParams
   if (tid == 0) p.sel_count[grp] = k;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) {
+// PT pages per thread: chunks of kSelThreads * PT pages (2048, or 4096 when the
+// grid of 2048-page chunks would not fit the chip in one round).
+template <int PT>
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void select_chunk_kernel(SelParams p) {
+  constexpr int kPerThread = PT;
+  constexpr int kUnroll = (PT == 2) ? 8 : 4;   // partials in flight per lane
   const int chunk = blockIdx.x, tab = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int hpt = p.hq / p.ntab;   // query heads of this table (a multiple of 4)
@@ -242,7 +249,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
   // every thread adds the batch's heads to its keys, four heads at a time.
   __shared__ float l2s[kSelThreads / 64];
   const int lane = tid & 63, wave = tid >> 6;
-  const int jbase = chunk * kSelChunk + kPerThread * tid;
+  const int jbase = chunk * (kSelThreads * kPerThread) + kPerThread * tid;
   uint32_t key[kPerThread];
   int nvalid = 0;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -258,15 +265,15 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
       if (wave < nb) {
         const float2* pp = p.partials + ((size_t)b * p.hq + hb + wave) * p.n_partials;
         float m = -INFINITY, sm = 0.f;
-        for (int c0 = lane; c0 < p.n_partials; c0 += 8 * 64) {
-          float2 v[8];
+        for (int c0 = lane; c0 < p.n_partials; c0 += kUnroll * 64) {
+          float2 v[kUnroll];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
+          for (int u = 0; u < kUnroll; ++u) {
             const int c = c0 + 64 * u;
             v[u] = (c < p.n_partials) ? pp[c] : make_float2(-INFINITY, 0.f);
           }
 #pragma unroll
-          for (int u = 0; u < 8; ++u) lse2_merge(m, sm, v[u].x, v[u].y);
+          for (int u = 0; u < kUnroll; ++u) lse2_merge(m, sm, v[u].x, v[u].y);
         }
         wave_lse2(m, sm);
         if (lane == 0) l2s[wave] = (sm > 0.f) ? m + fast_log2(sm) : -INFINITY;
@@ -356,10 +363,13 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(SelParams p) 
 
 }  // namespace
 
-SelectPlan plan_select(int32_t max_pages, int32_t budget_pages) {
+SelectPlan plan_select(int32_t max_pages, int32_t budget_pages, int64_t groups) {
   SelectPlan pl;
-  pl.n_chunks = (max_pages + kSelChunk - 1) / kSelChunk;
-  pl.slots = budget_pages < kSelChunk ? budget_pages : kSelChunk;
+  pl.chunk_pages = kSelChunk;
+  if ((long long)((max_pages + kSelChunk - 1) / kSelChunk) * groups > kSelOneRound)
+    pl.chunk_pages = 2 * kSelChunk;
+  pl.n_chunks = (max_pages + pl.chunk_pages - 1) / pl.chunk_pages;
+  pl.slots = budget_pages < pl.chunk_pages ? budget_pages : pl.chunk_pages;
   if (pl.slots < 1) pl.slots = 1;
   return pl;
 }
@@ -379,8 +389,13 @@ hipError_t launch_select_stage1(const float* page_lse, int32_t max_pages,
                                 int32_t* cand_idx, const SelectPlan& plan, hipStream_t stream) {
   SelParams p{page_lse, seq_lens, partials, n_partials, cand_key, cand_idx, nullptr, nullptr,
               max_pages, hq, ntab, budget_pages, plan.n_chunks, plan.slots};
-  hipLaunchKernelGGL(select_chunk_kernel, dim3(plan.n_chunks, ntab, batch), dim3(kSelThreads), 0,
-                     stream, p);
+  const dim3 grid(plan.n_chunks, ntab, batch);
+  if (plan.chunk_pages > kSelChunk)
+    hipLaunchKernelGGL(select_chunk_kernel<2 * kSelChunk / kSelThreads>, grid, dim3(kSelThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL(select_chunk_kernel<kSelChunk / kSelThreads>, grid, dim3(kSelThreads), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
