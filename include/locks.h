@@ -111,7 +111,8 @@ locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
  * attention run back to back inside the step's graph), with outputs
  * identical to those two calls.  The last selection stage runs inside the
  * attention kernel when budget_pages <= 1024 and the chunk candidates number
- * at most 8192 (contexts up to 2M tokens at budget 2048 tokens); otherwise
+ * at most 8192 (for one sequence, contexts up to 2M tokens at budget 2048
+ * tokens; large batches use 4096-page chunks and fit twice that); otherwise
  * the stages run as in the two calls.
  *   summaries, k_cache, v_cache share the physical block numbering
  *   (num_blocks) and the block table.

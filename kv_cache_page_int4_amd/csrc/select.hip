@@ -11,13 +11,13 @@
 // and the k = min(budget, valid pages) largest m_j are kept, ties to the lower
 // page index, listed in ascending page order.
 //
-// Two kernels.  Stage 1: one workgroup per 2048-page chunk first merges the
-// (max, sum) partials of its table's query heads into L_h (one head per
-// wave; a few kilobytes per head, cheaper than a kernel boundary), then turns
-// scores into order-preserving 32-bit keys and radix-selects the chunk's top
-// min(k, 2048)
-// (8-bit digits, LDS histograms); survivors are written in page
-// order.  Stage 2: one workgroup per (sequence, KV head) radix-selects the
+// Two kernels.  Stage 1: one workgroup per chunk of 2048 pages (4096 when the
+// grid would otherwise need a second round) first merges the (max, sum)
+// partials of its table's query heads into L_h (one head per wave; a few
+// kilobytes per head, cheaper than a kernel boundary), then turns scores into
+// order-preserving 32-bit keys and radix-selects the chunk's top
+// min(k, chunk pages) (8-bit digits, LDS histograms); survivors are written
+// in page order.  Stage 2: one workgroup per (sequence, KV head) radix-selects the
 // global top k over all candidates.  Because each chunk emits its survivors in
 // page order and chunks are in page order, stream compaction of the winners
 // yields ascending page ids directly, and "lowest index among equal keys" is
