@@ -64,6 +64,28 @@ def test_workspace_sizes_monotone():
     assert L.attend_workspace_bytes(d, 8, 129) >= L.attend_workspace_bytes(d, 1, 129)
 
 
+def test_stage1_chunks_widen_for_large_grids():
+    """Stage-1 selection chunks are 2048 pages, or 4096 once 2048-page chunks
+    would need more than 512 workgroups (batch x KV heads x chunks): the
+    candidate arrays in the score workspace (key + index, 4 bytes each, per
+    (sequence, KV head), chunk and slot) follow that plan."""
+    _lib_or_skip()
+    d = L.dims(32, 8)
+
+    def cand_bytes(batch, pages, budget):
+        lse = batch * 32 * pages * 4
+        part = batch * 32 * max(-(-pages // 64), -(-pages // 2048)) * 8
+        rnd = lambda x: -(-x // 256) * 256
+        return L.score_workspace_bytes(d, batch, pages, budget) - rnd(lse) - rnd(part)
+
+    # 1M context, batch 1: 32 chunks x 8 heads = 256 workgroups -> 2048 pages
+    assert cand_bytes(1, 65536, 128) == 2 * 1 * 8 * 32 * 128 * 4
+    # 256K, batch 16: 8 x 8 x 16 = 1024 workgroups -> 4096-page chunks
+    assert cand_bytes(16, 16384, 128) == 2 * 16 * 8 * 4 * 128 * 4
+    # budget above the chunk: a chunk keeps all of its pages
+    assert cand_bytes(1, 2048, 4000) == 2 * 1 * 8 * 1 * 2048 * 4
+
+
 def _raw_score(lib, d, **kw):
     args = dict(q=1, summ=1, num_blocks=1, bt=1, max_pages=1, seq=1, batch=1, lse=1, ws=1,
                 ws_bytes=1 << 40)
