@@ -276,9 +276,14 @@ struct FusedSel {
 };
 
 constexpr int kFusedThreads = 256;
+constexpr long long kFusedWideGrid = 256;   // fused workgroups up to which 1024 threads select
 
-template <int RUN>
-__global__ __launch_bounds__(kFusedThreads) void select_attend_kernel(AttendParams p, FusedSel f) {
+// NT threads run the selection (NT = 1024 when the grid leaves a CU per
+// workgroup: four candidates per thread instead of sixteen at 1M); the first
+// kWaves waves then attend and the others leave.
+template <int RUN, int NT>
+__global__ __launch_bounds__(NT) void select_attend_kernel(AttendParams p, FusedSel f) {
+  constexpr int kFusedThreads = NT;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   __shared__ int hist[2][256];
@@ -354,7 +359,7 @@ __global__ __launch_bounds__(kFusedThreads) void select_attend_kernel(AttendPara
   }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int split = blockIdx.x * kWaves + wave;
-  if (split < p.n_splits) attend_wave(p, split, kvh, b, k, sel_lds, &ring[wave][0]);
+  if (wave < kWaves && split < p.n_splits) attend_wave(p, split, kvh, b, k, sel_lds, &ring[wave][0]);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp weights of the
@@ -455,14 +460,27 @@ hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
                  plan.pages_per_split, plan.n_splits, ntab};
   FusedSel f{cand_key, cand_idx, sel, sel_count, sp.n_chunks, sp.slots};
   const int32_t n_cand = sp.n_chunks * sp.slots;
-  const int per = (n_cand + kFusedThreads - 1) / kFusedThreads;
   dim3 grid((plan.n_splits + kWaves - 1) / kWaves, hkv, batch);
-  if (per <= 4)
-    hipLaunchKernelGGL(select_attend_kernel<4>, grid, dim3(kFusedThreads), 0, stream, p, f);
-  else if (per <= 16)
-    hipLaunchKernelGGL(select_attend_kernel<16>, grid, dim3(kFusedThreads), 0, stream, p, f);
-  else
-    hipLaunchKernelGGL(select_attend_kernel<32>, grid, dim3(kFusedThreads), 0, stream, p, f);
+  const long long wgs = (long long)grid.x * grid.y * grid.z;
+  if (wgs <= kFusedWideGrid && n_cand > 4 * kFusedThreads) {
+    // one workgroup per CU at most: select with 1024 threads
+    const int per = (n_cand + 1023) / 1024;
+    if (per <= 4)
+      hipLaunchKernelGGL((select_attend_kernel<4, 1024>), grid, dim3(1024), 0, stream, p, f);
+    else
+      hipLaunchKernelGGL((select_attend_kernel<8, 1024>), grid, dim3(1024), 0, stream, p, f);
+  } else {
+    const int per = (n_cand + kFusedThreads - 1) / kFusedThreads;
+    if (per <= 4)
+      hipLaunchKernelGGL((select_attend_kernel<4, kFusedThreads>), grid, dim3(kFusedThreads), 0,
+                         stream, p, f);
+    else if (per <= 16)
+      hipLaunchKernelGGL((select_attend_kernel<16, kFusedThreads>), grid, dim3(kFusedThreads), 0,
+                         stream, p, f);
+    else
+      hipLaunchKernelGGL((select_attend_kernel<32, kFusedThreads>), grid, dim3(kFusedThreads), 0,
+                         stream, p, f);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attend_merge_kernel, dim3(hq, batch), dim3(kMergeThreads), 0, stream, p);
