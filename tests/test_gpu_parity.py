@@ -300,6 +300,7 @@ def test_long_candidate_lists(ctx, budget):
     ("llama8b-32k", {}, 128),
     ("tiny-4k", {"ctx": 16 * 8192, "carriers": 8}, 128),     # 4 chunks x 128 candidates
     ("tiny-4k", {"ctx": 16 * 8192, "carriers": 8}, 1000),    # budget near the fused limit
+    ("tiny-4k", {"ctx": 16 * 16384, "carriers": 8}, 600),    # 4800 candidates, 1024 selectors
     ("tiny-4k", {"ctx": 16 * 12000 + 7, "carriers": 8}, 2000),   # budget above it: two calls
     ("tiny-4k", {"ctx": 16 * 40000 + 3, "carriers": 8}, 512),    # 40960 candidates: two calls
 ])
