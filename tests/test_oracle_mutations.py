@@ -79,6 +79,25 @@ def _scale_no_fp16(x):
     return np.asarray(x, np.float64)                          # mistake: scale not rounded to fp16
 
 
+def _bf16_wrong_shift(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 15   # mistake: shift by 15
+    return b.view(np.float32).astype(np.float64)
+
+
+def _bf16_as_fp16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)  # mistake: fp16
+
+
+def _quant_half_away(x, qmax, axis):
+    m = np.max(np.abs(x), axis=axis, keepdims=True)
+    s = OL.fp16_round(m / qmax)
+    safe = np.where(s > 0, s, 1.0)
+    q = x / safe
+    code = np.clip(np.sign(q) * np.floor(np.abs(q) + 0.5), -qmax, qmax)   # mistake: half away from 0
+    code = np.where(s > 0, code, 0.0)
+    return code.astype(np.int8), np.squeeze(s, axis=axis)
+
+
 MUTANTS = [
     ("page_summary", _no_centering, lambda: P.test_estimate_exact_when_rank_le_r(8)),
     ("page_summary", _no_centering, P.test_basis_matches_scatter_eigenvectors),
@@ -91,6 +110,9 @@ MUTANTS = [
     ("table_selection", _tables_strided, P.test_table_selection_layer_wide_differs_from_per_kv_head),
     ("gather_pages", _gather_no_tail, lambda: P.test_full_budget_equals_dense(4096 - 5)),
     ("fp16_round", _scale_no_fp16, P.test_quantization_codes_and_scales),
+    ("bf16_to_f64", _bf16_wrong_shift, P.test_bf16_decoding_fixed_patterns),
+    ("bf16_to_f64", _bf16_as_fp16, P.test_bf16_decoding_fixed_patterns),
+    ("_sym_quant", _quant_half_away, P.test_quantization_rounds_half_to_even),
 ]
 
 

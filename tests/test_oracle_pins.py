@@ -296,6 +296,52 @@ def test_records_with_own_basis_equal_locks_records():
 
 # --- quantization and packing ------------------------------------------------
 
+def test_bf16_decoding_fixed_patterns():
+    """bf16 is the upper half of an IEEE-754 binary32: 1 sign bit, 8 exponent
+    bits (bias 127), 7 fraction bits.  Values worked by hand from that
+    definition, subnormals and infinities included."""
+    cases = {
+        0x3F80: 1.0,                                   # exponent 127, fraction 0
+        0xC040: -3.0,                                  # -(1 + 64/128) * 2^1
+        0x4049: 3.140625,                              # (1 + 73/128) * 2^1
+        0x3E00: 0.125,                                 # exponent 124
+        0x0001: math.ldexp(1.0, -133),                 # smallest subnormal: 2^-126 * 2^-7
+        0x0080: math.ldexp(1.0, -126),                 # smallest normal
+        0x7F7F: math.ldexp(2.0 - 2.0 ** -7, 127),      # largest finite
+        0x8000: -0.0,
+        0x7F80: math.inf,
+        0xFF80: -math.inf,
+    }
+    bits = np.array(list(cases), dtype=np.uint16)
+    got = O.bf16_to_f64(bits)
+    assert got.dtype == np.float64
+    for b, g in zip(bits, got):
+        want = cases[int(b)]
+        assert g == want, (hex(int(b)), g, want)
+    assert math.copysign(1.0, float(got[list(cases).index(0x8000)])) == -1.0
+    nan = O.bf16_to_f64(np.array([0x7FC0], dtype=np.uint16))
+    assert np.isnan(nan).all()
+
+
+def test_quantization_rounds_half_to_even():
+    """Exact half-way quotients x / s go to the even code (the reading of the
+    rounding rule), with scales chosen so that fp16(max|x| / qmax) is exact."""
+    # basis column: max|x| = 3.5 gives s = 3.5 / 7 = 0.5 exactly in fp16
+    V = np.zeros((128, 8))
+    V[:8, 0] = [3.5, 1.25, 1.75, -1.25, 0.25, -0.25, 0.75, -3.5]   # x/s = 7, 2.5, 3.5, -2.5, .5, -.5, 1.5, -7
+    # coefficient column: max|x| = 31.75 gives s = 0.25 exactly
+    C = np.zeros((16, 8))
+    C[:6, 0] = [31.75, 0.625, 0.875, -0.625, 0.125, 0.375]        # x/s = 127, 2.5, 3.5, -2.5, .5, 1.5
+    # centroid: max|x| = 127 gives s = 1
+    mu = np.zeros(128)
+    mu[:5] = [127.0, 2.5, -3.5, 4.5, -0.5]
+    qz = O.quantize_summary(mu, V, C)
+    assert float(qz["s_v"][0]) == 0.5 and float(qz["s_c"][0]) == 0.25 and float(qz["s_mu"]) == 1.0
+    assert qz["v_q"][:8, 0].tolist() == [7, 2, 4, -2, 0, 0, 2, -7]
+    assert qz["c_q"][:6, 0].tolist() == [127, 2, 4, -2, 0, 2]
+    assert qz["mu_q"][:5].tolist() == [127, 2, -4, 4, 0]
+
+
 def test_quantization_codes_and_scales():
     rng = np.random.default_rng(31)
     K = rng.standard_normal((50, 16, 128)) * 3
