@@ -20,7 +20,9 @@
  *    caller's next synchronization.
  *  - Supported shape: head_dim 128, page_size 16, rank 4, 8 or 16 (8 is the
  *    pages' setting; 4 and 16 are the same method at other state sizes), and
- *    num_q_heads = 4 * num_kv_heads (GQA group of 4); anything else returns
+ *    num_q_heads a multiple of num_kv_heads with a GQA group G = Hq / Hkv of
+ *    1, 2, 4 or 8 query heads per KV head (sec. 2 group-shared selection: the
+ *    G heads of a group share one page table); anything else returns
  *    LOCKS_ERR_UNSUPPORTED.
  *  - bf16 tensors are raw bfloat16 bit patterns (uint16).
  *  - Device-side data (seq_lens, block tables, selections) is range-checked
@@ -71,7 +73,20 @@ size_t locks_summary_bytes(const locks_dims* dims);
 
 /* Workspace sizes (bytes).  max_pages is the block-table row length; the
  * budget is in pages.  Workspace contents need no initialization; a
- * workspace must not be shared by calls that may run concurrently. */
+ * workspace must not be shared by calls that may run concurrently.
+ *
+ * locks_workspace_bytes: one size that serves every decode-path call with
+ * these sizes -- the `workspace` of locks_score_pages, locks_select_pages,
+ * locks_score_select and locks_sparse_attend (sparse or dense), and the
+ * single workspace of locks_decode_layer when its attend_ws is NULL.
+ * Returns 0 for unsupported dims or sizes (budget_pages must be >= 1).
+ *
+ * locks_score_workspace_bytes / locks_attend_workspace_bytes: the smaller
+ * sizes of the scoring-and-selection part and of the attention part alone
+ * (max_attended_pages = budget_pages + 1 for a sparse pass, max_pages + 1 for
+ * a dense one). */
+size_t locks_workspace_bytes(const locks_dims* dims, int32_t batch, int32_t max_pages,
+                             int32_t budget_pages);
 size_t locks_score_workspace_bytes(const locks_dims* dims, int32_t batch,
                                    int32_t max_pages, int32_t budget_pages);
 size_t locks_attend_workspace_bytes(const locks_dims* dims, int32_t batch,
@@ -109,7 +124,9 @@ locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
 /* One layer of the decode step in one call: locks_score_select followed by
  * locks_sparse_attend (sec. 2 implementation: scoring, selection and sparse
  * attention run back to back inside the step's graph), with outputs
- * identical to those two calls.  The last selection stage runs inside the
+ * identical to those two calls when softmax_scale = 1/sqrt(d).  Pages are
+ * scored at the logit scale they are attended with: the estimate's 1/sqrt(d)
+ * (sec. 2 equation) is replaced by softmax_scale.  The last selection stage runs inside the
  * attention kernel when budget_pages <= 1024 and the chunk candidates number
  * at most 8192 (for one sequence, contexts up to 2M tokens at budget 2048
  * tokens; large batches use 4096-page chunks and fit twice that); otherwise
@@ -119,9 +136,12 @@ locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
  *   sel, sel_count : written as by locks_select_pages.
  *   out, out_lse   : as written by locks_sparse_attend.
  *   score_ws       : >= locks_score_workspace_bytes(dims, batch, max_pages,
- *                    budget_pages).
+ *                    budget_pages), 16-byte aligned.
  *   attend_ws      : >= locks_attend_workspace_bytes(dims, batch,
- *                    budget_pages + 1). */
+ *                    budget_pages + 1); or NULL, in which case score_ws holds
+ *                    both parts and must be >= locks_workspace_bytes(dims,
+ *                    batch, max_pages, budget_pages) (score_ws_bytes is
+ *                    checked against the two parts). */
 locks_status locks_decode_layer(const locks_dims* dims, const void* q, const void* summaries,
                                 const void* k_cache, const void* v_cache, locks_kv_layout layout,
                                 int32_t num_blocks, const int32_t* block_table, int32_t max_pages,

@@ -5,8 +5,8 @@
 // Split-K: the attended page list of a (sequence, KV head) -- the selected
 // pages in ascending order, then the partial tail page -- is cut into splits
 // of `pages_per_split` pages, one wave each, streamed page by page through
-// LDS (see attend_wave).  The 4 query heads of the group share every K/V
-// load.  A second kernel merges the splits by log-sum-exp into bf16 output.
+// LDS (see attend_wave).  The query heads of the group share every K/V load.
+// A second kernel merges the splits by log-sum-exp into bf16 output.
 #include "locks_device.h"
 #include "locks_internal.h"
 #include "select_common.h"
@@ -36,11 +36,13 @@ struct AttendParams {
   float scale2;
   int32_t num_blocks, max_pages, budget, hq, hkv, pages_per_split, n_splits;
   int32_t ntab;   // selection tables per sequence; KV head kvh reads table kvh / (hkv / ntab)
+  int32_t group;  // query heads per KV head (1, 2, 4 or 8)
 };
 
 // Global -> LDS copy of 16 bytes per lane: lane l writes LDS bytes
-// [lds + 16 l, +16) from sbase + voff.  M0 carries the LDS address; the
-// compiler treats M0 as reserved and these kernels have no other user of it.
+// [lds + 16 l, +16) from sbase + voff.  M0 carries the LDS address and is
+// declared clobbered, so the compiler keeps no value of its own in M0 across
+// the copy.
 // The copy is non-temporal: each K/V page is read once per step, and
 // streaming it past the cache's normal allocation raises the read rate
 // (each instruction reads one contiguous kilobyte, so no line is split
@@ -48,7 +50,7 @@ struct AttendParams {
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff),
                "s"(sbase), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -73,16 +75,20 @@ constexpr int kRingBytes = kAttRing * kPageBytes;
 // and a wait for "at most 8n outstanding" with n younger pages issued means
 // this page has landed.  Any other memory instruction only makes it stricter.
 //  * QK^T on the matrix cores: rows = the 16 tokens, K = head dim, columns =
-//    the 4 query heads repeated 4 times; lane l gets tokens 4*(l/16)+r
-//    (r = 0..3) of head l%4.
+//    4 query heads repeated 4 times; lane l gets tokens 4*(l/16)+r
+//    (r = 0..3) of head slot l%4.  NSUB such 4-head sub-passes cover the
+//    group: 2 for a group of 8 heads; a group of 1 or 2 fills the 4 slots
+//    with its heads repeated (the duplicate slots are computed and dropped).
 //  * online softmax in base 2 per page.
 //  * P.V on the vector units: lane l keeps the same 4 tokens and dims
-//    8*(l%16)..+8; the 4 heads' probabilities come from its quad by DPP.
+//    8*(l%16)..+8; the 4 slots' probabilities come from its quad by DPP.
+template <int NSUB>
 __device__ __forceinline__ void attend_wave(const AttendParams& p, int split, int kvh, int b,
                                             int count, const int32_t* selrow, uint8_t* ring) {
   const int lane = threadIdx.x & 63;
   const int row = lane >> 4, col = lane & 15, h = lane & 3;
-  const int qhead0 = kvh * kG;
+  const int G = p.group;
+  const int qhead0 = kvh * G;
   int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
   const int n_fin = seq / kB;
   const int tail = seq - n_fin * kB;
@@ -90,21 +96,32 @@ __device__ __forceinline__ void attend_wave(const AttendParams& p, int split, in
   const int e0 = split * p.pages_per_split;
   const int n = max(0, min(e0 + p.pages_per_split, n_att) - e0);
 
-  float M = -INFINITY, lsum = 0.f;
-  float acc[4][8];
+  float M[NSUB], lsum[NSUB];
+  float acc[NSUB][4][8];
 #pragma unroll
-  for (int hh = 0; hh < 4; ++hh)
+  for (int sub = 0; sub < NSUB; ++sub) {
+    M[sub] = -INFINITY;
+    lsum[sub] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+    for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[sub][hh][e] = 0.f;
+  }
 
   if (n > 0) {
-    const uint16_t* qrow = p.q + ((size_t)b * p.hq + qhead0 + h) * kD + 32 * row;
-    uint4 qv[4];
-    bf16x8 bq[4];
+    // slot 4 sub + h holds head 4 sub + h of the group (h % G when G < 4)
+    uint4 qv[NSUB][4];
+    bf16x8 bq[NSUB][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      qv[s] = *reinterpret_cast<const uint4*>(qrow + 8 * s);
-      bq[s] = as_bf16x8(qv[s]);
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const int hs = 4 * sub + h;
+      const uint16_t* qrow =
+          p.q + ((size_t)b * p.hq + qhead0 + (hs < G ? hs : hs % G)) * kD + 32 * row;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        qv[sub][s] = *reinterpret_cast<const uint4*>(qrow + 8 * s);
+        bq[sub][s] = as_bf16x8(qv[sub][s]);
+      }
     }
     // unit u = 64 i + lane of a 4 KB half lands at LDS token u / 16, 16-byte
     // part u % 16.  Keys are stored XOR-swizzled (part c of token t holds the
@@ -144,8 +161,11 @@ __device__ __forceinline__ void attend_wave(const AttendParams& p, int split, in
       }
       // consume the loads above here, so that the compiler's waits for them
       // come before the first page copies are issued
-      asm volatile("" ::"v"(mbid), "v"(mnt), "v"(qv[0].x), "v"(qv[1].x), "v"(qv[2].x),
-                   "v"(qv[3].x));
+      asm volatile("" ::"v"(mbid), "v"(mnt), "v"(qv[0][0].x), "v"(qv[0][1].x), "v"(qv[0][2].x),
+                   "v"(qv[0][3].x));
+      if constexpr (NSUB > 1)
+        asm volatile("" ::"v"(qv[NSUB - 1][0].x), "v"(qv[NSUB - 1][1].x),
+                     "v"(qv[NSUB - 1][2].x), "v"(qv[NSUB - 1][3].x));
       auto issue = [&](int k) {
         const int bid = __builtin_amdgcn_readlane(mbid, k);
         const uint16_t* kb = p.kc + (size_t)bid * p.bs + (size_t)kvh * p.hs;
@@ -172,75 +192,93 @@ __device__ __forceinline__ void attend_wave(const AttendParams& p, int split, in
         else wait_vm<0>();
         const uint8_t* S = ring + (k % kAttRing) * kPageBytes;
         const int ntok = __builtin_amdgcn_readlane(mnt, k);
-        // ---- logits of tokens 4 row + r for head col % 4 ----
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        // ---- logits of tokens 4 row + r for head slot col % 4 ----
+        float P[NSUB][4];
+        auto logits = [&](const int sub) __attribute__((always_inline)) {
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(S + col * 256 + 16 * ((4 * row + s) ^ col));
-          a = mfma16x16x32(as_bf16x8(kv), bq[s], a);
-        }
-        float x[4];
+          for (int s = 0; s < 4; ++s) {
+            const uint4 kv = *reinterpret_cast<const uint4*>(S + col * 256 + 16 * ((4 * row + s) ^ col));
+            a = mfma16x16x32(as_bf16x8(kv), bq[sub][s], a);
+          }
+          float x[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = (4 * row + r < ntok) ? a[r] * p.scale2 : -INFINITY;
-        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        mx = cross_rows_max(mx);
-        const float Mn = fmaxf(M, mx);
-        const float alpha = (Mn == -INFINITY) ? 1.f : fast_exp2(M - Mn);
-        float P[4];
-        float ps = 0.f;
+          for (int r = 0; r < 4; ++r) x[r] = (4 * row + r < ntok) ? a[r] * p.scale2 : -INFINITY;
+          float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+          mx = cross_rows_max(mx);
+          const float Mn = fmaxf(M[sub], mx);
+          const float alpha = (Mn == -INFINITY) ? 1.f : fast_exp2(M[sub] - Mn);
+          float ps = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          P[r] = (x[r] == -INFINITY) ? 0.f : fast_exp2(x[r] - Mn);
-          ps += P[r];
-        }
-        lsum = lsum * alpha + ps;
-        M = Mn;
-        const float al[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha),
-                             quad_bcast<3>(alpha)};
+          for (int r = 0; r < 4; ++r) {
+            P[sub][r] = (x[r] == -INFINITY) ? 0.f : fast_exp2(x[r] - Mn);
+            ps += P[sub][r];
+          }
+          lsum[sub] = lsum[sub] * alpha + ps;
+          M[sub] = Mn;
+          const float al[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha),
+                               quad_bcast<3>(alpha)};
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh)
+          for (int hh = 0; hh < 4; ++hh)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[hh][e] *= al[hh];
-        // ---- P.V: tokens 4 row + r, dims 8 col .. 8 col + 7, all 4 heads ----
+            for (int e = 0; e < 8; ++e) acc[sub][hh][e] *= al[hh];
+        };
+        logits(0);
+        if constexpr (NSUB > 1) logits(1);
+        // ---- P.V: tokens 4 row + r, dims 8 col .. 8 col + 7, all head slots ----
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const uint4 v = *reinterpret_cast<const uint4*>(S + 4096 + (4 * row + r) * 256 + 16 * col);
           const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-          const float p0 = quad_bcast<0>(P[r]), p1 = quad_bcast<1>(P[r]);
-          const float p2 = quad_bcast<2>(P[r]), p3 = quad_bcast<3>(P[r]);
+          auto pv = [&](const int sub) __attribute__((always_inline)) {
+            const float p0 = quad_bcast<0>(P[sub][r]), p1 = quad_bcast<1>(P[sub][r]);
+            const float p2 = quad_bcast<2>(P[sub][r]), p3 = quad_bcast<3>(P[sub][r]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            acc[0][e] = fmaf(p0, vf[e], acc[0][e]);
-            acc[1][e] = fmaf(p1, vf[e], acc[1][e]);
-            acc[2][e] = fmaf(p2, vf[e], acc[2][e]);
-            acc[3][e] = fmaf(p3, vf[e], acc[3][e]);
-          }
+            for (int e = 0; e < 8; ++e) {
+              acc[sub][0][e] = fmaf(p0, vf[e], acc[sub][0][e]);
+              acc[sub][1][e] = fmaf(p1, vf[e], acc[sub][1][e]);
+              acc[sub][2][e] = fmaf(p2, vf[e], acc[sub][2][e]);
+              acc[sub][3][e] = fmaf(p3, vf[e], acc[sub][3][e]);
+            }
+          };
+          pv(0);
+          if constexpr (NSUB > 1) pv(1);
         }
       }
     }
   }
   // each row of lanes holds a quarter of the tokens: sum the rows
 #pragma unroll
-  for (int hh = 0; hh < 4; ++hh)
+  for (int sub = 0; sub < NSUB; ++sub) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[hh][e] = cross_rows_sum(acc[hh][e]);
-    }
-  lsum = cross_rows_sum(lsum);
+    for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[sub][hh][e] = cross_rows_sum(acc[sub][hh][e]);
+    lsum[sub] = cross_rows_sum(lsum[sub]);
+  }
   if (row == 0) {
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      float* o = p.part_o + (((size_t)b * p.hq + qhead0 + hh) * p.n_splits + split) * kD + 8 * col;
-      *reinterpret_cast<float4*>(o) = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
-      *reinterpret_cast<float4*>(o + 4) = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
+    for (int sub = 0; sub < NSUB; ++sub) {
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        if (4 * sub + hh >= G) continue;   // a repeated head slot
+        float* o = p.part_o +
+                   (((size_t)b * p.hq + qhead0 + 4 * sub + hh) * p.n_splits + split) * kD + 8 * col;
+        *reinterpret_cast<float4*>(o) =
+            make_float4(acc[sub][hh][0], acc[sub][hh][1], acc[sub][hh][2], acc[sub][hh][3]);
+        *reinterpret_cast<float4*>(o + 4) =
+            make_float4(acc[sub][hh][4], acc[sub][hh][5], acc[sub][hh][6], acc[sub][hh][7]);
+      }
+      if (col < 4 && 4 * sub + col < G)
+        p.part_ml[((size_t)b * p.hq + qhead0 + 4 * sub + col) * p.n_splits + split] =
+            make_float2(M[sub], lsum[sub]);
     }
-    if (col < 4)
-      p.part_ml[((size_t)b * p.hq + qhead0 + col) * p.n_splits + split] = make_float2(M, lsum);
   }
 }
 
 // One wave per workgroup: 16 KB of LDS each, so up to ten waves share a CU.
+template <int NSUB>
 __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[1][kRingBytes];
   const int wave = 0;
@@ -256,7 +294,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   } else {
     count = max(0, min(p.seq_lens[b], p.max_pages * kB)) / kB;
   }
-  attend_wave(p, split, kvh, b, count, selrow, &ring[wave][0]);
+  attend_wave<NSUB>(p, split, kvh, b, count, selrow, &ring[wave][0]);
 }
 
 // ---- final selection fused with the attention --------------------------------
@@ -281,7 +319,7 @@ constexpr long long kFusedWideGrid = 256;   // fused workgroups up to which 1024
 // NT threads run the selection (NT = 1024 when the grid leaves a CU per
 // workgroup: four candidates per thread instead of sixteen at 1M); the first
 // kWaves waves then attend and the others leave.
-template <int RUN, int NT>
+template <int RUN, int NT, int NSUB>
 __global__ __launch_bounds__(NT) void select_attend_kernel(AttendParams p, FusedSel f) {
   constexpr int kFusedThreads = NT;
   const int kvh = blockIdx.y, b = blockIdx.z;
@@ -359,7 +397,8 @@ __global__ __launch_bounds__(NT) void select_attend_kernel(AttendParams p, Fused
   }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int split = blockIdx.x * kWaves + wave;
-  if (wave < kWaves && split < p.n_splits) attend_wave(p, split, kvh, b, k, sel_lds, &ring[wave][0]);
+  if (wave < kWaves && split < p.n_splits)
+    attend_wave<NSUB>(p, split, kvh, b, k, sel_lds, &ring[wave][0]);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp weights of the
@@ -457,30 +496,34 @@ hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
   AttendParams p{q, k_cache, v_cache, block_stride, head_stride, token_stride, block_table,
                  seq_lens, sel, sel_count, part_o, part_ml, out, out_lse,
                  scale * kLog2e, num_blocks, max_pages, budget_pages, hq, hkv,
-                 plan.pages_per_split, plan.n_splits, ntab};
+                 plan.pages_per_split, plan.n_splits, ntab, hq / hkv};
   FusedSel f{cand_key, cand_idx, sel, sel_count, sp.n_chunks, sp.slots};
   const int32_t n_cand = sp.n_chunks * sp.slots;
   dim3 grid((plan.n_splits + kWaves - 1) / kWaves, hkv, batch);
   const long long wgs = (long long)grid.x * grid.y * grid.z;
-  if (wgs <= kFusedWideGrid && n_cand > 4 * kFusedThreads) {
-    // one workgroup per CU at most: select with 1024 threads
+  const bool two = p.group > 4;   // two 4-head sub-passes
+#define LOCKS_SA(RUN, NT)                                                                     \
+  do {                                                                                        \
+    if (two)                                                                                  \
+      hipLaunchKernelGGL((select_attend_kernel<RUN, NT, 2>), grid, dim3(NT), 0, stream, p, f); \
+    else                                                                                      \
+      hipLaunchKernelGGL((select_attend_kernel<RUN, NT, 1>), grid, dim3(NT), 0, stream, p, f); \
+  } while (0)
+  if (!two && wgs <= kFusedWideGrid && n_cand > 4 * kFusedThreads) {
+    // one workgroup per CU at most: select with 1024 threads (a group of 8
+    // heads needs more registers than 1024 threads leave, and keeps 256)
     const int per = (n_cand + 1023) / 1024;
     if (per <= 4)
-      hipLaunchKernelGGL((select_attend_kernel<4, 1024>), grid, dim3(1024), 0, stream, p, f);
+      hipLaunchKernelGGL((select_attend_kernel<4, 1024, 1>), grid, dim3(1024), 0, stream, p, f);
     else
-      hipLaunchKernelGGL((select_attend_kernel<8, 1024>), grid, dim3(1024), 0, stream, p, f);
+      hipLaunchKernelGGL((select_attend_kernel<8, 1024, 1>), grid, dim3(1024), 0, stream, p, f);
   } else {
     const int per = (n_cand + kFusedThreads - 1) / kFusedThreads;
-    if (per <= 4)
-      hipLaunchKernelGGL((select_attend_kernel<4, kFusedThreads>), grid, dim3(kFusedThreads), 0,
-                         stream, p, f);
-    else if (per <= 16)
-      hipLaunchKernelGGL((select_attend_kernel<16, kFusedThreads>), grid, dim3(kFusedThreads), 0,
-                         stream, p, f);
-    else
-      hipLaunchKernelGGL((select_attend_kernel<32, kFusedThreads>), grid, dim3(kFusedThreads), 0,
-                         stream, p, f);
+    if (per <= 4) LOCKS_SA(4, kFusedThreads);
+    else if (per <= 16) LOCKS_SA(16, kFusedThreads);
+    else LOCKS_SA(32, kFusedThreads);
   }
+#undef LOCKS_SA
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attend_merge_kernel, dim3(hq, batch), dim3(kMergeThreads), 0, stream, p);
@@ -512,9 +555,12 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k_cache, const uint1
   AttendParams p{q, k_cache, v_cache, block_stride, head_stride, token_stride, block_table,
                  seq_lens, sel, sel_count, part_o, part_ml, out, out_lse,
                  scale * kLog2e, num_blocks, max_pages, budget_pages, hq, hkv,
-                 plan.pages_per_split, plan.n_splits, ntab};
+                 plan.pages_per_split, plan.n_splits, ntab, hq / hkv};
   dim3 grid(plan.n_splits, hkv, batch);
-  hipLaunchKernelGGL(attend_kernel, grid, dim3(64), 0, stream, p);
+  if (p.group > 4)
+    hipLaunchKernelGGL(attend_kernel<2>, grid, dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attend_kernel<1>, grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attend_merge_kernel, dim3(hq, batch), dim3(kMergeThreads), 0, stream, p);

@@ -12,8 +12,10 @@
 // bytes each (token lane%16, dims 32*(lane/16)..+32), two pages ahead of the
 // one being computed.
 //  * QK^T on the matrix cores: rows = the 16 tokens, K = head dim, columns =
-//    the 4 query heads repeated 4 times; lane l gets tokens 4*(l/16)+r
-//    (r = 0..3) of head l%4.
+//    4 query heads repeated 4 times; lane l gets tokens 4*(l/16)+r
+//    (r = 0..3) of head slot l%4.  A GQA group of 8 heads takes two such
+//    4-head sub-passes over the same keys; a group of 1 or 2 fills the 4
+//    slots with its heads repeated.
 //  * LSE over the 16 tokens: max and sum over the 4 registers, then over the
 //    lanes 16 and 32 apart.
 #include "locks_device.h"
@@ -36,33 +38,46 @@ struct ExactParams {
   float* page_lse;
   float scale2;   // softmax scale * log2(e)
   int32_t num_blocks, max_pages, hq, hkv, n_wg;
+  int32_t group;   // query heads per KV head (1, 2, 4 or 8)
 };
 
+// NSUB: 4-head sub-passes (2 for a group of 8 heads, else 1).
+template <int NSUB>
 __global__ __launch_bounds__(64) void exact_lse_kernel(ExactParams p) {
+  constexpr int kSlots = 4 * NSUB;
   const int lane = threadIdx.x;
   const int w = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int W = p.n_wg;
+  const int G = p.group;
   const int row = lane >> 4, col = lane & 15, h = lane & 3;
-  const int qhead0 = kvh * kG;
+  const int qhead0 = kvh * G;
 
   int seq = p.seq_lens[b];
   seq = max(0, min(seq, p.max_pages * kB));
   const int n_fin = seq / kB;
   const int j0 = w * kExactPages;                          // first page of this workgroup
   const int n = max(0, min(kExactPages, n_fin - j0));     // its pages
-  __shared__ __attribute__((aligned(16))) float outl[kG][kExactPages];
+  __shared__ __attribute__((aligned(16))) float outl[kSlots][kExactPages];
   float* __restrict__ lse_out = p.page_lse + ((size_t)b * p.hq + qhead0) * p.max_pages;
 
   // pages that are not finalized score -inf
   for (int j = n_fin + 64 * w + lane; j < p.max_pages; j += 64 * W)
 #pragma unroll
-    for (int hh = 0; hh < kG; ++hh) lse_out[(size_t)hh * p.max_pages + j] = -INFINITY;
+    for (int hh = 0; hh < kSlots; ++hh)
+      if (hh < G) lse_out[(size_t)hh * p.max_pages + j] = -INFINITY;
   if (n == 0) return;   // uniform: the whole (one-wave) workgroup leaves
 
-  const uint16_t* qrow = p.q + ((size_t)b * p.hq + qhead0 + h) * kD + 32 * row;
-  bf16x8 bq[4];
+  // slot 4 sub + h holds head 4 sub + h of the group (h % G when G < 4)
+  bf16x8 bq[NSUB][4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 8 * s));
+  for (int sub = 0; sub < NSUB; ++sub) {
+    const int hs = 4 * sub + h;
+    const uint16_t* qrow =
+        p.q + ((size_t)b * p.hq + qhead0 + (hs < G ? hs : hs % G)) * kD + 32 * row;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      bq[sub][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 8 * s));
+  }
 
   const int32_t* __restrict__ bt = p.block_table + (size_t)b * p.max_pages;
   const uint16_t* kbase = p.kc + (size_t)kvh * p.hs + (size_t)col * p.ts + 32 * row;
@@ -97,25 +112,29 @@ __global__ __launch_bounds__(64) void exact_lse_kernel(ExactParams p) {
     if (k + 2 < n) load(b1, k1);
     b2 = bid_of(k + 3);
 
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    auto sub_pass = [&](const int sub) __attribute__((always_inline)) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) a = mfma16x16x32(as_bf16x8(cur[s]), bq[s], a);
-    float x[4];
+      for (int s = 0; s < 4; ++s) a = mfma16x16x32(as_bf16x8(cur[s]), bq[sub][s], a);
+      float x[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = a[r] * p.scale2;
-    float m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    m = cross_rows_max(m);
-    float e = fast_exp2(x[0] - m) + fast_exp2(x[1] - m) + fast_exp2(x[2] - m) +
-              fast_exp2(x[3] - m);
-    e = cross_rows_sum(e);
-    if (lane < kG) outl[h][k] = (bcur >= 0) ? (m + fast_log2(e)) * kLn2 : -INFINITY;
+      for (int r = 0; r < 4; ++r) x[r] = a[r] * p.scale2;
+      float m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      m = cross_rows_max(m);
+      float e = fast_exp2(x[0] - m) + fast_exp2(x[1] - m) + fast_exp2(x[2] - m) +
+                fast_exp2(x[3] - m);
+      e = cross_rows_sum(e);
+      if (lane < 4) outl[4 * sub + h][k] = (bcur >= 0) ? (m + fast_log2(e)) * kLn2 : -INFINITY;
+    };
+    sub_pass(0);
+    if constexpr (NSUB > 1) sub_pass(1);
   }
   // 4 lanes per head, 4 pages each
   __syncthreads();
   const int hh = lane >> 2, part = lane & 3;
   float* dst = lse_out + (size_t)hh * p.max_pages + j0 + 4 * part;
   const bool vec = (p.max_pages & 3) == 0 && ((uintptr_t)p.page_lse & 15) == 0;
-  if (lane < 16 && 4 * part < n) {
+  if (hh < G && 4 * part < n) {
     const float4 v = *reinterpret_cast<const float4*>(&outl[hh][4 * part]);
     if (vec && 4 * part + 4 <= n) {
       *reinterpret_cast<float4*>(dst) = v;
@@ -135,9 +154,13 @@ hipError_t launch_exact_lse(const uint16_t* q, const uint16_t* k_cache, int64_t 
                             float scale, float* page_lse, hipStream_t stream) {
   // kExactPages pages per wave: many short waves keep the end-of-launch tail small
   const int32_t W = std::max(1, (max_pages + kExactPages - 1) / kExactPages);
+  const int32_t group = hq / hkv;
   ExactParams p{q, k_cache, block_stride, head_stride, token_stride, block_table, seq_lens,
-                page_lse, scale * kLog2e, num_blocks, max_pages, hq, hkv, W};
-  hipLaunchKernelGGL(exact_lse_kernel, dim3(W, hkv, batch), dim3(64), 0, stream, p);
+                page_lse, scale * kLog2e, num_blocks, max_pages, hq, hkv, W, group};
+  if (group > 4)
+    hipLaunchKernelGGL(exact_lse_kernel<2>, dim3(W, hkv, batch), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(exact_lse_kernel<1>, dim3(W, hkv, batch), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -17,9 +17,15 @@ locks_status check_dims(const locks_dims* d) {
   if (d->num_q_heads <= 0 || d->num_kv_heads <= 0) return LOCKS_ERR_SHAPE;
   if (d->head_dim != 128 || d->page_size != 16 || !rank_supported(d->rank))
     return LOCKS_ERR_UNSUPPORTED;
-  if (d->num_q_heads != 4 * d->num_kv_heads) return LOCKS_ERR_UNSUPPORTED;
+  // GQA: every KV head serves G = Hq / Hkv query heads, G in {1, 2, 4, 8}
+  if (d->num_q_heads % d->num_kv_heads) return LOCKS_ERR_UNSUPPORTED;
+  const int32_t g = d->num_q_heads / d->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return LOCKS_ERR_UNSUPPORTED;
   return LOCKS_OK;
 }
+
+// Logit scale the pages' estimate uses: 1 / sqrt(d).
+constexpr float kDefaultScale = 0.08838834764831845f;
 
 // The page grid is indexed with 32-bit integers on the device.
 constexpr int64_t kMaxPages = (int64_t)1 << 26;
@@ -89,6 +95,18 @@ size_t locks_attend_workspace_bytes(const locks_dims* dims, int32_t batch,
   return attend_ws_layout(dims, batch, max_attended_pages).total;
 }
 
+size_t locks_workspace_bytes(const locks_dims* dims, int32_t batch, int32_t max_pages,
+                             int32_t budget_pages) {
+  if (check_dims(dims) != LOCKS_OK || batch <= 0 || max_pages <= 0 || max_pages > kMaxPages ||
+      budget_pages <= 0)
+    return 0;
+  // the scoring / selection part first, then room for the attention
+  // partials of a sparse or a dense pass
+  const size_t score = align_up(score_ws_layout(dims, batch, max_pages, budget_pages, true).total);
+  const int32_t att = (budget_pages > max_pages ? budget_pages : max_pages) + 1;
+  return score + attend_ws_layout(dims, batch, att).total;
+}
+
 locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
                                    locks_kv_layout layout, const int32_t* block_ids,
                                    int32_t n_blocks, int32_t num_blocks, void* summaries,
@@ -135,7 +153,7 @@ locks_status locks_score_pages(const locks_dims* dims, const void* q, const void
   if (!workspace || workspace_bytes < w.total) return LOCKS_ERR_WORKSPACE;
   hipError_t e = launch_score(dims->rank, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
                               num_blocks, block_table, max_pages, seq_lens, batch,
-                              dims->num_q_heads, dims->num_kv_heads, page_lse,
+                              dims->num_q_heads, dims->num_kv_heads, kDefaultScale, page_lse,
                               reinterpret_cast<float2*>(ws_at(workspace, w.part_off)), w.sp,
                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
@@ -201,7 +219,8 @@ locks_status locks_score_select(const locks_dims* dims, const void* q, const voi
   float2* part = reinterpret_cast<float2*>(ws_at(workspace, w.part_off));
   hipError_t e = launch_score(dims->rank, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
                               num_blocks, block_table, max_pages, seq_lens, batch,
-                              dims->num_q_heads, dims->num_kv_heads, lse, part, w.sp, s);
+                              dims->num_q_heads, dims->num_kv_heads, kDefaultScale, lse, part,
+                              w.sp, s);
   if (e == hipSuccess)
     e = launch_select(lse, max_pages, seq_lens, batch, dims->num_q_heads, dims->num_kv_heads,
                       budget_pages, part, w.sp.n_chunks,
@@ -232,9 +251,16 @@ static locks_status decode_layer_impl(const locks_dims* dims, const void* q,
     return LOCKS_ERR_SHAPE;
   if (!(softmax_scale > 0.f) || softmax_scale != softmax_scale) return LOCKS_ERR_SHAPE;
   const ScoreWs w = score_ws_layout(dims, batch, max_pages, budget_pages, true);
-  if (!score_ws || score_ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
   const AttendWs a = attend_ws_layout(dims, batch, budget_pages + 1);
-  if (!attend_ws || attend_ws_bytes < a.total) return LOCKS_ERR_WORKSPACE;
+  if (!score_ws) return LOCKS_ERR_WORKSPACE;
+  if (attend_ws) {
+    if (score_ws_bytes < w.total || attend_ws_bytes < a.total) return LOCKS_ERR_WORKSPACE;
+  } else {
+    // one workspace: the attention part follows the scoring part
+    if (score_ws_bytes < align_up(w.total) + a.total) return LOCKS_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(score_ws) & 15) return LOCKS_ERR_WORKSPACE;
+    attend_ws = ws_at(score_ws, align_up(w.total));
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* lse = reinterpret_cast<float*>(ws_at(score_ws, w.lse_off));
   float2* part = reinterpret_cast<float2*>(ws_at(score_ws, w.part_off));
@@ -243,9 +269,10 @@ static locks_status decode_layer_impl(const locks_dims* dims, const void* q,
   float* po = reinterpret_cast<float*>(ws_at(attend_ws, a.o_off));
   float2* pml = reinterpret_cast<float2*>(ws_at(attend_ws, a.ml_off));
   const int hq = dims->num_q_heads, hkv = dims->num_kv_heads;
+  // pages are scored at the temperature they are attended with
   hipError_t e = launch_score(dims->rank, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
-                              num_blocks, block_table, max_pages, seq_lens, batch, hq, hkv, lse,
-                              part, w.sp, s);
+                              num_blocks, block_table, max_pages, seq_lens, batch, hq, hkv,
+                              softmax_scale, lse, part, w.sp, s);
   if (e != hipSuccess) return LOCKS_ERR_LAUNCH;
   const int32_t n_cand = w.sel.n_chunks * w.sel.slots;
   if (fused_select_attend_fits(n_cand, budget_pages)) {
@@ -484,7 +511,8 @@ const char* locks_status_str(locks_status status) {
     case LOCKS_OK: return "ok";
     case LOCKS_ERR_NULL: return "required pointer is NULL";
     case LOCKS_ERR_SHAPE: return "size, stride or alignment out of range";
-    case LOCKS_ERR_UNSUPPORTED: return "unsupported dims (need d=128, page 16, rank 8, GQA 4)";
+    case LOCKS_ERR_UNSUPPORTED:
+      return "unsupported dims (need head_dim 128, page 16, rank 4/8/16, Hq/Hkv in {1,2,4,8})";
     case LOCKS_ERR_WORKSPACE: return "workspace missing or too small";
     case LOCKS_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";

@@ -9,7 +9,6 @@ namespace locks {
 constexpr int kD = 128;        // head dim
 constexpr int kB = 16;         // tokens per page
 constexpr int kR = 8;          // basis vectors per page
-constexpr int kG = 4;          // query heads per KV head
 constexpr int kRec = 832;      // bytes per summary record
 constexpr int kOffV = 0, kOffC = 512, kOffMu = 640, kOffSv = 768, kOffSc = 784, kOffSmu = 800;
 constexpr float kLog2e = 1.4426950408889634f;

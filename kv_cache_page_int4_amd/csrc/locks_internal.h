@@ -24,7 +24,7 @@ ScorePlan plan_score(int32_t batch, int32_t hkv, int32_t max_pages);
 
 hipError_t launch_score(int32_t rank, const uint16_t* q, const uint8_t* summ, int32_t num_blocks,
                         const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
-                        int32_t batch, int32_t hq, int32_t hkv, float* page_lse,
+                        int32_t batch, int32_t hq, int32_t hkv, float scale, float* page_lse,
                         float2* partials, const ScorePlan& plan, hipStream_t stream);
 
 // ---- selection -------------------------------------------------------------

@@ -25,9 +25,15 @@
 // issue and the waits are written out: a step is the only copy in flight when
 // it is waited for, so waiting for zero outstanding means it has landed.
 //
-// Per step one wave does:
+// GQA groups of G = 1, 2, 4 or 8 query heads.  The matrix-core tiles below
+// have 4 head columns (each repeated 4 times); a group of 8 runs the per-step
+// arithmetic twice on the same LDS-resident records (two 4-head sub-passes),
+// and a group of 1 or 2 fills the 4 columns with its heads repeated (the
+// duplicate columns are computed and dropped).
+//
+// Per step one wave does (for each 4-head sub-pass):
 //  * V^T q on the matrix cores: rows = (page, basis) pairs, K = head dim,
-//    columns = the 4 query heads of the group repeated 4 times.  The int4
+//    columns = 4 query heads of the group repeated 4 times.  The int4
 //    basis codes become bf16 values 136+n exactly (byte permute onto the
 //    exponent of 128); the accumulator starts at -136*sum(q).  With the
 //    rows ordered (page = lane/16, basis = register), lane l ends up holding
@@ -101,17 +107,19 @@ struct ScoreParams {
   const int32_t* seq_lens;
   float* page_lse;
   float2* partials;
+  float c0;   // logit scale times log2(e): base-2 logits
   int32_t num_blocks, max_pages, hq, hkv, n_wg;
+  int32_t group;   // query heads per KV head (1, 2, 4 or 8)
 };
 
 // Global -> LDS copy of 16 bytes per active lane: lane l writes LDS bytes
 // [lds + 16 l, lds + 16 l + 16) from sbase + voff.  M0 carries the LDS
-// address; the compiler treats M0 as reserved and this kernel has no other
-// user of it.
+// address and is declared clobbered, so the compiler keeps no value of its
+// own in M0 across the copy.
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff),
                "s"(sbase), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -121,7 +129,8 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-template <int R>
+// NSUB: 4-head sub-passes per step (2 for a group of 8 heads, else 1).
+template <int R, int NSUB>
 __global__ __launch_bounds__(64 * kScoreWaves) __attribute__((amdgpu_waves_per_eu(7, 7))) void
 score_kernel(ScoreParams p) {
   using SL = ScoreLayout<R>;
@@ -131,9 +140,10 @@ score_kernel(ScoreParams p) {
   constexpr int kWavePages = 4 * kScoreSteps;             // pages of one wave
   constexpr int kWgPages = kScoreWaves * kWavePages;       // pages of the workgroup
   __shared__ __attribute__((aligned(16))) uint8_t ring_all[kScoreWaves][kStepBytes];
-  __shared__ __attribute__((aligned(16))) uint4 qs_all[kScoreWaves][kG * kD / 8];
-  __shared__ __attribute__((aligned(16))) float outl[kG][kWgPages];
-  __shared__ float2 red[kScoreWaves][kG];
+  constexpr int kSlots = 4 * NSUB;   // head slots: 4 per sub-pass
+  __shared__ __attribute__((aligned(16))) uint4 qs_all[kScoreWaves][kSlots * kD / 8];
+  __shared__ __attribute__((aligned(16))) float outl[kSlots][kWgPages];
+  __shared__ float2 red[kScoreWaves][kSlots];
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave in the workgroup
@@ -141,10 +151,11 @@ score_kernel(ScoreParams p) {
   uint4* qs = qs_all[wv];                // this wave's copy of the group's query heads
   const int g = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int W = p.n_wg;
-  const int qhead0 = kvh * kG;
+  const int G = p.group;
+  const int qhead0 = kvh * G;
   const int row = lane >> 4;   // page slot of this lane in a step
   const int tok = lane & 15;
-  const int h = lane & 3;      // query head of this lane within the group
+  const int h = lane & 3;      // head slot of this lane within a sub-pass
 
   int seq = p.seq_lens[b];
   seq = max(0, min(seq, p.max_pages * kB));
@@ -161,31 +172,45 @@ score_kernel(ScoreParams p) {
   // loop over all threads of the (sequence, KV head)'s workgroups)
   constexpr int kThreads = 64 * kScoreWaves;
   for (int j = n_fin + kThreads * g + (int)threadIdx.x; j < p.max_pages; j += kThreads * W)
-#pragma unroll
-    for (int hh = 0; hh < kG; ++hh) lse_out[(size_t)hh * p.max_pages + j] = -INFINITY;
+    for (int hh = 0; hh < G; ++hh) lse_out[(size_t)hh * p.max_pages + j] = -INFINITY;
 
-  float pm = -INFINITY, ps = 0.f;   // running base-2 (max, sum) of head h (lanes tok < 4)
-  if (n > 0) {
-    // The group's 4 query heads (1 KB of bf16) are staged in LDS once and
-    // each step reads its MFMA B operands from there, which keeps them out of
-    // VGPRs.  For V^T q, column (lane%16) is head lane%4 and K element
-    // (step s, lane group g, e) is dim 32g + 8s + e.
-    qs[lane] = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.hq + qhead0) * kD + 8 * lane);
-    auto qpiece = [&](int s) -> uint4 { return qs[h * (kD / 8) + 4 * row + s]; };
-    float qsum = 0.f;
+  // running base-2 (max, sum) of head slot 4 sub + h (lanes tok < 4)
+  float pm[NSUB], ps[NSUB];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint4 v = qpiece(s);
-      qsum += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
-              bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
+  for (int sub = 0; sub < NSUB; ++sub) {
+    pm[sub] = -INFINITY;
+    ps[sub] = 0.f;
+  }
+  if (n > 0) {
+    // The group's query heads (1 KB of bf16 per sub-pass) are staged in LDS
+    // once and each step reads its MFMA B operands from there, which keeps
+    // them out of VGPRs.  Slot hs holds head hs of the group (head hs % G
+    // when G < 4).  For V^T q, column (lane%16) is slot lane%4 of the
+    // sub-pass and K element (step s, lane group g, e) is dim 32g + 8s + e.
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) {
+      const int u = 64 * i + lane, hs = u >> 4;
+      const int src = qhead0 + (hs < G ? hs : hs % G);
+      qs[u] = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.hq + src) * kD + 8 * (u & 15));
     }
-    qsum = cross_rows_sum(qsum);
+    auto qpiece = [&](int sub, int s) -> uint4 { return qs[(4 * sub + h) * (kD / 8) + 4 * row + s]; };
     // the codes enter the product as 136 + n: start the accumulator at -136 sum(q)
-    const float acc0_init = -136.f * qsum;
-    // for q.mu, column (lane%16) = (dim group s' = (lane/4)%4, head lane%4) and
+    float acc0_init[NSUB];
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      float qsum = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 v = qpiece(sub, s);
+        qsum += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
+                bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
+      }
+      acc0_init[sub] = -136.f * cross_rows_sum(qsum);
+    }
+    // for q.mu, column (lane%16) = (dim group s' = (lane/4)%4, slot lane%4) and
     // K element (lane group g, e) is dim 32g + 8s' + e
     const int sq = (lane >> 2) & 3;
-    const float c0 = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
+    const float c0 = p.c0;   // base-2 logit scale
 
     const uint32_t ring0 =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&ring[0];
@@ -284,105 +309,116 @@ score_kernel(ScoreParams p) {
       b0 = b1;
       b1 = (k + 2 < n) ? step_bids(k + 2) : none;
 
-      // ---- V^T q on the matrix cores ----
-      f32x4 acc[kAcc];
+      auto sub_pass = [&](const int sub) __attribute__((always_inline)) {
+        // ---- V^T q on the matrix cores ----
+        f32x4 acc[kAcc];
+        const float a0 = acc0_init[sub];
 #pragma unroll
-      for (int j = 0; j < kAcc; ++j) acc[j] = f32x4{acc0_init, acc0_init, acc0_init, acc0_init};
+        for (int j = 0; j < kAcc; ++j) acc[j] = f32x4{a0, a0, a0, a0};
 #pragma unroll
-      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].x), as_bf16x8(qpiece(0)), acc[j]);
+        for (int j = 0; j < kAcc; ++j)
+          acc[j] = mfma16x16x32(nib8_to_bf16(va[j].x), as_bf16x8(qpiece(sub, 0)), acc[j]);
 #pragma unroll
-      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].y), as_bf16x8(qpiece(1)), acc[j]);
+        for (int j = 0; j < kAcc; ++j)
+          acc[j] = mfma16x16x32(nib8_to_bf16(va[j].y), as_bf16x8(qpiece(sub, 1)), acc[j]);
 #pragma unroll
-      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].z), as_bf16x8(qpiece(2)), acc[j]);
+        for (int j = 0; j < kAcc; ++j)
+          acc[j] = mfma16x16x32(nib8_to_bf16(va[j].z), as_bf16x8(qpiece(sub, 2)), acc[j]);
 #pragma unroll
-      for (int j = 0; j < kAcc; ++j) acc[j] = mfma16x16x32(nib8_to_bf16(va[j].w), as_bf16x8(qpiece(3)), acc[j]);
+        for (int j = 0; j < kAcc; ++j)
+          acc[j] = mfma16x16x32(nib8_to_bf16(va[j].w), as_bf16x8(qpiece(sub, 3)), acc[j]);
 
-      // ---- q.mu ----
-      f32x4 dmu = {0.f, 0.f, 0.f, 0.f};
-      dmu = mfma16x16x32(i8x8_to_bf16(mq), as_bf16x8(qpiece(sq)), dmu);
-      // lane (page row, s' = sq, head h) holds D[(row, r)][(sq, h)] in register r
-      float qmu = (sq == 0) ? dmu[0] : (sq == 1) ? dmu[1] : (sq == 2) ? dmu[2] : dmu[3];
-      qmu += dpp<kRowRor4>(qmu);
-      qmu += dpp<kRowRor8>(qmu);
-      const float smu = half_lo(smu_raw);
-      const float qmu2 = qmu * smu * c0;
+        // ---- q.mu ----
+        f32x4 dmu = {0.f, 0.f, 0.f, 0.f};
+        dmu = mfma16x16x32(i8x8_to_bf16(mq), as_bf16x8(qpiece(sub, sq)), dmu);
+        // lane (page row, s' = sq, slot h) holds D[(row, r)][(sq, h)] in register r
+        float qmu = (sq == 0) ? dmu[0] : (sq == 1) ? dmu[1] : (sq == 2) ? dmu[2] : dmu[3];
+        qmu += dpp<kRowRor4>(qmu);
+        qmu += dpp<kRowRor8>(qmu);
+        const float qmu2 = qmu * half_lo(smu_raw) * c0;
 
-      // ---- w[k] = (q_h.v_k) * s_V[k] * s_c[k] for this lane's page and head ----
-      // fp16 operand times fp32 with a +0 addend: one mixed-precision FMA each
-      auto hmul = [](uint32_t pair, int hi, float x) {
-        return __builtin_fmaf(hi ? half_hi(pair) : half_lo(pair), x, 0.0f);
-      };
-      float wk[R];
+        // ---- w[k] = (q_h.v_k) * s_V[k] * s_c[k] for this lane's page and head ----
+        // fp16 operand times fp32 with a +0 addend: one mixed-precision FMA each
+        auto hmul = [](uint32_t pair, int hi, float x) {
+          return __builtin_fmaf(hi ? half_hi(pair) : half_lo(pair), x, 0.0f);
+        };
+        float wk[R];
 #pragma unroll
-      for (int j = 0; j < kAcc; ++j)
+        for (int j = 0; j < kAcc; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kk = 4 * j + r;
-          wk[kk] = hmul(scw[kk >> 1], kk & 1, hmul(svw[kk >> 1], kk & 1, acc[j][r]));
+          for (int r = 0; r < 4; ++r) {
+            const int kk = 4 * j + r;
+            wk[kk] = hmul(scw[kk >> 1], kk & 1, hmul(svw[kk >> 1], kk & 1, acc[j][r]));
+          }
+        // ---- deviation logits (base 2, without q.mu) of tokens 4cg..4cg+3 ----
+        // One 16-block 4x4x1 MFMA per basis index k: block l/4 is (page, token
+        // quarter cg), its rows the 4 tokens, its columns the 4 head slots.
+        // Lane l gives A = c[token l%16][k] and B = w[k] of its own page and
+        // slot; it gets back tokens 4cg..4cg+3 of slot l%4.  Each code is
+        // converted once instead of once per head, and the products stay fp32.
+        f32x4 dv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < R; ++kk)
+          dv = __builtin_amdgcn_mfma_f32_4x4x1f32((float)(int8_t)(cw[kk >> 2] >> (8 * (kk & 3))),
+                                                  wk[kk], dv, 0, 0, 0);
+        float dl[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) dl[t] = dv[t] * c0;
+        // page LSE over 16 tokens: 4 in this lane, the rest in the lanes 4 and 8
+        // apart in this row (same page and slot, other token quarters)
+        float sm = fast_exp2(dl[0]) + fast_exp2(dl[1]) + fast_exp2(dl[2]) + fast_exp2(dl[3]);
+        sm += dpp<kRowRor4>(sm);
+        sm += dpp<kRowRor8>(sm);
+        float lse2;
+        if (__any(!(sm >= 1e-30f && sm <= 1e30f))) {
+          float mx = fmaxf(fmaxf(dl[0], dl[1]), fmaxf(dl[2], dl[3]));
+          mx = fmaxf(mx, dpp<kRowRor4>(mx));
+          mx = fmaxf(mx, dpp<kRowRor8>(mx));
+          float s3 = fast_exp2(dl[0] - mx) + fast_exp2(dl[1] - mx) + fast_exp2(dl[2] - mx) +
+                     fast_exp2(dl[3] - mx);
+          s3 += dpp<kRowRor4>(s3);
+          s3 += dpp<kRowRor8>(s3);
+          lse2 = mx + fast_log2(s3);
+        } else {
+          lse2 = fast_log2(sm);
         }
-      // ---- deviation logits (base 2, without q.mu) of tokens 4cg..4cg+3 ----
-      // One 16-block 4x4x1 MFMA per basis index k: block l/4 is (page, token
-      // quarter cg), its rows the 4 tokens, its columns the 4 heads.  Lane l
-      // gives A = c[token l%16][k] and B = w[k] of its own page and head; it
-      // gets back tokens 4cg..4cg+3 of head l%4.  Each code is converted once
-      // instead of once per head, and the products stay fp32.
-      f32x4 dv = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < R; ++kk)
-        dv = __builtin_amdgcn_mfma_f32_4x4x1f32((float)(int8_t)(cw[kk >> 2] >> (8 * (kk & 3))),
-                                                wk[kk], dv, 0, 0, 0);
-      float dl[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) dl[t] = dv[t] * c0;
-      // page LSE over 16 tokens: 4 in this lane, the rest in the lanes 4 and 8
-      // apart in this row (same page and head, other token quarters)
-      float sm = fast_exp2(dl[0]) + fast_exp2(dl[1]) + fast_exp2(dl[2]) + fast_exp2(dl[3]);
-      sm += dpp<kRowRor4>(sm);
-      sm += dpp<kRowRor8>(sm);
-      float lse2;
-      if (__any(!(sm >= 1e-30f && sm <= 1e30f))) {
-        float mx = fmaxf(fmaxf(dl[0], dl[1]), fmaxf(dl[2], dl[3]));
-        mx = fmaxf(mx, dpp<kRowRor4>(mx));
-        mx = fmaxf(mx, dpp<kRowRor8>(mx));
-        float s3 = fast_exp2(dl[0] - mx) + fast_exp2(dl[1] - mx) + fast_exp2(dl[2] - mx) +
-                   fast_exp2(dl[3] - mx);
-        s3 += dpp<kRowRor4>(s3);
-        s3 += dpp<kRowRor8>(s3);
-        lse2 = mx + fast_log2(s3);
-      } else {
-        lse2 = fast_log2(sm);
-      }
-      const float s2 = qmu2 + lse2;
-      if (tok < 4 && jpg < n_fin) {
-        outl[h][kWavePages * wv + 4 * k + row] = okp ? s2 * kLn2 : -INFINITY;
-        if (okp) lse2_merge(pm, ps, s2, 1.f);
-      }
+        const float s2 = qmu2 + lse2;
+        if (tok < 4 && jpg < n_fin) {
+          outl[4 * sub + h][kWavePages * wv + 4 * k + row] = okp ? s2 * kLn2 : -INFINITY;
+          if (okp) lse2_merge(pm[sub], ps[sub], s2, 1.f);
+        }
+      };
+      sub_pass(0);
+      if constexpr (NSUB > 1) sub_pass(1);
     }
   }
 
-  // ---- this wave's (max, sum) of each head, for the page-mass normalization ----
-  // over the lanes 16 and 32 apart, by row swaps (lse2_merge gives the same
-  // bits with its operands exchanged, so both lanes of a pair agree)
-  {
+  // ---- this wave's (max, sum) of each head slot, for the page-mass
+  // normalization: over the lanes 16 and 32 apart, by row swaps (lse2_merge
+  // gives the same bits with its operands exchanged, so both lanes of a pair
+  // agree) ----
+#pragma unroll
+  for (int sub = 0; sub < NSUB; ++sub) {
     float ma, mb, sa, sb;
-    swap16(pm, ma, mb);
-    swap16(ps, sa, sb);
-    pm = ma;
-    ps = sa;
-    lse2_merge(pm, ps, mb, sb);
-    swap32(pm, ma, mb);
-    swap32(ps, sa, sb);
-    pm = ma;
-    ps = sa;
-    lse2_merge(pm, ps, mb, sb);
+    float m = pm[sub], sm = ps[sub];
+    swap16(m, ma, mb);
+    swap16(sm, sa, sb);
+    m = ma;
+    sm = sa;
+    lse2_merge(m, sm, mb, sb);
+    swap32(m, ma, mb);
+    swap32(sm, sa, sb);
+    m = ma;
+    sm = sa;
+    lse2_merge(m, sm, mb, sb);
+    if (lane < 4) red[wv][4 * sub + lane] = make_float2(m, sm);
   }
-  if (lane < kG) red[wv][lane] = make_float2(pm, ps);
   __syncthreads();
 
   // ---- the workgroup's finalized pages: one 4-page piece per thread, each
   // head's kWgPages scores leave as one contiguous run ----
   constexpr int kPieces = kWgPages / 4;   // per head
-  static_assert(kG * kPieces <= 64 * kScoreWaves, "one 4-page piece per thread");
+  static_assert(kSlots * kPieces <= 64 * kScoreWaves, "one 4-page piece per thread");
   {
     const int t = threadIdx.x;
     const int p0 = kWgPages * g;
@@ -390,7 +426,7 @@ score_kernel(ScoreParams p) {
     const int hh = t / kPieces, part = t % kPieces;
     float* dst = lse_out + (size_t)hh * p.max_pages + p0 + 4 * part;
     const bool vec = (p.max_pages & 3) == 0 && ((uintptr_t)p.page_lse & 15) == 0;
-    if (t < kG * kPieces && 4 * part < nval) {
+    if (hh < G && 4 * part < nval) {
       const float4 v = *reinterpret_cast<const float4*>(&outl[hh][4 * part]);
       if (vec && 4 * part + 4 <= nval) {
         *reinterpret_cast<float4*>(dst) = v;
@@ -400,7 +436,7 @@ score_kernel(ScoreParams p) {
       }
     }
     // one (max, sum) partial per workgroup and head
-    if (t < kG && p.partials) {
+    if (t < G && p.partials) {
       float pm2 = -INFINITY, ps2 = 0.f;
 #pragma unroll
       for (int v2 = 0; v2 < kScoreWaves; ++v2) lse2_merge(pm2, ps2, red[v2][t].x, red[v2][t].y);
@@ -425,15 +461,27 @@ ScorePlan plan_score(int32_t batch, int32_t hkv, int32_t max_pages) {
 
 hipError_t launch_score(int32_t rank, const uint16_t* q, const uint8_t* summ, int32_t num_blocks,
                         const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
-                        int32_t batch, int32_t hq, int32_t hkv, float* page_lse,
+                        int32_t batch, int32_t hq, int32_t hkv, float scale, float* page_lse,
                         float2* partials, const ScorePlan& plan, hipStream_t stream) {
-  ScoreParams p{q, summ, block_table, seq_lens, page_lse, partials, num_blocks, max_pages, hq,
-                hkv, plan.n_chunks};
+  const int32_t group = hq / hkv;
+  ScoreParams p{q, summ, block_table, seq_lens, page_lse, partials, scale * kLog2e, num_blocks,
+                max_pages, hq, hkv, plan.n_chunks, group};
   dim3 grid(plan.n_chunks, hkv, batch);
+  const dim3 blk(64 * kScoreWaves);
+  const bool two = group > 4;   // two 4-head sub-passes
   switch (rank) {
-    case 4: hipLaunchKernelGGL(score_kernel<4>, grid, dim3(64 * kScoreWaves), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(score_kernel<8>, grid, dim3(64 * kScoreWaves), 0, stream, p); break;
-    case 16: hipLaunchKernelGGL(score_kernel<16>, grid, dim3(64 * kScoreWaves), 0, stream, p); break;
+    case 4:
+      if (two) hipLaunchKernelGGL((score_kernel<4, 2>), grid, blk, 0, stream, p);
+      else hipLaunchKernelGGL((score_kernel<4, 1>), grid, blk, 0, stream, p);
+      break;
+    case 8:
+      if (two) hipLaunchKernelGGL((score_kernel<8, 2>), grid, blk, 0, stream, p);
+      else hipLaunchKernelGGL((score_kernel<8, 1>), grid, blk, 0, stream, p);
+      break;
+    case 16:
+      if (two) hipLaunchKernelGGL((score_kernel<16, 2>), grid, blk, 0, stream, p);
+      else hipLaunchKernelGGL((score_kernel<16, 1>), grid, blk, 0, stream, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

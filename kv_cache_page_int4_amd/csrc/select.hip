@@ -234,7 +234,7 @@ void select_chunk_kernel(SelParams p) {
   constexpr int kUnroll = (PT == 2) ? 8 : 4;   // partials in flight per lane
   const int chunk = blockIdx.x, tab = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int hpt = p.hq / p.ntab;   // query heads of this table (a multiple of 4)
+  const int hpt = p.hq / p.ntab;   // query heads of this table
   int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
   const int n_fin = seq / kB;
 
@@ -279,18 +279,21 @@ void select_chunk_kernel(SelParams p) {
         if (lane == 0) l2s[wave] = (sm > 0.f) ? m + fast_log2(sm) : -INFINITY;
       }
       __syncthreads();
-      for (int h0 = hb; h0 < hb + nb; h0 += kG) {
-        float sv[kG][kPerThread];
-        float l2[kG];
+      // four heads at a time; a head past the batch (tables of 1 or 2 heads)
+      // adds -inf, which leaves the key unchanged
+      for (int h0 = hb; h0 < hb + nb; h0 += 4) {
+        float sv[4][kPerThread];
+        float l2[4];
 #pragma unroll
-        for (int hh = 0; hh < kG; ++hh) {
-          const float* s = p.page_lse + ((size_t)b * p.hq + h0 + hh) * p.max_pages;
+        for (int hh = 0; hh < 4; ++hh) {
+          const bool real = h0 + hh < hb + nb;
+          const float* s = p.page_lse + ((size_t)b * p.hq + (real ? h0 + hh : h0)) * p.max_pages;
 #pragma unroll
-          for (int t = 0; t < kPerThread; ++t) sv[hh][t] = s[min(jbase + t, jmax)];
-          l2[hh] = l2s[h0 - hb + hh];
+          for (int t = 0; t < kPerThread; ++t) sv[hh][t] = real ? s[min(jbase + t, jmax)] : -INFINITY;
+          l2[hh] = real ? l2s[h0 - hb + hh] : 0.f;
         }
 #pragma unroll
-        for (int hh = 0; hh < kG; ++hh) {
+        for (int hh = 0; hh < 4; ++hh) {
 #pragma unroll
           for (int t = 0; t < kPerThread; ++t) {
             const float a = sv[hh][t] * kLog2e - l2[hh];

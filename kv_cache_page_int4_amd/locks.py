@@ -44,6 +44,7 @@ _DP = ctypes.POINTER(Dims)
 
 _SIGS = {
     "locks_summary_bytes": (_SZ, [_DP]),
+    "locks_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I32]),
     "locks_score_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I32]),
     "locks_attend_workspace_bytes": (_SZ, [_DP, _I32, _I32]),
     "locks_build_summaries": (_I32, [_DP, _P, KVLayout, _P, _I32, _I32, _P, _P, _P]),
@@ -153,6 +154,20 @@ def summary_bytes(d: Dims) -> int:
     return lib().locks_summary_bytes(ctypes.byref(d))
 
 
+def workspace_bytes(d: Dims, batch, max_pages, budget_pages) -> int:
+    """One workspace size that serves every decode-path call with these sizes
+    (and decode_layer with attend_ws=None)."""
+    return lib().locks_workspace_bytes(ctypes.byref(d), batch, max_pages, budget_pages)
+
+
+def workspace(d: Dims, batch, max_pages, budget_pages, device="cuda") -> torch.Tensor:
+    """A workspace of workspace_bytes(...) bytes."""
+    n = workspace_bytes(d, batch, max_pages, budget_pages)
+    if n == 0:
+        raise ValueError("unsupported dims or sizes for a workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def score_workspace_bytes(d: Dims, batch, max_pages, budget_pages=0) -> int:
     return lib().locks_score_workspace_bytes(ctypes.byref(d), batch, max_pages, budget_pages)
 
@@ -193,7 +208,7 @@ def score_pages(d: Dims, q, summaries, num_blocks, block_table, seq_lens, page_l
     _need(seq_lens, "seq_lens", torch.int32, numel=B)
     _need(page_lse, "page_lse", torch.float32, numel=B * hq * P)
     _on_device(q=q, summaries=summaries, block_table=block_table, seq_lens=seq_lens,
-               page_lse=page_lse)
+               page_lse=page_lse, workspace=workspace)
     st = lib().locks_score_pages(ctypes.byref(d), _ptr(q), _ptr(summaries), num_blocks,
                                  _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
                                  block_table.shape[0], _ptr(page_lse), _ptr(workspace),
@@ -211,7 +226,8 @@ def select_pages(d: Dims, page_lse, seq_lens, budget_pages, sel, sel_count, work
     _need(seq_lens, "seq_lens", torch.int32, numel=B)
     _need(sel, "sel", torch.int32, numel=B * ntab * budget_pages)
     _need(sel_count, "sel_count", torch.int32, numel=B * ntab)
-    _on_device(page_lse=page_lse, seq_lens=seq_lens, sel=sel, sel_count=sel_count)
+    _on_device(page_lse=page_lse, seq_lens=seq_lens, sel=sel, sel_count=sel_count,
+               workspace=workspace)
     args = [ctypes.byref(d), _ptr(page_lse), page_lse.shape[-1], _ptr(seq_lens),
             page_lse.shape[0], budget_pages]
     rest = [_ptr(sel), _ptr(sel_count), _ptr(workspace),
@@ -234,7 +250,7 @@ def score_select(d: Dims, q, summaries, num_blocks, block_table, seq_lens, budge
     _need(sel_count, "sel_count", torch.int32, numel=B * hkv)
     _need(page_lse, "page_lse", torch.float32, numel=B * hq * P)
     _on_device(q=q, summaries=summaries, block_table=block_table, seq_lens=seq_lens, sel=sel,
-               sel_count=sel_count, page_lse=page_lse)
+               sel_count=sel_count, page_lse=page_lse, workspace=workspace)
     st = lib().locks_score_select(ctypes.byref(d), _ptr(q), _ptr(summaries), num_blocks,
                                   _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
                                   block_table.shape[0], budget_pages, _ptr(sel), _ptr(sel_count),
@@ -263,7 +279,7 @@ def sparse_attend(d: Dims, q, k_cache, v_cache, block_table, seq_lens, sel, sel_
     _need(out, "out", torch.bfloat16, numel=B * hq * d.head_dim)
     _need(out_lse, "out_lse", torch.float32, numel=B * hq)
     _on_device(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, seq_lens=seq_lens,
-               sel=sel, sel_count=sel_count, out=out, out_lse=out_lse)
+               sel=sel, sel_count=sel_count, out=out, out_lse=out_lse, workspace=workspace)
     lay = kv_layout(k_cache)
     lv = kv_layout(v_cache)
     if (lay.block_stride, lay.head_stride, lay.token_stride) != (
@@ -335,10 +351,12 @@ def finalize_pages(d: Dims, k_cache, block_table, seq_lens, summaries, stream=No
 
 
 def decode_layer(d: Dims, q, summaries, k_cache, v_cache, block_table, seq_lens, budget_pages,
-                 sel, sel_count, out, score_ws, attend_ws, out_lse=None, softmax_scale=None,
+                 sel, sel_count, out, score_ws, attend_ws=None, out_lse=None, softmax_scale=None,
                  stream=None, n_tables=None):
     """score_select followed by sparse_attend in one call (identical outputs);
-    n_tables as for select_pages."""
+    n_tables as for select_pages.  attend_ws=None: score_ws is one workspace of
+    workspace_bytes(...) bytes holding both parts.  softmax_scale (default
+    1/sqrt(d)) is the logit scale of both the page estimate and the attention."""
     B, P, hq = block_table.shape[0], block_table.shape[1], d.num_q_heads
     ntab = d.num_kv_heads if n_tables is None else int(n_tables)
     _need(q, "q", torch.bfloat16, numel=B * hq * d.head_dim)
@@ -355,7 +373,8 @@ def decode_layer(d: Dims, q, summaries, k_cache, v_cache, block_table, seq_lens,
     _need(out, "out", torch.bfloat16, numel=B * hq * d.head_dim)
     _need(out_lse, "out_lse", torch.float32, numel=B * hq)
     _on_device(q=q, summaries=summaries, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
-               seq_lens=seq_lens, sel=sel, sel_count=sel_count, out=out, out_lse=out_lse)
+               seq_lens=seq_lens, sel=sel, sel_count=sel_count, out=out, out_lse=out_lse,
+               score_ws=score_ws, attend_ws=attend_ws)
     lay = kv_layout(k_cache)
     lv = kv_layout(v_cache)
     if (lay.block_stride, lay.head_stride, lay.token_stride) != (
@@ -368,7 +387,8 @@ def decode_layer(d: Dims, q, summaries, k_cache, v_cache, block_table, seq_lens,
             block_table.shape[0], budget_pages]
     tail = [float(softmax_scale), _ptr(sel), _ptr(sel_count), _ptr(out), _ptr(out_lse),
             _ptr(score_ws), score_ws.numel() * score_ws.element_size(), _ptr(attend_ws),
-            attend_ws.numel() * attend_ws.element_size(), _stream(stream)]
+            0 if attend_ws is None else attend_ws.numel() * attend_ws.element_size(),
+            _stream(stream)]
     if n_tables is None:
         _check("locks_decode_layer", lib().locks_decode_layer(*head, *tail))
     else:
@@ -385,7 +405,8 @@ def shared_basis(d: Dims, k_cache, block_ids, basis, eigvals=None, workspace=Non
     _need(block_ids, "block_ids", torch.int32, numel=n)
     _need(basis, "basis", torch.float32, numel=hkv * d.rank * d.head_dim)
     _need(eigvals, "eigvals", torch.float32, numel=hkv * d.head_dim)
-    _on_device(k_cache=k_cache, block_ids=block_ids, basis=basis, eigvals=eigvals)
+    _on_device(k_cache=k_cache, block_ids=block_ids, basis=basis, eigvals=eigvals,
+               workspace=workspace)
     if workspace is None:
         nbytes = lib().locks_shared_basis_workspace_bytes(ctypes.byref(d), n)
         workspace = torch.empty(max(1, nbytes), dtype=torch.uint8, device=k_cache.device)

@@ -3,10 +3,16 @@
 The decode step (technical summary sec. 2, implementation paragraph: scoring,
 selection and sparse attention run inside one full graph with no Python
 dispatch) is, per layer, locks_decode_layer (locks_score_select followed by
-locks_sparse_attend, with the last selection stage inside the attention);
-with finalize=True the step first calls locks_finalize_pages once for all
-layers, which builds the summary of any page that the newest token completed
-(decided on the device, so the same graph serves every step).
+locks_sparse_attend, with the last selection stage inside the attention).
+With finalize=True each layer first calls locks_finalize_pages for that
+layer, which builds the summary of any page that the newest token completed
+(decided on the device, so the same graph serves every step).  In a model the
+newest token's key of layer l is written during layer l, so the page it
+completes can be summarized only after that write and before the layer's
+scorer: per layer, not once for all layers at the start of the step.  An
+optional before_layer(l) callback, recorded into the graph too, stands for
+the model's work that precedes layer l's attention (appending the token's
+key and value, for instance).
 This module only allocates the per-layer outputs and the workspaces, issues
 the library calls in order on the current stream and records them into a
 torch.cuda.CUDAGraph (a hipGraph on ROCm).  Layers run in sequence because in
@@ -23,7 +29,9 @@ class DecodeStep:
     [layers, hkv, blocks, record bytes]; q: bf16 [layers, batch, hq, 128];
     block_table: int32 [batch, max_pages]; seq_lens: int32 [batch].
     dense=True attends every finalized page instead (no scoring/selection);
-    finalize=True summarizes pages completed by the newest token first;
+    finalize=True summarizes, per layer, the page the newest token completed
+    before that layer is scored; before_layer(layer) is called (and captured)
+    at the head of every layer;
     fused=True issues each layer as one locks_decode_layer call (the last
     selection stage runs inside the attention kernel), fused=False as
     locks_score_select + locks_sparse_attend.  n_tables sets the number of
@@ -31,10 +39,11 @@ class DecodeStep:
     the whole layer); sel and cnt then hold n_tables rows per sequence."""
 
     def __init__(self, d, k, v, summaries, q, block_table, seq_lens, budget_pages, dense=False,
-                 finalize=False, fused=True, n_tables=None):
+                 finalize=False, fused=True, n_tables=None, before_layer=None):
         self.d, self.k, self.v, self.summ, self.q = d, k, v, summaries, q
         self.bt, self.seq, self.budget, self.dense = block_table, seq_lens, budget_pages, dense
         self.finalize = finalize
+        self.before_layer = before_layer
         self.fused = fused
         self.n_tables = n_tables
         ntab = d.num_kv_heads if n_tables is None else n_tables
@@ -60,6 +69,10 @@ class DecodeStep:
 
     def run_layer(self, layer, stream=None):
         d = self.d
+        if self.before_layer is not None:
+            self.before_layer(layer)
+        if self.finalize:   # the page this layer's newest key completed, if any
+            L.finalize_pages(d, self.k[layer], self.bt, self.seq, self.summ[layer], stream=stream)
         if not self.dense and self.fused:
             L.decode_layer(d, self.q[layer], self.summ[layer], self.k[layer], self.v[layer],
                            self.bt, self.seq, self.budget, self.sel[layer], self.cnt[layer],
@@ -82,8 +95,6 @@ class DecodeStep:
                         n_tables=self.n_tables)
 
     def run(self):
-        if self.finalize:   # every layer's completed pages, in one launch
-            L.finalize_pages(self.d, self.k, self.bt, self.seq, self.summ)
         for layer in range(self.layers):
             self.run_layer(layer)
 

@@ -189,18 +189,45 @@ def exempt_columns(lam, V):
     return ex
 
 
+def quant_error_rms(qz, r=8):
+    """Expected RMS error (Frobenius) that quantization adds to a page's
+    reconstruction C V^T, from the record's own scales: rounding to a step s
+    leaves an error uniform on [-s/2, s/2], of variance s^2 / 12, in each of
+    the 128 entries of basis column k (step s_V[k]) and the 16 entries of
+    coefficient column k (step s_c[k]); column k's error term is
+    |c_k| |dv_k| + |dc_k| |v_k|, so its expected square is
+    |c_k|^2 128 s_V[k]^2 / 12 + |v_k|^2 16 s_c[k]^2 / 12."""
+    mu, V, C = O.dequantize_summary(qz)
+    sv, sc = np.asarray(qz["s_v"]), np.asarray(qz["s_c"])
+    cn2 = (C * C).sum(axis=-2)          # [..., r]
+    vn2 = (V * V).sum(axis=-2)
+    return np.sqrt((cn2 * 128 * sv ** 2 / 12 + vn2 * 16 * sc ** 2 / 12).sum(axis=-1))
+
+
 def compare_build_codes(K, recs_gpu, where="", r=8):
     """K: fp64 keys [n, 16, 128]; recs_gpu: the GPU's rank-r records [n, bytes] for
     the same page-heads.  Codes within 1 LSB and scales within 1 fp16 ulp
-    outside the exempt columns; exempt pages compared by reconstruction.
-    Returns (columns, exempt columns, worst exempt-page reconstruction diff)."""
+    outside the exempt columns.  An exempt page (a near-degenerate eigenvalue,
+    an ambiguous sign or an eigenvalue at the rank floor) has no unique basis:
+    any orthonormal basis of a near-degenerate cluster is an equally valid
+    eigenbasis, so its codes cannot be compared.  What is unique is the
+    residual: by Eckart-Young a rank-r basis of the top-r eigenspace leaves
+    |X - X V V^T|^2 = sum_{k>r} lam_k, swapping an eigenvector across a gap
+    below 1e-3 lam_1 (the exemption threshold) adds exactly that gap, and
+    quantization adds e_q^2 on average, e_q the expected RMS quantization
+    error of the record (quant_error_rms, from its own int4/int8 steps).  The
+    GPU record's dequantized reconstruction must leave
+        residual^2 <= sum_{k>r} lam_k + n_ex * 1e-3 lam_1 + (1.5 e_q)^2.
+    On oracle records sqrt(residual^2 - sum_{k>r} lam_k) / e_q is 0.99-1.07
+    for ranks 4, 8 and 16; a random basis gives 6 or more.  Returns (columns,
+    exempt columns, worst exempt-page ratio sqrt(residual^2 - optimum) / e_q)."""
     mu, V, C, lam = O.page_summary(K, r)
     qo = O.quantize_summary(mu, V, C)
     qg = O.unpack_records(recs_gpu, r=r)
     assert np.abs(qg["mu_q"].astype(int) - qo["mu_q"]).max() <= 1, where
     assert np.all(np.abs(qg["s_mu"] - qo["s_mu"]) <= fp16_ulp(qo["s_mu"])), where
     n_cols = n_ex = 0
-    worst_rec = 0.0
+    worst = 0.0
     for i in range(K.shape[0]):
         ex = exempt_columns(lam[i], V[i])
         n_cols += len(ex)
@@ -213,10 +240,14 @@ def compare_build_codes(K, recs_gpu, where="", r=8):
         assert np.all(np.abs(qg["s_v"][i][ok] - qo["s_v"][i][ok]) <= fp16_ulp(qo["s_v"][i][ok]))
         assert np.all(np.abs(qg["s_c"][i][ok] - qo["s_c"][i][ok]) <= fp16_ulp(qo["s_c"][i][ok]))
         if ex.any():
-            Rg = dequant_recon({k: v[i] for k, v in qg.items()})
-            Ro = dequant_recon({k: v[i] for k, v in qo.items()})
+            gi = {k: v[i] for k, v in qg.items()}
+            _, Vg, Cg = O.dequantize_summary(gi)
             X = K[i] - mu[i]
-            rel = np.linalg.norm(Rg - Ro) / max(np.linalg.norm(X), 1e-30)
-            worst_rec = max(worst_rec, rel)
-            assert rel <= 0.15, f"reconstruction of an exempt page differs by {rel} ({where})"
-    return n_cols, n_ex, worst_rec
+            res2 = float(np.sum((X - Cg @ Vg.T) ** 2))
+            opt2 = max(float(lam[i][r:].sum()), 0.0)
+            eq = float(quant_error_rms(gi, r))
+            bound = opt2 + ex.sum() * 1e-3 * lam[i][0] + (1.5 * eq) ** 2
+            assert res2 <= bound, (
+                f"exempt page residual^2 {res2:.4g} above {bound:.4g} ({where}, page {i})")
+            worst = max(worst, np.sqrt(max(res2 - opt2, 0.0)) / max(eq, 1e-30))
+    return n_cols, n_ex, worst

@@ -30,8 +30,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["locks_build_summaries", "locks_score_select", "locks_sparse_attend",
                  "locks_score_pages", "locks_select_pages", "locks_summary_bytes",
-                 "locks_score_workspace_bytes", "locks_attend_workspace_bytes",
-                 "locks_status_str"]:
+                 "locks_workspace_bytes", "locks_score_workspace_bytes",
+                 "locks_attend_workspace_bytes", "locks_status_str"]:
         assert want in names
 
 
@@ -50,7 +50,11 @@ def test_summary_bytes_and_unsupported_dims():
     assert L.summary_bytes(L.dims(32, 8, rank=16)) == 1536
     assert L.summary_bytes(L.dims(32, 8, rank=5)) == 0
     assert L.summary_bytes(L.dims(32, 8, rank=32)) == 0
-    assert L.summary_bytes(L.dims(16, 8)) == 0       # group of 2 not supported
+    # GQA groups of 1, 2, 4 and 8 query heads per KV head; others refused
+    for hq, hkv in ((8, 8), (16, 8), (32, 8), (64, 8), (4, 1), (8, 1), (1, 1)):
+        assert L.summary_bytes(L.dims(hq, hkv)) == 832, (hq, hkv)
+    for hq, hkv in ((24, 8), (12, 4), (128, 8), (6, 4), (4, 8), (3, 1)):
+        assert L.summary_bytes(L.dims(hq, hkv)) == 0, (hq, hkv)
 
 
 def test_workspace_sizes_monotone():
@@ -62,6 +66,58 @@ def test_workspace_sizes_monotone():
     assert L.score_workspace_bytes(d, 0, 2048, 128) == 0
     assert L.attend_workspace_bytes(d, 1, 129) > 0
     assert L.attend_workspace_bytes(d, 8, 129) >= L.attend_workspace_bytes(d, 1, 129)
+
+
+def test_one_workspace_serves_every_call():
+    """locks_workspace_bytes covers the scoring part followed by the
+    attention part of a sparse or a dense pass, and grows with the group."""
+    _lib_or_skip()
+    rnd = lambda x: -(-x // 256) * 256  # noqa: E731
+    for hq, hkv, batch, pages, budget in ((32, 8, 1, 65536, 128), (32, 8, 16, 16384, 128),
+                                         (8, 8, 2, 2048, 128), (64, 8, 1, 2048, 128),
+                                         (4, 1, 1, 256, 32), (32, 8, 1, 64, 512)):
+        d = L.dims(hq, hkv)
+        n = L.workspace_bytes(d, batch, pages, budget)
+        sc = L.score_workspace_bytes(d, batch, pages, budget)
+        att_sparse = L.attend_workspace_bytes(d, batch, budget + 1)
+        att_dense = L.attend_workspace_bytes(d, batch, pages + 1)
+        assert n == rnd(sc) + max(att_sparse, att_dense, L.attend_workspace_bytes(
+            d, batch, max(budget, pages) + 1)), (hq, hkv)
+        assert n >= sc + att_sparse and n >= att_dense
+    d = L.dims(32, 8)
+    assert L.workspace_bytes(d, 1, 2048, 0) == 0
+    assert L.workspace_bytes(d, 0, 2048, 128) == 0
+    assert L.workspace_bytes(L.dims(24, 8), 1, 2048, 128) == 0
+    # a group of 8 keeps twice the query-head rows of a group of 4
+    assert L.workspace_bytes(L.dims(64, 8), 1, 2048, 128) > L.workspace_bytes(d, 1, 2048, 128)
+
+
+def test_decode_layer_single_workspace_checks():
+    """With attend_ws NULL the one workspace must hold both parts and be
+    16-byte aligned; nothing is launched when it does not."""
+    lib = _lib_or_skip()
+    d = L.dims(32, 8)
+    P = ctypes.c_void_p
+    lay = L.KVLayout(32768, 4096, 128)
+    B, MP, BUD = 1, 2048, 128
+    sc = L.score_workspace_bytes(d, B, MP, BUD)
+    att = L.attend_workspace_bytes(d, B, BUD + 1)
+    need = -(-sc // 256) * 256 + att          # what the call checks: both parts
+    assert L.workspace_bytes(d, B, MP, BUD) >= need
+    full = need
+
+    def call(ws=P(256), ws_bytes=full, att=None, att_bytes=0):
+        return lib.locks_decode_layer(ctypes.byref(d), P(256), P(256), P(256), P(256), lay, 4096,
+                                      P(256), MP, P(256), B, BUD, 0.0883, P(256), P(256), P(256),
+                                      None, ws, ws_bytes, att, att_bytes, None)
+
+    assert call(ws_bytes=sc) == L.ERR_WORKSPACE            # no room for the attention part
+    assert call(ws_bytes=full - 1) == L.ERR_WORKSPACE
+    assert call(ws=P(264)) == L.ERR_WORKSPACE              # misaligned single workspace
+    assert call(ws=None) == L.ERR_WORKSPACE
+    # separate workspaces: each checked against its own part
+    assert call(ws_bytes=sc - 1, att=P(256), att_bytes=att) == L.ERR_WORKSPACE
+    assert call(ws_bytes=sc, att=P(256), att_bytes=att - 1) == L.ERR_WORKSPACE
 
 
 def test_stage1_chunks_widen_for_large_grids():
@@ -151,6 +207,9 @@ def test_status_strings():
     _lib_or_skip()
     for st in (L.OK, L.ERR_NULL, L.ERR_SHAPE, L.ERR_UNSUPPORTED, L.ERR_WORKSPACE, L.ERR_LAUNCH):
         assert len(L.status_str(st)) > 0
+    # the unsupported-shape message names every accepted rank and group
+    msg = L.status_str(L.ERR_UNSUPPORTED)
+    assert "4/8/16" in msg and "{1,2,4,8}" in msg
     assert L.status_str(-99) == "unknown status"
 
 

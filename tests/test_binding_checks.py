@@ -91,3 +91,49 @@ def test_build_and_basis_sizes():
     with pytest.raises(ValueError, match="summaries holds"):
         L.build_summaries_basis(L.dims(32, 8, rank=4), a["k"], ids, t((8, 4, 128), torch.float32),
                                 t((8, 100, 511), torch.uint8))
+
+
+def test_workspaces_are_checked_to_be_on_the_device(monkeypatch):
+    """Every workspace a call hands to the kernels goes through the device
+    check, with the call's other buffers (a host workspace would give the
+    kernels a host pointer)."""
+    a = base()
+    seen = []
+
+    def spy(**tensors):
+        seen.append(set(k for k, v in tensors.items() if v is not None))
+        raise ValueError("stop before any launch")
+
+    monkeypatch.setattr(L, "_on_device", spy)
+    calls = [
+        (lambda: L.score_pages(D, a["q"], a["summ"], 100, a["bt"], a["seq"], a["lse"], a["ws"]),
+         {"workspace"}),
+        (lambda: L.select_pages(D, a["lse"], a["seq"], BUD, a["sel"], a["cnt"], a["ws"]),
+         {"workspace"}),
+        (lambda: L.score_select(D, a["q"], a["summ"], 100, a["bt"], a["seq"], BUD, a["sel"],
+                                a["cnt"], a["ws"]), {"workspace"}),
+        (lambda: L.sparse_attend(D, a["q"], a["k"], a["v"], a["bt"], a["seq"], a["sel"], a["cnt"],
+                                 BUD, a["out"], a["ws"]), {"workspace"}),
+        (lambda: L.decode_layer(D, a["q"], a["summ"], a["k"], a["v"], a["bt"], a["seq"], BUD,
+                                a["sel"], a["cnt"], a["out"], a["ws"], a["ws"]),
+         {"score_ws", "attend_ws"}),
+        (lambda: L.decode_layer(D, a["q"], a["summ"], a["k"], a["v"], a["bt"], a["seq"], BUD,
+                                a["sel"], a["cnt"], a["out"], a["ws"]), {"score_ws"}),
+        (lambda: L.shared_basis(D, a["k"], t((10,), torch.int32), t((8, 8, 128), torch.float32),
+                                workspace=a["ws"]), {"workspace"}),
+    ]
+    for fn, want in calls:
+        seen.clear()
+        with pytest.raises(ValueError, match="stop before any launch"):
+            fn()
+        assert seen and want <= seen[-1], (want, seen)
+
+
+def test_host_workspace_is_refused():
+    """A host workspace with otherwise valid shapes raises before the library
+    is reached (CPU tensors throughout: the first non-device buffer named)."""
+    a = base()
+    with pytest.raises(ValueError, match="must be a device tensor"):
+        L.score_pages(D, a["q"], a["summ"], 100, a["bt"], a["seq"], a["lse"], a["ws"])
+    with pytest.raises(ValueError, match="must be a device tensor"):
+        L._on_device(workspace=a["ws"])

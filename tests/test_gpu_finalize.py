@@ -1,7 +1,9 @@
 """Incremental finalization on the GPU: locks_finalize_pages builds exactly
 the records locks_build_summaries builds, only for sequences whose newest
-token completed a page, and a captured decode step that includes it keeps
-the summaries current while tokens are appended between replays."""
+token completed a page, and a captured decode step that appends each layer's
+newest key and summarizes the page it completes keeps the summaries current
+while tokens are appended between replays; its records, selections and
+outputs are checked against the oracle."""
 
 import numpy as np
 import pytest
@@ -17,7 +19,9 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
-from tests.gpu_common import log  # noqa: E402
+import oracle as O  # noqa: E402
+from tests.gpu_common import (LSE_TOL, OUT_TOL, check_selection, compare_build_codes,  # noqa: E402
+                              from_dev_bf16, log)
 
 
 def _dev(a):
@@ -51,9 +55,12 @@ def test_finalize_builds_only_completed_pages():
 
 
 def test_decode_graph_with_incremental_finalization():
-    """Tokens are appended between replays of one captured step; whenever a
-    page fills, the replay summarizes it, and every output equals the eager
-    library calls on the same state."""
+    """A captured step that, per layer, appends the newest token's key and
+    value (the model's work, inside the graph), summarizes the page that key
+    completed and then runs that layer's decode.  Tokens are appended between
+    replays; every record finalized during the replays is checked against the
+    oracle's build of the same keys, two replays' selections and outputs
+    against the oracle, and others against the eager library calls."""
     w = get_workload("llama8b-32k", batch=2, layers=2, ctx=16 * 512)
     start = [16 * 300 - 3, 16 * 500 - 1]
     x = generate(w, seq_lens=start)
@@ -62,35 +69,57 @@ def test_decode_graph_with_incremental_finalization():
     bt = torch.from_numpy(x.block_table).cuda()
     seq = torch.from_numpy(x.seq_lens.copy()).cuda()
     nb = w.num_blocks
+    budget = 32
     summ = torch.zeros((w.layers, w.hkv, nb, 832), dtype=torch.uint8, device="cuda")
     for layer in range(w.layers):   # pages finalized before decoding starts
         for b, s in enumerate(start):
             blocks = torch.from_numpy(x.block_table[b, :s // 16].astype(np.int32)).cuda()
             L.build_summaries(d, k[layer], blocks, summ[layer])
-    step = DecodeStep(d, k, v, summ, q, bt, seq, 32, finalize=True)
-    step.run()
-    torch.cuda.synchronize()
+    # the newest token's key and value of every layer, written by the step
+    # itself at position seq_lens - 1 (staged here between replays)
+    new_k = torch.empty((w.layers, w.batch, w.hkv, 128), dtype=torch.bfloat16, device="cuda")
+    new_v = torch.empty_like(new_k)
+    rows = torch.arange(w.batch, device="cuda")
+    for b, s in enumerate(start):   # staged = the current last token: the warm-up rewrites it
+        blk = int(x.block_table[b, (s - 1) // 16])
+        new_k[:, b] = k[:, blk, :, (s - 1) % 16]
+        new_v[:, b] = v[:, blk, :, (s - 1) % 16]
+
+    def append(layer):
+        pos = (seq - 1).long()
+        blk = bt[rows, pos // 16].long()
+        slot = pos % 16
+        k[layer][blk, :, slot] = new_k[layer]
+        v[layer][blk, :, slot] = new_v[layer]
+
+    step = DecodeStep(d, k, v, summ, q, bt, seq, budget, finalize=True, before_layer=append)
     step.capture()
     gen = torch.Generator(device="cuda").manual_seed(7)
     cur = list(start)
     completed = []
+    oracle_checked = []
     for t in range(20):
-        # append one token per sequence (eager work outside the graph)
+        new_k.copy_(torch.randn(new_k.shape, generator=gen, device="cuda").to(torch.bfloat16))
+        new_v.copy_(torch.randn(new_v.shape, generator=gen, device="cuda").to(torch.bfloat16))
+        done_now = []
         for b in range(w.batch):
-            pos = cur[b]
-            blk = int(x.block_table[b, pos // 16])
-            k[:, blk, :, pos % 16, :] = torch.randn((w.layers, w.hkv, 128), generator=gen,
-                                                    device="cuda").to(torch.bfloat16)
-            v[:, blk, :, pos % 16, :] = torch.randn((w.layers, w.hkv, 128), generator=gen,
-                                                    device="cuda").to(torch.bfloat16)
             cur[b] += 1
             if cur[b] % 16 == 0:
+                done_now.append((b, cur[b] // 16 - 1))
                 completed.append((b, cur[b] // 16 - 1, t))
         seq.copy_(torch.tensor(cur, dtype=torch.int32))
         torch.cuda.synchronize()
+        for a in (step.sel, step.cnt, step.out, step.out_lse):
+            a.fill_(-3)
         step.replay()
         torch.cuda.synchronize()
-        if t in (2, 7, 19):
+        for b in range(w.batch):   # the staged token landed at its position in every layer
+            blk = int(x.block_table[b, (cur[b] - 1) // 16])
+            assert torch.equal(k[:, blk, :, (cur[b] - 1) % 16], new_k[:, b])
+        if done_now or t == 19:
+            _check_against_oracle(d, k, v, q, summ, bt, seq, step, budget, cur, done_now)
+            oracle_checked.append(t)
+        if t in (5, 11):
             # eager reference on the same state
             sel_r = torch.empty_like(step.sel[0])
             cnt_r = torch.empty_like(step.cnt[0])
@@ -98,9 +127,9 @@ def test_decode_graph_with_incremental_finalization():
             ws = torch.empty_like(step.ws_score)
             wa = torch.empty_like(step.ws_att)
             for layer in range(w.layers):
-                L.score_select(d, q[layer], summ[layer], nb, bt, seq, 32, sel_r, cnt_r, ws)
-                L.sparse_attend(d, q[layer], k[layer], v[layer], bt, seq, sel_r, cnt_r, 32, out_r,
-                                wa)
+                L.score_select(d, q[layer], summ[layer], nb, bt, seq, budget, sel_r, cnt_r, ws)
+                L.sparse_attend(d, q[layer], k[layer], v[layer], bt, seq, sel_r, cnt_r, budget,
+                                out_r, wa)
                 torch.cuda.synchronize()
                 assert torch.equal(sel_r, step.sel[layer]) and torch.equal(cnt_r, step.cnt[layer])
                 assert torch.equal(out_r, step.out[layer]), f"replay {t} layer {layer} output"
@@ -117,4 +146,48 @@ def test_decode_graph_with_incremental_finalization():
             for j in range(cur[b] // 16):
                 blk = int(x.block_table[b, j])
                 assert torch.equal(summ[layer, :, blk], ref[layer, :, blk]), (layer, b, j)
-    log(f"[finalize graph] pages completed during decoding: {completed}")
+    log(f"[finalize graph] pages completed during decoding: {completed}; "
+        f"replays checked against the oracle: {oracle_checked}")
+
+
+def _check_against_oracle(d, k, v, q, summ, bt, seq, step, budget, cur, done_now):
+    """The replay's state against the oracle: records of the pages completed
+    in this replay (codes against the oracle's build of the keys now in the
+    cache), the page LSE of every page on the GPU's codes, the selection from
+    the GPU's scores and the output over the GPU's selection."""
+    layers, hkv, nb = summ.shape[0], summ.shape[1], summ.shape[2]
+    hq = q.shape[2]
+    G = hq // hkv
+    btn = bt.cpu().numpy()
+    P = btn.shape[1]
+    kb = from_dev_bf16(k)
+    vb = from_dev_bf16(v)
+    qb = from_dev_bf16(q)
+    recs_all = summ.cpu().numpy()
+    lse = torch.empty((len(cur), hq, P), dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.score_workspace_bytes(d, len(cur), P, 0), dtype=torch.uint8, device="cuda")
+    for layer in range(layers):
+        for b, j in done_now:
+            blk = int(btn[b, j])
+            for g in range(hkv):
+                K = O.bf16_to_f64(kb[layer, blk, g])[None]
+                compare_build_codes(K, recs_all[layer, g, blk][None],
+                                    where=f"finalized layer {layer} b={b} page {j} g={g}")
+        L.score_pages(d, q[layer], summ[layer], nb, bt, seq, lse, ws)
+        torch.cuda.synchronize()
+        for b in range(len(cur)):
+            n = cur[b] // 16
+            for g in range(hkv):
+                qd = O.bf16_to_f64(qb[layer, b, g * G:(g + 1) * G])
+                s_ref = O.score_records(qd, recs_all[layer, g, btn[b, :n]])
+                s_gpu = lse[b, g * G:(g + 1) * G, :n].double().cpu().numpy()
+                assert np.abs(s_gpu - s_ref).max() <= LSE_TOL
+                _, log_m, _ = O.group_mass(s_gpu)
+                c = int(step.cnt[layer, b, g])
+                got = step.sel[layer, b, g, :c].cpu().numpy()
+                check_selection(got, log_m, budget)
+                o_ref, l_ref = O.sparse_attention(qd, kb[layer], vb[layer], btn[b], g, got, cur[b])
+                o_gpu = step.out[layer, b, g * G:(g + 1) * G].float().cpu().numpy()
+                assert np.abs(o_gpu - o_ref).max() <= OUT_TOL
+                assert np.abs(step.out_lse[layer, b, g * G:(g + 1) * G].cpu().numpy()
+                              - l_ref).max() <= LSE_TOL

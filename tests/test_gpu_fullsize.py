@@ -10,6 +10,10 @@ sampled outputs the oracle can compute one by one:
   * summary codes of sampled page-heads against the oracle's build of the
     same keys.
 
+The outputs checked are those of a replay of the captured decode-step graph
+(cleared before the replay), so the graph itself is held to the oracle.  The
+first group's page LSE is checked on every page, the others' on samples.
+
 Also here: the device input generator's recipe statistics, and the captured
 decode-step graph replaying to the eager result."""
 
@@ -58,10 +62,16 @@ def test_full_size_sampled(name):
     summ = torch.empty((1, w.hkv, nb, L.summary_bytes(d)), dtype=torch.uint8, device="cuda")
     L.build_summaries(d, inp.k[0], torch.arange(nb, dtype=torch.int32, device="cuda"), summ[0])
     torch.cuda.synchronize()
-    log(f"[{name}] summaries built; decode step (eager, bench plans)")
+    log(f"[{name}] summaries built; decode step captured in a graph (bench plans), "
+        f"outputs cleared, replayed")
 
     step = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, inp.seq_lens, budget)
-    step.run()
+    step.capture()
+    for t in (step.sel, step.cnt, step.out, step.out_lse):
+        t.fill_(-3)
+    torch.cuda.synchronize()
+    step.replay()
+    torch.cuda.synchronize()
     P = inp.block_table.shape[1]
     lse = torch.empty((w.batch, w.hq, P), dtype=torch.float32, device="cuda")
     sel2 = torch.empty_like(step.sel[0])
@@ -70,13 +80,13 @@ def test_full_size_sampled(name):
                    step.ws_score, page_lse=lse)
     torch.cuda.synchronize()
     assert torch.equal(sel2, step.sel[0]) and torch.equal(cnt2, step.cnt[0]), \
-        "score_select is not repeatable"
+        "the replayed selection differs from an eager score_select"
 
     bt = inp.block_table.cpu().numpy()
     G = w.group
     worst_lse = worst_out = 0.0
     ties = n_cols = n_ex = 0
-    for b, g in _groups(w, rng):
+    for gi, (b, g) in enumerate(_groups(w, rng)):
         n = w.ctx // w.page
         log(f"[{name}] group b={b} kvh={g}")
         q = O.bf16_to_f64(_bits(inp.q[0, b, g * G:(g + 1) * G]))
@@ -84,8 +94,13 @@ def test_full_size_sampled(name):
         c = int(step.cnt[0, b, g])
         got = step.sel[0, b, g, :c].cpu().numpy()
 
-        # page LSE on sampled pages (plus the selected ones)
-        pages = np.unique(np.concatenate([rng.choice(n, 384, replace=False), [0, n - 1], got[:64]]))
+        # page LSE: every page of the first group, sampled pages (plus the
+        # selected ones) of the others
+        if gi == 0:
+            pages = np.arange(n)
+        else:
+            pages = np.unique(np.concatenate([rng.choice(n, 384, replace=False), [0, n - 1],
+                                              got[:64]]))
         blk = torch.from_numpy(bt[b, pages].astype(np.int64)).cuda()
         recs = summ[0, g].index_select(0, blk).cpu().numpy()
         s_ref = O.score_records(q, recs)

@@ -209,7 +209,7 @@ def test_builder_codes(name):
         mu = K.mean(axis=1)
         rmu = raw[blk, g, :128]
         assert np.abs(rmu - mu).max() <= 1e-5 * (1 + np.abs(mu).max())
-    log(f"[{name}] builder: {n_ex}/{n_cols} columns exempt, worst exempt-page recon diff {worst_rec:.3f}")
+    log(f"[{name}] builder: {n_ex}/{n_cols} columns exempt, worst exempt-page residual excess {worst_rec:.2f} e_q")
     assert n_ex <= 0.02 * n_cols
 
 
