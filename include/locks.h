@@ -150,6 +150,36 @@ locks_status locks_decode_layer(const locks_dims* dims, const void* q, const voi
                                 float* out_lse, void* score_ws, size_t score_ws_bytes,
                                 void* attend_ws, size_t attend_ws_bytes, void* stream);
 
+/* locks_decode_layer for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * kernels and outputs as locks_decode_layer (with one workspace), but the
+ * workspace is the library's own device array of LOCKS_NOALLOC_SCRATCH_BYTES
+ * (64 MiB), held by every GPU the library runs on until the process ends.
+ * The call allocates and frees nothing.
+ *   locks_decode_layer_noalloc_bytes : scratch bytes a call with these sizes
+ *     uses (0 for unsupported dims or sizes); at most 64 MiB is accepted:
+ *     about 10 MiB for one 1M-token sequence, 12 MiB for 8 x 128K tokens and
+ *     38 MiB for 16 x 256K tokens (32 query heads, budget 128 pages).
+ *   Larger requests return LOCKS_ERR_WORKSPACE before anything is launched;
+ *   invalid shapes return what locks_decode_layer would.
+ *   The first call on each device looks up that device's array address
+ *   (hipGetSymbolAddress; make it outside graph capture).  Every call on one
+ *   GPU shares that GPU's array and leaves its contents behind: calls that
+ *   may overlap on one GPU (two streams, two threads) race on it and must be
+ *   serialized by the caller.  Nothing in the array needs clearing between
+ *   calls: every byte a call reads it has written first. */
+#define LOCKS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+size_t locks_decode_layer_noalloc_bytes(const locks_dims* dims, int32_t batch, int32_t max_pages,
+                                        int32_t budget_pages);
+locks_status locks_decode_layer_noalloc(const locks_dims* dims, const void* q,
+                                        const void* summaries, const void* k_cache,
+                                        const void* v_cache, locks_kv_layout layout,
+                                        int32_t num_blocks, const int32_t* block_table,
+                                        int32_t max_pages, const int32_t* seq_lens,
+                                        int32_t batch, int32_t budget_pages, float softmax_scale,
+                                        int32_t* sel, int32_t* sel_count, void* out,
+                                        float* out_lse, void* stream);
+
 /* Incremental finalization inside the decode step (sec. 2 implementation:
  * a page is summarized once, when it is finalized, off the critical path).
  * For every sequence b whose length seq_lens[b] is a positive multiple of 16

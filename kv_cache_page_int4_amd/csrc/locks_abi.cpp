@@ -2,6 +2,8 @@
 // Nothing here allocates, synchronizes or touches device memory from the host.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/locks.h"
 #include "locks_internal.h"
 
@@ -326,6 +328,75 @@ locks_status locks_decode_layer_tables(const locks_dims* dims, const void* q,
                            max_pages, seq_lens, batch, budget_pages, n_tables, softmax_scale, sel,
                            sel_count, out, out_lse, score_ws, score_ws_bytes, attend_ws,
                            attend_ws_bytes, stream);
+}
+
+// ---- the decode layer without workspaces ------------------------------------
+// A file-scope device array stands in for the two workspaces.  Its name in
+// host code is only a host-side stand-in, never a device address: the device
+// address comes from hipGetSymbolAddress, once per device (each GPU holds its
+// own copy of the array), and only that address reaches the kernels.
+}  // extern "C"
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)64 << 20;   // LOCKS_NOALLOC_SCRATCH_BYTES
+static_assert(kScratchBytes == LOCKS_NOALLOC_SCRATCH_BYTES, "header and library agree");
+__device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on first use).
+locks_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LOCKS_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return LOCKS_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LOCKS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t locks_decode_layer_noalloc_bytes(const locks_dims* dims, int32_t batch, int32_t max_pages,
+                                        int32_t budget_pages) {
+  if (check_dims(dims) != LOCKS_OK || batch <= 0 || max_pages <= 0 || max_pages > kMaxPages ||
+      budget_pages <= 0)
+    return 0;
+  return align_up(score_ws_layout(dims, batch, max_pages, budget_pages, true).total) +
+         attend_ws_layout(dims, batch, budget_pages + 1).total;
+}
+
+locks_status locks_decode_layer_noalloc(const locks_dims* dims, const void* q,
+                                        const void* summaries, const void* k_cache,
+                                        const void* v_cache, locks_kv_layout layout,
+                                        int32_t num_blocks, const int32_t* block_table,
+                                        int32_t max_pages, const int32_t* seq_lens,
+                                        int32_t batch, int32_t budget_pages, float softmax_scale,
+                                        int32_t* sel, int32_t* sel_count, void* out,
+                                        float* out_lse, void* stream) {
+  const size_t need = locks_decode_layer_noalloc_bytes(dims, batch, max_pages, budget_pages);
+  if (need == 0) {
+    // the shape itself is invalid: report why, as the workspace call would
+    locks_status st = check_dims(dims);
+    return st != LOCKS_OK ? st : LOCKS_ERR_SHAPE;
+  }
+  if (need > kScratchBytes) return LOCKS_ERR_WORKSPACE;
+  void* ws = nullptr;
+  locks_status st = scratch_address(&ws);
+  if (st != LOCKS_OK) return st;
+  return decode_layer_impl(dims, q, summaries, k_cache, v_cache, layout, num_blocks, block_table,
+                           max_pages, seq_lens, batch, budget_pages, dims->num_kv_heads,
+                           softmax_scale, sel, sel_count, out, out_lse, ws, kScratchBytes, nullptr,
+                           0, stream);
 }
 
 locks_status locks_finalize_pages(const locks_dims* dims, const void* k_cache,

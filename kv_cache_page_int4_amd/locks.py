@@ -56,6 +56,9 @@ _SIGS = {
                                    _I32, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "locks_decode_layer": (_I32, [_DP, _P, _P, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32, _I32,
                                   ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
+    "locks_decode_layer_noalloc_bytes": (_SZ, [_DP, _I32, _I32, _I32]),
+    "locks_decode_layer_noalloc": (_I32, [_DP, _P, _P, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32,
+                                          _I32, ctypes.c_float, _P, _P, _P, _P, _P]),
     "locks_finalize_pages": (_I32, [_DP, _P, KVLayout, _I32, _P, _I32, _P, _I32, _P, _I32,
                                     ctypes.c_int64, ctypes.c_int64, _P]),
     "locks_exact_page_lse": (_I32, [_DP, _P, _P, KVLayout, _I32, _P, _I32, _P, _I32,
@@ -394,6 +397,50 @@ def decode_layer(d: Dims, q, summaries, k_cache, v_cache, block_table, seq_lens,
     else:
         _check("locks_decode_layer_tables",
                lib().locks_decode_layer_tables(*head, int(n_tables), *tail))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_layer_noalloc_bytes(d: Dims, batch, max_pages, budget_pages) -> int:
+    return lib().locks_decode_layer_noalloc_bytes(ctypes.byref(d), batch, max_pages, budget_pages)
+
+
+def decode_layer_noalloc(d: Dims, q, summaries, k_cache, v_cache, block_table, seq_lens,
+                         budget_pages, sel, sel_count, out, out_lse=None, softmax_scale=None,
+                         stream=None):
+    """decode_layer without workspaces: the library's own device scratch array
+    (64 MiB per GPU) stands in for them.  Calls that overlap on one GPU race
+    on that array."""
+    B, P, hq = block_table.shape[0], block_table.shape[1], d.num_q_heads
+    _need(q, "q", torch.bfloat16, numel=B * hq * d.head_dim)
+    _need(summaries, "summaries", torch.uint8,
+          numel=d.num_kv_heads * k_cache.shape[0] * _rec_bytes(d))
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(v_cache, "v_cache", torch.bfloat16)
+    _kv_heads(d, k_cache, "k_cache")
+    _kv_heads(d, v_cache, "v_cache")
+    _need(block_table, "block_table", torch.int32, numel=B * P)
+    _need(seq_lens, "seq_lens", torch.int32, numel=B)
+    _need(sel, "sel", torch.int32, numel=B * d.num_kv_heads * budget_pages)
+    _need(sel_count, "sel_count", torch.int32, numel=B * d.num_kv_heads)
+    _need(out, "out", torch.bfloat16, numel=B * hq * d.head_dim)
+    _need(out_lse, "out_lse", torch.float32, numel=B * hq)
+    _on_device(q=q, summaries=summaries, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+               seq_lens=seq_lens, sel=sel, sel_count=sel_count, out=out, out_lse=out_lse)
+    lay = kv_layout(k_cache)
+    lv = kv_layout(v_cache)
+    if (lay.block_stride, lay.head_stride, lay.token_stride) != (
+            lv.block_stride, lv.head_stride, lv.token_stride):
+        raise ValueError("k_cache and v_cache must share one layout")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / (d.head_dim ** 0.5)
+    st = lib().locks_decode_layer_noalloc(
+        ctypes.byref(d), _ptr(q), _ptr(summaries), _ptr(k_cache), _ptr(v_cache), lay,
+        k_cache.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+        block_table.shape[0], budget_pages, float(softmax_scale), _ptr(sel), _ptr(sel_count),
+        _ptr(out), _ptr(out_lse), _stream(stream))
+    _check("locks_decode_layer_noalloc", st)
 
 
 def shared_basis(d: Dims, k_cache, block_ids, basis, eigvals=None, workspace=None, stream=None):
