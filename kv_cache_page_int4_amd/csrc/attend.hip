@@ -4,9 +4,13 @@
 //
 // Split-K: the attended page list of a (sequence, KV head) -- the selected
 // pages in ascending order, then the partial tail page -- is cut into splits
-// of `pages_per_split` pages, one wave each, streamed page by page through
-// LDS (see attend_wave).  The query heads of the group share every K/V load.
-// A second kernel merges the splits by log-sum-exp into bf16 output.
+// of `pages_per_split` pages, one workgroup of 4 waves each; the waves take
+// the split's pages in turn (wave w every 4th from the w-th), stream them
+// page by page through LDS (see attend_wave) and merge their results in LDS
+// into one partial per split.  Workgroups of 4 waves are dispatched 4 times
+// faster than single waves, and the interleaving gives the waves of a split
+// equal shares.  The query heads of the group share every K/V load.  A
+// second kernel merges the splits by log-sum-exp into bf16 output.
 #include "locks_device.h"
 #include "locks_internal.h"
 #include "select_common.h"
@@ -18,7 +22,7 @@ namespace locks {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr long long kAttendWaves = 2048;   // target waves per launch
+constexpr long long kAttendWgs = 512;   // target workgroups (splits) per launch
 
 struct AttendParams {
   const uint16_t* q;
@@ -62,10 +66,14 @@ constexpr int kPageBytes = 2 * kB * kD * 2;   // K then V of one page-head, bf16
 constexpr int kAttRing = 2;                    // LDS page slots per wave: 1 in flight
 constexpr int kRingBytes = kAttRing * kPageBytes;
 
-// One wave's split of the attended page list of (sequence b, KV head kvh):
-// the first `count` entries of `selrow` (logical pages, ascending; nullptr
-// means pages 0..count-1) and then the partial tail page.  `selrow` may point
-// to global memory or to LDS.  `ring` is this wave's LDS (kRingBytes).
+// One wave's share of the attended page list of (sequence b, KV head kvh):
+// the list is the first `count` entries of `selrow` (logical pages,
+// ascending; nullptr means pages 0..count-1) and then the partial tail page;
+// the wave takes its entries e_first, e_first + stride, ... (n_mine of
+// them).  `selrow` may point to global memory or to LDS.  `ring` is this
+// wave's LDS (kRingBytes); when the wave is done it holds the wave's
+// unnormalized output and its (max, sum) per head slot (see wave_result),
+// for the workgroup's merge.
 //
 // The split's block ids and token counts are resolved 64 pages at a time, one
 // page per lane.  Each page-head's keys and values (8 KB) are then copied straight from
@@ -83,8 +91,9 @@ constexpr int kRingBytes = kAttRing * kPageBytes;
 //  * P.V on the vector units: lane l keeps the same 4 tokens and dims
 //    8*(l%16)..+8; the 4 slots' probabilities come from its quad by DPP.
 template <int NSUB>
-__device__ __forceinline__ void attend_wave(const AttendParams& p, int split, int kvh, int b,
-                                            int count, const int32_t* selrow, uint8_t* ring) {
+__device__ __forceinline__ void attend_wave(const AttendParams& p, int kvh, int b, int count,
+                                            const int32_t* selrow, uint8_t* ring, int e_first,
+                                            int stride, int n_mine) {
   const int lane = threadIdx.x & 63;
   const int row = lane >> 4, col = lane & 15, h = lane & 3;
   const int G = p.group;
@@ -92,9 +101,7 @@ __device__ __forceinline__ void attend_wave(const AttendParams& p, int split, in
   int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
   const int n_fin = seq / kB;
   const int tail = seq - n_fin * kB;
-  const int n_att = count + (tail > 0 ? 1 : 0);
-  const int e0 = split * p.pages_per_split;
-  const int n = max(0, min(e0 + p.pages_per_split, n_att) - e0);
+  const int n = n_mine;
 
   float M[NSUB], lsum[NSUB];
   float acc[NSUB][4][8];
@@ -136,13 +143,13 @@ __device__ __forceinline__ void attend_wave(const AttendParams& p, int split, in
     }
     const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
     const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
-    // chunks of up to 64 pages: block id and valid tokens of page
-    // e0 + c0 + lane in lane `lane`
+    // chunks of up to 64 pages: block id and valid tokens of the wave's page
+    // c0 + lane (list entry e_first + (c0 + lane) * stride) in lane `lane`
     for (int c0 = 0; c0 < n; c0 += 64) {
       const int nc = min(64, n - c0);
       int mbid = 0, mnt = 0;
       if (lane < nc) {
-        const int e = e0 + c0 + lane;
+        const int e = e_first + (c0 + lane) * stride;
         int j, nt;
         if (e < count) {
           j = selrow ? selrow[e] : e;
@@ -257,34 +264,96 @@ __device__ __forceinline__ void attend_wave(const AttendParams& p, int split, in
       for (int e = 0; e < 8; ++e) acc[sub][hh][e] = cross_rows_sum(acc[sub][hh][e]);
     lsum[sub] = cross_rows_sum(lsum[sub]);
   }
+  // the wave's result into its own ring (every copy into it has landed and
+  // every read of it has returned): wave_result layout
+  wait_lgkm0();
+  float* res = reinterpret_cast<float*>(ring);
   if (row == 0) {
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) {
-        if (4 * sub + hh >= G) continue;   // a repeated head slot
-        float* o = p.part_o +
-                   (((size_t)b * p.hq + qhead0 + 4 * sub + hh) * p.n_splits + split) * kD + 8 * col;
+        float* o = res + (4 * sub + hh) * kD + 8 * col;
         *reinterpret_cast<float4*>(o) =
             make_float4(acc[sub][hh][0], acc[sub][hh][1], acc[sub][hh][2], acc[sub][hh][3]);
         *reinterpret_cast<float4*>(o + 4) =
             make_float4(acc[sub][hh][4], acc[sub][hh][5], acc[sub][hh][6], acc[sub][hh][7]);
       }
-      if (col < 4 && 4 * sub + col < G)
-        p.part_ml[((size_t)b * p.hq + qhead0 + 4 * sub + col) * p.n_splits + split] =
-            make_float2(M[sub], lsum[sub]);
+      if (col < 4) {
+        res[4 * NSUB * kD + 2 * (4 * sub + col)] = M[sub];
+        res[4 * NSUB * kD + 2 * (4 * sub + col) + 1] = lsum[sub];
+      }
     }
   }
 }
 
-// One wave per workgroup: 16 KB of LDS each, so up to ten waves share a CU.
+// The kWaves waves of a workgroup took interleaved entries of one split of
+// the attended page list; each left its (unnormalized output, max, sum) per
+// head slot in its ring (floats: [slot][128] then (max, sum) per slot).
+// After a barrier the workgroup merges them by log-sum-exp into one partial
+// per real head and split: thread t of the first 256 takes head slot
+// t / 64 (+ 4 per pass) and dims 2 (t % 64), +1.
 template <int NSUB>
-__global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[1][kRingBytes];
-  const int wave = 0;
+__device__ __forceinline__ void wg_merge_store(const AttendParams& p, int split, int kvh, int b,
+                                               const uint8_t* rings) {
+  const int t = threadIdx.x;
+  if (t >= 64 * kWaves) return;
+  const int G = p.group;
+  const int qhead0 = kvh * G;
+  const int d0 = 2 * (t & 63);
+#pragma unroll
+  for (int pass = 0; pass < NSUB; ++pass) {
+    const int slot = 4 * pass + (t >> 6);
+    if (slot >= G) continue;   // a repeated head slot
+    float Mw[kWaves], Lw[kWaves];
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* res = reinterpret_cast<const float*>(rings + w * kRingBytes);
+      Mw[w] = res[4 * NSUB * kD + 2 * slot];
+      Lw[w] = res[4 * NSUB * kD + 2 * slot + 1];
+      Mx = fmaxf(Mx, Mw[w]);
+    }
+    float o0 = 0.f, o1 = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* res = reinterpret_cast<const float*>(rings + w * kRingBytes);
+      const float sc = (Mw[w] == -INFINITY) ? 0.f : fast_exp2(Mw[w] - Mx);
+      const float2 v = *reinterpret_cast<const float2*>(res + slot * kD + d0);
+      o0 = fmaf(sc, v.x, o0);
+      o1 = fmaf(sc, v.y, o1);
+      l = fmaf(sc, Lw[w], l);
+    }
+    const size_t prow = ((size_t)b * p.hq + qhead0 + slot) * p.n_splits + split;
+    *reinterpret_cast<float2*>(p.part_o + prow * kD + d0) = make_float2(o0, o1);
+    if ((t & 63) == 0) p.part_ml[prow] = make_float2(Mx, l);
+  }
+}
+
+// The waves' entries of split `split` of a list of n_att entries: wave w of
+// the workgroup takes entries base + w, base + w + kWaves, ... below the
+// split's end.
+__device__ __forceinline__ void split_share(const AttendParams& p, int split, int n_att, int wave,
+                                            int* e_first, int* n_mine) {
+  const int base = split * p.pages_per_split;
+  const int end = min(base + p.pages_per_split, n_att);
+  *e_first = base + wave;
+  *n_mine = (*e_first < end) ? (end - *e_first + kWaves - 1) / kWaves : 0;
+}
+
+__device__ __forceinline__ int attended_entries(const AttendParams& p, int b, int count) {
+  const int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
+  return count + ((seq % kB) > 0 ? 1 : 0);
+}
+
+// kWaves waves per workgroup, one split each, 16 KB of LDS per wave: two
+// workgroups (eight waves) share a CU.
+template <int NSUB>
+__global__ __launch_bounds__(64 * kWaves) void attend_kernel(AttendParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kRingBytes];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x;
   const int kvh = blockIdx.y, b = blockIdx.z;
-  if (split >= p.n_splits) return;
   int count;
   const int32_t* selrow = nullptr;
   if (p.sel) {
@@ -294,7 +363,11 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   } else {
     count = max(0, min(p.seq_lens[b], p.max_pages * kB)) / kB;
   }
-  attend_wave<NSUB>(p, split, kvh, b, count, selrow, &ring[wave][0]);
+  int e_first, n_mine;
+  split_share(p, split, attended_entries(p, b, count), wave, &e_first, &n_mine);
+  attend_wave<NSUB>(p, kvh, b, count, selrow, &ring[wave][0], e_first, kWaves, n_mine);
+  __syncthreads();
+  wg_merge_store<NSUB>(p, split, kvh, b, &ring[0][0]);
 }
 
 // ---- final selection fused with the attention --------------------------------
@@ -395,10 +468,17 @@ __global__ __launch_bounds__(NT) void select_attend_kernel(AttendParams p, Fused
     for (int s = tid; s < p.budget; s += kFusedThreads) out[s] = (s < k) ? sel_lds[s] : -1;
     if (tid == 0) f.sel_count[grp] = k;
   }
+  // the first kWaves waves attend split blockIdx.x (interleaved entries) and
+  // merge it; the others only pass the barrier
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int split = blockIdx.x * kWaves + wave;
-  if (wave < kWaves && split < p.n_splits)
-    attend_wave<NSUB>(p, split, kvh, b, k, sel_lds, &ring[wave][0]);
+  const int split = blockIdx.x;
+  if (wave < kWaves) {
+    int e_first, n_mine;
+    split_share(p, split, attended_entries(p, b, k), wave, &e_first, &n_mine);
+    attend_wave<NSUB>(p, kvh, b, k, sel_lds, &ring[wave][0], e_first, kWaves, n_mine);
+  }
+  __syncthreads();
+  wg_merge_store<NSUB>(p, split, kvh, b, &ring[0][0]);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp weights of the
@@ -499,7 +579,7 @@ hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
                  plan.pages_per_split, plan.n_splits, ntab, hq / hkv};
   FusedSel f{cand_key, cand_idx, sel, sel_count, sp.n_chunks, sp.slots};
   const int32_t n_cand = sp.n_chunks * sp.slots;
-  dim3 grid((plan.n_splits + kWaves - 1) / kWaves, hkv, batch);
+  dim3 grid(plan.n_splits, hkv, batch);
   const long long wgs = (long long)grid.x * grid.y * grid.z;
   const bool two = p.group > 4;   // two 4-head sub-passes
 #define LOCKS_SA(RUN, NT)                                                                     \
@@ -531,14 +611,14 @@ hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
 }
 
 AttendPlan plan_attend(int32_t batch, int32_t hkv, int32_t max_attended) {
-  // about kAttendWaves waves over all (sequence, KV head) groups (eight per
-  // CU, fewer than the ten that fit, so that no wave waits for a second
-  // round), 2 to 1024 pages each
+  // a split is one workgroup of kWaves waves: about kAttendWgs of them over
+  // all (sequence, KV head) groups (two per CU, so that none waits for a
+  // second round), at least two pages per wave
   AttendPlan pl;
   const long long groups = (long long)batch * hkv;
   const long long total = groups * (long long)max_attended;
-  long long pages = (total + kAttendWaves - 1) / kAttendWaves;
-  pages = std::max(2LL, std::min(1024LL, pages));
+  long long pages = (total + kAttendWgs - 1) / kAttendWgs;
+  pages = std::max(2LL * kWaves, std::min(8192LL, pages));
   pl.pages_per_split = (int32_t)pages;
   pl.n_splits = (int32_t)((max_attended + pages - 1) / pages);
   if (pl.n_splits < 1) pl.n_splits = 1;
@@ -558,9 +638,9 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k_cache, const uint1
                  plan.pages_per_split, plan.n_splits, ntab, hq / hkv};
   dim3 grid(plan.n_splits, hkv, batch);
   if (p.group > 4)
-    hipLaunchKernelGGL(attend_kernel<2>, grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(attend_kernel<2>, grid, dim3(64 * kWaves), 0, stream, p);
   else
-    hipLaunchKernelGGL(attend_kernel<1>, grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(attend_kernel<1>, grid, dim3(64 * kWaves), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attend_merge_kernel, dim3(hq, batch), dim3(kMergeThreads), 0, stream, p);

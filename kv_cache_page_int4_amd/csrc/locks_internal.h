@@ -61,7 +61,7 @@ hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t
 
 // ---- sparse attention ---------------------------------------------------------
 struct AttendPlan {
-  int32_t pages_per_split;  // 2 .. 1024
+  int32_t pages_per_split;  // 8 .. 8192; a split is one workgroup of 4 waves
   int32_t n_splits;         // splits per (sequence, KV head)
 };
 AttendPlan plan_attend(int32_t batch, int32_t hkv, int32_t max_attended);
