@@ -58,23 +58,20 @@ __device__ __forceinline__ int quant(float x, float s, int qmax) {
 }
 
 // Rotation (c, s) that zeroes G[p][q] of the 2x2 block [[app, apq], [apq, aqq]]
-// (classical symmetric Schur decomposition).
+// (classical symmetric Schur decomposition: t = tan of the angle =
+// sign(tau) w / (|tau| + sqrt(tau^2 + w^2)) with tau = aqq - app, w = 2 apq,
+// c = 1 / sqrt(1 + t^2), s = t c), branch-free, with the hardware's
+// reciprocal, square root and reciprocal square root (about 1 ulp each): any
+// rotation near the zeroing one serves Jacobi, which goes on until the
+// off-diagonal mass is negligible, and c^2 + s^2 = 1 holds to a few ulp.
 __device__ __forceinline__ void jacobi_rot(float app, float apq, float aqq, float& c, float& s) {
-  if (fabsf(apq) <= 1e-30f * (fabsf(app) + fabsf(aqq)) || apq == 0.f) {
-    c = 1.f;
-    s = 0.f;
-    return;
-  }
-  const float theta = (aqq - app) / (2.f * apq);
-  float t;
-  if (fabsf(theta) > 1e15f) {
-    t = 0.5f / theta;
-  } else {
-    t = 1.f / (fabsf(theta) + sqrtf(theta * theta + 1.f));
-    if (theta < 0.f) t = -t;
-  }
-  c = 1.f / sqrtf(t * t + 1.f);
-  s = t * c;
+  const bool skip = !(fabsf(apq) > 1e-30f * (fabsf(app) + fabsf(aqq)));   // also apq == 0
+  const float tau = aqq - app, w = 2.f * apq;
+  const float t = (tau < 0.f ? -w : w) *
+                  __builtin_amdgcn_rcpf(fabsf(tau) + __builtin_amdgcn_sqrtf(fmaf(tau, tau, w * w)));
+  const float cc = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f));
+  c = skip ? 1.f : cc;
+  s = skip ? 0.f : t * cc;
 }
 
 // Record of rank R (R = 4, 8, 16): the rank-8 layout with every field sized
@@ -94,7 +91,7 @@ struct BuildSmem {
   float X[kB][kD + 4];     // centered keys
   float G[kB][kB + 1];     // Gram matrix -> eigenvalues on the diagonal
   float U[kB][kB + 1];     // eigenvectors (columns)
-  float cs[8][2];          // rotations of the current step
+  float cs[8][2] __attribute__((aligned(16)));   // rotations of the current step
   float V[R][kD + 4];      // unquantized basis, [k][d]
   float C[kB][R];          // unquantized coefficients
   float mu[kD];
@@ -197,22 +194,46 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     __syncthreads();
 
     // ---- 3. cyclic Jacobi ----
+    // A step m (1..15) rotates the 8 disjoint index pairs (i, i ^ m).  Lane
+    // (ia, ib) owns the 2x2 block of G at row pair ia and column pair ib
+    // (read from and written back to LDS); the diagonal lanes compute their
+    // pair's rotation and publish (c, s) in LDS.  The eigenvector matrix stays
+    // in registers: lane l holds row l % 16 of U and turns it by all 8
+    // rotations of the step, whose column indices are constants once the
+    // steps are unrolled.  The workgroup is one wave (launch bound 64).
     const int ia = lane >> 3, ib = lane & 7;   // row pair, column pair of this lane's block
-    const int urow = lane & 15, upair0 = 2 * (lane >> 4);
+    const int urow = lane & 15;
+    float u[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) u[j] = (j == urow) ? 1.f : 0.f;
     for (int sweep = 0; sweep < kSweeps; ++sweep) {
+      // this lane's pair indices, opaque to the compiler: the block addresses
+      // of the 15 steps are recomputed in every sweep instead of being held
+      // in registers across the sweeps
+      int iav = ia, ibv = ib;
+      asm volatile("" : "+v"(iav), "+v"(ibv));
+#pragma unroll
       for (int m = 1; m < 16; ++m) {
-        const int hb = 31 - __clz(m);
+        const int hb = 31 - __builtin_clz(m);
         auto pair_p = [&](int pi) { return ((pi >> hb) << (hb + 1)) | (pi & ((1 << hb) - 1)); };
-        const int a0 = pair_p(ia), a1 = a0 ^ m, b0 = pair_p(ib), b1 = b0 ^ m;
+        const int a0 = pair_p(iav), a1 = a0 ^ m, b0 = pair_p(ibv), b1 = b0 ^ m;
         const float g00 = sm.G[a0][b0], g01 = sm.G[a0][b1], g10 = sm.G[a1][b0], g11 = sm.G[a1][b1];
-        if (ia == ib) {
+        {
+          // every lane computes (branch-free); the diagonal lanes publish
           float c, s;
           jacobi_rot(g00, 0.5f * (g01 + g10), g11, c, s);
-          sm.cs[ia][0] = c;
-          sm.cs[ia][1] = s;
+          if (ia == ib) *reinterpret_cast<float2*>(sm.cs[ia]) = make_float2(c, s);
         }
-        __syncthreads();
-        const float ca = sm.cs[ia][0], sa = sm.cs[ia][1], cb = sm.cs[ib][0], sb = sm.cs[ib][1];
+        // one wave: its LDS accesses complete in program order, so the reads
+        // below see the rotations just written; only the compiler is kept
+        // from reordering them.  All of the step's rotations are read at once.
+        asm volatile("" ::: "memory");
+        const float2 csa = *reinterpret_cast<const float2*>(sm.cs[ia]);
+        const float2 csb = *reinterpret_cast<const float2*>(sm.cs[ib]);
+        float4 cs4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs4[i] = *reinterpret_cast<const float4*>(&sm.cs[2 * i][0]);
+        const float ca = csa.x, sa = csa.y, cb = csb.x, sb = csb.y;
         // T = G J (columns b0, b1), then G' = J^T T (rows a0, a1)
         const float t00 = g00 * cb - g01 * sb, t01 = g00 * sb + g01 * cb;
         const float t10 = g10 * cb - g11 * sb, t11 = g10 * sb + g11 * cb;
@@ -226,17 +247,22 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
         sm.G[a0][b1] = n01;
         sm.G[a1][b0] = n10;
         sm.G[a1][b1] = n11;
-        // U' = U J for row urow and pairs upair0, upair0 + 1
+        // U' = U J on this lane's row: all 8 rotations
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int pi = upair0 + u;
-          const int p0 = pair_p(pi), p1 = p0 ^ m;
-          const float c = sm.cs[pi][0], s = sm.cs[pi][1];
-          const float up = sm.U[urow][p0], uq = sm.U[urow][p1];
-          sm.U[urow][p0] = c * up - s * uq;
-          sm.U[urow][p1] = s * up + c * uq;
+        for (int k = 0; k < 8; ++k) {
+          const float c = (k & 1) ? cs4[k >> 1].z : cs4[k >> 1].x;
+          const float s = (k & 1) ? cs4[k >> 1].w : cs4[k >> 1].y;
+          const int p0 = pair_p(k), p1 = p0 ^ m;
+          const float up = u[p0], uq = u[p1];
+          u[p0] = c * up - s * uq;
+          u[p1] = s * up + c * uq;
         }
-        __syncthreads();
+        // apply the rotations now: left free, the compiler sinks them to the
+        // end of the sweep and holds all 120 rotations in registers
+        asm volatile("" : "+v"(u[0]), "+v"(u[1]), "+v"(u[2]), "+v"(u[3]), "+v"(u[4]),
+                     "+v"(u[5]), "+v"(u[6]), "+v"(u[7]), "+v"(u[8]), "+v"(u[9]), "+v"(u[10]),
+                     "+v"(u[11]), "+v"(u[12]), "+v"(u[13]), "+v"(u[14]), "+v"(u[15])
+                     :: "memory");
       }
       // converged when the off-diagonal mass is below 1e-12 of the total
       // (off-norm 1e-6 relative: far below what the codes and fp16 scales resolve)
@@ -251,6 +277,10 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
       off = wave_sum(off);
       tot = wave_sum(tot);
       if (!(off > 1e-12f * tot)) break;
+    }
+    if (lane < kB) {
+#pragma unroll
+      for (int j = 0; j < kB; ++j) sm.U[urow][j] = u[j];
     }
 
     // ---- 4. order eigenpairs: descending eigenvalue, ties to the lower index ----
@@ -268,6 +298,9 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     const bool page_has_basis = lam1 > kEpsConst * ksq;
 
     // basis v_k = X^T u_k / |X^T u_k|; lane owns dims 2*lane, 2*lane+1
+    float2 xr[kB];
+#pragma unroll
+    for (int tt = 0; tt < kB; ++tt) xr[tt] = *reinterpret_cast<const float2*>(&sm.X[tt][d0]);
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const int j = sm.order[k];
@@ -276,34 +309,21 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
       float v0 = 0.f, v1 = 0.f;
 #pragma unroll
       for (int tt = 0; tt < kB; ++tt) {
-        const float u = sm.U[tt][j];
-        v0 = fmaf(sm.X[tt][d0], u, v0);
-        v1 = fmaf(sm.X[tt][d0 + 1], u, v1);
+        const float uu = sm.U[tt][j];
+        v0 = fmaf(xr[tt].x, uu, v0);
+        v1 = fmaf(xr[tt].y, uu, v1);
       }
       const float nrm2 = wave_sum(v0 * v0 + v1 * v1);
       const float inv = (keep && nrm2 > 0.f) ? 1.f / sqrtf(nrm2) : 0.f;
       v0 *= inv;
       v1 *= inv;
-      // sign: largest |v| (lowest dim on ties) positive
-      float best = fabsf(v0);
-      int bidx = d0;
-      float bval = v0;
-      if (fabsf(v1) > best) {
-        best = fabsf(v1);
-        bidx = d0 + 1;
-        bval = v1;
-      }
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float ob = __shfl_xor(best, o);
-        const int oi = __shfl_xor(bidx, o);
-        const float ov = __shfl_xor(bval, o);
-        if (ob > best || (ob == best && oi < bidx)) {
-          best = ob;
-          bidx = oi;
-          bval = ov;
-        }
-      }
+      // sign: the largest |v| (lowest dim on ties) is made positive
+      const float a0v = fabsf(v0), a1v = fabsf(v1);
+      const float amax = wave_max(fmaxf(a0v, a1v));
+      const uint32_t cand = (a0v == amax) ? (uint32_t)d0 : (a1v == amax) ? (uint32_t)(d0 + 1) : 0xFFFFu;
+      const int bidx = __builtin_amdgcn_readfirstlane((int)wave_min_u(cand));
+      const float mine = (bidx & 1) ? v1 : v0;
+      const float bval = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), bidx >> 1));
       if (bval < 0.f) {
         v0 = -v0;
         v1 = -v1;
