@@ -280,7 +280,8 @@ void select_chunk_kernel(SelParams p) {
       }
       __syncthreads();
       // four heads at a time; a head past the batch (tables of 1 or 2 heads)
-      // adds -inf, which leaves the key unchanged
+      // reads a real head's scores but gets the normalizer +inf, so it adds
+      // 2^-inf = 0 and leaves the key unchanged
       for (int h0 = hb; h0 < hb + nb; h0 += 4) {
         float sv[4][kPerThread];
         float l2[4];
@@ -289,8 +290,8 @@ void select_chunk_kernel(SelParams p) {
           const bool real = h0 + hh < hb + nb;
           const float* s = p.page_lse + ((size_t)b * p.hq + (real ? h0 + hh : h0)) * p.max_pages;
 #pragma unroll
-          for (int t = 0; t < kPerThread; ++t) sv[hh][t] = real ? s[min(jbase + t, jmax)] : -INFINITY;
-          l2[hh] = real ? l2s[h0 - hb + hh] : 0.f;
+          for (int t = 0; t < kPerThread; ++t) sv[hh][t] = s[min(jbase + t, jmax)];
+          l2[hh] = real ? l2s[h0 - hb + hh] : INFINITY;
         }
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh) {
