@@ -42,13 +42,20 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b-1m")
     ap.add_argument("--small-workload", default="llama8b-32k")
     ap.add_argument("--large-workload", default="llama8b-256k-b16",
                     help="large-batch configuration reported beside the main one")
     ap.add_argument("--no-large", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations (128K x 8, shuffled tables, seeds)")
+    ap.add_argument("--no-finalize", action="store_true",
+                    help="skip the finalization-inclusive step timing")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads for the all-core oracle timing (0: this process's cores, "
+                         "at most 16)")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -62,7 +69,7 @@ def parse():
                     help="layers sampled for the quality report")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run a plain 1 GiB copy kernel (byte-counter calibration)")
-    ap.add_argument("--kernel-reps", type=int, default=3,
+    ap.add_argument("--kernel-reps", type=int, default=5,
                     help="rounds of per-layer scorer / attention launches timed in isolation")
     return ap.parse_args()
 
@@ -145,9 +152,26 @@ def time_step(step, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline(w, inp, summ, budget):
-    """The oracle on every KV head of sequence 0 in layer 0 (one core), scaled
-    to a layer by the number of sequences (exact for batch 1)."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, inp, summ, budget, threads):
+    """The oracle on every KV head of sequence 0 in layer 0, scaled to a layer
+    by the number of sequences (exact for batch 1), timed twice: on one core
+    and with one thread per KV head on up to `threads` cores (numpy releases
+    the interpreter lock inside its array operations).  Each KV head: score
+    its summary records, the GQA share, the top-k, then attention over the
+    selected pages (their keys and values copied from the device between the
+    two timed phases)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -157,46 +181,72 @@ def cpu_baseline(w, inp, summ, budget):
     n = w.pages
     G = w.group
     blk = inp.block_table[0, :n].cpu().numpy()
-    t_sel = t_att = 0.0
-    n_att = 0
-    for g in range(w.hkv):
-        recs = summ[0, g].cpu().numpy()[blk]
-        qbits = inp.q[0, 0, g * G:(g + 1) * G].contiguous().view(torch.int16).cpu().numpy() \
-            .view(np.uint16)
+    recs = [summ[0, g].cpu().numpy()[blk] for g in range(w.hkv)]
+    qbits = [inp.q[0, 0, g * G:(g + 1) * G].contiguous().view(torch.int16).cpu().numpy()
+             .view(np.uint16) for g in range(w.hkv)]
+
+    def select(g):
+        q = O.bf16_to_f64(qbits[g])
+        s = O.score_records(q, recs[g])
+        _, log_m, _ = O.group_mass(s)
+        return O.select_top_pages(log_m, budget)
+
+    def gather(sels):
+        out = []
+        for g, sel in enumerate(sels):
+            ids = torch.as_tensor(blk[sel], device="cuda").long()
+            kb = inp.k[0][ids, g:g + 1].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            vb = inp.v[0][ids, g:g + 1].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            row = np.full(n + 1, -1, dtype=np.int64)
+            row[sel] = np.arange(len(sel))
+            out.append((kb, vb, row, sel))
+        return out
+
+    def attend(g, kv):
+        kb, vb, row, sel = kv
+        O.sparse_attention(O.bf16_to_f64(qbits[g]), kb, vb, row, 0, sel, n * w.page)
+
+    def run(nthreads):
         with threadpool_limits(1):
             t = time.perf_counter()
-            q = O.bf16_to_f64(qbits)
-            s = O.score_records(q, recs)
-            _, log_m, _ = O.group_mass(s)
-            sel = O.select_top_pages(log_m, budget)
-            t_sel += time.perf_counter() - t
-        kmini = inp.k[0][torch.as_tensor(blk[sel], device="cuda").long(), g:g + 1]
-        vmini = inp.v[0][torch.as_tensor(blk[sel], device="cuda").long(), g:g + 1]
-        kb = kmini.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        vb = vmini.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        row = np.full(n + 1, -1, dtype=np.int64)
-        row[sel] = np.arange(len(sel))
+            if nthreads == 1:
+                sels = [select(g) for g in range(w.hkv)]
+            else:
+                with ThreadPoolExecutor(nthreads) as ex:
+                    sels = list(ex.map(select, range(w.hkv)))
+            t_sel = time.perf_counter() - t
+        kvs = gather(sels)
         with threadpool_limits(1):
             t = time.perf_counter()
-            O.sparse_attention(q, kb, vb, row, 0, sel, n * w.page)
-            t_att += time.perf_counter() - t
-        n_att += len(sel)
-    per_layer_us = (t_sel + t_att) * w.batch * 1e6
+            if nthreads == 1:
+                for g in range(w.hkv):
+                    attend(g, kvs[g])
+            else:
+                with ThreadPoolExecutor(nthreads) as ex:
+                    list(ex.map(attend, range(w.hkv), kvs))
+            t_att = time.perf_counter() - t
+        return t_sel + t_att, sum(len(x) for x in sels)
+
+    t1, n_att = run(1)
+    tn, _ = run(threads) if threads > 1 else (t1, n_att)
     scale = f", scaled x{w.batch} (sequences) to one layer" if w.batch > 1 else ""
-    return {"value": per_layer_us, "unit": "us/layer", "cores": 1, "kind": "oracle",
-            "sample": (f"layer 0, sequence 0, all {w.hkv} KV heads of {w.name}: score "
-                       f"{n} summary records per KV head, GQA share, top-{budget}, attend "
-                       f"{n_att} pages in all; measured {(t_sel + t_att):.2f} s on one core"
-                       f"{scale}")}
+    sample = (f"layer 0, sequence 0, all {w.hkv} KV heads of {w.name}: score {n} summary "
+              f"records per KV head, GQA share, top-{budget}, attend {n_att} pages in all; "
+              f"{tn:.2f} s on {threads} threads (one KV head each), {t1:.2f} s on one core"
+              f"{scale}")
+    return {"value": tn * w.batch * 1e6, "unit": "us/layer", "cores": threads, "kind": "oracle",
+            "sample": sample, "cpu_model": _cpu_model(),
+            "one_core": {"value": t1 * w.batch * 1e6, "unit": "us/layer", "cores": 1}}
 
 
-def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps):
+def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps, light=False):
     """The read-every-key comparator and the selection quality of LOCKS
     against it: exact page LSE from the true keys (locks_exact_page_lse),
     the exact top-k from it (locks_select_pages), recall of the LOCKS page
     sets, retention of the planted carrier pages by both selectors, and the
     key-deviation energy captured by the rank-r bases (GPU builder's
-    unquantized output on sampled page-heads)."""
+    unquantized output on sampled page-heads).  light=True leaves out the
+    shared-basis selector."""
     import torch
     from kv_cache_page_int4_amd import locks as L
 
@@ -218,15 +268,16 @@ def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps):
     layers = sorted(set(int(round(i * (w.layers - 1) / max(1, n_layers - 1)))
                         for i in range(min(n_layers, w.layers))))
     inter = tot = inter_sh = 0
-    car_locks = car_exact = car_n = 0
+    car_locks = car_exact = car_both = car_n = 0
     # the shared-basis selector: one pooled basis per (layer, KV head) over
     # every finalized page, summaries in it, then the same scorer and selection
-    fin = torch.cat([inp.block_table[b, :int(inp.seq_lens[b]) // w.page]
-                     for b in range(w.batch)]).unique().to(torch.int32)
-    basis = torch.empty((w.hkv, 8, 128), dtype=torch.float32, device="cuda")
-    eig = torch.empty((w.hkv, 128), dtype=torch.float32, device="cuda")
-    summ_sh = torch.empty((w.hkv, w.num_blocks, L.summary_bytes(d)), dtype=torch.uint8,
-                          device="cuda")
+    if not light:
+        fin = torch.cat([inp.block_table[b, :int(inp.seq_lens[b]) // w.page]
+                         for b in range(w.batch)]).unique().to(torch.int32)
+        basis = torch.empty((w.hkv, 8, 128), dtype=torch.float32, device="cuda")
+        eig = torch.empty((w.hkv, 128), dtype=torch.float32, device="cuda")
+        summ_sh = torch.empty((w.hkv, w.num_blocks, L.summary_bytes(d)), dtype=torch.uint8,
+                              device="cuda")
     sel_sh = torch.empty_like(sel_x)
     cnt_sh = torch.empty_like(cnt_x)
     energy_sh = []
@@ -235,35 +286,39 @@ def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps):
         L.exact_page_lse(d, inp.q[layer], inp.k[layer], inp.block_table, inp.seq_lens, lse)
         L.select_pages(d, lse, inp.seq_lens, budget, sel_x, cnt_x, ws)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        L.shared_basis(d, inp.k[layer], fin, basis, eigvals=eig)
-        torch.cuda.synchronize()
-        shared_ms.append((time.perf_counter() - t0) * 1e3)
-        L.build_summaries_basis(d, inp.k[layer], fin, basis, summ_sh)
-        L.score_select(d, inp.q[layer], summ_sh, w.num_blocks, inp.block_table, inp.seq_lens,
-                       budget, sel_sh, cnt_sh, ws)
-        ev = eig.double()
-        energy_sh.append(float((ev[:, :8].sum(dim=1) / ev.clamp_min(0).sum(dim=1)).mean()))
+        if not light:
+            t0 = time.perf_counter()
+            L.shared_basis(d, inp.k[layer], fin, basis, eigvals=eig)
+            torch.cuda.synchronize()
+            shared_ms.append((time.perf_counter() - t0) * 1e3)
+            L.build_summaries_basis(d, inp.k[layer], fin, basis, summ_sh)
+            L.score_select(d, inp.q[layer], summ_sh, w.num_blocks, inp.block_table, inp.seq_lens,
+                           budget, sel_sh, cnt_sh, ws)
+            ev = eig.double()
+            energy_sh.append(float((ev[:, :8].sum(dim=1) / ev.clamp_min(0).sum(dim=1)).mean()))
         sl = step.sel[layer].cpu().numpy()
         cl = step.cnt[layer].cpu().numpy()
         sx = sel_x.cpu().numpy()
         cx = cnt_x.cpu().numpy()
-        ss = sel_sh.cpu().numpy()
-        cs = cnt_sh.cpu().numpy()
+        ss = sel_sh.cpu().numpy() if not light else None
+        cs = cnt_sh.cpu().numpy() if not light else None
         for b in range(w.batch):
             for g in range(w.hkv):
                 a = set(sl[b, g, :cl[b, g]].tolist())
                 e = set(sx[b, g, :cx[b, g]].tolist())
-                sh = set(ss[b, g, :cs[b, g]].tolist())
                 inter += len(a & e)
-                inter_sh += len(sh & e)
                 tot += len(e)
+                if not light:
+                    inter_sh += len(set(ss[b, g, :cs[b, g]].tolist()) & e)
         for (lay, b, g, page, _slot, _head) in inp.carriers:
             if lay != layer:
                 continue
             car_n += 1
-            car_locks += int(page in set(sl[b, g, :cl[b, g]].tolist()))
-            car_exact += int(page in set(sx[b, g, :cx[b, g]].tolist()))
+            in_l = page in set(sl[b, g, :cl[b, g]].tolist())
+            in_x = page in set(sx[b, g, :cx[b, g]].tolist())
+            car_locks += int(in_l)
+            car_exact += int(in_x)
+            car_both += int(in_l and in_x)
     # energy captured on sampled page-heads of layer 0
     n_smp = min(w.num_blocks, 2048)
     blocks = torch.randperm(w.num_blocks, device="cuda")[:n_smp].to(torch.int32)
@@ -274,22 +329,28 @@ def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps):
     X = K - raw[:, :, None, :128]
     C = raw[:, :, 1152:].reshape(n_smp, w.hkv, 16, 8)
     energy = float(((C * C).sum(dim=(2, 3)) / (X * X).sum(dim=(2, 3)).clamp_min(1e-30)).mean())
-    del tmp, raw, K, X, summ_sh
-    return {"exact_us_per_layer": round(exact_ms * 1e3, 3),
-            "exact_scorer_gbs": round(exact_gbs, 1),
-            "exact_scorer_frac": round(exact_gbs / PEAK_HBM_GBS, 4),
-            "recall_vs_exact": inter / max(tot, 1),
-            "carrier_retention_locks": car_locks / max(car_n, 1),
-            "carrier_retention_exact": car_exact / max(car_n, 1),
-            "carriers": car_n, "layers_sampled": layers,
-            "energy_captured_rank8": round(energy, 4),
-            "shared_basis": {"recall_vs_exact": inter_sh / max(tot, 1),
-                             "energy_captured_rank8": round(sum(energy_sh) / len(energy_sh), 4),
-                             "basis_ms_per_layer": round(sum(shared_ms) / len(shared_ms), 2),
-                             "note": ("one rank-8 basis per (layer, KV head) from the pooled page "
-                                      "deviations, same record size, scorer and selection")},
-            "note": ("exact = top-k from the true-key page LSE (reads every key); recall = "
-                     "fraction of the exact page set LOCKS also selects")}
+    del tmp, raw, K, X
+    rep = {"exact_us_per_layer": round(exact_ms * 1e3, 3),
+           "exact_scorer_gbs": round(exact_gbs, 1),
+           "exact_scorer_frac": round(exact_gbs / PEAK_HBM_GBS, 4),
+           "recall_vs_exact": inter / max(tot, 1),
+           "carrier_retention_locks": car_locks / max(car_n, 1),
+           "carrier_retention_exact": car_exact / max(car_n, 1),
+           "carriers_kept_by_both": car_both, "carriers_kept_by_exact": car_exact,
+           "carriers": car_n, "layers_sampled": layers,
+           "energy_captured_rank8": round(energy, 4),
+           "note": ("exact = top-k from the true-key page LSE (reads every key); recall = "
+                    "fraction of the exact page set LOCKS also selects; carriers kept by exact "
+                    "selection are the ones LOCKS can be asked to keep")}
+    if not light:
+        del summ_sh
+        rep["shared_basis"] = {
+            "recall_vs_exact": inter_sh / max(tot, 1),
+            "energy_captured_rank8": round(sum(energy_sh) / len(energy_sh), 4),
+            "basis_ms_per_layer": round(sum(shared_ms) / len(shared_ms), 2),
+            "note": ("one rank-8 basis per (layer, KV head) from the pooled page deviations, "
+                     "same record size, scorer and selection")}
+    return rep
 
 
 def traffic_if_current(workload):
@@ -309,6 +370,127 @@ def traffic_if_current(workload):
         return None
 
 
+def kernel_rates(w, d, inp, summ, step, budget, reps):
+    """The scorer and the stand-alone attention (with its split merge), each
+    timed in isolation over all layers from one captured graph on its launch
+    stream (`timed`: HIP events around `reps` replays of every layer's
+    launch, back to back).  Returns a dict: mean microseconds per launch and
+    GB/s from the algorithmic bytes (848 per scored page-head, 8192 per
+    attended page-head), and the selected page-heads per layer."""
+    import torch
+    from kv_cache_page_int4_amd import locks as L
+
+    P = inp.block_table.shape[1]
+    lse_buf = torch.empty((w.batch, w.hq, P), dtype=torch.float32, device="cuda")
+
+    def score_all_layers():
+        for layer in range(w.layers):
+            L.score_pages(d, inp.q[layer], summ[layer], w.num_blocks, inp.block_table,
+                          inp.seq_lens, lse_buf, step.ws_score)
+
+    def attend_all_layers():
+        for layer in range(w.layers):
+            L.sparse_attend(d, inp.q[layer], inp.k[layer], inp.v[layer], inp.block_table,
+                            inp.seq_lens, step.sel[layer], step.cnt[layer], budget,
+                            step.out[layer], step.ws_att)
+
+    score_ms = timed(score_all_layers, reps) / w.layers
+    attend_ms = timed(attend_all_layers, reps) / w.layers
+    page_heads = w.batch * w.hkv * w.pages
+    att_units = int(step.cnt.sum().item()) / w.layers
+    del lse_buf
+    return {"score_us": score_ms * 1e3,
+            "score_gbs": page_heads * SCORE_BYTES_PER_PAGE_HEAD / (score_ms * 1e-3) / 1e9,
+            "attend_us": attend_ms * 1e3,
+            "attend_gbs": att_units * ATTEND_BYTES_PER_PAGE_HEAD / (attend_ms * 1e-3) / 1e9,
+            "att_units": att_units, "launches": w.layers * reps}
+
+
+def finalize_timing(w, d, inp, summ, budget, steps, ms_plain):
+    """The step with incremental finalization (per layer, the page the newest
+    token completed is summarized before the layer is scored), timed twice:
+    with the sequence lengths a multiple of 16 (every layer builds one page
+    per sequence and KV head: a step in which a page completes) and one token
+    shorter (nothing to build: the other 15 steps of 16).  The amortized cost
+    is (completing + 15 x other) / 16 against the plain step."""
+    import torch
+    from kv_cache_page_int4_amd.step import DecodeStep
+
+    fin = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, inp.seq_lens, budget,
+                     finalize=True)
+    ms_done = time_step(fin, steps, 2)
+    del fin
+    short = (inp.seq_lens - 1).contiguous()
+    fin2 = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, short, budget,
+                      finalize=True)
+    ms_other = time_step(fin2, steps, 2)
+    plain2 = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, short, budget)
+    ms_plain2 = time_step(plain2, steps, 2)
+    del fin2, plain2
+    torch.cuda.synchronize()
+    amort = (ms_done + 15 * ms_other) / 16
+    return {"completing_step_us_per_layer": round(ms_done * 1e3 / w.layers, 3),
+            "other_step_us_per_layer": round(ms_other * 1e3 / w.layers, 3),
+            "plain_step_us_per_layer": round(ms_plain * 1e3 / w.layers, 3),
+            "plain_step_one_token_short_us_per_layer": round(ms_plain2 * 1e3 / w.layers, 3),
+            "amortized_extra_us_per_step": round((amort - (ms_plain + 15 * ms_plain2) / 16) * 1e3,
+                                                 3),
+            "note": ("per layer, locks_finalize_pages runs after the layer's newest key and "
+                     "before its scorer; completing = every sequence's newest token completes "
+                     "a page (one page per sequence, KV head and layer is summarized), other = "
+                     "nothing to build")}
+
+
+def config_entry(name, args, dense=False, quality_layers=0, finalize=False, **overrides):
+    """Step time, scorer and attention bandwidth (and optionally the dense
+    comparator, the quality report and the finalization cost) of one more
+    configuration, set up after the previous one's buffers are freed."""
+    import torch
+    from kv_cache_page_int4_amd.step import DecodeStep
+    from synth import get_workload
+
+    wl = get_workload(name, **overrides)
+    d3, inp3, summ3, _ = setup(wl)
+    st3 = DecodeStep(d3, inp3.k, inp3.v, summ3, inp3.q, inp3.block_table, inp3.seq_lens,
+                     wl.budget_pages)
+    ms3 = time_step(st3, max(10, args.steps // 2), 2)
+    kr = kernel_rates(wl, d3, inp3, summ3, st3, wl.budget_pages, args.kernel_reps)
+    sc_us, sc_gbs, at_us, at_gbs = kr["score_us"], kr["score_gbs"], kr["attend_us"], kr["attend_gbs"]
+    entry = {"us_per_layer": round(ms3 * 1e3 / wl.layers, 3),
+             "scorer_us": round(sc_us, 3), "scorer_gbs": round(sc_gbs, 1),
+             "scorer_frac": round(sc_gbs / PEAK_HBM_GBS, 4),
+             "attention_us": round(at_us, 3), "attention_gbs": round(at_gbs, 1),
+             "attention_frac": round(at_gbs / PEAK_HBM_GBS, 4),
+             "batch": wl.batch, "ctx": wl.ctx, "layers": wl.layers, "seed": wl.seed,
+             "shuffled_blocks": wl.shuffled_blocks}
+    log(f"[{wl.name}{' shuffled' if wl.shuffled_blocks else ''} seed {wl.seed}] decode step "
+        f"{entry['us_per_layer']:.2f} us/layer; scorer {sc_us:.2f} us = {sc_gbs:.0f} GB/s; "
+        f"attention {at_us:.2f} us = {at_gbs:.0f} GB/s")
+    if dense:
+        dn3 = DecodeStep(d3, inp3.k, inp3.v, summ3, inp3.q, inp3.block_table, inp3.seq_lens,
+                         1, dense=True)
+        dms3 = time_step(dn3, max(2, min(args.steps, 20)), 1)
+        entry["dense_us_per_layer"] = round(dms3 * 1e3 / wl.layers, 3)
+        entry["speedup_vs_dense"] = round(dms3 / ms3, 3)
+        log(f"[{wl.name}] dense {dms3 * 1e3 / wl.layers:.2f} us/layer, "
+            f"speedup {dms3 / ms3:.2f}x")
+        del dn3
+    if finalize:
+        entry["finalize"] = finalize_timing(wl, d3, inp3, summ3, wl.budget_pages,
+                                            max(10, args.steps // 2), ms3)
+        log(f"[{wl.name}] finalization: {entry['finalize']}")
+    if quality_layers:
+        entry["quality"] = quality_report(wl, d3, inp3, summ3, st3, wl.budget_pages,
+                                          quality_layers, args.kernel_reps, light=True)
+        q = entry["quality"]
+        log(f"[{wl.name}] recall vs exact {q['recall_vs_exact']:.4f}; carriers kept: LOCKS "
+            f"{q['carrier_retention_locks']:.3f}, exact {q['carrier_retention_exact']:.3f}, both "
+            f"{q['carriers_kept_by_both']}/{q['carriers_kept_by_exact']} of those exact keeps")
+    del st3, inp3, summ3
+    torch.cuda.empty_cache()
+    return entry
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -317,6 +499,7 @@ def main():
               "supported: the LOCKS decode path here runs on a single MI355X.", flush=True)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     from kv_cache_page_int4_amd import locks as L
@@ -334,10 +517,10 @@ def main():
     torch.cuda.synchronize()
     ms_step = time_step(step, args.steps, args.warmup)
     us_layer = ms_step * 1e3 / w.layers
-    log(f"[{w.name}] decode step {ms_step:.3f} ms = {us_layer:.2f} us/layer")
+    log(f"[{w.name}] decode step {ms_step:.3f} ms = {us_layer:.2f} us/layer "
+        f"({args.steps} timed replays)")
     # spread of single replays, each between its own pair of events (after the
     # timed region, so that the value above is untouched by the extra events)
-    import numpy as np
     per_replay = replay_times(step, args.steps)
     pct = np.percentile(np.array(per_replay) * 1e3 / w.layers, [10, 50, 90])
     step_spread = {"p10": round(float(pct[0]), 3), "p50": round(float(pct[1]), 3),
@@ -345,43 +528,23 @@ def main():
     log(f"[{w.name}] single replays: p10 {pct[0]:.2f}, median {pct[1]:.2f}, p90 {pct[2]:.2f} us/layer")
 
     # --- dominant kernel: the scorer, timed in isolation on the launch stream ---
-    P = inp.block_table.shape[1]
-    lse_buf = torch.empty((w.batch, w.hq, P), dtype=torch.float32, device="cuda")
-
-    def score_all_layers():
-        for layer in range(w.layers):
-            L.score_pages(d, inp.q[layer], summ[layer], w.num_blocks, inp.block_table,
-                          inp.seq_lens, lse_buf, step.ws_score)
-
-    score_ms = timed(score_all_layers, args.kernel_reps) / w.layers
+    kr = kernel_rates(w, d, inp, summ, step, budget, args.kernel_reps)
+    score_us, score_gbs = kr["score_us"], kr["score_gbs"]
+    attend_us, attend_gbs, att_units = kr["attend_us"], kr["attend_gbs"], kr["att_units"]
     page_heads = w.batch * w.hkv * w.pages
-    score_gbs = page_heads * SCORE_BYTES_PER_PAGE_HEAD / (score_ms * 1e-3) / 1e9
-
-    def attend_all_layers():
-        for layer in range(w.layers):
-            L.sparse_attend(d, inp.q[layer], inp.k[layer], inp.v[layer], inp.block_table,
-                            inp.seq_lens, step.sel[layer], step.cnt[layer], budget,
-                            step.out[layer], step.ws_att)
-
-    attend_ms = timed(attend_all_layers, args.kernel_reps) / w.layers
-
-    # incremental finalization as it sits at the head of a decode step: every
-    # sequence's length is a multiple of 16 here, so one launch rebuilds one
-    # page per (layer, sequence, KV head)
-    def finalize_all_layers():
-        L.finalize_pages(d, inp.k, inp.block_table, inp.seq_lens, summ)
-
-    finalize_ms = timed(finalize_all_layers, args.kernel_reps)
-    att_units = int(step.cnt.sum().item()) / w.layers
-    attend_gbs = att_units * ATTEND_BYTES_PER_PAGE_HEAD / (attend_ms * 1e-3) / 1e9
-    log(f"[{w.name}] scorer {score_ms * 1e3:.2f} us/launch = {score_gbs:.0f} GB/s; "
-        f"attention {attend_ms * 1e3:.2f} us/launch = {attend_gbs:.0f} GB/s")
+    log(f"[{w.name}] scorer {score_us:.2f} us/launch = {score_gbs:.0f} GB/s; "
+        f"attention {attend_us:.2f} us/launch = {attend_gbs:.0f} GB/s")
 
     extra = {}
+    if not args.no_finalize:
+        extra["finalize"] = finalize_timing(w, d, inp, summ, budget, max(10, args.steps // 2),
+                                            ms_step)
+        log(f"[{w.name}] finalization: {extra['finalize']}")
+
     if not args.no_dense:
         dense = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, inp.seq_lens, 1,
                            dense=True)
-        dense_ms = time_step(dense, max(2, args.steps // 5), 1)
+        dense_ms = time_step(dense, max(2, min(args.steps, 20)), 1)
         extra["dense_us_per_layer"] = dense_ms * 1e3 / w.layers
         extra["speedup_vs_dense"] = dense_ms / ms_step
         dense_bytes = w.batch * w.hkv * w.pages * ATTEND_BYTES_PER_PAGE_HEAD
@@ -443,7 +606,7 @@ def main():
                 L.build_summaries(dr, inp.k[layer], blocks, summ_r[layer])
             st_r = DecodeStep(dr, inp.k[:nl], inp.v[:nl], summ_r, inp.q[:nl], inp.block_table,
                               inp.seq_lens, budget)
-            ms_r = time_step(st_r, max(4, args.steps), 2)
+            ms_r = time_step(st_r, max(4, args.steps // 2), 2)
             inter = tot = 0
             for layer in range(nl):
                 for b in range(w.batch):
@@ -494,82 +657,38 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp, summ, budget)
-        log(f"[{w.name}] oracle {cpu['value']:.0f} us/layer on {cpu['cores']} core")
+        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        cpu = cpu_baseline(w, inp, summ, budget, threads)
+        log(f"[{w.name}] oracle {cpu['value']:.0f} us/layer on {cpu['cores']} threads, "
+            f"{cpu['one_core']['value']:.0f} us/layer on one core ({cpu['cpu_model']})")
 
     also = {}
-    del step
+    del step, inp, summ
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        # the main workload with a shuffled block table (records and K/V pages
+        # at random physical blocks), then seeds 1 and 2
+        also[f"{w.name}-shuffled"] = config_entry(args.workload, args, shuffled_blocks=True)
+        for seed in (1, 2):
+            also[f"{w.name}-seed{seed}"] = config_entry(args.workload, args, seed=seed)
     if not args.no_large and args.large_workload:
-        # the large-batch configuration, after the main one's buffers are freed
-        del inp, summ, lse_buf
-        torch.cuda.empty_cache()
-        wl = get_workload(args.large_workload)
-        d3, inp3, summ3, _ = setup(wl)
-        st3 = DecodeStep(d3, inp3.k, inp3.v, summ3, inp3.q, inp3.block_table, inp3.seq_lens,
-                         wl.budget_pages)
-        ms3 = time_step(st3, max(5, args.steps // 2), 2)
-        P3 = inp3.block_table.shape[1]
-        lse3 = torch.empty((wl.batch, wl.hq, P3), dtype=torch.float32, device="cuda")
-
-        def score_large():
-            for layer in range(wl.layers):
-                L.score_pages(d3, inp3.q[layer], summ3[layer], wl.num_blocks, inp3.block_table,
-                              inp3.seq_lens, lse3, st3.ws_score)
-
-        sc3 = timed(score_large, args.kernel_reps) / wl.layers
-
-        def attend_large():
-            for layer in range(wl.layers):
-                L.sparse_attend(d3, inp3.q[layer], inp3.k[layer], inp3.v[layer],
-                                inp3.block_table, inp3.seq_lens, st3.sel[layer], st3.cnt[layer],
-                                wl.budget_pages, st3.out[layer], st3.ws_att)
-
-        at3 = timed(attend_large, args.kernel_reps) / wl.layers
-        att3_units = int(st3.cnt.sum().item()) / wl.layers
-        ph3 = wl.batch * wl.hkv * wl.pages
-        entry = {"us_per_layer": round(ms3 * 1e3 / wl.layers, 3),
-                 "scorer_us": round(sc3 * 1e3, 3),
-                 "scorer_gbs": round(ph3 * SCORE_BYTES_PER_PAGE_HEAD / (sc3 * 1e-3) / 1e9, 1),
-                 "attention_us": round(at3 * 1e3, 3),
-                 "attention_gbs": round(att3_units * ATTEND_BYTES_PER_PAGE_HEAD
-                                        / (at3 * 1e-3) / 1e9, 1),
-                 "batch": wl.batch, "ctx": wl.ctx, "layers": wl.layers}
-        entry["scorer_frac"] = round(entry["scorer_gbs"] / PEAK_HBM_GBS, 4)
-        entry["attention_frac"] = round(entry["attention_gbs"] / PEAK_HBM_GBS, 4)
-        log(f"[{wl.name}] decode step {ms3 * 1e3 / wl.layers:.2f} us/layer; scorer "
-            f"{sc3 * 1e3:.2f} us = {entry['scorer_gbs']:.0f} GB/s; attention "
-            f"{at3 * 1e3:.2f} us = {entry['attention_gbs']:.0f} GB/s")
-        del st3
-        if not args.no_dense:
-            dn3 = DecodeStep(d3, inp3.k, inp3.v, summ3, inp3.q, inp3.block_table, inp3.seq_lens,
-                             1, dense=True)
-            dms3 = time_step(dn3, 2, 1)
-            entry["dense_us_per_layer"] = round(dms3 * 1e3 / wl.layers, 3)
-            entry["speedup_vs_dense"] = round(dms3 / ms3, 3)
-            log(f"[{wl.name}] dense {dms3 * 1e3 / wl.layers:.2f} us/layer, "
-                f"speedup {dms3 / ms3:.2f}x")
-            del dn3
-        also[wl.name] = entry
-        del inp3, summ3, lse3
-        torch.cuda.empty_cache()
+        also[args.large_workload] = config_entry(
+            args.large_workload, args, dense=not args.no_dense,
+            quality_layers=0 if args.no_quality else 2)
+    if not args.no_configs:
+        also["llama8b-128k-b8"] = config_entry("llama8b-128k-b8", args,
+                                               quality_layers=0 if args.no_quality else 2)
     if not args.no_small and args.small_workload:
-        ws = get_workload(args.small_workload)
-        d2, inp2, summ2, _ = setup(ws)
-        st2 = DecodeStep(d2, inp2.k, inp2.v, summ2, inp2.q, inp2.block_table, inp2.seq_lens,
-                         ws.budget_pages)
-        ms2 = time_step(st2, max(args.steps, 50), args.warmup)
-        also[ws.name] = {"us_per_layer": ms2 * 1e3 / ws.layers,
-                         "note": "working set fits the 256 MB Infinity Cache; latency-bound"}
-        log(f"[{ws.name}] decode step {ms2 * 1e3:.2f} us/layer")
-        if not args.no_dense:
-            dn2 = DecodeStep(d2, inp2.k, inp2.v, summ2, inp2.q, inp2.block_table, inp2.seq_lens,
-                             1, dense=True)
-            dms2 = time_step(dn2, max(args.steps, 50), args.warmup)
-            also[ws.name]["dense_us_per_layer"] = round(dms2 * 1e3 / ws.layers, 3)
-            also[ws.name]["speedup_vs_dense"] = round(dms2 / ms2, 3)
-            log(f"[{ws.name}] dense {dms2 * 1e3 / ws.layers:.2f} us/layer, speedup "
-                f"{dms2 / ms2:.2f}x")
-            del dn2
+        ent = config_entry(args.small_workload, args, dense=not args.no_dense,
+                           quality_layers=0 if args.no_quality else 1,
+                           finalize=not args.no_finalize)
+        ent["note"] = "working set fits the 256 MB Infinity Cache; latency-bound"
+        also[args.small_workload] = ent
+        if not args.no_configs:
+            for seed in (1, 2):
+                also[f"{args.small_workload}-seed{seed}"] = config_entry(
+                    args.small_workload, args, quality_layers=0 if args.no_quality else 1,
+                    seed=seed)
 
     result = {
         "metric": METRIC,
@@ -588,22 +707,25 @@ def main():
         "config": {"workload": w.name, "layers": w.layers, "batch": w.batch, "ctx": w.ctx,
                    "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d, "page": w.page,
                    "rank": w.rank, "budget_tokens": w.budget_tokens,
-                   "carriers_per_kv_head": w.carriers, "graph": "one hipGraph per step"},
+                   "carriers_per_kv_head": w.carriers, "seed": w.seed,
+                   "graph": "one hipGraph per step"},
         "roofline": {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(score_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic_if_current(w.name), "kernel": "score_kernel",
-                     "kernel_us": round(score_ms * 1e3, 3),
-                     "bytes_per_launch": page_heads * SCORE_BYTES_PER_PAGE_HEAD},
+                     "kernel_us": round(score_us, 3),
+                     "launches_timed": kr["launches"],
+                     "bytes_per_launch": page_heads * SCORE_BYTES_PER_PAGE_HEAD,
+                     "timing": ("HIP events on the launch stream around graph replays of every "
+                                "layer's locks_score_pages launch, back to back")},
         "attention": {"achieved": round(attend_gbs, 1), "unit": "GB/s",
                       "frac": round(attend_gbs / PEAK_HBM_GBS, 4),
-                      "kernel_us": round(attend_ms * 1e3, 3),
+                      "kernel_us": round(attend_us, 3),
                       "note": ("attention + split merge, selected K/V bytes only; "
                                f"{att_units * ATTEND_BYTES_PER_PAGE_HEAD / 2**20:.1f} MiB per "
                                "layer is latency-bound, see also.*.attention_gbs for the "
                                "large-batch rate")},
-        "finalize_us_per_step": round(finalize_ms * 1e3, 3),
         "stream_read_gbs": round(stream_read_gbs, 1),
-        "pages_scored_per_s": page_heads / (score_ms * 1e-3),
+        "pages_scored_per_s": page_heads / (score_us * 1e-6),
         "build_page_heads_per_s": w.layers * w.num_blocks * w.hkv / (build_ms * 1e-3),
         "cpu_baseline": cpu,
         "quality": quality,
