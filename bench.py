@@ -57,6 +57,9 @@ def parse():
                     help="threads for the all-core oracle timing (0: this process's cores, "
                          "at most 16)")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--shuffled", action="store_true",
+                    help="main workload with a shuffled block table (pages at random blocks)")
+    ap.add_argument("--seed", type=int, default=None, help="override the workload seed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
@@ -510,6 +513,10 @@ def main():
     w = get_workload(args.workload)
     if args.layers:
         w = w.with_(layers=args.layers)
+    if args.shuffled:
+        w = w.with_(shuffled_blocks=True)
+    if args.seed is not None:
+        w = w.with_(seed=args.seed)
     d, inp, summ, build_ms = setup(w)
     budget = w.budget_pages
 
@@ -708,6 +715,7 @@ def main():
                    "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d, "page": w.page,
                    "rank": w.rank, "budget_tokens": w.budget_tokens,
                    "carriers_per_kv_head": w.carriers, "seed": w.seed,
+                   "shuffled_blocks": w.shuffled_blocks,
                    "graph": "one hipGraph per step"},
         "roofline": {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(score_gbs / PEAK_HBM_GBS, 4),
