@@ -231,6 +231,7 @@ def cpu_baseline(w, inp, summ, budget, threads):
         return t_sel + t_att, sum(len(x) for x in sels)
 
     t1, n_att = run(1)
+    threads = min(threads, w.hkv)     # one task per KV head: more threads would sit idle
     tn, _ = run(threads) if threads > 1 else (t1, n_att)
     scale = f", scaled x{w.batch} (sequences) to one layer" if w.batch > 1 else ""
     sample = (f"layer 0, sequence 0, all {w.hkv} KV heads of {w.name}: score {n} summary "
