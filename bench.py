@@ -411,38 +411,46 @@ def kernel_rates(w, d, inp, summ, step, budget, reps):
 
 
 def finalize_timing(w, d, inp, summ, budget, steps, ms_plain):
-    """The step with incremental finalization (per layer, the page the newest
-    token completed is summarized before the layer is scored), timed twice:
-    with the sequence lengths a multiple of 16 (every layer builds one page
-    per sequence and KV head: a step in which a page completes) and one token
-    shorter (nothing to build: the other 15 steps of 16).  The amortized cost
-    is (completing + 15 x other) / 16 against the plain step."""
+    """The step with incremental finalization, in both forms: "step" (the
+    pages the step's token completed are summarized after the step, all
+    layers in one launch, with the newest page pending during it) and "layer"
+    (each layer's page is summarized before that layer is scored).  Each is
+    timed with the sequence lengths a multiple of 16 (every layer builds one
+    page per sequence and KV head: a step in which a page completes) and one
+    token shorter (nothing to build: the other 15 steps of 16).  The
+    amortized cost is (completing + 15 x other) / 16 against the plain step."""
     import torch
     from kv_cache_page_int4_amd.step import DecodeStep
 
-    fin = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, inp.seq_lens, budget,
-                     finalize=True)
-    ms_done = time_step(fin, steps, 2)
-    del fin
     short = (inp.seq_lens - 1).contiguous()
-    fin2 = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, short, budget,
-                      finalize=True)
-    ms_other = time_step(fin2, steps, 2)
     plain2 = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, short, budget)
     ms_plain2 = time_step(plain2, steps, 2)
-    del fin2, plain2
-    torch.cuda.synchronize()
-    amort = (ms_done + 15 * ms_other) / 16
-    return {"completing_step_us_per_layer": round(ms_done * 1e3 / w.layers, 3),
+    del plain2
+    base = (ms_plain + 15 * ms_plain2) / 16
+    res = {"plain_step_us_per_layer": round(ms_plain * 1e3 / w.layers, 3),
+           "plain_step_one_token_short_us_per_layer": round(ms_plain2 * 1e3 / w.layers, 3)}
+    for mode in ("step", "layer"):
+        fin = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, inp.seq_lens, budget,
+                         finalize=mode)
+        ms_done = time_step(fin, steps, 2)
+        del fin
+        fin2 = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, short, budget,
+                          finalize=mode)
+        ms_other = time_step(fin2, steps, 2)
+        del fin2
+        torch.cuda.synchronize()
+        amort = (ms_done + 15 * ms_other) / 16
+        res["after_step" if mode == "step" else "per_layer"] = {
+            "completing_step_us_per_layer": round(ms_done * 1e3 / w.layers, 3),
             "other_step_us_per_layer": round(ms_other * 1e3 / w.layers, 3),
-            "plain_step_us_per_layer": round(ms_plain * 1e3 / w.layers, 3),
-            "plain_step_one_token_short_us_per_layer": round(ms_plain2 * 1e3 / w.layers, 3),
-            "amortized_extra_us_per_step": round((amort - (ms_plain + 15 * ms_plain2) / 16) * 1e3,
-                                                 3),
-            "note": ("per layer, locks_finalize_pages runs after the layer's newest key and "
-                     "before its scorer; completing = every sequence's newest token completes "
-                     "a page (one page per sequence, KV head and layer is summarized), other = "
-                     "nothing to build")}
+            "amortized_extra_us_per_step": round((amort - base) * 1e3, 3)}
+    res["note"] = ("after_step: the pages a step's token completes are summarized after the "
+                   "step, every layer in one launch, and the step runs with the newest page "
+                   "pending (attended in full); per_layer: each layer's page is summarized "
+                   "after the layer's newest key and before its scorer.  completing = every "
+                   "sequence's newest token completes a page (one page per sequence, KV head "
+                   "and layer is summarized), other = nothing to build")
+    return res
 
 
 def config_entry(name, args, dense=False, quality_layers=0, finalize=False, **overrides):
@@ -482,7 +490,7 @@ def config_entry(name, args, dense=False, quality_layers=0, finalize=False, **ov
     if finalize:
         entry["finalize"] = finalize_timing(wl, d3, inp3, summ3, wl.budget_pages,
                                             max(10, args.steps // 2), ms3)
-        log(f"[{wl.name}] finalization: {entry['finalize']}")
+        log(f"[{wl.name}] finalization: { {k: v for k, v in entry['finalize'].items() if k != 'note'} }")
     if quality_layers:
         entry["quality"] = quality_report(wl, d3, inp3, summ3, st3, wl.budget_pages,
                                           quality_layers, args.kernel_reps, light=True)
@@ -547,7 +555,7 @@ def main():
     if not args.no_finalize:
         extra["finalize"] = finalize_timing(w, d, inp, summ, budget, max(10, args.steps // 2),
                                             ms_step)
-        log(f"[{w.name}] finalization: {extra['finalize']}")
+        log(f"[{w.name}] finalization: { {k: v for k, v in extra['finalize'].items() if k != 'note'} }")
 
     if not args.no_dense:
         dense = DecodeStep(d, inp.k, inp.v, summ, inp.q, inp.block_table, inp.seq_lens, 1,

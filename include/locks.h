@@ -54,7 +54,20 @@ typedef struct {
   int32_t head_dim;     /* d (128)                                 */
   int32_t page_size;    /* B, tokens per KV page (16)              */
   int32_t rank;         /* r, basis vectors per page summary (4, 8 or 16) */
+  int32_t newest_page_pending; /* 0 or 1, see below                  */
 } locks_dims;
+
+/* Summarized pages.  With newest_page_pending = 0 the summarized (finalized)
+ * pages of a sequence of n tokens are its n / 16 full pages, and the n % 16
+ * tokens after them (the partial tail page) are attended in full, outside
+ * the budget.  With newest_page_pending = 1 the page that holds the newest
+ * token is not summarized yet even when it is full: the summarized pages are
+ * the first (n - 1) / 16, and the 1 to 16 tokens after them are attended in
+ * full.  This is the decode step whose pages are summarized off its critical
+ * path (sec. 2 implementation): a page completed by the step's token is
+ * summarized after the step (locks_finalize_pages on the new lengths) and
+ * selected from the next step on.  Every call that scores, selects or
+ * attends reads the flag the same way; the builders ignore it. */
 
 /* Element strides (bf16 elements) of one layer's paged K or V cache:
  * element (block, kv_head, token, dim) sits at

@@ -3,7 +3,8 @@
 // attends the same page set).
 //
 // Split-K: the attended page list of a (sequence, KV head) -- the selected
-// pages in ascending order, then the partial tail page -- is cut into splits
+// pages in ascending order, then the tail page (the tokens after the
+// summarized pages, attended in full) -- is cut into splits
 // of `pages_per_split` pages, one workgroup of 4 waves each; the waves take
 // the split's pages in turn (wave w every 4th from the w-th), stream them
 // page by page through LDS (see attend_wave) and merge their results in LDS
@@ -41,6 +42,7 @@ struct AttendParams {
   int32_t num_blocks, max_pages, budget, hq, hkv, pages_per_split, n_splits;
   int32_t ntab;   // selection tables per sequence; KV head kvh reads table kvh / (hkv / ntab)
   int32_t group;  // query heads per KV head (1, 2, 4 or 8)
+  int32_t pending;  // 1: the page holding the newest token is not summarized
 };
 
 // Global -> LDS copy of 16 bytes per lane: lane l writes LDS bytes
@@ -68,7 +70,7 @@ constexpr int kRingBytes = kAttRing * kPageBytes;
 
 // One wave's share of the attended page list of (sequence b, KV head kvh):
 // the list is the first `count` entries of `selrow` (logical pages,
-// ascending; nullptr means pages 0..count-1) and then the partial tail page;
+// ascending; nullptr means pages 0..count-1) and then the tail page;
 // the wave takes its entries e_first, e_first + stride, ... (n_mine of
 // them).  `selrow` may point to global memory or to LDS.  `ring` is this
 // wave's LDS (kRingBytes); when the wave is done it holds the wave's
@@ -99,8 +101,8 @@ __device__ __forceinline__ void attend_wave(const AttendParams& p, int kvh, int 
   const int G = p.group;
   const int qhead0 = kvh * G;
   int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
-  const int n_fin = seq / kB;
-  const int tail = seq - n_fin * kB;
+  const int n_fin = summarized_pages(seq, p.pending);
+  const int tail = seq - n_fin * kB;   // tokens attended in full (up to 16)
   const int n = n_mine;
 
   float M[NSUB], lsum[NSUB];
@@ -343,7 +345,7 @@ __device__ __forceinline__ void split_share(const AttendParams& p, int split, in
 
 __device__ __forceinline__ int attended_entries(const AttendParams& p, int b, int count) {
   const int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
-  return count + ((seq % kB) > 0 ? 1 : 0);
+  return count + (seq > summarized_pages(seq, p.pending) * kB ? 1 : 0);
 }
 
 // kWaves waves per workgroup, one split each, 16 KB of LDS per wave: two
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_kernel(AttendParams p) {
     count = max(0, min(p.sel_count[tab], p.budget));
     selrow = p.sel + tab * p.budget;
   } else {
-    count = max(0, min(p.seq_lens[b], p.max_pages * kB)) / kB;
+    count = summarized_pages(max(0, min(p.seq_lens[b], p.max_pages * kB)), p.pending);
   }
   int e_first, n_mine;
   split_share(p, split, attended_entries(p, b, count), wave, &e_first, &n_mine);
@@ -568,15 +570,15 @@ hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
                                 int64_t head_stride, int64_t token_stride, int32_t num_blocks,
                                 const int32_t* block_table, int32_t max_pages,
                                 const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
-                                int32_t ntab, const uint32_t* cand_key, const int32_t* cand_idx,
-                                const SelectPlan& sp, int32_t* sel, int32_t* sel_count,
-                                int32_t budget_pages, float scale, float* part_o,
-                                float2* part_ml, const AttendPlan& plan, uint16_t* out,
-                                float* out_lse, hipStream_t stream) {
+                                int32_t ntab, int32_t pending, const uint32_t* cand_key,
+                                const int32_t* cand_idx, const SelectPlan& sp, int32_t* sel,
+                                int32_t* sel_count, int32_t budget_pages, float scale,
+                                float* part_o, float2* part_ml, const AttendPlan& plan,
+                                uint16_t* out, float* out_lse, hipStream_t stream) {
   AttendParams p{q, k_cache, v_cache, block_stride, head_stride, token_stride, block_table,
                  seq_lens, sel, sel_count, part_o, part_ml, out, out_lse,
                  scale * kLog2e, num_blocks, max_pages, budget_pages, hq, hkv,
-                 plan.pages_per_split, plan.n_splits, ntab, hq / hkv};
+                 plan.pages_per_split, plan.n_splits, ntab, hq / hkv, pending};
   FusedSel f{cand_key, cand_idx, sel, sel_count, sp.n_chunks, sp.slots};
   const int32_t n_cand = sp.n_chunks * sp.slots;
   dim3 grid(plan.n_splits, hkv, batch);
@@ -629,13 +631,14 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k_cache, const uint1
                          int64_t block_stride, int64_t head_stride, int64_t token_stride,
                          int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
                          const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
-                         int32_t ntab, const int32_t* sel, const int32_t* sel_count, int32_t budget_pages,
-                         float scale, float* part_o, float2* part_ml, const AttendPlan& plan,
-                         uint16_t* out, float* out_lse, hipStream_t stream) {
+                         int32_t ntab, int32_t pending, const int32_t* sel,
+                         const int32_t* sel_count, int32_t budget_pages, float scale,
+                         float* part_o, float2* part_ml, const AttendPlan& plan, uint16_t* out,
+                         float* out_lse, hipStream_t stream) {
   AttendParams p{q, k_cache, v_cache, block_stride, head_stride, token_stride, block_table,
                  seq_lens, sel, sel_count, part_o, part_ml, out, out_lse,
                  scale * kLog2e, num_blocks, max_pages, budget_pages, hq, hkv,
-                 plan.pages_per_split, plan.n_splits, ntab, hq / hkv};
+                 plan.pages_per_split, plan.n_splits, ntab, hq / hkv, pending};
   dim3 grid(plan.n_splits, hkv, batch);
   if (p.group > 4)
     hipLaunchKernelGGL(attend_kernel<2>, grid, dim3(64 * kWaves), 0, stream, p);

@@ -39,6 +39,7 @@ struct ExactParams {
   float scale2;   // softmax scale * log2(e)
   int32_t num_blocks, max_pages, hq, hkv, n_wg;
   int32_t group;   // query heads per KV head (1, 2, 4 or 8)
+  int32_t pending; // 1: the page holding the newest token is not summarized
 };
 
 // NSUB: 4-head sub-passes (2 for a group of 8 heads, else 1).
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(64) void exact_lse_kernel(ExactParams p) {
 
   int seq = p.seq_lens[b];
   seq = max(0, min(seq, p.max_pages * kB));
-  const int n_fin = seq / kB;
+  const int n_fin = summarized_pages(seq, p.pending);
   const int j0 = w * kExactPages;                          // first page of this workgroup
   const int n = max(0, min(kExactPages, n_fin - j0));     // its pages
   __shared__ __attribute__((aligned(16))) float outl[kSlots][kExactPages];
@@ -151,12 +152,12 @@ hipError_t launch_exact_lse(const uint16_t* q, const uint16_t* k_cache, int64_t 
                             int64_t head_stride, int64_t token_stride, int32_t num_blocks,
                             const int32_t* block_table, int32_t max_pages,
                             const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
-                            float scale, float* page_lse, hipStream_t stream) {
+                            int32_t pending, float scale, float* page_lse, hipStream_t stream) {
   // kExactPages pages per wave: many short waves keep the end-of-launch tail small
   const int32_t W = std::max(1, (max_pages + kExactPages - 1) / kExactPages);
   const int32_t group = hq / hkv;
   ExactParams p{q, k_cache, block_stride, head_stride, token_stride, block_table, seq_lens,
-                page_lse, scale * kLog2e, num_blocks, max_pages, hq, hkv, W, group};
+                page_lse, scale * kLog2e, num_blocks, max_pages, hq, hkv, W, group, pending};
   if (group > 4)
     hipLaunchKernelGGL(exact_lse_kernel<2>, dim3(W, hkv, batch), dim3(64), 0, stream, p);
   else

@@ -23,6 +23,7 @@ locks_status check_dims(const locks_dims* d) {
   if (d->num_q_heads % d->num_kv_heads) return LOCKS_ERR_UNSUPPORTED;
   const int32_t g = d->num_q_heads / d->num_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8) return LOCKS_ERR_UNSUPPORTED;
+  if (d->newest_page_pending != 0 && d->newest_page_pending != 1) return LOCKS_ERR_SHAPE;
   return LOCKS_OK;
 }
 
@@ -155,7 +156,8 @@ locks_status locks_score_pages(const locks_dims* dims, const void* q, const void
   if (!workspace || workspace_bytes < w.total) return LOCKS_ERR_WORKSPACE;
   hipError_t e = launch_score(dims->rank, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
                               num_blocks, block_table, max_pages, seq_lens, batch,
-                              dims->num_q_heads, dims->num_kv_heads, kDefaultScale, page_lse,
+                              dims->num_q_heads, dims->num_kv_heads, dims->newest_page_pending,
+                              kDefaultScale, page_lse,
                               reinterpret_cast<float2*>(ws_at(workspace, w.part_off)), w.sp,
                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
@@ -176,10 +178,11 @@ static locks_status select_pages_impl(const locks_dims* dims, const float* page_
   if (!workspace || workspace_bytes < w.total) return LOCKS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float2* part = reinterpret_cast<float2*>(ws_at(workspace, w.part_off));
-  hipError_t e = launch_lse_partials(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, part,
-                                     w.sel.n_chunks, w.sel.chunk_pages, s);
+  const int32_t pend = dims->newest_page_pending;
+  hipError_t e = launch_lse_partials(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, pend,
+                                     part, w.sel.n_chunks, w.sel.chunk_pages, s);
   if (e == hipSuccess)
-    e = launch_select(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, n_tables,
+    e = launch_select(page_lse, max_pages, seq_lens, batch, dims->num_q_heads, n_tables, pend,
                       budget_pages, part, w.sel.n_chunks,
                       reinterpret_cast<uint32_t*>(ws_at(workspace, w.key_off)),
                       reinterpret_cast<int32_t*>(ws_at(workspace, w.idx_off)), w.sel, sel,
@@ -221,11 +224,11 @@ locks_status locks_score_select(const locks_dims* dims, const void* q, const voi
   float2* part = reinterpret_cast<float2*>(ws_at(workspace, w.part_off));
   hipError_t e = launch_score(dims->rank, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
                               num_blocks, block_table, max_pages, seq_lens, batch,
-                              dims->num_q_heads, dims->num_kv_heads, kDefaultScale, lse, part,
-                              w.sp, s);
+                              dims->num_q_heads, dims->num_kv_heads, dims->newest_page_pending,
+                              kDefaultScale, lse, part, w.sp, s);
   if (e == hipSuccess)
     e = launch_select(lse, max_pages, seq_lens, batch, dims->num_q_heads, dims->num_kv_heads,
-                      budget_pages, part, w.sp.n_chunks,
+                      dims->newest_page_pending, budget_pages, part, w.sp.n_chunks,
                       reinterpret_cast<uint32_t*>(ws_at(workspace, w.key_off)),
                       reinterpret_cast<int32_t*>(ws_at(workspace, w.idx_off)), w.sel, sel,
                       sel_count, s);
@@ -271,32 +274,33 @@ static locks_status decode_layer_impl(const locks_dims* dims, const void* q,
   float* po = reinterpret_cast<float*>(ws_at(attend_ws, a.o_off));
   float2* pml = reinterpret_cast<float2*>(ws_at(attend_ws, a.ml_off));
   const int hq = dims->num_q_heads, hkv = dims->num_kv_heads;
+  const int32_t pend = dims->newest_page_pending;
   // pages are scored at the temperature they are attended with
   hipError_t e = launch_score(dims->rank, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
-                              num_blocks, block_table, max_pages, seq_lens, batch, hq, hkv,
+                              num_blocks, block_table, max_pages, seq_lens, batch, hq, hkv, pend,
                               softmax_scale, lse, part, w.sp, s);
   if (e != hipSuccess) return LOCKS_ERR_LAUNCH;
   const int32_t n_cand = w.sel.n_chunks * w.sel.slots;
   if (fused_select_attend_fits(n_cand, budget_pages)) {
-    e = launch_select_stage1(lse, max_pages, seq_lens, batch, hq, n_tables, budget_pages, part,
-                             w.sp.n_chunks, ck, ci, w.sel, s);
+    e = launch_select_stage1(lse, max_pages, seq_lens, batch, hq, n_tables, pend, budget_pages,
+                             part, w.sp.n_chunks, ck, ci, w.sel, s);
     if (e == hipSuccess)
       e = launch_select_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                                static_cast<const uint16_t*>(v_cache), layout.block_stride,
                                layout.head_stride, layout.token_stride, num_blocks, block_table,
-                               max_pages, seq_lens, batch, hq, hkv, n_tables, ck, ci, w.sel, sel,
-                               sel_count,
-                               budget_pages, softmax_scale, po, pml, a.ap,
+                               max_pages, seq_lens, batch, hq, hkv, n_tables, pend, ck, ci, w.sel,
+                               sel, sel_count, budget_pages, softmax_scale, po, pml, a.ap,
                                static_cast<uint16_t*>(out), out_lse, s);
   } else {
-    e = launch_select(lse, max_pages, seq_lens, batch, hq, n_tables, budget_pages, part,
+    e = launch_select(lse, max_pages, seq_lens, batch, hq, n_tables, pend, budget_pages, part,
                       w.sp.n_chunks, ck, ci, w.sel, sel, sel_count, s);
     if (e == hipSuccess)
       e = launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                         static_cast<const uint16_t*>(v_cache), layout.block_stride,
                         layout.head_stride, layout.token_stride, num_blocks, block_table,
-                        max_pages, seq_lens, batch, hq, hkv, n_tables, sel, sel_count, budget_pages,
-                        softmax_scale, po, pml, a.ap, static_cast<uint16_t*>(out), out_lse, s);
+                        max_pages, seq_lens, batch, hq, hkv, n_tables, pend, sel, sel_count,
+                        budget_pages, softmax_scale, po, pml, a.ap, static_cast<uint16_t*>(out),
+                        out_lse, s);
   }
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
 }
@@ -445,7 +449,8 @@ locks_status locks_exact_page_lse(const locks_dims* dims, const void* q, const v
                                   static_cast<const uint16_t*>(k_cache), layout.block_stride,
                                   layout.head_stride, layout.token_stride, num_blocks, block_table,
                                   max_pages, seq_lens, batch, dims->num_q_heads,
-                                  dims->num_kv_heads, softmax_scale, page_lse,
+                                  dims->num_kv_heads, dims->newest_page_pending, softmax_scale,
+                                  page_lse,
                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;
 }
@@ -481,8 +486,8 @@ static locks_status sparse_attend_impl(const locks_dims* dims, const void* q,
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
       static_cast<const uint16_t*>(v_cache), layout.block_stride, layout.head_stride,
       layout.token_stride, num_blocks, block_table, max_pages, seq_lens, batch, dims->num_q_heads,
-      dims->num_kv_heads, n_tables, sel, sel_count, budget_pages, softmax_scale,
-      reinterpret_cast<float*>(ws_at(workspace, w.o_off)),
+      dims->num_kv_heads, n_tables, dims->newest_page_pending, sel, sel_count, budget_pages,
+      softmax_scale, reinterpret_cast<float*>(ws_at(workspace, w.o_off)),
       reinterpret_cast<float2*>(ws_at(workspace, w.ml_off)), w.ap, static_cast<uint16_t*>(out),
       out_lse, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_LAUNCH;

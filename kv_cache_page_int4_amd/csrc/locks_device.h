@@ -14,6 +14,14 @@ constexpr int kOffV = 0, kOffC = 512, kOffMu = 640, kOffSv = 768, kOffSc = 784, 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Pages of a sequence of `seq` tokens (clamped to its table) whose summaries
+// are in use: every full page, or, when the newest page is pending, every
+// page before the one that holds the newest token.  The tokens after them
+// (0..15 of them, or 1..16 when pending) are attended in full.
+__device__ __forceinline__ int summarized_pages(int seq, int pending) {
+  return seq > 0 ? (seq - pending) / kB : 0;
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 

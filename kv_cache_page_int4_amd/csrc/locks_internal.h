@@ -24,8 +24,9 @@ ScorePlan plan_score(int32_t batch, int32_t hkv, int32_t max_pages);
 
 hipError_t launch_score(int32_t rank, const uint16_t* q, const uint8_t* summ, int32_t num_blocks,
                         const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
-                        int32_t batch, int32_t hq, int32_t hkv, float scale, float* page_lse,
-                        float2* partials, const ScorePlan& plan, hipStream_t stream);
+                        int32_t batch, int32_t hq, int32_t hkv, int32_t pending, float scale,
+                        float* page_lse, float2* partials, const ScorePlan& plan,
+                        hipStream_t stream);
 
 // ---- selection -------------------------------------------------------------
 constexpr int32_t kSelChunk = 2048;   // pages per first-stage select workgroup (at least)
@@ -39,25 +40,27 @@ SelectPlan plan_select(int32_t max_pages, int32_t budget_pages, int64_t groups);
 
 // Per-head (max, sum) base-2 partials straight from page scores.
 hipError_t launch_lse_partials(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
-                               int32_t batch, int32_t hq, float2* partials, int32_t n_chunks,
-                               int32_t pages_per_chunk, hipStream_t stream);
+                               int32_t batch, int32_t hq, int32_t pending, float2* partials,
+                               int32_t n_chunks, int32_t pages_per_chunk, hipStream_t stream);
 
 // Selection runs per (sequence, table): `ntab` tables per sequence, each over
-// hq / ntab query heads (ntab = hkv: one table per KV head).
+// hq / ntab query heads (ntab = hkv: one table per KV head).  `pending` = 1:
+// the page holding each sequence's newest token is not summarized (every
+// kernel of the path reads the page count the same way).
 //
 // Stage 1 only: every chunk's candidates (page order); each chunk workgroup
 // merges the per-head (max, sum) partials into the normalizers it needs.
 hipError_t launch_select_stage1(const float* page_lse, int32_t max_pages,
                                 const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t ntab,
-                                int32_t budget_pages, const float2* partials,
+                                int32_t pending, int32_t budget_pages, const float2* partials,
                                 int32_t n_partials, uint32_t* cand_key,
                                 int32_t* cand_idx, const SelectPlan& plan, hipStream_t stream);
 
 hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
-                         int32_t batch, int32_t hq, int32_t ntab, int32_t budget_pages,
-                         const float2* partials, int32_t n_partials, uint32_t* cand_key,
-                         int32_t* cand_idx, const SelectPlan& plan, int32_t* sel,
-                         int32_t* sel_count, hipStream_t stream);
+                         int32_t batch, int32_t hq, int32_t ntab, int32_t pending,
+                         int32_t budget_pages, const float2* partials, int32_t n_partials,
+                         uint32_t* cand_key, int32_t* cand_idx, const SelectPlan& plan,
+                         int32_t* sel, int32_t* sel_count, hipStream_t stream);
 
 // ---- sparse attention ---------------------------------------------------------
 struct AttendPlan {
@@ -70,10 +73,10 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k_cache, const uint1
                          int64_t block_stride, int64_t head_stride, int64_t token_stride,
                          int32_t num_blocks, const int32_t* block_table, int32_t max_pages,
                          const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
-                         int32_t ntab, const int32_t* sel, const int32_t* sel_count,
-                         int32_t budget_pages,
-                         float scale, float* part_o, float2* part_ml, const AttendPlan& plan,
-                         uint16_t* out, float* out_lse, hipStream_t stream);
+                         int32_t ntab, int32_t pending, const int32_t* sel,
+                         const int32_t* sel_count, int32_t budget_pages, float scale,
+                         float* part_o, float2* part_ml, const AttendPlan& plan, uint16_t* out,
+                         float* out_lse, hipStream_t stream);
 
 // Final selection stage fused with the attention (candidates from stage 1).
 constexpr int32_t kFusedMaxBudget = 1024;
@@ -83,11 +86,11 @@ hipError_t launch_select_attend(const uint16_t* q, const uint16_t* k_cache,
                                 int64_t head_stride, int64_t token_stride, int32_t num_blocks,
                                 const int32_t* block_table, int32_t max_pages,
                                 const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
-                                int32_t ntab, const uint32_t* cand_key, const int32_t* cand_idx,
-                                const SelectPlan& sp, int32_t* sel, int32_t* sel_count,
-                                int32_t budget_pages, float scale, float* part_o,
-                                float2* part_ml, const AttendPlan& plan, uint16_t* out,
-                                float* out_lse, hipStream_t stream);
+                                int32_t ntab, int32_t pending, const uint32_t* cand_key,
+                                const int32_t* cand_idx, const SelectPlan& sp, int32_t* sel,
+                                int32_t* sel_count, int32_t budget_pages, float scale,
+                                float* part_o, float2* part_ml, const AttendPlan& plan,
+                                uint16_t* out, float* out_lse, hipStream_t stream);
 
 // ---- shared basis (the rejected baseline, for comparison) ------------------------
 constexpr int32_t kSharedMaxChunks = 64;   // partial 128x128 sums per KV head
@@ -116,7 +119,7 @@ hipError_t launch_exact_lse(const uint16_t* q, const uint16_t* k_cache, int64_t 
                             int64_t head_stride, int64_t token_stride, int32_t num_blocks,
                             const int32_t* block_table, int32_t max_pages,
                             const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t hkv,
-                            float scale, float* page_lse, hipStream_t stream);
+                            int32_t pending, float scale, float* page_lse, hipStream_t stream);
 
 // ---- summary build -----------------------------------------------------------
 hipError_t launch_build(int32_t rank, const uint16_t* k_cache, int64_t block_stride,

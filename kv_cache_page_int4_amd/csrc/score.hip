@@ -110,6 +110,7 @@ struct ScoreParams {
   float c0;   // logit scale times log2(e): base-2 logits
   int32_t num_blocks, max_pages, hq, hkv, n_wg;
   int32_t group;   // query heads per KV head (1, 2, 4 or 8)
+  int32_t pending; // 1: the page holding the newest token is not summarized
 };
 
 // Global -> LDS copy of 16 bytes per active lane: lane l writes LDS bytes
@@ -159,7 +160,7 @@ score_kernel(ScoreParams p) {
 
   int seq = p.seq_lens[b];
   seq = max(0, min(seq, p.max_pages * kB));
-  const int n_fin = seq / kB;
+  const int n_fin = summarized_pages(seq, p.pending);
   const int nsteps = (n_fin + 3) / 4;
   const int s0 = (g * kScoreWaves + wv) * kScoreSteps;    // first step of this wave
   const int n = max(0, min(kScoreSteps, nsteps - s0));    // its steps
@@ -461,11 +462,12 @@ ScorePlan plan_score(int32_t batch, int32_t hkv, int32_t max_pages) {
 
 hipError_t launch_score(int32_t rank, const uint16_t* q, const uint8_t* summ, int32_t num_blocks,
                         const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
-                        int32_t batch, int32_t hq, int32_t hkv, float scale, float* page_lse,
-                        float2* partials, const ScorePlan& plan, hipStream_t stream) {
+                        int32_t batch, int32_t hq, int32_t hkv, int32_t pending, float scale,
+                        float* page_lse, float2* partials, const ScorePlan& plan,
+                        hipStream_t stream) {
   const int32_t group = hq / hkv;
   ScoreParams p{q, summ, block_table, seq_lens, page_lse, partials, scale * kLog2e, num_blocks,
-                max_pages, hq, hkv, plan.n_chunks, group};
+                max_pages, hq, hkv, plan.n_chunks, group, pending};
   dim3 grid(plan.n_chunks, hkv, batch);
   const dim3 blk(64 * kScoreWaves);
   const bool two = group > 4;   // two 4-head sub-passes

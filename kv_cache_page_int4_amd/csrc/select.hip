@@ -40,10 +40,10 @@ constexpr long long kSelOneRound = 512;
 
 __global__ __launch_bounds__(kSelThreads) void lse_partials_kernel(
     const float* page_lse, int32_t max_pages, const int32_t* seq_lens, int32_t hq,
-    float2* partials, int32_t n_chunks, int32_t pages_per_chunk) {
+    int32_t pending, float2* partials, int32_t n_chunks, int32_t pages_per_chunk) {
   const int chunk = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   int seq = max(0, min(seq_lens[b], max_pages * kB));
-  const int n_fin = seq / kB;
+  const int n_fin = summarized_pages(seq, pending);
   const float* s = page_lse + ((size_t)b * hq + head) * max_pages;
   float m = -INFINITY, sm = 0.f;
   const int j0 = chunk * pages_per_chunk, j1 = min(n_fin, j0 + pages_per_chunk);
@@ -72,6 +72,7 @@ struct SelParams {
   int32_t* sel_count;
   // ntab: selection tables per sequence; a table holds hq / ntab query heads
   int32_t max_pages, hq, ntab, budget, n_chunks, slots;
+  int32_t pending;   // 1: the page holding the newest token is not summarized
 };
 
 // Stage 2 over candidates held in registers: thread t owns the contiguous
@@ -236,7 +237,7 @@ void select_chunk_kernel(SelParams p) {
   const int tid = threadIdx.x;
   const int hpt = p.hq / p.ntab;   // query heads of this table
   int seq = max(0, min(p.seq_lens[b], p.max_pages * kB));
-  const int n_fin = seq / kB;
+  const int n_fin = summarized_pages(seq, p.pending);
 
   __shared__ int hist[2][256];
   __shared__ int sh[2][4];
@@ -379,20 +380,21 @@ SelectPlan plan_select(int32_t max_pages, int32_t budget_pages, int64_t groups) 
 }
 
 hipError_t launch_lse_partials(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
-                               int32_t batch, int32_t hq, float2* partials, int32_t n_chunks,
-                               int32_t pages_per_chunk, hipStream_t stream) {
+                               int32_t batch, int32_t hq, int32_t pending, float2* partials,
+                               int32_t n_chunks, int32_t pages_per_chunk, hipStream_t stream) {
   hipLaunchKernelGGL(lse_partials_kernel, dim3(n_chunks, hq, batch), dim3(kSelThreads), 0, stream,
-                     page_lse, max_pages, seq_lens, hq, partials, n_chunks, pages_per_chunk);
+                     page_lse, max_pages, seq_lens, hq, pending, partials, n_chunks,
+                     pages_per_chunk);
   return hipGetLastError();
 }
 
 hipError_t launch_select_stage1(const float* page_lse, int32_t max_pages,
                                 const int32_t* seq_lens, int32_t batch, int32_t hq, int32_t ntab,
-                                int32_t budget_pages, const float2* partials,
+                                int32_t pending, int32_t budget_pages, const float2* partials,
                                 int32_t n_partials, uint32_t* cand_key,
                                 int32_t* cand_idx, const SelectPlan& plan, hipStream_t stream) {
   SelParams p{page_lse, seq_lens, partials, n_partials, cand_key, cand_idx, nullptr, nullptr,
-              max_pages, hq, ntab, budget_pages, plan.n_chunks, plan.slots};
+              max_pages, hq, ntab, budget_pages, plan.n_chunks, plan.slots, pending};
   const dim3 grid(plan.n_chunks, ntab, batch);
   if (plan.chunk_pages > kSelChunk)
     hipLaunchKernelGGL(select_chunk_kernel<2 * kSelChunk / kSelThreads>, grid, dim3(kSelThreads), 0,
@@ -404,15 +406,16 @@ hipError_t launch_select_stage1(const float* page_lse, int32_t max_pages,
 }
 
 hipError_t launch_select(const float* page_lse, int32_t max_pages, const int32_t* seq_lens,
-                         int32_t batch, int32_t hq, int32_t ntab, int32_t budget_pages,
-                         const float2* partials, int32_t n_partials, uint32_t* cand_key,
-                         int32_t* cand_idx, const SelectPlan& plan, int32_t* sel,
-                         int32_t* sel_count, hipStream_t stream) {
-  hipError_t e = launch_select_stage1(page_lse, max_pages, seq_lens, batch, hq, ntab, budget_pages,
-                                      partials, n_partials, cand_key, cand_idx, plan, stream);
+                         int32_t batch, int32_t hq, int32_t ntab, int32_t pending,
+                         int32_t budget_pages, const float2* partials, int32_t n_partials,
+                         uint32_t* cand_key, int32_t* cand_idx, const SelectPlan& plan,
+                         int32_t* sel, int32_t* sel_count, hipStream_t stream) {
+  hipError_t e = launch_select_stage1(page_lse, max_pages, seq_lens, batch, hq, ntab, pending,
+                                      budget_pages, partials, n_partials, cand_key, cand_idx,
+                                      plan, stream);
   if (e != hipSuccess) return e;
   SelParams p{page_lse, seq_lens, partials, n_partials, cand_key, cand_idx, sel, sel_count,
-              max_pages, hq, ntab, budget_pages, plan.n_chunks, plan.slots};
+              max_pages, hq, ntab, budget_pages, plan.n_chunks, plan.slots, pending};
   const int per = (plan.n_chunks * plan.slots + kSelThreads - 1) / kSelThreads;
   if (per <= 8)
     hipLaunchKernelGGL(select_merge_kernel<8>, dim3(ntab, batch), dim3(kSelThreads), 0, stream, p);

@@ -28,7 +28,7 @@ class LocksError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
-                ("rank", ctypes.c_int32)]
+                ("rank", ctypes.c_int32), ("newest_page_pending", ctypes.c_int32)]
 
 
 class KVLayout(ctypes.Structure):
@@ -101,8 +101,12 @@ def _check(fn, st):
         raise LocksError(fn, st)
 
 
-def dims(num_q_heads, num_kv_heads, head_dim=128, page_size=16, rank=8) -> Dims:
-    return Dims(num_q_heads, num_kv_heads, head_dim, page_size, rank)
+def dims(num_q_heads, num_kv_heads, head_dim=128, page_size=16, rank=8,
+         newest_page_pending=False) -> Dims:
+    """newest_page_pending: the page holding each sequence's newest token is
+    not summarized yet (attended in full instead), as in a decode step whose
+    completed pages are summarized after it."""
+    return Dims(num_q_heads, num_kv_heads, head_dim, page_size, rank, int(bool(newest_page_pending)))
 
 
 def _ptr(t):

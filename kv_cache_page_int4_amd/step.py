@@ -4,15 +4,24 @@ The decode step (technical summary sec. 2, implementation paragraph: scoring,
 selection and sparse attention run inside one full graph with no Python
 dispatch) is, per layer, locks_decode_layer (locks_score_select followed by
 locks_sparse_attend, with the last selection stage inside the attention).
-With finalize=True each layer first calls locks_finalize_pages for that
-layer, which builds the summary of any page that the newest token completed
-(decided on the device, so the same graph serves every step).  In a model the
-newest token's key of layer l is written during layer l, so the page it
-completes can be summarized only after that write and before the layer's
-scorer: per layer, not once for all layers at the start of the step.  An
-optional before_layer(l) callback, recorded into the graph too, stands for
-the model's work that precedes layer l's attention (appending the token's
-key and value, for instance).
+
+Incremental finalization (a page is summarized once, when the token that
+fills it arrives, off the decode critical path) comes in two forms:
+
+  * finalize="step" (or True): the page that the step's token completes is
+    summarized after the step, for every layer in one launch, and selected
+    from the next step on.  During the step the page that holds the newest
+    token is not summarized yet, so the step's calls run with
+    newest_page_pending = 1: that page is attended in full, as the tail, and
+    the build is off the step's critical path.
+  * finalize="layer": the page is summarized inside the step, per layer,
+    before that layer is scored (newest_page_pending = 0).  In a model the
+    newest token's key of layer l is written during layer l, so the build of
+    that layer's page sits on the layer's path.
+
+An optional before_layer(l) callback, recorded into the graph too, stands for
+the model's work that precedes layer l's attention (appending the token's key
+and value, for instance).
 This module only allocates the per-layer outputs and the workspaces, issues
 the library calls in order on the current stream and records them into a
 torch.cuda.CUDAGraph (a hipGraph on ROCm).  Layers run in sequence because in
@@ -28,10 +37,12 @@ class DecodeStep:
     """k, v: bf16 [layers, blocks, hkv, 16, 128]; summaries: uint8
     [layers, hkv, blocks, record bytes]; q: bf16 [layers, batch, hq, 128];
     block_table: int32 [batch, max_pages]; seq_lens: int32 [batch].
-    dense=True attends every finalized page instead (no scoring/selection);
-    finalize=True summarizes, per layer, the page the newest token completed
-    before that layer is scored; before_layer(layer) is called (and captured)
-    at the head of every layer;
+    dense=True attends every summarized page instead (no scoring/selection);
+    finalize="step" (or True) summarizes the pages the step's token completed
+    after the step, all layers in one launch, and runs the step's calls with
+    the newest page pending; finalize="layer" summarizes them per layer before
+    the layer is scored; before_layer(layer) is called (and captured) at the
+    head of every layer;
     fused=True issues each layer as one locks_decode_layer call (the last
     selection stage runs inside the attention kernel), fused=False as
     locks_score_select + locks_sparse_attend.  n_tables sets the number of
@@ -40,9 +51,16 @@ class DecodeStep:
 
     def __init__(self, d, k, v, summaries, q, block_table, seq_lens, budget_pages, dense=False,
                  finalize=False, fused=True, n_tables=None, before_layer=None):
+        if finalize is True:
+            finalize = "step"
+        if finalize not in (False, None, "step", "layer"):
+            raise ValueError(f"finalize must be False, True, 'step' or 'layer', not {finalize!r}")
+        if finalize == "step":   # the step's newest page is summarized after it
+            d = L.dims(d.num_q_heads, d.num_kv_heads, d.head_dim, d.page_size, d.rank,
+                       newest_page_pending=True)
         self.d, self.k, self.v, self.summ, self.q = d, k, v, summaries, q
         self.bt, self.seq, self.budget, self.dense = block_table, seq_lens, budget_pages, dense
-        self.finalize = finalize
+        self.finalize = finalize or False
         self.before_layer = before_layer
         self.fused = fused
         self.n_tables = n_tables
@@ -71,7 +89,7 @@ class DecodeStep:
         d = self.d
         if self.before_layer is not None:
             self.before_layer(layer)
-        if self.finalize:   # the page this layer's newest key completed, if any
+        if self.finalize == "layer":   # the page this layer's newest key completed, if any
             L.finalize_pages(d, self.k[layer], self.bt, self.seq, self.summ[layer], stream=stream)
         if not self.dense and self.fused:
             L.decode_layer(d, self.q[layer], self.summ[layer], self.k[layer], self.v[layer],
@@ -97,6 +115,8 @@ class DecodeStep:
     def run(self):
         for layer in range(self.layers):
             self.run_layer(layer)
+        if self.finalize == "step":    # every layer's completed page, off the step's path
+            L.finalize_pages(self.d, self.k, self.bt, self.seq, self.summ)
 
     def capture(self):
         """Record one full step into a graph (after one eager warm-up run)."""

@@ -28,6 +28,11 @@ Readings where the pages are silent:
     ties to the lower page index, returned in ascending page order.
   * Sparse attention is an ordinary softmax renormalized over the selected
     pages' tokens plus the partial (unsummarized) tail page.
+  * When the page holding the newest token is pending (its summary is built
+    after the decode step, off the step's critical path: [P1] sec. 2,
+    implementation), the summarized pages are the first (n - 1) // 16 of a
+    sequence of n tokens, and the 1..16 tokens after them are attended in
+    full, as the tail page.
 """
 
 import numpy as np
@@ -443,12 +448,21 @@ def attention(q, K, V, scale=None):
     return p @ np.asarray(V, np.float64), lse
 
 
-def gather_pages(cache_layer, block_row, kvh, pages, seq_len, page=PAGE):
-    """Tokens of the given logical pages plus the partial tail page.
+def summarized_pages(seq_len, pending=0, page=PAGE):
+    """Pages of a sequence of seq_len tokens whose summaries are in use: every
+    full page, or, with pending=1, every page before the one holding the
+    newest token."""
+    return (seq_len - pending) // page if seq_len > 0 else 0
+
+
+def gather_pages(cache_layer, block_row, kvh, pages, seq_len, page=PAGE, pending=0):
+    """Tokens of the given logical pages plus the tail page.
 
     cache_layer: bf16 bits [num_blocks, hkv, page, d]; returns float64 [T, d].
-    The tail page (tokens past the last full page) is always appended."""
-    n_fin = seq_len // page
+    The tail page (the tokens past the summarized pages: the partial last
+    page, or with pending=1 the whole page holding the newest token) is
+    always appended."""
+    n_fin = summarized_pages(seq_len, pending, page)
     tail = seq_len - n_fin * page
     parts = [bf16_to_f64(cache_layer[block_row[j], kvh]) for j in pages]
     if tail:
@@ -458,11 +472,12 @@ def gather_pages(cache_layer, block_row, kvh, pages, seq_len, page=PAGE):
     return np.concatenate(parts, axis=0)
 
 
-def sparse_attention(q, k_layer, v_layer, block_row, kvh, pages, seq_len, scale=None):
+def sparse_attention(q, k_layer, v_layer, block_row, kvh, pages, seq_len, scale=None,
+                     pending=0):
     """Attention of the group's heads q [G, d] restricted to the selected
     pages' tokens plus the tail page.  Returns (out [G, d], lse [G])."""
-    K = gather_pages(k_layer, block_row, kvh, pages, seq_len)
-    V = gather_pages(v_layer, block_row, kvh, pages, seq_len)
+    K = gather_pages(k_layer, block_row, kvh, pages, seq_len, pending=pending)
+    V = gather_pages(v_layer, block_row, kvh, pages, seq_len, pending=pending)
     return attention(q, K, V, scale)
 
 
@@ -476,16 +491,17 @@ def page_keys_f64(k_layer, block_row, kvh, n_pages):
 
 
 def decode_group(q_group, k_layer, v_layer, block_row, kvh, seq_len, budget_pages,
-                 records=None, scale=None):
+                 records=None, scale=None, pending=0):
     """The whole LOCKS decode step for one KV-head group.
 
     q_group: float64 [G, d]; returns dict with s_hat [G, N], log_m [N],
     sel (ascending), out [G, d], lse [G]."""
-    n_fin = seq_len // PAGE
-    if records is None:
+    n_fin = summarized_pages(seq_len, pending)
+    if records is None and n_fin:
         records, _, _ = build_records(page_keys_f64(k_layer, block_row, kvh, n_fin))
     s_hat = score_records(q_group, records, scale) if n_fin else np.zeros((q_group.shape[0], 0))
     _, log_m, m = group_mass(s_hat) if n_fin else (None, np.zeros(0), np.zeros(0))
     sel = select_top_pages(log_m, budget_pages)
-    out, lse = sparse_attention(q_group, k_layer, v_layer, block_row, kvh, sel, seq_len, scale)
+    out, lse = sparse_attention(q_group, k_layer, v_layer, block_row, kvh, sel, seq_len, scale,
+                                pending)
     return dict(s_hat=s_hat, log_m=log_m, m=m, sel=sel, out=out, lse=lse)

@@ -164,6 +164,12 @@ def test_validation_errors_launch_nothing():
     assert _raw_score(lib, d, ws=0) == L.ERR_WORKSPACE
     assert _raw_score(lib, d, ws_bytes=16) == L.ERR_WORKSPACE
     assert _raw_score(lib, L.dims(32, 8, page_size=32)) == L.ERR_UNSUPPORTED
+    # the pending-newest-page flag is 0 or 1
+    bad = L.dims(32, 8)
+    bad.newest_page_pending = 2
+    assert _raw_score(lib, bad) == L.ERR_SHAPE
+    assert L.summary_bytes(bad) == 0 and L.workspace_bytes(bad, 1, 64, 8) == 0
+    assert L.dims(32, 8, newest_page_pending=True).newest_page_pending == 1
     assert lib.locks_score_pages(None, None, None, 0, None, 0, None, 0, None, None, 0, None) == L.ERR_NULL
     # misaligned q
     P = ctypes.c_void_p

@@ -3,7 +3,10 @@ the records locks_build_summaries builds, only for sequences whose newest
 token completed a page, and a captured decode step that appends each layer's
 newest key and summarizes the page it completes keeps the summaries current
 while tokens are appended between replays; its records, selections and
-outputs are checked against the oracle."""
+outputs are checked against the oracle.  Both forms of the step are held to
+it: the page summarized inside the step before the layer is scored, and
+summarized after the step (all layers in one launch) with the newest page
+pending during the step, attended in full."""
 
 import numpy as np
 import pytest
@@ -54,13 +57,16 @@ def test_finalize_builds_only_completed_pages():
     log(f"[finalize] built {len(want)} pages, others untouched")
 
 
-def test_decode_graph_with_incremental_finalization():
+@pytest.mark.parametrize("mode", ["layer", "step"])
+def test_decode_graph_with_incremental_finalization(mode):
     """A captured step that, per layer, appends the newest token's key and
-    value (the model's work, inside the graph), summarizes the page that key
-    completed and then runs that layer's decode.  Tokens are appended between
-    replays; every record finalized during the replays is checked against the
-    oracle's build of the same keys, two replays' selections and outputs
-    against the oracle, and others against the eager library calls."""
+    value (the model's work, inside the graph) and runs that layer's decode,
+    summarizing the page that key completed either before the layer is scored
+    (mode "layer") or after the step (mode "step", the newest page pending
+    during it).  Tokens are appended between replays; every record finalized
+    during the replays is checked against the oracle's build of the same keys,
+    the replays in which a page completes (and the last one) against the
+    oracle, and two others against the eager library calls."""
     w = get_workload("llama8b-32k", batch=2, layers=2, ctx=16 * 512)
     start = [16 * 300 - 3, 16 * 500 - 1]
     x = generate(w, seq_lens=start)
@@ -92,7 +98,9 @@ def test_decode_graph_with_incremental_finalization():
         k[layer][blk, :, slot] = new_k[layer]
         v[layer][blk, :, slot] = new_v[layer]
 
-    step = DecodeStep(d, k, v, summ, q, bt, seq, budget, finalize=True, before_layer=append)
+    step = DecodeStep(d, k, v, summ, q, bt, seq, budget, finalize=mode, before_layer=append)
+    assert step.d.newest_page_pending == (mode == "step")
+    d = step.d
     step.capture()
     gen = torch.Generator(device="cuda").manual_seed(7)
     cur = list(start)
@@ -146,15 +154,17 @@ def test_decode_graph_with_incremental_finalization():
             for j in range(cur[b] // 16):
                 blk = int(x.block_table[b, j])
                 assert torch.equal(summ[layer, :, blk], ref[layer, :, blk]), (layer, b, j)
-    log(f"[finalize graph] pages completed during decoding: {completed}; "
+    log(f"[finalize graph, {mode}] pages completed during decoding: {completed}; "
         f"replays checked against the oracle: {oracle_checked}")
 
 
 def _check_against_oracle(d, k, v, q, summ, bt, seq, step, budget, cur, done_now):
     """The replay's state against the oracle: records of the pages completed
     in this replay (codes against the oracle's build of the keys now in the
-    cache), the page LSE of every page on the GPU's codes, the selection from
-    the GPU's scores and the output over the GPU's selection."""
+    cache), the page LSE of every summarized page on the GPU's codes (with
+    the newest page pending, the page just completed is not one of them: it
+    was attended in full), the selection from the GPU's scores and the output
+    over the GPU's selection."""
     layers, hkv, nb = summ.shape[0], summ.shape[1], summ.shape[2]
     hq = q.shape[2]
     G = hq // hkv
@@ -175,8 +185,10 @@ def _check_against_oracle(d, k, v, q, summ, bt, seq, step, budget, cur, done_now
                                     where=f"finalized layer {layer} b={b} page {j} g={g}")
         L.score_pages(d, q[layer], summ[layer], nb, bt, seq, lse, ws)
         torch.cuda.synchronize()
+        pend = d.newest_page_pending
         for b in range(len(cur)):
-            n = cur[b] // 16
+            n = O.summarized_pages(cur[b], pend)
+            assert torch.all(torch.isneginf(lse[b, :, n:P]))
             for g in range(hkv):
                 qd = O.bf16_to_f64(qb[layer, b, g * G:(g + 1) * G])
                 s_ref = O.score_records(qd, recs_all[layer, g, btn[b, :n]])
@@ -186,7 +198,8 @@ def _check_against_oracle(d, k, v, q, summ, bt, seq, step, budget, cur, done_now
                 c = int(step.cnt[layer, b, g])
                 got = step.sel[layer, b, g, :c].cpu().numpy()
                 check_selection(got, log_m, budget)
-                o_ref, l_ref = O.sparse_attention(qd, kb[layer], vb[layer], btn[b], g, got, cur[b])
+                o_ref, l_ref = O.sparse_attention(qd, kb[layer], vb[layer], btn[b], g, got, cur[b],
+                                                  pending=pend)
                 o_gpu = step.out[layer, b, g * G:(g + 1) * G].float().cpu().numpy()
                 assert np.abs(o_gpu - o_ref).max() <= OUT_TOL
                 assert np.abs(step.out_lse[layer, b, g * G:(g + 1) * G].cpu().numpy()

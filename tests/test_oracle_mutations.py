@@ -61,9 +61,23 @@ def _group_mass_unnormalized(s_hat):
     return OL.logsumexp(s, axis=-1), np.log(m), m
 
 
-def _gather_no_tail(cache_layer, block_row, kvh, pages, seq_len, page=O.PAGE):
+def _gather_no_tail(cache_layer, block_row, kvh, pages, seq_len, page=O.PAGE, pending=0):
     parts = [O.bf16_to_f64(cache_layer[block_row[j], kvh]) for j in pages]   # mistake: tail dropped
     return np.concatenate(parts, axis=0) if parts else np.zeros((0, cache_layer.shape[-1]))
+
+
+def _gather_partial_tail_only(cache_layer, block_row, kvh, pages, seq_len, page=O.PAGE,
+                              pending=0):
+    n_fin = OL.summarized_pages(seq_len, pending, page)
+    tail = seq_len % page                                     # mistake: a full pending page dropped
+    parts = [O.bf16_to_f64(cache_layer[block_row[j], kvh]) for j in pages]
+    if tail:
+        parts.append(O.bf16_to_f64(cache_layer[block_row[n_fin], kvh, :tail]))
+    return np.concatenate(parts, axis=0) if parts else np.zeros((0, cache_layer.shape[-1]))
+
+
+def _summarized_ignores_pending(seq_len, pending=0, page=O.PAGE):
+    return seq_len // page if seq_len > 0 else 0              # mistake: pending page summarized
 
 
 def _tables_strided(s_hat, n_tables, budget_pages):
@@ -108,7 +122,9 @@ MUTANTS = [
     ("select_top_pages", _select_high_ties, P.test_share_hand_worked_cases),
     ("group_mass", _group_mass_unnormalized, P.test_share_hand_worked_cases),
     ("table_selection", _tables_strided, P.test_table_selection_layer_wide_differs_from_per_kv_head),
-    ("gather_pages", _gather_no_tail, lambda: P.test_full_budget_equals_dense(4096 - 5)),
+    ("gather_pages", _gather_no_tail, lambda: P.test_full_budget_equals_dense(4096 - 5, 0)),
+    ("gather_pages", _gather_partial_tail_only, lambda: P.test_full_budget_equals_dense(4096, 1)),
+    ("summarized_pages", _summarized_ignores_pending, P.test_pending_newest_page),
     ("fp16_round", _scale_no_fp16, P.test_quantization_codes_and_scales),
     ("bf16_to_f64", _bf16_wrong_shift, P.test_bf16_decoding_fixed_patterns),
     ("bf16_to_f64", _bf16_as_fp16, P.test_bf16_decoding_fixed_patterns),

@@ -503,22 +503,55 @@ def test_attention_bruteforce_loops():
     np.testing.assert_allclose(l, l2, atol=1e-13)
 
 
-@pytest.mark.parametrize("seq_len", [4096, 4096 - 5, 16 * 7 + 1])
-def test_full_budget_equals_dense(seq_len):
+@pytest.mark.parametrize("seq_len,pending", [(4096, 0), (4096 - 5, 0), (16 * 7 + 1, 0),
+                                             (4096, 1), (16 * 7 + 1, 1), (16, 1), (1, 1)])
+def test_full_budget_equals_dense(seq_len, pending):
+    """Every page selected is dense attention over all seq_len tokens, with
+    the tail page holding exactly the tokens past the summarized pages: the
+    partial last page, or with the newest page pending the whole page holding
+    the newest token (1 to 16 tokens)."""
     from synth import get_workload
     from synth.host import generate
     w = get_workload("tiny-4k", ctx=4096)
     x = generate(w, seq_lens=[seq_len])
     q = O.bf16_to_f64(x.q[0, 0])
     row = x.block_table[0]
-    n_fin = seq_len // 16
-    res = O.decode_group(q, x.k_cache[0], x.v_cache[0], row, 0, seq_len, budget_pages=10 ** 6)
+    n_fin = (seq_len - pending) // 16
+    assert O.summarized_pages(seq_len, pending) == n_fin
+    res = O.decode_group(q, x.k_cache[0], x.v_cache[0], row, 0, seq_len, budget_pages=10 ** 6,
+                         pending=pending)
     assert list(res["sel"]) == list(range(n_fin))
     Kall = O.bf16_to_f64(x.k_cache[0][row[:-(-seq_len // 16)], 0].reshape(-1, 128)[:seq_len])
     Vall = O.bf16_to_f64(x.v_cache[0][row[:-(-seq_len // 16)], 0].reshape(-1, 128)[:seq_len])
     o, l = O.attention(q, Kall, Vall)
     np.testing.assert_allclose(res["out"], o, atol=1e-12)
     np.testing.assert_allclose(res["lse"], l, atol=1e-12)
+
+
+def test_pending_newest_page():
+    """The page that holds the newest token, when pending, is not a candidate
+    and is attended in full: at 32 tokens only page 0 is summarized and page
+    1's 16 tokens are the tail; a length that is not a multiple of 16 gives the
+    same page count and the same result either way; and an empty sequence
+    has no pages."""
+    from synth import get_workload
+    from synth.host import generate
+    assert [O.summarized_pages(n, 1) for n in (0, 1, 15, 16, 17, 32, 33)] == [0, 0, 0, 0, 1, 1, 2]
+    assert [O.summarized_pages(n, 0) for n in (0, 1, 15, 16, 17, 32, 33)] == [0, 0, 0, 1, 1, 2, 2]
+    w = get_workload("tiny-4k", ctx=4096)
+    x = generate(w, seq_lens=[32])
+    q = O.bf16_to_f64(x.q[0, 0])
+    row = x.block_table[0]
+    res = O.decode_group(q, x.k_cache[0], x.v_cache[0], row, 0, 32, budget_pages=1, pending=1)
+    assert res["s_hat"].shape == (4, 1) and list(res["sel"]) == [0]
+    K = O.gather_pages(x.k_cache[0], row, 0, [0], 32, pending=1)
+    assert K.shape == (32, 128)
+    np.testing.assert_array_equal(K[16:], O.bf16_to_f64(x.k_cache[0][row[1], 0]))
+    for n in (16 * 40 + 3, 16 * 40 + 15):
+        a = O.decode_group(q, x.k_cache[0], x.v_cache[0], row, 0, n, budget_pages=8)
+        b = O.decode_group(q, x.k_cache[0], x.v_cache[0], row, 0, n, budget_pages=8, pending=1)
+        assert list(a["sel"]) == list(b["sel"])
+        np.testing.assert_array_equal(a["out"], b["out"])
 
 
 def test_sparse_attention_is_dense_over_selected_tokens():
