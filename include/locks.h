@@ -216,16 +216,17 @@ locks_status locks_finalize_pages(const locks_dims* dims, const void* k_cache,
                                   int32_t n_layers, int64_t k_layer_stride,
                                   int64_t summ_layer_stride, void* stream);
 
-/* Score every finalized page of every sequence from its summary alone
+/* Score every summarized page of every sequence from its summary alone
  * (sec. 2 reconstruction and selection, the equation for s_hat_j(q)):
  *   s_hat[b][h][j] = LSE_i ( (q_h.mu_j + (V_j^T q_h).c_i) / sqrt(d) ),
- * natural log, for query head h and logical page j < seq_lens[b] / 16.
+ * natural log, for query head h and every summarized logical page j (j <
+ * seq_lens[b] / 16, or (seq_lens[b] - 1) / 16 with the newest page pending).
  *   q           : bf16 [batch][Hq][d].
  *   summaries   : this layer's records, [Hkv][num_blocks][locks_summary_bytes].
  *   block_table : [batch][max_pages] physical block of each logical page.
  *   seq_lens    : [batch] tokens per sequence.
  *   page_lse    : fp32 [batch][Hq][max_pages]; entries for pages that are not
- *                 finalized (or whose block id is out of range) get -inf.
+ *                 summarized (or whose block id is out of range) get -inf.
  *   workspace   : >= locks_score_workspace_bytes(dims, batch, max_pages, 0).
  * No candidate key or value is read. */
 locks_status locks_score_pages(const locks_dims* dims, const void* q, const void* summaries,
@@ -236,7 +237,7 @@ locks_status locks_score_pages(const locks_dims* dims, const void* q, const void
 /* Select pages from scores (sec. 2 group-shared selection): for each
  * (sequence, KV head) the mass share of page j for query head h is
  * exp(s_hat_hj - LSE_j' s_hat_hj'); shares are averaged over the G query
- * heads of the group and the k = min(budget_pages, finalized pages) largest
+ * heads of the group and the k = min(budget_pages, summarized pages) largest
  * are kept (ties to the lower page index).
  *   page_lse  : fp32 [batch][Hq][max_pages] as written by locks_score_pages.
  *   sel       : int32 [batch][Hkv][budget_pages] logical page ids in
@@ -257,11 +258,13 @@ locks_status locks_score_select(const locks_dims* dims, const void* q, const voi
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Attention of each query head over the selected pages' tokens plus the
- * partial tail page (tokens past the last full page), an ordinary softmax
- * renormalized over those tokens (abstract: attend only the top pages).
+ * tail page (the tokens past the summarized pages: the partial last page, or
+ * with the newest page pending the page that holds the newest token), an
+ * ordinary softmax renormalized over those tokens (abstract: attend only the
+ * top pages).
  *   k_cache, v_cache : bf16 caches of this layer, strides `layout`.
  *   sel, sel_count   : as written by locks_select_pages; sel == NULL means
- *                      every finalized page (dense attention).
+ *                      every summarized page (dense attention).
  *   budget_pages     : row length of sel (ignored when sel is NULL).
  *   softmax_scale    : logit scale, normally 1/sqrt(d).
  *   out              : bf16 [batch][Hq][d].
@@ -362,12 +365,12 @@ locks_status locks_build_summaries_basis(const locks_dims* dims, const void* k_c
  * pages measure LOCKS against (sec. 3 contributions: selection quality
  * against exact page attention mass):
  *   page_lse[b][h][j] = LSE_i ( q_h . k_ij * softmax_scale ),
- * natural log, over the 16 tokens of each finalized logical page j.  The
+ * natural log, over the 16 tokens of each summarized logical page j.  The
  * output has the layout of locks_score_pages', so locks_select_pages turns it
- * into the exact top-k page set.  Reads every key of every finalized page.
+ * into the exact top-k page set.  Reads every key of every summarized page.
  *   k_cache       : bf16 key cache of this layer, strides `layout`.
  *   softmax_scale : logit scale, normally 1/sqrt(d).
- *   page_lse      : fp32 [batch][Hq][max_pages]; pages that are not finalized
+ *   page_lse      : fp32 [batch][Hq][max_pages]; pages that are not summarized
  *                   (or whose block id is out of range) get -inf.
  * Needs no workspace. */
 locks_status locks_exact_page_lse(const locks_dims* dims, const void* q, const void* k_cache,

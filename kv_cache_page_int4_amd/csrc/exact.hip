@@ -1,5 +1,5 @@
 // Exact page log-sum-exp from the true keys: s_hj = LSE_i(q_h . k_ij / sqrt(d))
-// over the 16 tokens of every finalized page.  This is the "read every key"
+// over the 16 tokens of every summarized page.  This is the "read every key"
 // selector the LOCKS pages compare against (LOCKS explainer, technical summary
 // sec. 3, contributions: selection quality against exact page attention mass).
 // Its output has the layout of the estimated page LSE, so the same selection

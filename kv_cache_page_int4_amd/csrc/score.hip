@@ -416,7 +416,7 @@ score_kernel(ScoreParams p) {
   }
   __syncthreads();
 
-  // ---- the workgroup's finalized pages: one 4-page piece per thread, each
+  // ---- the workgroup's summarized pages: one 4-page piece per thread, each
   // head's kWgPages scores leave as one contiguous run ----
   constexpr int kPieces = kWgPages / 4;   // per head
   static_assert(kSlots * kPieces <= 64 * kScoreWaves, "one 4-page piece per thread");

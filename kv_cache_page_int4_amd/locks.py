@@ -269,7 +269,7 @@ def score_select(d: Dims, q, summaries, num_blocks, block_table, seq_lens, budge
 def sparse_attend(d: Dims, q, k_cache, v_cache, block_table, seq_lens, sel, sel_count,
                   budget_pages, out, workspace, out_lse=None, softmax_scale=None, stream=None,
                   n_tables=None):
-    """sel=None attends every finalized page (dense attention); n_tables as
+    """sel=None attends every summarized page (dense attention); n_tables as
     for select_pages."""
     B, P, hq = block_table.shape[0], block_table.shape[1], d.num_q_heads
     ntab = d.num_kv_heads if n_tables is None else int(n_tables)
