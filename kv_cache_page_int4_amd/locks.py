@@ -106,7 +106,8 @@ def dims(num_q_heads, num_kv_heads, head_dim=128, page_size=16, rank=8,
     """newest_page_pending: the page holding each sequence's newest token is
     not summarized yet (attended in full instead), as in a decode step whose
     completed pages are summarized after it."""
-    return Dims(num_q_heads, num_kv_heads, head_dim, page_size, rank, int(bool(newest_page_pending)))
+    return Dims(num_q_heads, num_kv_heads, head_dim, page_size, rank,
+                int(bool(newest_page_pending)))
 
 
 def _ptr(t):
