@@ -131,8 +131,14 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // NSUB: 4-head sub-passes per step (2 for a group of 8 heads, else 1).
+// Waves per SIMD the register budget is cut for: 7 (at most 72 registers)
+// for one head pass; a group of 8 heads at rank 8 needs a little more than
+// 96 registers and is held to 96 (5 waves instead of 4).
+constexpr int score_waves(int r, int nsub) { return nsub == 1 || r == 4 ? 7 : (r == 8 ? 5 : 3); }
+
 template <int R, int NSUB>
-__global__ __launch_bounds__(64 * kScoreWaves) __attribute__((amdgpu_waves_per_eu(7, 7))) void
+__global__ __launch_bounds__(64 * kScoreWaves) __attribute__((
+    amdgpu_waves_per_eu(score_waves(R, NSUB), score_waves(R, NSUB)))) void
 score_kernel(ScoreParams p) {
   using SL = ScoreLayout<R>;
   constexpr int kSlotRec = SL::kSlotRec, kStepBytes = SL::kStepBytes;
