@@ -24,7 +24,7 @@ if not torch.cuda.is_available():
 
 from kv_cache_page_int4_amd import locks as L  # noqa: E402
 from tests.gpu_common import (LSE_TOL, OUT_TOL, Layer, check_selection,  # noqa: E402
-                              compare_build_codes, log, oracle_scores)
+                              compare_build_codes, log)
 
 _CACHE = {}
 
@@ -36,12 +36,14 @@ def gen(name, seq_lens=None, **kw):
     return _CACHE[key]
 
 
-CASES = [("tiny-4k", {}, None), ("llama8b-32k", {"batch": 2}, [32768 - 5, 16 * 700 + 3])]
+CASES = [("tiny-4k", {}, None, False),
+         ("llama8b-32k", {"batch": 2}, [32768 - 5, 16 * 700 + 3], False),
+         ("tiny-4k", {}, None, True)]        # the newest (full) page pending
 
 
 @pytest.mark.parametrize("rank", [4, 16])
-@pytest.mark.parametrize("name,kw,seq", CASES)
-def test_rank_pipeline(rank, name, kw, seq):
+@pytest.mark.parametrize("name,kw,seq,pending", CASES)
+def test_rank_pipeline(rank, name, kw, seq, pending):
     x = gen(name, seq_lens=seq, **kw)
     w = x.w
     lay = Layer(x, 0, rank=rank)
@@ -61,6 +63,7 @@ def test_rank_pipeline(rank, name, kw, seq):
         n_cols, n_ex = n_cols + c, n_ex + e
     assert n_ex <= 0.05 * n_cols, (n_ex, n_cols)
     # score, select, attend
+    lay.d = L.dims(w.hq, w.hkv, rank=rank, newest_page_pending=pending)
     budget = w.budget_pages
     sel, cnt, lse = lay.score_select(budget)
     out, olse = lay.attend(sel, cnt, budget)
@@ -69,10 +72,12 @@ def test_rank_pipeline(rank, name, kw, seq):
     worst_lse = worst_out = 0.0
     ties = 0
     for b in range(w.batch):
-        n = int(x.seq_lens[b]) // 16
+        n = O.summarized_pages(int(x.seq_lens[b]), int(pending))
+        assert torch.all(torch.isneginf(lse[b, :, n:]))
         for g in range(w.hkv):
             s_gpu = lse[b, g * G:(g + 1) * G, :n].double().cpu().numpy()
-            s_ref = oracle_scores(x, recs, 0, b, g, r=rank)
+            s_ref = O.score_records(O.bf16_to_f64(x.q[0, b, g * G:(g + 1) * G]),
+                                    recs[g, x.block_table[b, :n]], r=rank)
             err = float(np.abs(s_gpu - s_ref).max())
             worst_lse = max(worst_lse, err)
             assert err <= LSE_TOL, f"page LSE off by {err} (rank {rank}, b={b}, g={g})"
@@ -82,7 +87,7 @@ def test_rank_pipeline(rank, name, kw, seq):
             ties += check_selection(got, log_m, budget)
             q = O.bf16_to_f64(x.q[0, b, g * G:(g + 1) * G])
             o_ref, l_ref = O.sparse_attention(q, x.k_cache[0], x.v_cache[0], x.block_table[b], g,
-                                              got, int(x.seq_lens[b]))
+                                              got, int(x.seq_lens[b]), pending=int(pending))
             e = float(np.abs(out[b, g * G:(g + 1) * G].float().cpu().numpy() - o_ref).max())
             worst_out = max(worst_out, e)
             assert e <= OUT_TOL
@@ -98,7 +103,7 @@ def test_rank_pipeline(rank, name, kw, seq):
                    out2, ws, L.attend_workspace(lay.d, w.batch, budget + 1), out_lse=olse2)
     torch.cuda.synchronize()
     assert torch.equal(sel, sel2) and torch.equal(cnt, cnt2) and torch.equal(out, out2)
-    log(f"[rank {rank} {name}] codes exempt {n_ex}/{n_cols}; max|dLSE|={worst_lse:.2e} "
+    log(f"[rank {rank} {name} pending={pending}] codes exempt {n_ex}/{n_cols}; max|dLSE|={worst_lse:.2e} "
         f"max|dOut|={worst_out:.2e} tie-window pages={ties}")
 
 

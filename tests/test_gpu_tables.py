@@ -36,21 +36,24 @@ def gen(name, seq_lens=None, **kw):
 
 
 CASES = [
-    # (workload, kwargs, seq_lens, n_tables, budget)
-    ("llama8b-32k", {"batch": 2}, [32768 - 5, 16 * 700 + 3], 1, 128),
-    ("llama8b-32k", {"batch": 2}, [32768 - 5, 16 * 700 + 3], 2, 128),
-    ("llama8b-32k", {}, None, 4, 37),
-    ("llama8b-32k", {"ctx": 16 * 5000 + 9}, None, 1, 300),      # 3 chunks of candidates
-    ("llama8b-32k", {"batch": 3}, [16 * 5 + 2, 7, 16 * 64], 1, 128),   # budget >= pages
+    # (workload, kwargs, seq_lens, n_tables, budget, newest page pending)
+    ("llama8b-32k", {"batch": 2}, [32768 - 5, 16 * 700 + 3], 1, 128, False),
+    ("llama8b-32k", {"batch": 2}, [32768 - 5, 16 * 700 + 3], 2, 128, False),
+    ("llama8b-32k", {}, None, 4, 37, False),
+    ("llama8b-32k", {"ctx": 16 * 5000 + 9}, None, 1, 300, False),      # 3 chunks of candidates
+    ("llama8b-32k", {"batch": 3}, [16 * 5 + 2, 7, 16 * 64], 1, 128, False),   # budget >= pages
+    ("llama8b-32k", {"batch": 2}, [32768, 16 * 700], 1, 128, True),    # full last pages pending
+    ("llama8b-32k", {"batch": 3}, [16 * 64, 16, 16 * 9 + 4], 2, 128, True),
 ]
 
 
-@pytest.mark.parametrize("name,kw,seq,n_tables,budget", CASES)
-def test_tables_against_oracle(name, kw, seq, n_tables, budget):
+@pytest.mark.parametrize("name,kw,seq,n_tables,budget,pending", CASES)
+def test_tables_against_oracle(name, kw, seq, n_tables, budget, pending):
     x = gen(name, seq_lens=seq, **kw)
     w = x.w
     lay = Layer(x, 0)
     lay.gpu_build()
+    lay.d = L.dims(w.hq, w.hkv, newest_page_pending=pending)
     torch.cuda.synchronize()
     recs = lay.summ.cpu().numpy()
     lse = lay.score()
@@ -71,7 +74,8 @@ def test_tables_against_oracle(name, kw, seq, n_tables, budget):
     worst_lse = worst_out = 0.0
     ties = 0
     for b in range(w.batch):
-        n = int(x.seq_lens[b]) // 16
+        n = O.summarized_pages(int(x.seq_lens[b]), int(pending))
+        assert torch.all(torch.isneginf(lse[b, :, n:]))
         s_gpu = lse[b, :, :n].double().cpu().numpy()
         if n:
             for g in range(w.hkv):
@@ -89,14 +93,14 @@ def test_tables_against_oracle(name, kw, seq, n_tables, budget):
             for g in range(t * kv_per_tab, (t + 1) * kv_per_tab):
                 q = O.bf16_to_f64(x.q[0, b, g * G:(g + 1) * G])
                 o_ref, l_ref = O.sparse_attention(q, x.k_cache[0], x.v_cache[0], x.block_table[b],
-                                                  g, got, int(x.seq_lens[b]))
+                                                  g, got, int(x.seq_lens[b]), pending=int(pending))
                 if not (o_ref.shape[0] and np.isfinite(l_ref).all()):
                     continue
                 e = float(np.abs(out[b, g * G:(g + 1) * G].float().cpu().numpy() - o_ref).max())
                 worst_out = max(worst_out, e)
                 assert e <= OUT_TOL, f"attention output off by {e} (b={b}, g={g}, table {t})"
                 assert np.abs(olse[b, g * G:(g + 1) * G].cpu().numpy() - l_ref).max() <= LSE_TOL
-    log(f"[tables {name} b={w.batch} n_tables={n_tables} budget={budget}] "
+    log(f"[tables {name} b={w.batch} n_tables={n_tables} budget={budget} pending={pending}] "
         f"max|dLSE|={worst_lse:.2e} max|dOut|={worst_out:.2e} tie-window pages={ties}")
 
     # the one-call layer (last selection stage inside attention) is identical
