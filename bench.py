@@ -184,7 +184,8 @@ def cpu_baseline(w, inp, summ, budget, threads):
     n = w.pages
     G = w.group
     blk = inp.block_table[0, :n].cpu().numpy()
-    recs = [summ[0, g].cpu().numpy()[blk] for g in range(w.hkv)]
+    blk_t = inp.block_table[0, :n].long()
+    recs = [summ[0, g].index_select(0, blk_t).cpu().numpy() for g in range(w.hkv)]
     qbits = [inp.q[0, 0, g * G:(g + 1) * G].contiguous().view(torch.int16).cpu().numpy()
              .view(np.uint16) for g in range(w.hkv)]
 
@@ -453,7 +454,8 @@ def finalize_timing(w, d, inp, summ, budget, steps, ms_plain):
     return res
 
 
-def config_entry(name, args, dense=False, quality_layers=0, finalize=False, **overrides):
+def config_entry(name, args, dense=False, quality_layers=0, finalize=False, cpu=False,
+                 **overrides):
     """Step time, scorer and attention bandwidth (and optionally the dense
     comparator, the quality report and the finalization cost) of one more
     configuration, set up after the previous one's buffers are freed."""
@@ -498,6 +500,12 @@ def config_entry(name, args, dense=False, quality_layers=0, finalize=False, **ov
         log(f"[{wl.name}] recall vs exact {q['recall_vs_exact']:.4f}; carriers kept: LOCKS "
             f"{q['carrier_retention_locks']:.3f}, exact {q['carrier_retention_exact']:.3f}, both "
             f"{q['carriers_kept_by_both']}/{q['carriers_kept_by_exact']} of those exact keeps")
+    if cpu and not args.no_cpu_baseline:
+        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        entry["cpu_baseline"] = cpu_baseline(wl, inp3, summ3, wl.budget_pages, threads)
+        c = entry["cpu_baseline"]
+        log(f"[{wl.name}] oracle {c['value']:.0f} us/layer on {c['cores']} threads, "
+            f"{c['one_core']['value']:.0f} us/layer on one core")
     del st3, inp3, summ3
     torch.cuda.empty_cache()
     return entry
@@ -690,14 +698,15 @@ def main():
     if not args.no_large and args.large_workload:
         also[args.large_workload] = config_entry(
             args.large_workload, args, dense=not args.no_dense,
-            quality_layers=0 if args.no_quality else 2)
+            quality_layers=0 if args.no_quality else 2, cpu=True)
     if not args.no_configs:
         also["llama8b-128k-b8"] = config_entry("llama8b-128k-b8", args,
-                                               quality_layers=0 if args.no_quality else 2)
+                                               quality_layers=0 if args.no_quality else 2,
+                                               cpu=True)
     if not args.no_small and args.small_workload:
         ent = config_entry(args.small_workload, args, dense=not args.no_dense,
                            quality_layers=0 if args.no_quality else 1,
-                           finalize=not args.no_finalize)
+                           finalize=not args.no_finalize, cpu=True)
         ent["note"] = "working set fits the 256 MB Infinity Cache; latency-bound"
         also[args.small_workload] = ent
         if not args.no_configs:
@@ -706,6 +715,7 @@ def main():
                     args.small_workload, args, quality_layers=0 if args.no_quality else 1,
                     seed=seed)
 
+    traffic = traffic_if_current(w.name)
     result = {
         "metric": METRIC,
         "value": round(us_layer, 3),
@@ -728,7 +738,9 @@ def main():
                    "graph": "one hipGraph per step"},
         "roofline": {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(score_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_if_current(w.name), "kernel": "score_kernel",
+                     "traffic": traffic, "kernel": "score_kernel",
+                     "traffic_gbs": (round(traffic / (score_us * 1e-6) / 1e9, 1)
+                                     if traffic else None),
                      "kernel_us": round(score_us, 3),
                      "launches_timed": kr["launches"],
                      "bytes_per_launch": page_heads * SCORE_BYTES_PER_PAGE_HEAD,
