@@ -205,7 +205,7 @@ locks_status locks_decode_layer_noalloc(const locks_dims* dims, const void* q,
  * Called after the step, for every layer at once, when the step's calls run
  * with newest_page_pending = 1 (the page is selected from the next step on);
  * or per layer, after the layer's newest key is written and before it is
- * scored, when they run with 0 (the page is selected in the same step). */
+ * scored, when they run with 0 (the page is selected in the same step).
  *   k_cache     : bf16 key cache of layer 0, strides `layout`; layer l
  *                 starts k_layer_stride bf16 elements further on.
  *   block_table : [batch][max_pages]; a block id outside [0, num_blocks)
