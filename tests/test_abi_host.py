@@ -35,6 +35,23 @@ def test_header_declares_the_entry_points():
         assert want in names
 
 
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    """The public header is valid C and C++ on its own (a stray comment
+    terminator or a C++-only construct would break callers)."""
+    import shutil
+    import subprocess
+    hdr = os.path.join(ROOT, "include", "locks.h")
+    for cc, lang in (("gcc", "c"), ("g++", "c++")):
+        exe = shutil.which(cc)
+        if exe is None:
+            pytest.skip(f"{cc} not found")
+        src = tmp_path / f"use.{'c' if lang == 'c' else 'cpp'}"
+        src.write_text(f'#include "{hdr}"\nint main(void) {{ return (int)sizeof(locks_dims); }}\n')
+        r = subprocess.run([exe, "-fsyntax-only", "-Wall", "-Werror", str(src)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
 def test_library_exports_every_declared_symbol():
     lib = _lib_or_skip()
     h = ctypes.CDLL(L.LIB_PATH)
