@@ -244,6 +244,43 @@ def cpu_baseline(w, inp, summ, budget, threads):
             "one_core": {"value": t1 * w.batch * 1e6, "unit": "us/layer", "cores": 1}}
 
 
+def cpu_build_baseline(w, inp, threads, n_sample=16384):
+    """The oracle's summary build (bf16 decode, page spectrum, quantization,
+    packing) on the first n_sample pages of KV head 0, layer 0, sequence 0,
+    timed on one core and split into equal runs of pages over `threads`
+    threads.  Returns page-heads per second for both."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    n = min(n_sample, w.pages)
+    blk = inp.block_table[0, :n].long()
+    kb = inp.k[0][blk, 0].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def build(lo_hi):
+        lo, hi = lo_hi
+        O.build_records(O.bf16_to_f64(kb[lo:hi]), w.rank)
+
+    with threadpool_limits(1):
+        t = time.perf_counter()
+        build((0, n))
+        t1 = time.perf_counter() - t
+        edges = np.linspace(0, n, threads + 1).astype(int)
+        t = time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(build, zip(edges[:-1], edges[1:])))
+        tn = time.perf_counter() - t
+    return {"page_heads_per_s": n / tn, "cores": threads,
+            "one_core_page_heads_per_s": n / t1,
+            "sample": (f"{n} page-heads (layer 0, sequence 0, KV head 0 of {w.name}): "
+                       f"{tn:.2f} s on {threads} threads ({n // threads} pages each), "
+                       f"{t1:.2f} s on one core")}
+
+
 def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps, light=False):
     """The read-every-key comparator and the selection quality of LOCKS
     against it: exact page LSE from the true keys (locks_exact_page_lse),
@@ -685,6 +722,9 @@ def main():
         cpu = cpu_baseline(w, inp, summ, budget, threads)
         log(f"[{w.name}] oracle {cpu['value']:.0f} us/layer on {cpu['cores']} threads, "
             f"{cpu['one_core']['value']:.0f} us/layer on one core ({cpu['cpu_model']})")
+        cpu["build"] = cpu_build_baseline(w, inp, threads)
+        log(f"[{w.name}] oracle build {cpu['build']['page_heads_per_s']:.0f} page-heads/s on "
+            f"{threads} threads, {cpu['build']['one_core_page_heads_per_s']:.0f} on one core")
 
     also = {}
     del step, inp, summ
