@@ -25,6 +25,9 @@
  *    G heads of a group share one page table); anything else returns
  *    LOCKS_ERR_UNSUPPORTED.
  *  - bf16 tensors are raw bfloat16 bit patterns (uint16).
+ *  - Alignment: q, k_cache, v_cache and summaries 16 bytes; every other array
+ *    (int32 and fp32 arrays, the bf16 output) 4 bytes; a misaligned one
+ *    returns LOCKS_ERR_SHAPE.  Workspaces 16 bytes, else LOCKS_ERR_WORKSPACE.
  *  - Device-side data (seq_lens, block tables, selections) is range-checked
  *    in the kernels: a sequence length is clamped to max_pages * 16, and a
  *    block id outside [0, num_blocks) makes that page count as absent.

@@ -14,6 +14,14 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Alignment the kernels' accesses need: 16 bytes for bf16 tensors read in
+// 16-byte pieces, summaries and workspaces, 4 bytes for int32 / fp32 arrays
+// and the bf16 output (written two values at a time).  NULL counts as
+// aligned: presence is checked separately.
+inline bool misaligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
+}
+
 locks_status check_dims(const locks_dims* d) {
   if (!d) return LOCKS_ERR_NULL;
   if (d->num_q_heads <= 0 || d->num_kv_heads <= 0) return LOCKS_ERR_SHAPE;
@@ -122,7 +130,8 @@ locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
   if (layout.token_stride < 128 || layout.block_stride <= 0 || layout.head_stride <= 0 ||
       (layout.token_stride % 8) || (layout.head_stride % 8) || (layout.block_stride % 8))
     return LOCKS_ERR_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(k_cache) & 15) || (reinterpret_cast<uintptr_t>(summaries) & 15))
+  if (misaligned(k_cache, 16) || misaligned(summaries, 16) || misaligned(block_ids, 4) ||
+      misaligned(raw_debug, 4))
     return LOCKS_ERR_SHAPE;
   hipError_t e = launch_build(dims->rank, static_cast<const uint16_t*>(k_cache), layout.block_stride,
                               layout.head_stride, layout.token_stride, block_ids, n_blocks,
@@ -139,7 +148,8 @@ static locks_status score_checks(const locks_dims* dims, const void* q, const vo
   if (!q || !summaries || !block_table || !seq_lens) return LOCKS_ERR_NULL;
   if (batch <= 0 || max_pages <= 0 || max_pages > kMaxPages || num_blocks <= 0)
     return LOCKS_ERR_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(summaries) & 15))
+  if (misaligned(q, 16) || misaligned(summaries, 16) || misaligned(block_table, 4) ||
+      misaligned(seq_lens, 4))
     return LOCKS_ERR_SHAPE;
   if (batch > 65535 || dims->num_kv_heads > 65535) return LOCKS_ERR_SHAPE;
   return LOCKS_OK;
@@ -152,8 +162,10 @@ locks_status locks_score_pages(const locks_dims* dims, const void* q, const void
   locks_status st = score_checks(dims, q, summaries, num_blocks, block_table, max_pages, seq_lens, batch);
   if (st != LOCKS_OK) return st;
   if (!page_lse) return LOCKS_ERR_NULL;
+  if (misaligned(page_lse, 4)) return LOCKS_ERR_SHAPE;
   const ScoreWs w = score_ws_layout(dims, batch, max_pages, 0, true);
-  if (!workspace || workspace_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < w.total || misaligned(workspace, 16))
+    return LOCKS_ERR_WORKSPACE;
   hipError_t e = launch_score(dims->rank, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(summaries),
                               num_blocks, block_table, max_pages, seq_lens, batch,
                               dims->num_q_heads, dims->num_kv_heads, dims->newest_page_pending,
@@ -174,8 +186,12 @@ static locks_status select_pages_impl(const locks_dims* dims, const float* page_
   if (!page_lse || !seq_lens || !sel || !sel_count) return LOCKS_ERR_NULL;
   if (batch <= 0 || max_pages <= 0 || max_pages > kMaxPages || budget_pages <= 0)
     return LOCKS_ERR_SHAPE;
+  if (misaligned(page_lse, 4) || misaligned(seq_lens, 4) || misaligned(sel, 4) ||
+      misaligned(sel_count, 4))
+    return LOCKS_ERR_SHAPE;
   const ScoreWs w = score_ws_layout(dims, batch, max_pages, budget_pages, true);
-  if (!workspace || workspace_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < w.total || misaligned(workspace, 16))
+    return LOCKS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float2* part = reinterpret_cast<float2*>(ws_at(workspace, w.part_off));
   const int32_t pend = dims->newest_page_pending;
@@ -217,8 +233,11 @@ locks_status locks_score_select(const locks_dims* dims, const void* q, const voi
   if (st != LOCKS_OK) return st;
   if (!sel || !sel_count) return LOCKS_ERR_NULL;
   if (budget_pages <= 0) return LOCKS_ERR_SHAPE;
+  if (misaligned(sel, 4) || misaligned(sel_count, 4) || misaligned(page_lse, 4))
+    return LOCKS_ERR_SHAPE;
   const ScoreWs w = score_ws_layout(dims, batch, max_pages, budget_pages, true);
-  if (!workspace || workspace_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < w.total || misaligned(workspace, 16))
+    return LOCKS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* lse = page_lse ? page_lse : reinterpret_cast<float*>(ws_at(workspace, w.lse_off));
   float2* part = reinterpret_cast<float2*>(ws_at(workspace, w.part_off));
@@ -252,18 +271,19 @@ static locks_status decode_layer_impl(const locks_dims* dims, const void* q,
   if (layout.token_stride < 128 || layout.block_stride <= 0 || layout.head_stride <= 0 ||
       (layout.token_stride % 8) || (layout.head_stride % 8) || (layout.block_stride % 8))
     return LOCKS_ERR_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(k_cache) & 15) || (reinterpret_cast<uintptr_t>(v_cache) & 15))
+  if (misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(sel, 4) ||
+      misaligned(sel_count, 4) || misaligned(out, 4) || misaligned(out_lse, 4))
     return LOCKS_ERR_SHAPE;
   if (!(softmax_scale > 0.f) || softmax_scale != softmax_scale) return LOCKS_ERR_SHAPE;
   const ScoreWs w = score_ws_layout(dims, batch, max_pages, budget_pages, true);
   const AttendWs a = attend_ws_layout(dims, batch, budget_pages + 1);
-  if (!score_ws) return LOCKS_ERR_WORKSPACE;
+  if (!score_ws || misaligned(score_ws, 16) || misaligned(attend_ws, 16))
+    return LOCKS_ERR_WORKSPACE;
   if (attend_ws) {
     if (score_ws_bytes < w.total || attend_ws_bytes < a.total) return LOCKS_ERR_WORKSPACE;
   } else {
     // one workspace: the attention part follows the scoring part
     if (score_ws_bytes < align_up(w.total) + a.total) return LOCKS_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(score_ws) & 15) return LOCKS_ERR_WORKSPACE;
     attend_ws = ws_at(score_ws, align_up(w.total));
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -417,7 +437,9 @@ locks_status locks_finalize_pages(const locks_dims* dims, const void* k_cache,
   if (layout.token_stride < 128 || layout.block_stride <= 0 || layout.head_stride <= 0 ||
       (layout.token_stride % 8) || (layout.head_stride % 8) || (layout.block_stride % 8))
     return LOCKS_ERR_SHAPE;
-  if (reinterpret_cast<uintptr_t>(k_cache) & 15) return LOCKS_ERR_SHAPE;
+  if (misaligned(k_cache, 16) || misaligned(summaries, 16) || misaligned(block_table, 4) ||
+      misaligned(seq_lens, 4))
+    return LOCKS_ERR_SHAPE;
   if (n_layers <= 0 || n_layers > 65535 || (n_layers > 1 && (k_layer_stride <= 0 ||
       summ_layer_stride <= 0 || (k_layer_stride % 8) || (summ_layer_stride % 16))))
     return LOCKS_ERR_SHAPE;
@@ -442,7 +464,8 @@ locks_status locks_exact_page_lse(const locks_dims* dims, const void* q, const v
   if (layout.token_stride < 128 || layout.block_stride <= 0 || layout.head_stride <= 0 ||
       (layout.token_stride % 8) || (layout.head_stride % 8) || (layout.block_stride % 8))
     return LOCKS_ERR_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(k_cache) & 15))
+  if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(block_table, 4) ||
+      misaligned(seq_lens, 4) || misaligned(page_lse, 4))
     return LOCKS_ERR_SHAPE;
   if (!(softmax_scale > 0.f) || softmax_scale != softmax_scale) return LOCKS_ERR_SHAPE;
   hipError_t e = launch_exact_lse(static_cast<const uint16_t*>(q),
@@ -475,13 +498,15 @@ static locks_status sparse_attend_impl(const locks_dims* dims, const void* q,
   if (layout.token_stride < 128 || layout.block_stride <= 0 || layout.head_stride <= 0 ||
       (layout.token_stride % 8) || (layout.head_stride % 8) || (layout.block_stride % 8))
     return LOCKS_ERR_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(k_cache) & 15) ||
-      (reinterpret_cast<uintptr_t>(v_cache) & 15))
+  if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) ||
+      misaligned(block_table, 4) || misaligned(seq_lens, 4) || misaligned(sel, 4) ||
+      misaligned(sel_count, 4) || misaligned(out, 4) || misaligned(out_lse, 4))
     return LOCKS_ERR_SHAPE;
   if (!(softmax_scale > 0.f) || softmax_scale != softmax_scale) return LOCKS_ERR_SHAPE;
   const int32_t max_att = (sel ? budget_pages : max_pages) + 1;
   const AttendWs w = attend_ws_layout(dims, batch, max_att);
-  if (!workspace || workspace_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < w.total || misaligned(workspace, 16))
+    return LOCKS_ERR_WORKSPACE;
   hipError_t e = launch_attend(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
       static_cast<const uint16_t*>(v_cache), layout.block_stride, layout.head_stride,
@@ -530,7 +555,7 @@ static locks_status kv_layout_checks(const void* k_cache, locks_kv_layout layout
   if (layout.token_stride < 128 || layout.block_stride <= 0 || layout.head_stride <= 0 ||
       (layout.token_stride % 8) || (layout.head_stride % 8) || (layout.block_stride % 8))
     return LOCKS_ERR_SHAPE;
-  if (reinterpret_cast<uintptr_t>(k_cache) & 15) return LOCKS_ERR_SHAPE;
+  if (misaligned(k_cache, 16)) return LOCKS_ERR_SHAPE;
   return LOCKS_OK;
 }
 
@@ -545,11 +570,11 @@ locks_status locks_shared_basis(const locks_dims* dims, const void* k_cache,
   if (n_blocks <= 0 || num_blocks <= 0 || dims->num_kv_heads > 65535) return LOCKS_ERR_SHAPE;
   st = kv_layout_checks(k_cache, layout);
   if (st != LOCKS_OK) return st;
-  if ((reinterpret_cast<uintptr_t>(basis) & 3) || (reinterpret_cast<uintptr_t>(eigvals) & 3))
+  if (misaligned(basis, 4) || misaligned(eigvals, 4) || misaligned(block_ids, 4))
     return LOCKS_ERR_SHAPE;
   const SharedPlan pl = plan_shared(n_blocks);
   const size_t need = locks_shared_basis_workspace_bytes(dims, n_blocks);
-  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15))
+  if (!workspace || workspace_bytes < need || misaligned(workspace, 16))
     return LOCKS_ERR_WORKSPACE;
   hipError_t e = launch_shared_basis(dims->rank, static_cast<const uint16_t*>(k_cache),
                                      layout.block_stride,
@@ -571,7 +596,7 @@ locks_status locks_build_summaries_basis(const locks_dims* dims, const void* k_c
   if (!k_cache || !block_ids || !basis || !summaries) return LOCKS_ERR_NULL;
   st = kv_layout_checks(k_cache, layout);
   if (st != LOCKS_OK) return st;
-  if ((reinterpret_cast<uintptr_t>(summaries) & 15) || (reinterpret_cast<uintptr_t>(basis) & 3))
+  if (misaligned(summaries, 16) || misaligned(basis, 4) || misaligned(block_ids, 4))
     return LOCKS_ERR_SHAPE;
   hipError_t e = launch_build_basis(dims->rank, static_cast<const uint16_t*>(k_cache),
                                     layout.block_stride,

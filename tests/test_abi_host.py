@@ -194,6 +194,68 @@ def test_validation_errors_launch_nothing():
                                  P(256), 1 << 40, None) == L.ERR_SHAPE
 
 
+def test_misaligned_buffers_are_refused_before_any_launch():
+    """16 bytes for q / K / V / summaries and workspaces, 4 bytes for int32
+    and fp32 arrays and the bf16 output; the fake pointers never reach a
+    kernel because validation fails first."""
+    lib = _lib_or_skip()
+    d = L.dims(32, 8)
+    P = ctypes.c_void_p
+    A, W = P(256), 1 << 40
+
+    def score(q=A, summ=A, bt=A, seq=A, lse=A, ws=A):
+        return lib.locks_score_pages(ctypes.byref(d), q, summ, 4, bt, 4, seq, 1, lse, ws, W, None)
+
+    assert score(summ=P(264)) == L.ERR_SHAPE
+    assert score(bt=P(258)) == L.ERR_SHAPE
+    assert score(seq=P(258)) == L.ERR_SHAPE
+    assert score(lse=P(258)) == L.ERR_SHAPE
+    assert score(ws=P(264)) == L.ERR_WORKSPACE
+
+    def select(lse=A, seq=A, sel=A, cnt=A, ws=A):
+        return lib.locks_select_pages(ctypes.byref(d), lse, 16, seq, 1, 4, sel, cnt, ws, W, None)
+
+    assert select(lse=P(258)) == L.ERR_SHAPE
+    assert select(sel=P(258)) == L.ERR_SHAPE
+    assert select(cnt=P(258)) == L.ERR_SHAPE
+    assert select(ws=P(264)) == L.ERR_WORKSPACE
+
+    def score_select(sel=A, cnt=A, lse=None, ws=A):
+        return lib.locks_score_select(ctypes.byref(d), A, A, 4, A, 4, A, 1, 4, sel, cnt, lse, ws,
+                                      W, None)
+
+    assert score_select(sel=P(258)) == L.ERR_SHAPE
+    assert score_select(lse=P(258)) == L.ERR_SHAPE
+    assert score_select(ws=P(264)) == L.ERR_WORKSPACE
+
+    lay = L.KVLayout(16384, 2048, 128)
+
+    def attend(q=A, k=A, v=A, sel=A, cnt=A, out=A, olse=None, ws=A):
+        return lib.locks_sparse_attend(ctypes.byref(d), q, k, v, lay, 4, A, 4, A, 1, sel, cnt, 4,
+                                       0.1, out, olse, ws, W, None)
+
+    assert attend(v=P(264)) == L.ERR_SHAPE
+    assert attend(out=P(258)) == L.ERR_SHAPE
+    assert attend(olse=P(258)) == L.ERR_SHAPE
+    assert attend(sel=P(258)) == L.ERR_SHAPE
+    assert attend(ws=P(264)) == L.ERR_WORKSPACE
+
+    def layer(out=A, ws=A, att=None, att_bytes=0):
+        return lib.locks_decode_layer(ctypes.byref(d), A, A, A, A, lay, 4, A, 4, A, 1, 4, 0.1, A,
+                                      A, out, None, ws, W, att, att_bytes, None)
+
+    assert layer(out=P(258)) == L.ERR_SHAPE
+    assert layer(ws=P(264), att=A, att_bytes=W) == L.ERR_WORKSPACE
+    assert layer(att=P(264), att_bytes=W) == L.ERR_WORKSPACE
+
+    assert lib.locks_exact_page_lse(ctypes.byref(d), A, A, lay, 4, A, 4, A, 1, 0.1, P(258),
+                                    None) == L.ERR_SHAPE
+    assert lib.locks_finalize_pages(ctypes.byref(d), A, lay, 4, A, 4, A, 1, P(264), 1, 0, 0,
+                                    None) == L.ERR_SHAPE
+    assert lib.locks_build_summaries(ctypes.byref(d), A, lay, P(258), 3, 4, A, None,
+                                     None) == L.ERR_SHAPE
+
+
 def test_attend_and_build_validation():
     lib = _lib_or_skip()
     d = L.dims(4, 1)
