@@ -137,11 +137,11 @@ class DecodeStep:
         self.graph.replay()
 
 
-def build_all_layers(d, k, summaries, n_fin_blocks=None):
-    """Summarize every block of every layer (prefill finalization)."""
+def build_all_layers(d, k, summaries, blocks=None):
+    """Summarize the given physical blocks (int32 device tensor; default:
+    every block) of every layer (prefill finalization)."""
     n_layers, nb = k.shape[0], k.shape[1]
-    blocks = torch.arange(nb, dtype=torch.int32, device=k.device)
-    if n_fin_blocks is not None:
-        blocks = n_fin_blocks
+    if blocks is None:
+        blocks = torch.arange(nb, dtype=torch.int32, device=k.device)
     for layer in range(n_layers):
         L.build_summaries(d, k[layer], blocks, summaries[layer])
