@@ -72,8 +72,9 @@ def parse():
                     help="layers sampled for the quality report")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run a plain 1 GiB copy kernel (byte-counter calibration)")
-    ap.add_argument("--kernel-reps", type=int, default=5,
-                    help="rounds of per-layer scorer / attention launches timed in isolation")
+    ap.add_argument("--kernel-reps", type=int, default=20,
+                    help="timed replays of the graph of per-layer scorer / attention launches "
+                         "(median reported)")
     return ap.parse_args()
 
 
@@ -101,6 +102,33 @@ def timed(fn, reps, warm=1):
     torch.cuda.synchronize()
     del g
     return e0.elapsed_time(e1) / reps
+
+
+def timed_replays(fn, reps, warm=1):
+    """ms of each of `reps` replays of fn() captured in one graph, each replay
+    between its own pair of HIP events on the launch stream."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    del g
+    return [a.elapsed_time(b) for a, b in ev]
 
 
 def replay_times(step, n):
@@ -414,38 +442,51 @@ def traffic_if_current(workload):
 
 def kernel_rates(w, d, inp, summ, step, budget, reps):
     """The scorer and the stand-alone attention (with its split merge), each
-    timed in isolation over all layers from one captured graph on its launch
-    stream (`timed`: HIP events around `reps` replays of every layer's
-    launch, back to back).  Returns a dict: mean microseconds per launch and
-    GB/s from the algorithmic bytes (848 per scored page-head, 8192 per
-    attended page-head), and the selected page-heads per layer."""
+    timed in isolation from one captured graph of every layer's launch, back
+    to back (each layer's launch repeated so that a graph holds at least 16
+    launches), on its launch stream: `reps` replays, each between its own
+    pair of HIP events.  Returns a dict: the mean microseconds per launch
+    over all replays (and p10 / p50 / p90 of the replays' own means), GB/s
+    from the algorithmic bytes (848 per scored page-head, 8192 per attended
+    page-head), and the selected page-heads per layer."""
     import torch
     from kv_cache_page_int4_amd import locks as L
 
     P = inp.block_table.shape[1]
     lse_buf = torch.empty((w.batch, w.hq, P), dtype=torch.float32, device="cuda")
 
+    rounds = -(-16 // w.layers)   # passes over the layers per replay
+    launches = rounds * w.layers
+
     def score_all_layers():
-        for layer in range(w.layers):
-            L.score_pages(d, inp.q[layer], summ[layer], w.num_blocks, inp.block_table,
-                          inp.seq_lens, lse_buf, step.ws_score)
+        for _ in range(rounds):
+            for layer in range(w.layers):
+                L.score_pages(d, inp.q[layer], summ[layer], w.num_blocks, inp.block_table,
+                              inp.seq_lens, lse_buf, step.ws_score)
 
     def attend_all_layers():
-        for layer in range(w.layers):
-            L.sparse_attend(d, inp.q[layer], inp.k[layer], inp.v[layer], inp.block_table,
-                            inp.seq_lens, step.sel[layer], step.cnt[layer], budget,
-                            step.out[layer], step.ws_att)
+        for _ in range(rounds):
+            for layer in range(w.layers):
+                L.sparse_attend(d, inp.q[layer], inp.k[layer], inp.v[layer], inp.block_table,
+                                inp.seq_lens, step.sel[layer], step.cnt[layer], budget,
+                                step.out[layer], step.ws_att)
 
-    score_ms = timed(score_all_layers, reps) / w.layers
-    attend_ms = timed(attend_all_layers, reps) / w.layers
+    def per_launch_us(fn):
+        import numpy as np
+        us = np.array(timed_replays(fn, reps)) * 1e3 / launches
+        p10, p50, p90 = np.percentile(us, [10, 50, 90])
+        return float(us.mean()), [round(float(x), 3) for x in (p10, p50, p90)]
+
+    score_us, score_pct = per_launch_us(score_all_layers)
+    attend_us, attend_pct = per_launch_us(attend_all_layers)
     page_heads = w.batch * w.hkv * w.pages
     att_units = int(step.cnt.sum().item()) / w.layers
     del lse_buf
-    return {"score_us": score_ms * 1e3,
-            "score_gbs": page_heads * SCORE_BYTES_PER_PAGE_HEAD / (score_ms * 1e-3) / 1e9,
-            "attend_us": attend_ms * 1e3,
-            "attend_gbs": att_units * ATTEND_BYTES_PER_PAGE_HEAD / (attend_ms * 1e-3) / 1e9,
-            "att_units": att_units, "launches": w.layers * reps}
+    return {"score_us": score_us, "score_us_p10_p50_p90": score_pct,
+            "score_gbs": page_heads * SCORE_BYTES_PER_PAGE_HEAD / (score_us * 1e-6) / 1e9,
+            "attend_us": attend_us, "attend_us_p10_p50_p90": attend_pct,
+            "attend_gbs": att_units * ATTEND_BYTES_PER_PAGE_HEAD / (attend_us * 1e-6) / 1e9,
+            "att_units": att_units, "launches": launches * reps}
 
 
 def finalize_timing(w, d, inp, summ, budget, steps, ms_plain):
@@ -782,13 +823,16 @@ def main():
                      "traffic_gbs": (round(traffic / (score_us * 1e-6) / 1e9, 1)
                                      if traffic else None),
                      "kernel_us": round(score_us, 3),
+                     "kernel_us_replays_p10_p50_p90": kr["score_us_p10_p50_p90"],
                      "launches_timed": kr["launches"],
                      "bytes_per_launch": page_heads * SCORE_BYTES_PER_PAGE_HEAD,
-                     "timing": ("HIP events on the launch stream around graph replays of every "
-                                "layer's locks_score_pages launch, back to back")},
+                     "timing": ("mean over graph replays of every layer's "
+                                "locks_score_pages launch, back to back, each replay between "
+                                "its own HIP events on the launch stream")},
         "attention": {"achieved": round(attend_gbs, 1), "unit": "GB/s",
                       "frac": round(attend_gbs / PEAK_HBM_GBS, 4),
                       "kernel_us": round(attend_us, 3),
+                      "kernel_us_replays_p10_p50_p90": kr["attend_us_p10_p50_p90"],
                       "note": ("attention + split merge, selected K/V bytes only; "
                                f"{att_units * ATTEND_BYTES_PER_PAGE_HEAD / 2**20:.1f} MiB per "
                                "layer is latency-bound, see also.*.attention_gbs for the "
