@@ -86,18 +86,29 @@ struct RecLayout {
   static constexpr int kWSc = kWSv + R / 2, kWSmu = kWSc + R / 2;
 };
 
+// LDS of one build (one wave).  The keys stay as their bf16 bits and are
+// centred again where they are read (k - mu in fp32, the same values the
+// centring step computes), which halves their footprint; the eigen-solver's
+// matrices are dead once the basis is formed, and the packing buffers take
+// their place.  About 11.9 KB at rank 8, so that 13 builds fit a CU.
 template <int R>
 struct BuildSmem {
-  float X[kB][kD + 4];     // centered keys
-  float G[kB][kB + 1];     // Gram matrix -> eigenvalues on the diagonal
-  float U[kB][kB + 1];     // eigenvectors (columns)
-  float cs[8][2] __attribute__((aligned(16)));   // rotations of the current step
+  uint16_t K[kB][kD + 8] __attribute__((aligned(16)));  // keys, bf16 bits (row stride 68 words)
+  union {
+    struct {
+      float G[kB][kB + 1];     // Gram matrix -> eigenvalues on the diagonal
+      float U[kB][kB + 1];     // eigenvectors (columns)
+      float cs[8][2] __attribute__((aligned(16)));   // rotations of the current step
+    } e;                       // eigen-solver, until the basis is formed
+    struct {
+      int8_t vq[R][kD];
+      uint32_t rec[RecLayout<R>::kBytes / 4];
+    } q;                       // quantization and packing, after it
+  } u;
   float V[R][kD + 4];      // unquantized basis, [k][d]
   float C[kB][R];          // unquantized coefficients
-  float mu[kD];
+  float mu[kD] __attribute__((aligned(16)));
   int order[kB];
-  int8_t vq[R][kD];
-  uint32_t rec[RecLayout<R>::kBytes / 4];
 };
 
 // Which block a workgroup summarizes: entry blockIdx.x of a list, or (for
@@ -146,6 +157,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const uint4 v = *reinterpret_cast<const uint4*>(kp + 8 * s);
+    *reinterpret_cast<uint4*>(&sm.K[t][32 * g + 8 * s]) = v;
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -161,8 +173,6 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     if (t == 0) sm.mu[32 * g + e] = m;
   }
   ksq = wave_sum(ksq);
-#pragma unroll
-  for (int e = 0; e < 32; ++e) sm.X[t][32 * g + e] = x[e];
 
   const int d0 = 2 * lane;   // basis dims owned by this lane: d0, d0 + 1
   if (basis) {
@@ -179,16 +189,16 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 #pragma unroll
     for (int s = 0; s < 32; ++s) gacc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], x[s], gacc, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.G[4 * g + r][t] = gacc[r];
-    for (int i = lane; i < kB * kB; i += 64) sm.U[i >> 4][i & 15] = ((i >> 4) == (i & 15)) ? 1.f : 0.f;
+    for (int r = 0; r < 4; ++r) sm.u.e.G[4 * g + r][t] = gacc[r];
+    for (int i = lane; i < kB * kB; i += 64) sm.u.e.U[i >> 4][i & 15] = ((i >> 4) == (i & 15)) ? 1.f : 0.f;
     __syncthreads();
     // symmetrize (the product is symmetric up to rounding order)
     for (int i = lane; i < kB * kB; i += 64) {
       const int a = i >> 4, b = i & 15;
       if (a < b) {
-        const float v = 0.5f * (sm.G[a][b] + sm.G[b][a]);
-        sm.G[a][b] = v;
-        sm.G[b][a] = v;
+        const float v = 0.5f * (sm.u.e.G[a][b] + sm.u.e.G[b][a]);
+        sm.u.e.G[a][b] = v;
+        sm.u.e.G[b][a] = v;
       }
     }
     __syncthreads();
@@ -217,22 +227,22 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
         const int hb = 31 - __builtin_clz(m);
         auto pair_p = [&](int pi) { return ((pi >> hb) << (hb + 1)) | (pi & ((1 << hb) - 1)); };
         const int a0 = pair_p(iav), a1 = a0 ^ m, b0 = pair_p(ibv), b1 = b0 ^ m;
-        const float g00 = sm.G[a0][b0], g01 = sm.G[a0][b1], g10 = sm.G[a1][b0], g11 = sm.G[a1][b1];
+        const float g00 = sm.u.e.G[a0][b0], g01 = sm.u.e.G[a0][b1], g10 = sm.u.e.G[a1][b0], g11 = sm.u.e.G[a1][b1];
         {
           // every lane computes (branch-free); the diagonal lanes publish
           float c, s;
           jacobi_rot(g00, 0.5f * (g01 + g10), g11, c, s);
-          if (ia == ib) *reinterpret_cast<float2*>(sm.cs[ia]) = make_float2(c, s);
+          if (ia == ib) *reinterpret_cast<float2*>(sm.u.e.cs[ia]) = make_float2(c, s);
         }
         // one wave: its LDS accesses complete in program order, so the reads
         // below see the rotations just written; only the compiler is kept
         // from reordering them.  All of the step's rotations are read at once.
         asm volatile("" ::: "memory");
-        const float2 csa = *reinterpret_cast<const float2*>(sm.cs[ia]);
-        const float2 csb = *reinterpret_cast<const float2*>(sm.cs[ib]);
+        const float2 csa = *reinterpret_cast<const float2*>(sm.u.e.cs[ia]);
+        const float2 csb = *reinterpret_cast<const float2*>(sm.u.e.cs[ib]);
         float4 cs4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cs4[i] = *reinterpret_cast<const float4*>(&sm.cs[2 * i][0]);
+        for (int i = 0; i < 4; ++i) cs4[i] = *reinterpret_cast<const float4*>(&sm.u.e.cs[2 * i][0]);
         const float ca = csa.x, sa = csa.y, cb = csb.x, sb = csb.y;
         // T = G J (columns b0, b1), then G' = J^T T (rows a0, a1)
         const float t00 = g00 * cb - g01 * sb, t01 = g00 * sb + g01 * cb;
@@ -243,10 +253,10 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
           n01 = 0.f;
           n10 = 0.f;
         }
-        sm.G[a0][b0] = n00;
-        sm.G[a0][b1] = n01;
-        sm.G[a1][b0] = n10;
-        sm.G[a1][b1] = n11;
+        sm.u.e.G[a0][b0] = n00;
+        sm.u.e.G[a0][b1] = n01;
+        sm.u.e.G[a1][b0] = n10;
+        sm.u.e.G[a1][b1] = n11;
         // U' = U J on this lane's row: all 8 rotations
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -270,7 +280,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * lane + e, a = i >> 4, b = i & 15;
-        const float v = sm.G[a][b];
+        const float v = sm.u.e.G[a][b];
         tot = fmaf(v, v, tot);
         if (a != b) off = fmaf(v, v, off);
       }
@@ -280,40 +290,44 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     }
     if (lane < kB) {
 #pragma unroll
-      for (int j = 0; j < kB; ++j) sm.U[urow][j] = u[j];
+      for (int j = 0; j < kB; ++j) sm.u.e.U[urow][j] = u[j];
     }
 
     // ---- 4. order eigenpairs: descending eigenvalue, ties to the lower index ----
     if (lane < 16) {
-      const float lj = sm.G[lane][lane];
+      const float lj = sm.u.e.G[lane][lane];
       int rank = 0;
       for (int i = 0; i < 16; ++i) {
-        const float li = sm.G[i][i];
+        const float li = sm.u.e.G[i][i];
         rank += (li > lj) || (li == lj && i < lane);
       }
       sm.order[rank] = lane;
     }
     __syncthreads();
-    const float lam1 = sm.G[sm.order[0]][sm.order[0]];
+    const float lam1 = sm.u.e.G[sm.order[0]][sm.order[0]];
     const bool page_has_basis = lam1 > kEpsConst * ksq;
 
     // basis v_k = X^T u_k / |X^T u_k|; lane owns dims 2*lane, 2*lane+1
+    const float mu0 = sm.mu[d0], mu1 = sm.mu[d0 + 1];
     float2 xr[kB];
 #pragma unroll
-    for (int tt = 0; tt < kB; ++tt) xr[tt] = *reinterpret_cast<const float2*>(&sm.X[tt][d0]);
+    for (int tt = 0; tt < kB; ++tt) {
+      const uint32_t kw = *reinterpret_cast<const uint32_t*>(&sm.K[tt][d0]);
+      xr[tt] = make_float2(bf16_lo(kw) - mu0, bf16_hi(kw) - mu1);
+    }
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const int j = sm.order[k];
-      const float lk = sm.G[j][j];
+      const float lk = sm.u.e.G[j][j];
       const bool keep = page_has_basis && (lk > kTau * lam1);
       float v0 = 0.f, v1 = 0.f;
 #pragma unroll
       for (int tt = 0; tt < kB; ++tt) {
-        const float uu = sm.U[tt][j];
+        const float uu = sm.u.e.U[tt][j];
         v0 = fmaf(xr[tt].x, uu, v0);
         v1 = fmaf(xr[tt].y, uu, v1);
       }
-      const float nrm2 = wave_sum(v0 * v0 + v1 * v1);
+      const float nrm2 = wave_sum(fmaf(v1, v1, v0 * v0));
       const float inv = (keep && nrm2 > 0.f) ? 1.f / sqrtf(nrm2) : 0.f;
       v0 *= inv;
       v1 *= inv;
@@ -342,10 +356,14 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     float cc[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) cc[j] = 0.f;
-    for (int d = 0; d < kD; ++d) {
-      const float xv = sm.X[tk][d];
+    for (int d = 0; d < kD; d += 2) {
+      const uint32_t kw = *reinterpret_cast<const uint32_t*>(&sm.K[tk][d]);
+      const float2 m = *reinterpret_cast<const float2*>(&sm.mu[d]);
+      const float xa = bf16_lo(kw) - m.x, xb = bf16_hi(kw) - m.y;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) cc[j] = fmaf(xv, sm.V[k0 + j][d], cc[j]);
+      for (int j = 0; j < kPer; ++j) cc[j] = fmaf(xa, sm.V[k0 + j][d], cc[j]);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) cc[j] = fmaf(xb, sm.V[k0 + j][d + 1], cc[j]);
     }
 #pragma unroll
     for (int j = 0; j < kPer; ++j) sm.C[tk][k0 + j] = cc[j];
@@ -363,8 +381,8 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
   for (int k = 0; k < R; ++k) {
     const float a = sm.V[k][d0], b2 = sm.V[k][d0 + 1];
     s_v[k] = fp16_scale(wave_max(fmaxf(fabsf(a), fabsf(b2))), 7.f);
-    sm.vq[k][d0] = (int8_t)quant(a, s_v[k], 7);
-    sm.vq[k][d0 + 1] = (int8_t)quant(b2, s_v[k], 7);
+    sm.u.q.vq[k][d0] = (int8_t)quant(a, s_v[k], 7);
+    sm.u.q.vq[k][d0 + 1] = (int8_t)quant(b2, s_v[k], 7);
   }
   // coefficient scales: column k max over the 16 tokens
   float s_c[R];
@@ -375,7 +393,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
   }
   __syncthreads();
   // record words: basis, coefficients, centroid, s_V, s_c, s_mu, zero
-  uint8_t* mub = reinterpret_cast<uint8_t*>(&sm.rec[RL::kWMu]);
+  uint8_t* mub = reinterpret_cast<uint8_t*>(&sm.u.q.rec[RL::kWMu]);
   mub[d0] = (uint8_t)(int8_t)mq0;
   mub[d0 + 1] = (uint8_t)(int8_t)mq1;
   for (int wi = lane; wi < 16 * R; wi += 64) {
@@ -383,11 +401,11 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     uint32_t word = 0;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint32_t lo = (uint32_t)sm.vq[k][8 * w + m] & 0xFu;
-      const uint32_t hi = (uint32_t)sm.vq[k][8 * w + 4 + m] & 0xFu;
+      const uint32_t lo = (uint32_t)sm.u.q.vq[k][8 * w + m] & 0xFu;
+      const uint32_t hi = (uint32_t)sm.u.q.vq[k][8 * w + 4 + m] & 0xFu;
       word |= (lo | (hi << 4)) << (8 * m);
     }
-    sm.rec[wi] = word;
+    sm.u.q.rec[wi] = word;
   }
   // coefficient words: token tk holds R/4 words of 4 codes each
   if (lane < 4 * R) {
@@ -401,21 +419,21 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
       for (int k = 1; k < R; ++k) sce = (k == kh + e) ? s_c[k] : sce;
       word |= ((uint32_t)(uint8_t)(int8_t)quant(sm.C[tk][kh + e], sce, 127)) << (8 * e);
     }
-    sm.rec[RL::kWC + lane] = word;
+    sm.u.q.rec[RL::kWC + lane] = word;
   }
   if (lane == 0) {
 #pragma unroll
     for (int i = 0; i < R / 2; ++i) {
-      sm.rec[RL::kWSv + i] = fp16_bits(s_v[2 * i]) | (fp16_bits(s_v[2 * i + 1]) << 16);
-      sm.rec[RL::kWSc + i] = fp16_bits(s_c[2 * i]) | (fp16_bits(s_c[2 * i + 1]) << 16);
+      sm.u.q.rec[RL::kWSv + i] = fp16_bits(s_v[2 * i]) | (fp16_bits(s_v[2 * i + 1]) << 16);
+      sm.u.q.rec[RL::kWSc + i] = fp16_bits(s_c[2 * i]) | (fp16_bits(s_c[2 * i + 1]) << 16);
     }
-    sm.rec[RL::kWSmu] = fp16_bits(s_mu);
-    for (int i = RL::kWSmu + 1; i < RL::kBytes / 4; ++i) sm.rec[i] = 0u;
+    sm.u.q.rec[RL::kWSmu] = fp16_bits(s_mu);
+    for (int i = RL::kWSmu + 1; i < RL::kBytes / 4; ++i) sm.u.q.rec[i] = 0u;
   }
   __syncthreads();
   uint32_t* dst =
       reinterpret_cast<uint32_t*>(summ + ((size_t)kvh * num_blocks + blk) * RL::kBytes);
-  for (int wi = lane; wi < RL::kBytes / 4; wi += 64) dst[wi] = sm.rec[wi];
+  for (int wi = lane; wi < RL::kBytes / 4; wi += 64) dst[wi] = sm.u.q.rec[wi];
 
   if (raw) {   // [128 + 144 R] floats: mu, V [R][128], C [16][R]
     float* r = raw + ((size_t)bi * hkv + kvh) * raw_floats(R);
