@@ -86,14 +86,14 @@ struct RecLayout {
   static constexpr int kWSc = kWSv + R / 2, kWSmu = kWSc + R / 2;
 };
 
-// LDS of one build (one wave).  The keys stay as their bf16 bits and are
-// centred again where they are read (k - mu in fp32, the same values the
-// centring step computes), which halves their footprint; the eigen-solver's
-// matrices are dead once the basis is formed, and the packing buffers take
-// their place.  About 11.9 KB at rank 8, so that 13 builds fit a CU.
+// LDS of one build (one wave).  The keys are not kept: the basis and the
+// coefficients read the page-head's 4 KB again (from L2, where the first
+// read left it) and centre it again (k - mu in fp32, the same values the
+// centring step computes).  The eigen-solver's matrices are dead once the
+// basis is formed, and the packing buffers and the coefficients take their
+// place.  7 KB at rank 8: the registers, not the LDS, bound the builds per CU.
 template <int R>
 struct BuildSmem {
-  uint16_t K[kB][kD + 8] __attribute__((aligned(16)));  // keys, bf16 bits (row stride 68 words)
   union {
     struct {
       float G[kB][kB + 1];     // Gram matrix -> eigenvalues on the diagonal
@@ -103,10 +103,10 @@ struct BuildSmem {
     struct {
       int8_t vq[R][kD];
       uint32_t rec[RecLayout<R>::kBytes / 4];
-    } q;                       // quantization and packing, after it
+      float C[kB][R];          // unquantized coefficients
+    } q;                       // coefficients, quantization and packing, after it
   } u;
   float V[R][kD + 4];      // unquantized basis, [k][d]
-  float C[kB][R];          // unquantized coefficients
   float mu[kD] __attribute__((aligned(16)));
   int order[kB];
 };
@@ -157,7 +157,6 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const uint4 v = *reinterpret_cast<const uint4*>(kp + 8 * s);
-    *reinterpret_cast<uint4*>(&sm.K[t][32 * g + 8 * s]) = v;
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -175,6 +174,11 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
   ksq = wave_sum(ksq);
 
   const int d0 = 2 * lane;   // basis dims owned by this lane: d0, d0 + 1
+  // this page-head's keys, read again below: token tt, dims d .. d + 1
+  const uint16_t* kpage = kc + (size_t)blk * bs + (size_t)kvh * hs;
+  auto key_pair = [&](int tt, int d) {
+    return *reinterpret_cast<const uint32_t*>(kpage + (size_t)tt * ts + d);
+  };
   if (basis) {
     const float* bk = basis + (size_t)kvh * R * kD;
 #pragma unroll
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     float2 xr[kB];
 #pragma unroll
     for (int tt = 0; tt < kB; ++tt) {
-      const uint32_t kw = *reinterpret_cast<const uint32_t*>(&sm.K[tt][d0]);
+      const uint32_t kw = key_pair(tt, d0);
       xr[tt] = make_float2(bf16_lo(kw) - mu0, bf16_hi(kw) - mu1);
     }
 #pragma unroll
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < kPer; ++j) cc[j] = 0.f;
     for (int d = 0; d < kD; d += 2) {
-      const uint32_t kw = *reinterpret_cast<const uint32_t*>(&sm.K[tk][d]);
+      const uint32_t kw = key_pair(tk, d);
       const float2 m = *reinterpret_cast<const float2*>(&sm.mu[d]);
       const float xa = bf16_lo(kw) - m.x, xb = bf16_hi(kw) - m.y;
 #pragma unroll
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
       for (int j = 0; j < kPer; ++j) cc[j] = fmaf(xb, sm.V[k0 + j][d + 1], cc[j]);
     }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) sm.C[tk][k0 + j] = cc[j];
+    for (int j = 0; j < kPer; ++j) sm.u.q.C[tk][k0 + j] = cc[j];
   }
   __syncthreads();
 
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
   float s_c[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
-    const float a = (lane < 16) ? fabsf(sm.C[lane][k]) : 0.f;
+    const float a = (lane < 16) ? fabsf(sm.u.q.C[lane][k]) : 0.f;
     s_c[k] = fp16_scale(wave_max(a), 127.f);
   }
   __syncthreads();
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
       float sce = s_c[0];
 #pragma unroll
       for (int k = 1; k < R; ++k) sce = (k == kh + e) ? s_c[k] : sce;
-      word |= ((uint32_t)(uint8_t)(int8_t)quant(sm.C[tk][kh + e], sce, 127)) << (8 * e);
+      word |= ((uint32_t)(uint8_t)(int8_t)quant(sm.u.q.C[tk][kh + e], sce, 127)) << (8 * e);
     }
     sm.u.q.rec[RL::kWC + lane] = word;
   }
@@ -439,7 +443,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     float* r = raw + ((size_t)bi * hkv + kvh) * raw_floats(R);
     for (int i = lane; i < kD; i += 64) r[i] = sm.mu[i];
     for (int i = lane; i < R * kD; i += 64) r[kD + i] = sm.V[i >> 7][i & 127];
-    for (int i = lane; i < kB * R; i += 64) r[kD + R * kD + i] = sm.C[i / R][i % R];
+    for (int i = lane; i < kB * R; i += 64) r[kD + R * kD + i] = sm.u.q.C[i / R][i % R];
   }
 }
 
