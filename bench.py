@@ -352,9 +352,40 @@ def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps, light=F
     cnt_sh = torch.empty_like(cnt_x)
     energy_sh = []
     shared_ms = []
+    # exact attention mass captured, at the configured budget and at others:
+    # the page shares m_j of the true-key page LSE (each query head's softmax
+    # over pages, averaged over its group), summed over the pages LOCKS
+    # selects and over the exact top-k pages (the most any k pages hold)
+    budgets = sorted({bb for bb in (16, 32, 64, 128, 256, 512, budget) if bb <= w.pages})
+    ws_b = torch.empty(L.score_workspace_bytes(d, w.batch, P, max(budgets)), dtype=torch.uint8,
+                       device="cuda")
+    mass = {bb: [0.0, 0.0, 0, 0] for bb in budgets}   # locks mass, exact mass, overlap, exact count
+
+    def share_of_pages(sel_t, cnt_t, m_t):
+        idx = sel_t.long().clamp_min(0)
+        keep = torch.arange(sel_t.shape[-1], device="cuda")[None, None, :] < cnt_t[..., None]
+        return (m_t.gather(2, idx) * keep).sum(dim=2)
+
     for layer in layers:
         L.exact_page_lse(d, inp.q[layer], inp.k[layer], inp.block_table, inp.seq_lens, lse)
         L.select_pages(d, lse, inp.seq_lens, budget, sel_x, cnt_x, ws)
+        m_ex = torch.softmax(lse.double().view(w.batch, w.hkv, w.group, P), dim=-1).mean(dim=2)
+        for bb in budgets:
+            s_l = torch.empty((w.batch, w.hkv, bb), dtype=torch.int32, device="cuda")
+            c_l = torch.empty((w.batch, w.hkv), dtype=torch.int32, device="cuda")
+            s_e, c_e = torch.empty_like(s_l), torch.empty_like(c_l)
+            L.score_select(d, inp.q[layer], summ[layer], w.num_blocks, inp.block_table,
+                           inp.seq_lens, bb, s_l, c_l, ws_b)
+            L.select_pages(d, lse, inp.seq_lens, bb, s_e, c_e, ws_b)
+            mass[bb][0] += float(share_of_pages(s_l, c_l, m_ex).sum())
+            mass[bb][1] += float(share_of_pages(s_e, c_e, m_ex).sum())
+            for b in range(w.batch):
+                for g in range(w.hkv):
+                    a = set(s_l[b, g, :int(c_l[b, g])].tolist())
+                    e = set(s_e[b, g, :int(c_e[b, g])].tolist())
+                    mass[bb][2] += len(a & e)
+                    mass[bb][3] += len(e)
+        del m_ex
         torch.cuda.synchronize()
         if not light:
             t0 = time.perf_counter()
@@ -409,9 +440,17 @@ def quality_report(w, d, inp, summ, step, budget, n_layers, kernel_reps, light=F
            "carriers_kept_by_both": car_both, "carriers_kept_by_exact": car_exact,
            "carriers": car_n, "layers_sampled": layers,
            "energy_captured_rank8": round(energy, 4),
+           "by_budget": {str(bb): {"recall_vs_exact": round(v[2] / max(v[3], 1), 4),
+                                   "exact_mass_captured": round(v[0] / max(v[1], 1e-300), 4),
+                                   "exact_mass_of_exact_topk": round(v[1] / (len(layers) * w.batch * w.hkv), 4)}
+                         for bb, v in mass.items()},
            "note": ("exact = top-k from the true-key page LSE (reads every key); recall = "
                     "fraction of the exact page set LOCKS also selects; carriers kept by exact "
-                    "selection are the ones LOCKS can be asked to keep")}
+                    "selection are the ones LOCKS can be asked to keep; by_budget (pages): "
+                    "exact_mass_captured = the true-key attention mass (page shares averaged "
+                    "over a group's query heads) on the pages LOCKS selects, over the mass on "
+                    "the exact top-k pages; exact_mass_of_exact_topk = the latter per (sequence, "
+                    "KV head), out of 1")}
     if not light:
         del summ_sh
         rep["shared_basis"] = {
