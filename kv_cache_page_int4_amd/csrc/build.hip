@@ -4,17 +4,19 @@
 // eigenvectors and one coefficient vector per token; int4 basis, int8
 // coefficients and centroid).
 //
-// One wave per (page, KV head):
-//  1. load the 16x128 bf16 keys, centroid mu by DPP row sums, X = K - mu in fp32;
+// One wave per four (page, KV head) items:
+//  1. per page, load the 16x128 bf16 keys, centroid mu by DPP row sums,
+//     X = K - mu in fp32;
 //  2. Gram matrix X X^T (16x16) on the matrix cores (fp32 16x16x4);
-//  3. cyclic Jacobi on the Gram matrix in LDS: pairs (i, i^m) for m = 1..15
-//     form 8 disjoint rotations per step; each lane owns one 2x2 block of the
-//     matrix and one row-pair of the eigenvector matrix; sweeps stop once the
-//     off-diagonal mass is below 1e-12 of the total (at most 10);
-//  4. the top-8 eigenpairs (descending, ties to the lower index) give the
-//     basis v_k = X^T u_k normalized to unit length (the dual of the d x d
-//     scatter's eigenproblem), zeroed when lambda_k <= 1e-5 lambda_1 or when
-//     the page is constant to rounding;
+//  3. cyclic Jacobi on the four Gram matrices at once, one per 16-lane row
+//     of the wave: pairs (i, i^m) for m = 1..15 form 8 disjoint rotations
+//     per step; lane i of a row holds row i of its page's matrix and of the
+//     eigenvector matrix, in registers; sweeps stop once every page's
+//     off-diagonal mass is below 1e-12 of its total (at most 10);
+//  4. per page, the top-r eigenpairs (descending, ties to the lower index)
+//     give the basis v_k = X^T u_k normalized to unit length (the dual of the
+//     d x d scatter's eigenproblem), zeroed when lambda_k <= 1e-5 lambda_1 or
+//     when the page is constant to rounding;
 //  5. sign: the largest-|entry| component of v_k is made positive (lowest dim
 //     on ties); coefficients c_i = V^T x_i are projections on the unquantized
 //     basis;
@@ -22,8 +24,11 @@
 //     max|x|/127 for coefficients and centroid, round half to even) and
 //     packing into the 832-byte record.
 // With a given basis (the shared-basis selector the pages contrast LOCKS
-// with), steps 2-5 are replaced by that basis: the record keeps the page's own
-// centroid and coefficients c_i = V^T x_i in the given basis.
+// with), steps 2-5 are replaced by that basis, one page per wave: the record
+// keeps the page's own centroid and coefficients c_i = V^T x_i in the given
+// basis.
+#include <utility>
+
 #include "locks_device.h"
 #include "locks_internal.h"
 
@@ -86,37 +91,23 @@ struct RecLayout {
   static constexpr int kWSc = kWSv + R / 2, kWSmu = kWSc + R / 2;
 };
 
-// LDS of one build (one wave).  The keys are not kept: the basis and the
-// coefficients read the page-head's 4 KB again (from L2, where the first
-// read left it) and centre it again (k - mu in fp32, the same values the
-// centring step computes).  The eigen-solver's matrices are dead once the
-// basis is formed, and the packing buffers and the coefficients take their
-// place.  7 KB at rank 8: the registers, not the LDS, bound the builds per CU.
+// Buffers of the basis, coefficient and packing phases of one page-head
+// (phases 4-6), in LDS.
 template <int R>
-struct BuildSmem {
-  union {
-    struct {
-      float G[kB][kB + 1];     // Gram matrix -> eigenvalues on the diagonal
-      float U[kB][kB + 1];     // eigenvectors (columns)
-      float cs[8][2] __attribute__((aligned(16)));   // rotations of the current step
-    } e;                       // eigen-solver, until the basis is formed
-    struct {
-      int8_t vq[R][kD];
-      uint32_t rec[RecLayout<R>::kBytes / 4];
-      float C[kB][R];          // unquantized coefficients
-    } q;                       // coefficients, quantization and packing, after it
-  } u;
+struct PackSmem {
   float V[R][kD + 4];      // unquantized basis, [k][d]
-  float mu[kD] __attribute__((aligned(16)));
-  int order[kB];
+  float mu[kD] __attribute__((aligned(16)));   // centroid
+  float C[kB][R];          // unquantized coefficients
+  int8_t vq[R][kD];
+  uint32_t rec[RecLayout<R>::kBytes / 4];
 };
 
-// Which block a workgroup summarizes: entry blockIdx.x of a list, or (for
-// incremental finalization) the last full page of sequence blockIdx.x when
-// that sequence's length is a positive multiple of the page size -- the page
-// that the newest token just completed.
+// Which blocks a workgroup summarizes: entries of a list, or (for
+// incremental finalization) for each sequence the last full page when that
+// sequence's length is a positive multiple of the page size -- the page that
+// the newest token just completed.
 struct BlockSource {
-  const int32_t* block_ids;    // list mode
+  const int32_t* block_ids;    // list mode: [n]
   const int32_t* seq_lens;     // finalize mode: [batch]
   const int32_t* block_table;  // finalize mode: [batch][max_pages]
   int32_t max_pages;
@@ -125,19 +116,11 @@ struct BlockSource {
   int64_t summ_layer_stride;
 };
 
-template <int R>
-__global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ kc, int64_t bs,
-                                                   int64_t hs, int64_t ts, BlockSource src,
-                                                   int32_t n_blocks, int32_t num_blocks,
-                                                   int32_t hkv, uint8_t* __restrict__ summ,
-                                                   float* __restrict__ raw,
-                                                   const float* __restrict__ basis) {
-  using RL = RecLayout<R>;
-  __shared__ BuildSmem<R> sm;
-  const int lane = threadIdx.x;
-  const int bi = blockIdx.x, kvh = blockIdx.y;
-  kc += (size_t)blockIdx.z * src.k_layer_stride;
-  summ += (size_t)blockIdx.z * src.summ_layer_stride;
+// Block of item bi (list entry or sequence), -1 when there is none or it is
+// out of range.
+__device__ __forceinline__ int item_block(const BlockSource& src, int bi, int n_items,
+                                          int num_blocks) {
+  if (bi >= n_items) return -1;
   int blk;
   if (src.from_seq) {
     const int seq = src.seq_lens[bi];
@@ -147,11 +130,19 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
   } else {
     blk = src.block_ids[bi];
   }
-  if ((unsigned)blk >= (unsigned)num_blocks) return;   // whole workgroup, uniform
-  const int t = lane & 15, g = lane >> 4;
+  return ((unsigned)blk < (unsigned)num_blocks) ? blk : -1;
+}
 
-  // ---- 1. keys, centroid, deviations ----
-  const uint16_t* kp = kc + (size_t)blk * bs + (size_t)kvh * hs + (size_t)t * ts + 32 * g;
+// ---- 1-2. one page-head's keys: centroid mu (to LDS when mu is given), and
+// with GRAM the Gram matrix of the deviations (LDS, symmetrized).  Returns the keys' squared
+// norm (wave-uniform).  Lane (t = token lane % 16, g = lane / 16) holds dims
+// 32g .. 32g + 31 of token t.
+template <bool GRAM>
+__device__ __forceinline__ float centre_and_gram(const uint16_t* kpage, int64_t ts, float* mu,
+                                                 float (*G)[kB + 1]) {
+  const int lane = threadIdx.x;
+  const int t = lane & 15, g = lane >> 4;
+  const uint16_t* kp = kpage + (size_t)t * ts + 32 * g;
   float x[32];
   float ksq = 0.f;
 #pragma unroll
@@ -169,191 +160,217 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     ksq = fmaf(x[e], x[e], ksq);
     const float m = row_sum16(x[e]) * (1.f / 16.f);
     x[e] -= m;
-    if (t == 0) sm.mu[32 * g + e] = m;
+    if (mu && t == 0) mu[32 * g + e] = m;
   }
   ksq = wave_sum(ksq);
-
-  const int d0 = 2 * lane;   // basis dims owned by this lane: d0, d0 + 1
-  // this page-head's keys, read again below: token tt, dims d .. d + 1
-  const uint16_t* kpage = kc + (size_t)blk * bs + (size_t)kvh * hs;
-  auto key_pair = [&](int tt, int d) {
-    return *reinterpret_cast<const uint32_t*>(kpage + (size_t)tt * ts + d);
-  };
-  if (basis) {
-    const float* bk = basis + (size_t)kvh * R * kD;
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      sm.V[k][d0] = bk[k * kD + d0];
-      sm.V[k][d0 + 1] = bk[k * kD + d0 + 1];
-    }
-    __syncthreads();
-  } else {
-    // ---- 2. Gram matrix on the matrix cores: K index (step s, group g) = dim 32g+s ----
+  if constexpr (GRAM) {
+    // Gram matrix on the matrix cores: K index (step s, group g) = dim 32g+s
     f32x4v gacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 32; ++s) gacc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], x[s], gacc, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.u.e.G[4 * g + r][t] = gacc[r];
-    for (int i = lane; i < kB * kB; i += 64) sm.u.e.U[i >> 4][i & 15] = ((i >> 4) == (i & 15)) ? 1.f : 0.f;
+    for (int r = 0; r < 4; ++r) G[4 * g + r][t] = gacc[r];
     __syncthreads();
     // symmetrize (the product is symmetric up to rounding order)
     for (int i = lane; i < kB * kB; i += 64) {
       const int a = i >> 4, b = i & 15;
       if (a < b) {
-        const float v = 0.5f * (sm.u.e.G[a][b] + sm.u.e.G[b][a]);
-        sm.u.e.G[a][b] = v;
-        sm.u.e.G[b][a] = v;
+        const float v = 0.5f * (G[a][b] + G[b][a]);
+        G[a][b] = v;
+        G[b][a] = v;
       }
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  return ksq;
+}
 
-    // ---- 3. cyclic Jacobi ----
-    // A step m (1..15) rotates the 8 disjoint index pairs (i, i ^ m).  Lane
-    // (ia, ib) owns the 2x2 block of G at row pair ia and column pair ib
-    // (read from and written back to LDS); the diagonal lanes compute their
-    // pair's rotation and publish (c, s) in LDS.  The eigenvector matrix stays
-    // in registers: lane l holds row l % 16 of U and turns it by all 8
-    // rotations of the step, whose column indices are constants once the
-    // steps are unrolled.  The workgroup is one wave (launch bound 64).
-    const int ia = lane >> 3, ib = lane & 7;   // row pair, column pair of this lane's block
-    const int urow = lane & 15;
-    float u[kB];
-#pragma unroll
-    for (int j = 0; j < kB; ++j) u[j] = (j == urow) ? 1.f : 0.f;
-    for (int sweep = 0; sweep < kSweeps; ++sweep) {
-      // this lane's pair indices, opaque to the compiler: the block addresses
-      // of the 15 steps are recomputed in every sweep instead of being held
-      // in registers across the sweeps
-      int iav = ia, ibv = ib;
-      asm volatile("" : "+v"(iav), "+v"(ibv));
-#pragma unroll
-      for (int m = 1; m < 16; ++m) {
-        const int hb = 31 - __builtin_clz(m);
-        auto pair_p = [&](int pi) { return ((pi >> hb) << (hb + 1)) | (pi & ((1 << hb) - 1)); };
-        const int a0 = pair_p(iav), a1 = a0 ^ m, b0 = pair_p(ibv), b1 = b0 ^ m;
-        const float g00 = sm.u.e.G[a0][b0], g01 = sm.u.e.G[a0][b1], g10 = sm.u.e.G[a1][b0], g11 = sm.u.e.G[a1][b1];
-        {
-          // every lane computes (branch-free); the diagonal lanes publish
-          float c, s;
-          jacobi_rot(g00, 0.5f * (g01 + g10), g11, c, s);
-          if (ia == ib) *reinterpret_cast<float2*>(sm.u.e.cs[ia]) = make_float2(c, s);
-        }
-        // one wave: its LDS accesses complete in program order, so the reads
-        // below see the rotations just written; only the compiler is kept
-        // from reordering them.  All of the step's rotations are read at once.
-        asm volatile("" ::: "memory");
-        const float2 csa = *reinterpret_cast<const float2*>(sm.u.e.cs[ia]);
-        const float2 csb = *reinterpret_cast<const float2*>(sm.u.e.cs[ib]);
-        float4 cs4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cs4[i] = *reinterpret_cast<const float4*>(&sm.u.e.cs[2 * i][0]);
-        const float ca = csa.x, sa = csa.y, cb = csb.x, sb = csb.y;
-        // T = G J (columns b0, b1), then G' = J^T T (rows a0, a1)
-        const float t00 = g00 * cb - g01 * sb, t01 = g00 * sb + g01 * cb;
-        const float t10 = g10 * cb - g11 * sb, t11 = g10 * sb + g11 * cb;
-        float n00 = ca * t00 - sa * t10, n01 = ca * t01 - sa * t11;
-        float n10 = sa * t00 + ca * t10, n11 = sa * t01 + ca * t11;
-        if (ia == ib) {
-          n01 = 0.f;
-          n10 = 0.f;
-        }
-        sm.u.e.G[a0][b0] = n00;
-        sm.u.e.G[a0][b1] = n01;
-        sm.u.e.G[a1][b0] = n10;
-        sm.u.e.G[a1][b1] = n11;
-        // U' = U J on this lane's row: all 8 rotations
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float c = (k & 1) ? cs4[k >> 1].z : cs4[k >> 1].x;
-          const float s = (k & 1) ? cs4[k >> 1].w : cs4[k >> 1].y;
-          const int p0 = pair_p(k), p1 = p0 ^ m;
-          const float up = u[p0], uq = u[p1];
-          u[p0] = c * up - s * uq;
-          u[p1] = s * up + c * uq;
-        }
-        // apply the rotations now: left free, the compiler sinks them to the
-        // end of the sweep and holds all 120 rotations in registers
-        asm volatile("" : "+v"(u[0]), "+v"(u[1]), "+v"(u[2]), "+v"(u[3]), "+v"(u[4]),
-                     "+v"(u[5]), "+v"(u[6]), "+v"(u[7]), "+v"(u[8]), "+v"(u[9]), "+v"(u[10]),
-                     "+v"(u[11]), "+v"(u[12]), "+v"(u[13]), "+v"(u[14]), "+v"(u[15])
-                     :: "memory");
-      }
-      // converged when the off-diagonal mass is below 1e-12 of the total
-      // (off-norm 1e-6 relative: far below what the codes and fp16 scales resolve)
-      float off = 0.f, tot = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * lane + e, a = i >> 4, b = i & 15;
-        const float v = sm.u.e.G[a][b];
-        tot = fmaf(v, v, tot);
-        if (a != b) off = fmaf(v, v, off);
-      }
-      off = wave_sum(off);
-      tot = wave_sum(tot);
-      if (!(off > 1e-12f * tot)) break;
-    }
-    if (lane < kB) {
-#pragma unroll
-      for (int j = 0; j < kB; ++j) sm.u.e.U[urow][j] = u[j];
-    }
+// ---- 3. cyclic Jacobi, one 16x16 matrix per 16-lane group ----
+// A step m (1..15) rotates the 8 disjoint index pairs (i, i ^ m).  Lane i of
+// a group holds row i of G and of the eigenvector matrix U in XOR order:
+// slot c holds column i ^ c, so the diagonal is slot 0, the pair's
+// off-diagonal element slot m, and the column pairs of a step are the slot
+// pairs (c, c ^ m) in every lane.  Values of other rows come from lanes of
+// the same group: lane i reads lane i ^ X, by DPP where a DPP pattern is
+// that permutation (X = 1, 2, 3 within quads, 7 and 15 by the row's half and
+// full mirrors, 8 by a rotation of the row by half its width), else by the
+// LDS unit's swizzle in its xor-mask mode.
+template <int X>
+__device__ __forceinline__ float swz(float v) {
+  if constexpr (X == 0) return v;
+  else if constexpr (X == 1) return dpp<qp(1, 0, 3, 2)>(v);
+  else if constexpr (X == 2) return dpp<qp(2, 3, 0, 1)>(v);
+  else if constexpr (X == 3) return dpp<qp(3, 2, 1, 0)>(v);
+  else if constexpr (X == 7) return dpp<kRowHalfMirror>(v);
+  else if constexpr (X == 8) return dpp<kRowRor8>(v);
+  else if constexpr (X == 15) return dpp<kRowMirror>(v);
+  else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (X << 10) | 0x1F));
+}
 
-    // ---- 4. order eigenpairs: descending eigenvalue, ties to the lower index ----
-    if (lane < 16) {
-      const float lj = sm.u.e.G[lane][lane];
-      int rank = 0;
-      for (int i = 0; i < 16; ++i) {
-        const float li = sm.u.e.G[i][i];
-        rank += (li > lj) || (li == lj && i < lane);
-      }
-      sm.order[rank] = lane;
-    }
-    __syncthreads();
-    const float lam1 = sm.u.e.G[sm.order[0]][sm.order[0]];
-    const bool page_has_basis = lam1 > kEpsConst * ksq;
+// Column pair of slots (LO, LO ^ M) of T = G J and U' = U J.  The pair's
+// rotation is held by lane i ^ LO; its first column is slot LO when this
+// lane's row is first (bit kHb of i ^ LO is that of i), else slot LO ^ M,
+// which the sign sg accounts for.
+template <int M, int LO>
+__device__ __forceinline__ void jacobi_cols(float (&a)[kB], float (&u)[kB], float (&tr)[kB],
+                                            float c, float s, float sg) {
+  constexpr int kHb = 31 - __builtin_clz(M);
+  if constexpr ((LO & (1 << kHb)) == 0) {
+    constexpr int HI = LO ^ M;
+    const float cc = swz<LO>(c), ss = swz<LO>(s) * sg;
+    tr[LO] = fmaf(a[LO], cc, -(a[HI] * ss));
+    tr[HI] = fmaf(a[HI], cc, a[LO] * ss);
+    const float ul = u[LO], uh = u[HI];
+    u[LO] = fmaf(ul, cc, -(uh * ss));
+    u[HI] = fmaf(uh, cc, ul * ss);
+  }
+}
 
-    // basis v_k = X^T u_k / |X^T u_k|; lane owns dims 2*lane, 2*lane+1
-    const float mu0 = sm.mu[d0], mu1 = sm.mu[d0 + 1];
-    float2 xr[kB];
+// Slot L of G' = J^T T: rows i and i ^ M, the partner's value of column
+// i ^ L from its slot L ^ M.
+template <int M, int L>
+__device__ __forceinline__ void jacobi_row(float (&a)[kB], const float (&tr)[kB], float c,
+                                           float sr) {
+  const float par = swz<M>(tr[L ^ M]);
+  a[L] = fmaf(c, tr[L], -(sr * par));
+}
+
+template <int M, int... L>
+__device__ __forceinline__ void jacobi_step(float (&a)[kB], float (&u)[kB], int i,
+                                            std::integer_sequence<int, L...>) {
+  constexpr int kHb = 31 - __builtin_clz(M);
+  // this lane's row is the pair's first (lower) index
+  const bool first = !(i & (1 << kHb));
+  // the pair's rotation, computed alike in both of its lanes
+  const float d_par = swz<M>(a[0]), o_par = swz<M>(a[M]);
+  const float app = first ? a[0] : d_par, aqq = first ? d_par : a[0];
+  const float gpq = first ? a[M] : o_par, gqp = first ? o_par : a[M];
+  float c, s;
+  jacobi_rot(app, 0.5f * (gpq + gqp), aqq, c, s);
+  const float sg = first ? 1.f : -1.f;
+  float tr[kB];
+  (jacobi_cols<M, L>(a, u, tr, c, s, sg), ...);
+  (jacobi_row<M, L>(a, tr, c, s * sg), ...);
+  a[M] = 0.f;   // the pair's off-diagonal element, zero by construction
+}
+
+template <int... M>
+__device__ __forceinline__ void jacobi_sweep(float (&a)[kB], float (&u)[kB], int i,
+                                             std::integer_sequence<int, M...>) {
+  (jacobi_step<M + 1>(a, u, i, std::make_integer_sequence<int, kB>{}), ...);
+}
+
+// Whether eigenvalue i ^ C ranks before eigenvalue i (li, held by lane i):
+// descending order, ties to the lower index.
+template <int C>
+__device__ __forceinline__ int ranks_before(float li, int i) {
+  const float lj = swz<C>(li);
+  return (lj > li) || (lj == li && (i ^ C) < i);
+}
+
+// Column i ^ C of U (slot C of lane i's row) goes to column rank(i ^ C) of
+// the top-R eigenvector matrix when that rank is below R.
+template <int R, int C>
+__device__ __forceinline__ void put_top_column(float (*Ut)[R], const float (&u)[kB], int rank,
+                                               int i) {
+  const int rj = __float_as_int(swz<C>(__int_as_float(rank)));
+  if (rj < R) Ut[i][rj] = u[C];
+}
+
+// Eigenvalues a[0] of the 16 lanes of a group, ranked; the top R of them and
+// their eigenvectors (columns of U, lane i holding row i in XOR order) go
+// to lam[0 .. R) and Ut[.][0 .. R) in descending order.
+template <int R, int... C>
+__device__ __forceinline__ void store_top_eigenpairs(const float (&a)[kB], const float (&u)[kB],
+                                                     int i, float* lam, float (*Ut)[R],
+                                                     std::integer_sequence<int, C...>) {
+  const float li = a[0];
+  const int rank = (ranks_before<C + 1>(li, i) + ...);
+  put_top_column<R, 0>(Ut, u, rank, i);
+  (put_top_column<R, C + 1>(Ut, u, rank, i), ...);
+  if (rank < R) lam[rank] = li;
+}
+
+// ---- 4. the basis from the top-R eigenpairs (lam[k], column k of U, in
+// descending order): v_k = X^T u_k / |X^T u_k|, zero below the floors; sign
+// by the largest-|entry| component.  Lane owns dims 2 lane, 2 lane + 1; it
+// forms the centroid of those dims from the keys it reads, summing the 16
+// tokens in the order of the butterfly of phase 1 (pairs, quads, eights,
+// halves), so mu is the same value bit for bit, and leaves it in pk.mu.
+template <int R, typename KeyPair>
+__device__ __forceinline__ void basis_from_eig(const float* lam, const float (*U)[R], float ksq,
+                                               KeyPair key_pair, PackSmem<R>& pk) {
+  const int lane = threadIdx.x;
+  const int d0 = 2 * lane;
+  const float lam1 = lam[0];
+  const bool page_has_basis = lam1 > kEpsConst * ksq;
+  float2 xr[kB];
+#pragma unroll
+  for (int tt = 0; tt < kB; ++tt) {
+    const uint32_t kw = key_pair(tt, d0);
+    xr[tt] = make_float2(bf16_lo(kw), bf16_hi(kw));
+  }
+  float2 s[kB];
+#pragma unroll
+  for (int tt = 0; tt < kB; ++tt) s[tt] = xr[tt];
+#pragma unroll
+  for (int w = 1; w < kB; w *= 2) {
+#pragma unroll
+    for (int tt = 0; tt < kB; tt += 2 * w) {
+      s[tt].x += s[tt + w].x;
+      s[tt].y += s[tt + w].y;
+    }
+  }
+  const float mu0 = s[0].x * (1.f / 16.f), mu1 = s[0].y * (1.f / 16.f);
+  pk.mu[d0] = mu0;
+  pk.mu[d0 + 1] = mu1;
+#pragma unroll
+  for (int tt = 0; tt < kB; ++tt) {
+    xr[tt].x -= mu0;
+    xr[tt].y -= mu1;
+  }
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const bool keep = page_has_basis && (lam[k] > kTau * lam1);
+    float v0 = 0.f, v1 = 0.f;
 #pragma unroll
     for (int tt = 0; tt < kB; ++tt) {
-      const uint32_t kw = key_pair(tt, d0);
-      xr[tt] = make_float2(bf16_lo(kw) - mu0, bf16_hi(kw) - mu1);
+      const float uu = U[tt][k];
+      v0 = fmaf(xr[tt].x, uu, v0);
+      v1 = fmaf(xr[tt].y, uu, v1);
     }
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      const int j = sm.order[k];
-      const float lk = sm.u.e.G[j][j];
-      const bool keep = page_has_basis && (lk > kTau * lam1);
-      float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < kB; ++tt) {
-        const float uu = sm.u.e.U[tt][j];
-        v0 = fmaf(xr[tt].x, uu, v0);
-        v1 = fmaf(xr[tt].y, uu, v1);
-      }
-      const float nrm2 = wave_sum(fmaf(v1, v1, v0 * v0));
-      const float inv = (keep && nrm2 > 0.f) ? 1.f / sqrtf(nrm2) : 0.f;
-      v0 *= inv;
-      v1 *= inv;
-      // sign: the largest |v| (lowest dim on ties) is made positive
-      const float a0v = fabsf(v0), a1v = fabsf(v1);
-      const float amax = wave_max(fmaxf(a0v, a1v));
-      const uint32_t cand = (a0v == amax) ? (uint32_t)d0 : (a1v == amax) ? (uint32_t)(d0 + 1) : 0xFFFFu;
-      const int bidx = __builtin_amdgcn_readfirstlane((int)wave_min_u(cand));
-      const float mine = (bidx & 1) ? v1 : v0;
-      const float bval = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), bidx >> 1));
-      if (bval < 0.f) {
-        v0 = -v0;
-        v1 = -v1;
-      }
-      sm.V[k][d0] = v0;
-      sm.V[k][d0 + 1] = v1;
+    const float nrm2 = wave_sum(fmaf(v1, v1, v0 * v0));
+    const float inv = (keep && nrm2 > 0.f) ? 1.f / sqrtf(nrm2) : 0.f;
+    v0 *= inv;
+    v1 *= inv;
+    // sign: the largest |v| (lowest dim on ties) is made positive
+    const float a0v = fabsf(v0), a1v = fabsf(v1);
+    const float amax = wave_max(fmaxf(a0v, a1v));
+    const uint32_t cand = (a0v == amax) ? (uint32_t)d0 : (a1v == amax) ? (uint32_t)(d0 + 1) : 0xFFFFu;
+    const int bidx = __builtin_amdgcn_readfirstlane((int)wave_min_u(cand));
+    const float mine = (bidx & 1) ? v1 : v0;
+    const float bval = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), bidx >> 1));
+    if (bval < 0.f) {
+      v0 = -v0;
+      v1 = -v1;
     }
-    __syncthreads();
+    pk.V[k][d0] = v0;
+    pk.V[k][d0 + 1] = v1;
   }
+  __syncthreads();
+}
 
-  // coefficients c_ik = v_k . x_i : lane -> token t, columns
-  // (R/4)*(lane>>4) .. +R/4
+// ---- 5-6. coefficients c_ik = v_k . x_i on the unquantized basis, then
+// symmetric quantization with fp16 scales and packing; the record is
+// written to dst, and with raw the unquantized mu, V, C.
+template <int R, typename KeyPair>
+__device__ __forceinline__ void coeffs_and_pack(KeyPair key_pair, PackSmem<R>& pk,
+                                                uint32_t* __restrict__ dst, float* raw) {
+  using RL = RecLayout<R>;
+  const float* mu = pk.mu;
+  const int lane = threadIdx.x;
+  const int d0 = 2 * lane;
+  // lane -> token lane % 16, columns (R/4)*(lane/16) .. +R/4
   {
     constexpr int kPer = R / 4;
     const int tk = lane & 15, k0 = kPer * (lane >> 4);
@@ -362,42 +379,41 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     for (int j = 0; j < kPer; ++j) cc[j] = 0.f;
     for (int d = 0; d < kD; d += 2) {
       const uint32_t kw = key_pair(tk, d);
-      const float2 m = *reinterpret_cast<const float2*>(&sm.mu[d]);
+      const float2 m = *reinterpret_cast<const float2*>(&mu[d]);
       const float xa = bf16_lo(kw) - m.x, xb = bf16_hi(kw) - m.y;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) cc[j] = fmaf(xa, sm.V[k0 + j][d], cc[j]);
+      for (int j = 0; j < kPer; ++j) cc[j] = fmaf(xa, pk.V[k0 + j][d], cc[j]);
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) cc[j] = fmaf(xb, sm.V[k0 + j][d + 1], cc[j]);
+      for (int j = 0; j < kPer; ++j) cc[j] = fmaf(xb, pk.V[k0 + j][d + 1], cc[j]);
     }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) sm.u.q.C[tk][k0 + j] = cc[j];
+    for (int j = 0; j < kPer; ++j) pk.C[tk][k0 + j] = cc[j];
   }
   __syncthreads();
 
-  // ---- 6. quantize + pack ----
   // centroid
-  const float mu0 = sm.mu[d0], mu1 = sm.mu[d0 + 1];
+  const float mu0 = mu[d0], mu1 = mu[d0 + 1];
   const float s_mu = fp16_scale(wave_max(fmaxf(fabsf(mu0), fabsf(mu1))), 127.f);
   const int mq0 = quant(mu0, s_mu, 127), mq1 = quant(mu1, s_mu, 127);
   // basis scales and codes
   float s_v[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
-    const float a = sm.V[k][d0], b2 = sm.V[k][d0 + 1];
+    const float a = pk.V[k][d0], b2 = pk.V[k][d0 + 1];
     s_v[k] = fp16_scale(wave_max(fmaxf(fabsf(a), fabsf(b2))), 7.f);
-    sm.u.q.vq[k][d0] = (int8_t)quant(a, s_v[k], 7);
-    sm.u.q.vq[k][d0 + 1] = (int8_t)quant(b2, s_v[k], 7);
+    pk.vq[k][d0] = (int8_t)quant(a, s_v[k], 7);
+    pk.vq[k][d0 + 1] = (int8_t)quant(b2, s_v[k], 7);
   }
   // coefficient scales: column k max over the 16 tokens
   float s_c[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
-    const float a = (lane < 16) ? fabsf(sm.u.q.C[lane][k]) : 0.f;
+    const float a = (lane < 16) ? fabsf(pk.C[lane][k]) : 0.f;
     s_c[k] = fp16_scale(wave_max(a), 127.f);
   }
   __syncthreads();
   // record words: basis, coefficients, centroid, s_V, s_c, s_mu, zero
-  uint8_t* mub = reinterpret_cast<uint8_t*>(&sm.u.q.rec[RL::kWMu]);
+  uint8_t* mub = reinterpret_cast<uint8_t*>(&pk.rec[RL::kWMu]);
   mub[d0] = (uint8_t)(int8_t)mq0;
   mub[d0 + 1] = (uint8_t)(int8_t)mq1;
   for (int wi = lane; wi < 16 * R; wi += 64) {
@@ -405,11 +421,11 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     uint32_t word = 0;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint32_t lo = (uint32_t)sm.u.q.vq[k][8 * w + m] & 0xFu;
-      const uint32_t hi = (uint32_t)sm.u.q.vq[k][8 * w + 4 + m] & 0xFu;
+      const uint32_t lo = (uint32_t)pk.vq[k][8 * w + m] & 0xFu;
+      const uint32_t hi = (uint32_t)pk.vq[k][8 * w + 4 + m] & 0xFu;
       word |= (lo | (hi << 4)) << (8 * m);
     }
-    sm.u.q.rec[wi] = word;
+    pk.rec[wi] = word;
   }
   // coefficient words: token tk holds R/4 words of 4 codes each
   if (lane < 4 * R) {
@@ -421,58 +437,188 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
       float sce = s_c[0];
 #pragma unroll
       for (int k = 1; k < R; ++k) sce = (k == kh + e) ? s_c[k] : sce;
-      word |= ((uint32_t)(uint8_t)(int8_t)quant(sm.u.q.C[tk][kh + e], sce, 127)) << (8 * e);
+      word |= ((uint32_t)(uint8_t)(int8_t)quant(pk.C[tk][kh + e], sce, 127)) << (8 * e);
     }
-    sm.u.q.rec[RL::kWC + lane] = word;
+    pk.rec[RL::kWC + lane] = word;
   }
   if (lane == 0) {
 #pragma unroll
     for (int i = 0; i < R / 2; ++i) {
-      sm.u.q.rec[RL::kWSv + i] = fp16_bits(s_v[2 * i]) | (fp16_bits(s_v[2 * i + 1]) << 16);
-      sm.u.q.rec[RL::kWSc + i] = fp16_bits(s_c[2 * i]) | (fp16_bits(s_c[2 * i + 1]) << 16);
+      pk.rec[RL::kWSv + i] = fp16_bits(s_v[2 * i]) | (fp16_bits(s_v[2 * i + 1]) << 16);
+      pk.rec[RL::kWSc + i] = fp16_bits(s_c[2 * i]) | (fp16_bits(s_c[2 * i + 1]) << 16);
     }
-    sm.u.q.rec[RL::kWSmu] = fp16_bits(s_mu);
-    for (int i = RL::kWSmu + 1; i < RL::kBytes / 4; ++i) sm.u.q.rec[i] = 0u;
+    pk.rec[RL::kWSmu] = fp16_bits(s_mu);
+    for (int i = RL::kWSmu + 1; i < RL::kBytes / 4; ++i) pk.rec[i] = 0u;
   }
   __syncthreads();
-  uint32_t* dst =
-      reinterpret_cast<uint32_t*>(summ + ((size_t)kvh * num_blocks + blk) * RL::kBytes);
-  for (int wi = lane; wi < RL::kBytes / 4; wi += 64) dst[wi] = sm.u.q.rec[wi];
+  for (int wi = lane; wi < RL::kBytes / 4; wi += 64) dst[wi] = pk.rec[wi];
 
   if (raw) {   // [128 + 144 R] floats: mu, V [R][128], C [16][R]
-    float* r = raw + ((size_t)bi * hkv + kvh) * raw_floats(R);
-    for (int i = lane; i < kD; i += 64) r[i] = sm.mu[i];
-    for (int i = lane; i < R * kD; i += 64) r[kD + i] = sm.V[i >> 7][i & 127];
-    for (int i = lane; i < kB * R; i += 64) r[kD + R * kD + i] = sm.u.q.C[i / R][i % R];
+    for (int i = lane; i < kD; i += 64) raw[i] = mu[i];
+    for (int i = lane; i < R * kD; i += 64) raw[kD + i] = pk.V[i >> 7][i & 127];
+    for (int i = lane; i < kB * R; i += 64) raw[kD + R * kD + i] = pk.C[i / R][i % R];
   }
+  __syncthreads();   // the buffers are free for the next page-head
+}
+
+// Pages per workgroup of the eigen-solving builder: one per 16-lane group.
+constexpr int kBuildPages = 4;
+
+// Summaries of kBuildPages page-heads (items kBuildPages * blockIdx.x + p,
+// KV head blockIdx.y) per one-wave workgroup: phases 1-2 page by page, the
+// Jacobi sweeps of all four at once (16 lanes each, no lane duplicating
+// another's work), then phases 4-6 page by page.  LDS: the Gram matrices
+// until the sweeps have read them, then the eigenvectors; the packing
+// buffers are reused from page to page.
+template <int R>
+__global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ kc, int64_t bs,
+                                                   int64_t hs, int64_t ts, BlockSource src,
+                                                   int32_t n_items, int32_t num_blocks,
+                                                   int32_t hkv, uint8_t* __restrict__ summ,
+                                                   float* __restrict__ raw) {
+  using RL = RecLayout<R>;
+  __shared__ union {
+    float G[kBuildPages][kB][kB + 1];   // Gram matrices, until the sweeps have read them
+    PackSmem<R> pk;                     // then the packing buffers, page by page
+  } sm;
+  __shared__ float Ut[kBuildPages][kB][R];   // top-R eigenvectors, columns in rank order
+  __shared__ float lam[kBuildPages][R];      // their eigenvalues
+  const int lane = threadIdx.x;
+  const int kvh = blockIdx.y;
+  kc += (size_t)blockIdx.z * src.k_layer_stride;
+  summ += (size_t)blockIdx.z * src.summ_layer_stride;
+  int blk[kBuildPages];
+  bool any = false;
+#pragma unroll
+  for (int p = 0; p < kBuildPages; ++p) {
+    blk[p] = item_block(src, kBuildPages * blockIdx.x + p, n_items, num_blocks);
+    any |= blk[p] >= 0;
+  }
+  if (!any) return;   // whole workgroup, uniform
+
+  // ---- 1-2. per page: Gram matrix of the centred keys (a zero matrix for
+  // an absent page, which the sweeps leave as it is) ----
+  float ksq[kBuildPages];
+#pragma unroll
+  for (int p = 0; p < kBuildPages; ++p) {
+    ksq[p] = 0.f;
+    if (blk[p] >= 0) {
+      ksq[p] = centre_and_gram<true>(kc + (size_t)blk[p] * bs + (size_t)kvh * hs, ts, nullptr,
+                                     sm.G[p]);
+    } else {
+      for (int i = lane; i < kB * (kB + 1); i += 64) (&sm.G[p][0][0])[i] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. Jacobi, page lane / 16 in lanes 16 (lane / 16) .. +15 ----
+  {
+    const int grp = lane >> 4, i = lane & 15;
+    float a[kB], u[kB];
+#pragma unroll
+    for (int c = 0; c < kB; ++c) {
+      a[c] = sm.G[grp][i][i ^ c];
+      u[c] = (c == 0) ? 1.f : 0.f;
+    }
+    for (int sweep = 0; sweep < kSweeps; ++sweep) {
+      jacobi_sweep(a, u, i, std::make_integer_sequence<int, kB - 1>{});
+      // a page has converged when its off-diagonal mass is below 1e-12 of
+      // the total (off-norm 1e-6 relative: far below what the codes and fp16
+      // scales resolve); the sweeps go on until all four have
+      float off = 0.f;
+#pragma unroll
+      for (int c = 1; c < kB; ++c) off = fmaf(a[c], a[c], off);
+      const float tot = row_sum16(fmaf(a[0], a[0], off));
+      off = row_sum16(off);
+      if (__all(!(off > 1e-12f * tot))) break;
+    }
+    store_top_eigenpairs<R>(a, u, i, lam[grp], Ut[grp], std::make_integer_sequence<int, kB - 1>{});
+  }
+  __syncthreads();   // the Gram matrices are read: the LDS takes the packing buffers
+
+  // ---- 4-6. per page: basis, coefficients, quantization, record ----
+#pragma unroll 1
+  for (int p = 0; p < kBuildPages; ++p) {
+    if (blk[p] < 0) continue;   // uniform
+    const uint16_t* kpage = kc + (size_t)blk[p] * bs + (size_t)kvh * hs;
+    auto key_pair = [&](int tt, int d) {
+      return *reinterpret_cast<const uint32_t*>(kpage + (size_t)tt * ts + d);
+    };
+    basis_from_eig<R>(lam[p], Ut[p], ksq[p], key_pair, sm.pk);
+    uint32_t* dst =
+        reinterpret_cast<uint32_t*>(summ + ((size_t)kvh * num_blocks + blk[p]) * RL::kBytes);
+    float* r = raw ? raw + ((size_t)(kBuildPages * blockIdx.x + p) * hkv + kvh) * raw_floats(R)
+                   : nullptr;
+    coeffs_and_pack<R>(key_pair, sm.pk, dst, r);
+  }
+}
+
+// Summaries in a given basis (the shared-basis selector the pages contrast
+// LOCKS with): one page-head per one-wave workgroup, phases 1, 5 and 6 with
+// V = the given basis of KV head blockIdx.y.
+template <int R>
+__global__ __launch_bounds__(64) void build_basis_kernel(const uint16_t* __restrict__ kc,
+                                                         int64_t bs, int64_t hs, int64_t ts,
+                                                         BlockSource src, int32_t n_items,
+                                                         int32_t num_blocks, int32_t hkv,
+                                                         uint8_t* __restrict__ summ,
+                                                         const float* __restrict__ basis) {
+  using RL = RecLayout<R>;
+  __shared__ PackSmem<R> pk;
+  const int lane = threadIdx.x;
+  const int kvh = blockIdx.y;
+  const int blk = item_block(src, blockIdx.x, n_items, num_blocks);
+  if (blk < 0) return;   // whole workgroup, uniform
+  const uint16_t* kpage = kc + (size_t)blk * bs + (size_t)kvh * hs;
+  centre_and_gram<false>(kpage, ts, pk.mu, nullptr);
+  const int d0 = 2 * lane;
+  const float* bk = basis + (size_t)kvh * R * kD;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    pk.V[k][d0] = bk[k * kD + d0];
+    pk.V[k][d0 + 1] = bk[k * kD + d0 + 1];
+  }
+  __syncthreads();
+  auto key_pair = [&](int tt, int d) {
+    return *reinterpret_cast<const uint32_t*>(kpage + (size_t)tt * ts + d);
+  };
+  uint32_t* dst = reinterpret_cast<uint32_t*>(summ + ((size_t)kvh * num_blocks + blk) * RL::kBytes);
+  coeffs_and_pack<R>(key_pair, pk, dst, nullptr);
 }
 
 template <int R>
 hipError_t launch_build_r(const uint16_t* k_cache, int64_t block_stride, int64_t head_stride,
-                          int64_t token_stride, const BlockSource& src, dim3 grid,
-                          int32_t n_blocks, int32_t num_blocks, int32_t hkv, uint8_t* summaries,
+                          int64_t token_stride, const BlockSource& src, int32_t n_items,
+                          int32_t hkv, int32_t n_layers, int32_t num_blocks, uint8_t* summaries,
                           float* raw_debug, const float* basis, hipStream_t stream) {
-  hipLaunchKernelGGL(build_kernel<R>, grid, dim3(64), 0, stream, k_cache, block_stride,
-                     head_stride, token_stride, src, n_blocks, num_blocks, hkv, summaries,
-                     raw_debug, basis);
+  if (basis) {
+    hipLaunchKernelGGL(build_basis_kernel<R>, dim3(n_items, hkv, n_layers), dim3(64), 0, stream,
+                       k_cache, block_stride, head_stride, token_stride, src, n_items,
+                       num_blocks, hkv, summaries, basis);
+  } else {
+    const int32_t wgs = (n_items + kBuildPages - 1) / kBuildPages;
+    hipLaunchKernelGGL(build_kernel<R>, dim3(wgs, hkv, n_layers), dim3(64), 0, stream, k_cache,
+                       block_stride, head_stride, token_stride, src, n_items, num_blocks, hkv,
+                       summaries, raw_debug);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_build_any(int32_t rank, const uint16_t* k_cache, int64_t block_stride,
                             int64_t head_stride, int64_t token_stride, const BlockSource& src,
-                            dim3 grid, int32_t n_blocks, int32_t num_blocks, int32_t hkv,
+                            int32_t n_items, int32_t hkv, int32_t n_layers, int32_t num_blocks,
                             uint8_t* summaries, float* raw_debug, const float* basis,
                             hipStream_t stream) {
   switch (rank) {
     case 4:
-      return launch_build_r<4>(k_cache, block_stride, head_stride, token_stride, src, grid,
-                               n_blocks, num_blocks, hkv, summaries, raw_debug, basis, stream);
+      return launch_build_r<4>(k_cache, block_stride, head_stride, token_stride, src, n_items,
+                               hkv, n_layers, num_blocks, summaries, raw_debug, basis, stream);
     case 8:
-      return launch_build_r<8>(k_cache, block_stride, head_stride, token_stride, src, grid,
-                               n_blocks, num_blocks, hkv, summaries, raw_debug, basis, stream);
+      return launch_build_r<8>(k_cache, block_stride, head_stride, token_stride, src, n_items,
+                               hkv, n_layers, num_blocks, summaries, raw_debug, basis, stream);
     case 16:
-      return launch_build_r<16>(k_cache, block_stride, head_stride, token_stride, src, grid,
-                                n_blocks, num_blocks, hkv, summaries, raw_debug, basis, stream);
+      return launch_build_r<16>(k_cache, block_stride, head_stride, token_stride, src, n_items,
+                                hkv, n_layers, num_blocks, summaries, raw_debug, basis, stream);
     default:
       return hipErrorInvalidValue;
   }
@@ -486,9 +632,8 @@ hipError_t launch_build(int32_t rank, const uint16_t* k_cache, int64_t block_str
                         float* raw_debug, hipStream_t stream) {
   if (n_blocks == 0) return hipSuccess;
   BlockSource src{block_ids, nullptr, nullptr, 0, false, 0, 0};
-  return launch_build_any(rank, k_cache, block_stride, head_stride, token_stride, src,
-                          dim3(n_blocks, hkv), n_blocks, num_blocks, hkv, summaries, raw_debug,
-                          nullptr, stream);
+  return launch_build_any(rank, k_cache, block_stride, head_stride, token_stride, src, n_blocks,
+                          hkv, 1, num_blocks, summaries, raw_debug, nullptr, stream);
 }
 
 hipError_t launch_build_basis(int32_t rank, const uint16_t* k_cache, int64_t block_stride,
@@ -498,9 +643,8 @@ hipError_t launch_build_basis(int32_t rank, const uint16_t* k_cache, int64_t blo
                               hipStream_t stream) {
   if (n_blocks == 0) return hipSuccess;
   BlockSource src{block_ids, nullptr, nullptr, 0, false, 0, 0};
-  return launch_build_any(rank, k_cache, block_stride, head_stride, token_stride, src,
-                          dim3(n_blocks, hkv), n_blocks, num_blocks, hkv, summaries, nullptr,
-                          basis, stream);
+  return launch_build_any(rank, k_cache, block_stride, head_stride, token_stride, src, n_blocks,
+                          hkv, 1, num_blocks, summaries, nullptr, basis, stream);
 }
 
 hipError_t launch_finalize(int32_t rank, const uint16_t* k_cache, int64_t block_stride,
@@ -511,9 +655,8 @@ hipError_t launch_finalize(int32_t rank, const uint16_t* k_cache, int64_t block_
                            hipStream_t stream) {
   BlockSource src{nullptr, seq_lens, block_table, max_pages, true, k_layer_stride,
                   summ_layer_stride};
-  return launch_build_any(rank, k_cache, block_stride, head_stride, token_stride, src,
-                          dim3(batch, hkv, n_layers), batch, num_blocks, hkv, summaries, nullptr,
-                          nullptr, stream);
+  return launch_build_any(rank, k_cache, block_stride, head_stride, token_stride, src, batch,
+                          hkv, n_layers, num_blocks, summaries, nullptr, nullptr, stream);
 }
 
 }  // namespace locks
