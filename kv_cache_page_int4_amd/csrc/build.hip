@@ -11,8 +11,9 @@
 //  3. cyclic Jacobi on the four Gram matrices at once, one per 16-lane row
 //     of the wave: pairs (i, i^m) for m = 1..15 form 8 disjoint rotations
 //     per step; lane i of a row holds row i of its page's matrix and of the
-//     eigenvector matrix, in registers; sweeps stop once every page's
-//     off-diagonal mass is below 1e-12 of its total (at most 10);
+//     eigenvector matrix, in registers; a page whose off-diagonal mass is
+//     below 1e-12 of its total is held from then on, and the sweeps stop
+//     once every page is (at most 10);
 //  4. per page, the top-r eigenpairs (descending, ties to the lower index)
 //     give the basis v_k = X^T u_k normalized to unit length (the dual of the
 //     d x d scatter's eigenproblem), zeroed when lambda_k <= 1e-5 lambda_1 or
@@ -236,7 +237,7 @@ __device__ __forceinline__ void jacobi_row(float (&a)[kB], const float (&tr)[kB]
 }
 
 template <int M, int... L>
-__device__ __forceinline__ void jacobi_step(float (&a)[kB], float (&u)[kB], int i,
+__device__ __forceinline__ void jacobi_step(float (&a)[kB], float (&u)[kB], int i, bool done,
                                             std::integer_sequence<int, L...>) {
   constexpr int kHb = 31 - __builtin_clz(M);
   // this lane's row is the pair's first (lower) index
@@ -247,6 +248,10 @@ __device__ __forceinline__ void jacobi_step(float (&a)[kB], float (&u)[kB], int 
   const float gpq = first ? a[M] : o_par, gqp = first ? o_par : a[M];
   float c, s;
   jacobi_rot(app, 0.5f * (gpq + gqp), aqq, c, s);
+  // a page that has converged turns by the identity: its diagonal and
+  // eigenvectors stay what they were when it converged
+  c = done ? 1.f : c;
+  s = done ? 0.f : s;
   const float sg = first ? 1.f : -1.f;
   float tr[kB];
   (jacobi_cols<M, L>(a, u, tr, c, s, sg), ...);
@@ -255,9 +260,9 @@ __device__ __forceinline__ void jacobi_step(float (&a)[kB], float (&u)[kB], int 
 }
 
 template <int... M>
-__device__ __forceinline__ void jacobi_sweep(float (&a)[kB], float (&u)[kB], int i,
+__device__ __forceinline__ void jacobi_sweep(float (&a)[kB], float (&u)[kB], int i, bool done,
                                              std::integer_sequence<int, M...>) {
-  (jacobi_step<M + 1>(a, u, i, std::make_integer_sequence<int, kB>{}), ...);
+  (jacobi_step<M + 1>(a, u, i, done, std::make_integer_sequence<int, kB>{}), ...);
 }
 
 // Whether eigenvalue i ^ C ranks before eigenvalue i (li, held by lane i):
@@ -520,17 +525,22 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
       a[c] = sm.G[grp][i][i ^ c];
       u[c] = (c == 0) ? 1.f : 0.f;
     }
+    // whether this lane's page has converged (the same in all 16 lanes of a
+    // page): its off-diagonal mass is below 1e-12 of the total (off-norm
+    // 1e-6 relative: far below what the codes and fp16 scales resolve).  The
+    // sweeps go on until all four pages have; a page that converged earlier
+    // is held where it converged, so a record does not depend on the pages
+    // that share its wave.
+    bool done = false;
     for (int sweep = 0; sweep < kSweeps; ++sweep) {
-      jacobi_sweep(a, u, i, std::make_integer_sequence<int, kB - 1>{});
-      // a page has converged when its off-diagonal mass is below 1e-12 of
-      // the total (off-norm 1e-6 relative: far below what the codes and fp16
-      // scales resolve); the sweeps go on until all four have
+      jacobi_sweep(a, u, i, done, std::make_integer_sequence<int, kB - 1>{});
       float off = 0.f;
 #pragma unroll
       for (int c = 1; c < kB; ++c) off = fmaf(a[c], a[c], off);
       const float tot = row_sum16(fmaf(a[0], a[0], off));
       off = row_sum16(off);
-      if (__all(!(off > 1e-12f * tot))) break;
+      done = done || !(off > 1e-12f * tot);
+      if (__all(done)) break;
     }
     store_top_eigenpairs<R>(a, u, i, lam[grp], Ut[grp], std::make_integer_sequence<int, kB - 1>{});
   }

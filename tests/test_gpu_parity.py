@@ -21,6 +21,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
+from kv_cache_page_int4_amd import locks as L  # noqa: E402
 from tests.gpu_common import (LSE_TOL, OUT_TOL, Layer, check_selection,  # noqa: E402
                               compare_build_codes, log, oracle_scores, scores_of)
 
@@ -211,6 +212,50 @@ def test_builder_codes(name):
         assert np.abs(rmu - mu).max() <= 1e-5 * (1 + np.abs(mu).max())
     log(f"[{name}] builder: {n_ex}/{n_cols} columns exempt, worst exempt-page residual excess {worst_rec:.2f} e_q")
     assert n_ex <= 0.02 * n_cols
+
+
+def test_builder_record_does_not_depend_on_the_call():
+    """A page-head's record is the same whatever else the call summarizes:
+    the blocks in another order, one block per call, short lists of 2, 3, 5
+    and 7 blocks, and a list with duplicates and out-of-range ids (skipped)
+    all give the bytes of one call over every block.  The builder solves
+    several pages per wave; this holds only if each page's eigensolve stops
+    where that page converges, not where its neighbours do."""
+    x = gen("llama8b-32k")
+    lay = Layer(x, 0)
+    lay.gpu_build()
+    ref = lay.summ.clone()
+    nb = lay.nb
+    rng = np.random.default_rng(11)
+
+    def build(ids):
+        summ = torch.zeros_like(ref)
+        L.build_summaries(lay.d, lay.k, torch.tensor(ids, dtype=torch.int32, device="cuda"), summ)
+        return summ
+
+    perm = rng.permutation(nb)
+    got = build(perm.tolist())
+    assert torch.equal(got, ref), "records differ when the blocks come in another order"
+    picks = rng.choice(nb, 24, replace=False).tolist()
+    summ = torch.zeros_like(ref)
+    for b in picks:
+        L.build_summaries(lay.d, lay.k, torch.tensor([b], dtype=torch.int32, device="cuda"), summ)
+    for n in (2, 3, 5, 7):
+        ids = rng.choice(nb, n, replace=False).tolist()
+        picks += ids
+        L.build_summaries(lay.d, lay.k, torch.tensor(ids, dtype=torch.int32, device="cuda"), summ)
+    mixed = [-1, picks[0], nb, picks[1], picks[1], 10**6, picks[2], -5, picks[0]]
+    summ2 = build(mixed)
+    torch.cuda.synchronize()
+    sel = torch.tensor(sorted(set(picks)), dtype=torch.long, device="cuda")
+    assert torch.equal(summ[:, sel], ref[:, sel]), "records differ in calls of 1 to 7 blocks"
+    m = torch.tensor(sorted(set(picks[:3])), dtype=torch.long, device="cuda")
+    assert torch.equal(summ2[:, m], ref[:, m]), "records differ with duplicates and skipped ids"
+    untouched = torch.ones(nb, dtype=torch.bool, device="cuda")
+    untouched[m] = False
+    assert int(summ2[:, untouched].abs().sum()) == 0, "a skipped id wrote a record"
+    log(f"[builder] records identical across {len(set(picks))} blocks in calls of 1-7 blocks, "
+        f"a permuted call and a call with duplicates and out-of-range ids")
 
 
 def test_builder_exact_low_rank_pages():
