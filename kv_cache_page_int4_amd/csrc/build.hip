@@ -192,33 +192,40 @@ __device__ __forceinline__ float centre_and_gram(const uint16_t* kpage, int64_t 
 // slot c holds column i ^ c, so the diagonal is slot 0, the pair's
 // off-diagonal element slot m, and the column pairs of a step are the slot
 // pairs (c, c ^ m) in every lane.  Values of other rows come from lanes of
-// the same group: lane i reads lane i ^ X, by DPP where a DPP pattern is
-// that permutation (X = 1, 2, 3 within quads, 7 and 15 by the row's half and
-// full mirrors, 8 by a rotation of the row by half its width), else by the
-// LDS unit's swizzle in its xor-mask mode.
-template <int X>
+// the same group: lane i reads lane i ^ X.  Six of the fifteen XORs are one
+// DPP move (1, 2, 3 within quads, 7 and 15 by the row's half and full
+// mirrors, 8 by a rotation of the row by half its width); every other one is
+// a quad XOR after the half mirror (4, 5, 6), the rotation by 8 (9, 10, 11)
+// or the full mirror (12, 13, 14).  With DPP2 those take the two moves;
+// otherwise they take one swizzle of the LDS unit in its xor-mask mode,
+// which costs no VALU issue but has the latency of an LDS access.  Both
+// move the same bits.
+template <int X, bool DPP2>
 __device__ __forceinline__ float swz(float v) {
+  constexpr int kQuadXor[4] = {qp(0, 1, 2, 3), qp(1, 0, 3, 2), qp(2, 3, 0, 1), qp(3, 2, 1, 0)};
   if constexpr (X == 0) return v;
-  else if constexpr (X == 1) return dpp<qp(1, 0, 3, 2)>(v);
-  else if constexpr (X == 2) return dpp<qp(2, 3, 0, 1)>(v);
-  else if constexpr (X == 3) return dpp<qp(3, 2, 1, 0)>(v);
+  else if constexpr (X <= 3) return dpp<kQuadXor[X]>(v);
   else if constexpr (X == 7) return dpp<kRowHalfMirror>(v);
   else if constexpr (X == 8) return dpp<kRowRor8>(v);
   else if constexpr (X == 15) return dpp<kRowMirror>(v);
-  else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (X << 10) | 0x1F));
+  else if constexpr (!DPP2)
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (X << 10) | 0x1F));
+  else if constexpr (X < 7) return dpp<kQuadXor[X ^ 7]>(dpp<kRowHalfMirror>(v));
+  else if constexpr (X < 12) return dpp<kQuadXor[X ^ 8]>(dpp<kRowRor8>(v));
+  else return dpp<kQuadXor[X ^ 15]>(dpp<kRowMirror>(v));
 }
 
 // Column pair of slots (LO, LO ^ M) of T = G J and U' = U J.  The pair's
 // rotation is held by lane i ^ LO; its first column is slot LO when this
 // lane's row is first (bit kHb of i ^ LO is that of i), else slot LO ^ M,
 // which the sign sg accounts for.
-template <int M, int LO>
+template <int M, int LO, bool DPP2>
 __device__ __forceinline__ void jacobi_cols(float (&a)[kB], float (&u)[kB], float (&tr)[kB],
                                             float c, float s, float sg) {
   constexpr int kHb = 31 - __builtin_clz(M);
   if constexpr ((LO & (1 << kHb)) == 0) {
     constexpr int HI = LO ^ M;
-    const float cc = swz<LO>(c), ss = swz<LO>(s) * sg;
+    const float cc = swz<LO, DPP2>(c), ss = swz<LO, DPP2>(s) * sg;
     tr[LO] = fmaf(a[LO], cc, -(a[HI] * ss));
     tr[HI] = fmaf(a[HI], cc, a[LO] * ss);
     const float ul = u[LO], uh = u[HI];
@@ -229,21 +236,21 @@ __device__ __forceinline__ void jacobi_cols(float (&a)[kB], float (&u)[kB], floa
 
 // Slot L of G' = J^T T: rows i and i ^ M, the partner's value of column
 // i ^ L from its slot L ^ M.
-template <int M, int L>
+template <int M, int L, bool DPP2>
 __device__ __forceinline__ void jacobi_row(float (&a)[kB], const float (&tr)[kB], float c,
                                            float sr) {
-  const float par = swz<M>(tr[L ^ M]);
+  const float par = swz<M, DPP2>(tr[L ^ M]);
   a[L] = fmaf(c, tr[L], -(sr * par));
 }
 
-template <int M, int... L>
+template <int M, bool DPP2, int... L>
 __device__ __forceinline__ void jacobi_step(float (&a)[kB], float (&u)[kB], int i, bool done,
                                             std::integer_sequence<int, L...>) {
   constexpr int kHb = 31 - __builtin_clz(M);
   // this lane's row is the pair's first (lower) index
   const bool first = !(i & (1 << kHb));
   // the pair's rotation, computed alike in both of its lanes
-  const float d_par = swz<M>(a[0]), o_par = swz<M>(a[M]);
+  const float d_par = swz<M, DPP2>(a[0]), o_par = swz<M, DPP2>(a[M]);
   const float app = first ? a[0] : d_par, aqq = first ? d_par : a[0];
   const float gpq = first ? a[M] : o_par, gqp = first ? o_par : a[M];
   float c, s;
@@ -254,22 +261,22 @@ __device__ __forceinline__ void jacobi_step(float (&a)[kB], float (&u)[kB], int 
   s = done ? 0.f : s;
   const float sg = first ? 1.f : -1.f;
   float tr[kB];
-  (jacobi_cols<M, L>(a, u, tr, c, s, sg), ...);
-  (jacobi_row<M, L>(a, tr, c, s * sg), ...);
+  (jacobi_cols<M, L, DPP2>(a, u, tr, c, s, sg), ...);
+  (jacobi_row<M, L, DPP2>(a, tr, c, s * sg), ...);
   a[M] = 0.f;   // the pair's off-diagonal element, zero by construction
 }
 
-template <int... M>
+template <bool DPP2, int... M>
 __device__ __forceinline__ void jacobi_sweep(float (&a)[kB], float (&u)[kB], int i, bool done,
                                              std::integer_sequence<int, M...>) {
-  (jacobi_step<M + 1>(a, u, i, done, std::make_integer_sequence<int, kB>{}), ...);
+  (jacobi_step<M + 1, DPP2>(a, u, i, done, std::make_integer_sequence<int, kB>{}), ...);
 }
 
 // Whether eigenvalue i ^ C ranks before eigenvalue i (li, held by lane i):
 // descending order, ties to the lower index.
 template <int C>
 __device__ __forceinline__ int ranks_before(float li, int i) {
-  const float lj = swz<C>(li);
+  const float lj = swz<C, true>(li);
   return (lj > li) || (lj == li && (i ^ C) < i);
 }
 
@@ -278,7 +285,7 @@ __device__ __forceinline__ int ranks_before(float li, int i) {
 template <int R, int C>
 __device__ __forceinline__ void put_top_column(float (*Ut)[R], const float (&u)[kB], int rank,
                                                int i) {
-  const int rj = __float_as_int(swz<C>(__int_as_float(rank)));
+  const int rj = __float_as_int(swz<C, true>(__int_as_float(rank)));
   if (rj < R) Ut[i][rj] = u[C];
 }
 
@@ -469,13 +476,20 @@ __device__ __forceinline__ void coeffs_and_pack(KeyPair key_pair, PackSmem<R>& p
 // Pages per workgroup of the eigen-solving builder: one per 16-lane group.
 constexpr int kBuildPages = 4;
 
+// Launches of at most this many workgroups use the DPP-only exchanges (one
+// wave per SIMD of the 256 CUs or fewer: nothing hides a swizzle's latency);
+// larger ones use the swizzles, which spare the VALU.  The two forms move the
+// same bits, so the records are the same.
+constexpr int64_t kDppOnlyMaxWorkgroups = 1024;
+
 // Summaries of kBuildPages page-heads (items kBuildPages * blockIdx.x + p,
 // KV head blockIdx.y) per one-wave workgroup: phases 1-2 page by page, the
 // Jacobi sweeps of all four at once (16 lanes each, no lane duplicating
 // another's work), then phases 4-6 page by page.  LDS: the Gram matrices
 // until the sweeps have read them, then the eigenvectors; the packing
-// buffers are reused from page to page.
-template <int R>
+// buffers are reused from page to page.  DPP2: the Jacobi's lane exchanges
+// by DPP moves only.
+template <int R, bool DPP2>
 __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ kc, int64_t bs,
                                                    int64_t hs, int64_t ts, BlockSource src,
                                                    int32_t n_items, int32_t num_blocks,
@@ -533,7 +547,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
     // that share its wave.
     bool done = false;
     for (int sweep = 0; sweep < kSweeps; ++sweep) {
-      jacobi_sweep(a, u, i, done, std::make_integer_sequence<int, kB - 1>{});
+      jacobi_sweep<DPP2>(a, u, i, done, std::make_integer_sequence<int, kB - 1>{});
       float off = 0.f;
 #pragma unroll
       for (int c = 1; c < kB; ++c) off = fmaf(a[c], a[c], off);
@@ -607,7 +621,9 @@ hipError_t launch_build_r(const uint16_t* k_cache, int64_t block_stride, int64_t
                        num_blocks, hkv, summaries, basis);
   } else {
     const int32_t wgs = (n_items + kBuildPages - 1) / kBuildPages;
-    hipLaunchKernelGGL(build_kernel<R>, dim3(wgs, hkv, n_layers), dim3(64), 0, stream, k_cache,
+    const bool dpp_only = (int64_t)wgs * hkv * n_layers <= kDppOnlyMaxWorkgroups;
+    auto* kernel = dpp_only ? build_kernel<R, true> : build_kernel<R, false>;
+    hipLaunchKernelGGL(kernel, dim3(wgs, hkv, n_layers), dim3(64), 0, stream, k_cache,
                        block_stride, head_stride, token_stride, src, n_items, num_blocks, hkv,
                        summaries, raw_debug);
   }
