@@ -20,7 +20,7 @@
 //     when the page is constant to rounding;
 //  5. sign: the largest-|entry| component of v_k is made positive (lowest dim
 //     on ties); coefficients c_i = V^T x_i are projections on the unquantized
-//     basis;
+//     basis (C = X V on the matrix cores, fp32 16x16x4);
 //  6. symmetric quantization with fp16 scales (max|x|/7 for the basis,
 //     max|x|/127 for coefficients and centroid, round half to even) and
 //     packing into the 832-byte record.
@@ -96,7 +96,7 @@ struct RecLayout {
 // (phases 4-6), in LDS.
 template <int R>
 struct PackSmem {
-  float V[R][kD + 4];      // unquantized basis, [k][d]
+  float V[R][kD + 4] __attribute__((aligned(16)));   // unquantized basis, [k][d]
   float mu[kD] __attribute__((aligned(16)));   // centroid
   float C[kB][R];          // unquantized coefficients
   int8_t vq[R][kD];
@@ -375,31 +375,44 @@ __device__ __forceinline__ void basis_from_eig(const float* lam, const float (*U
 // ---- 5-6. coefficients c_ik = v_k . x_i on the unquantized basis, then
 // symmetric quantization with fp16 scales and packing; the record is
 // written to dst, and with raw the unquantized mu, V, C.
-template <int R, typename KeyPair>
-__device__ __forceinline__ void coeffs_and_pack(KeyPair key_pair, PackSmem<R>& pk,
+template <int R>
+__device__ __forceinline__ void coeffs_and_pack(const uint16_t* kpage, int64_t ts, PackSmem<R>& pk,
                                                 uint32_t* __restrict__ dst, float* raw) {
   using RL = RecLayout<R>;
   const float* mu = pk.mu;
   const int lane = threadIdx.x;
   const int d0 = 2 * lane;
-  // lane -> token lane % 16, columns (R/4)*(lane/16) .. +R/4
+  // C = X V on the matrix cores (fp32 16x16x4), laid out as the Gram of
+  // phase 2: lane (t = lane % 16, g = lane / 16) brings token t's centred
+  // dims 32g .. 32g + 31 as the A operand and column t of V (basis vector
+  // t, zero for t >= R) at the same dims as the B operand, one dim per step;
+  // it ends holding C[4g + r][t], r = 0..3.
   {
-    constexpr int kPer = R / 4;
-    const int tk = lane & 15, k0 = kPer * (lane >> 4);
-    float cc[kPer];
+    const int t = lane & 15, g = lane >> 4;
+    const uint16_t* kp = kpage + (size_t)t * ts + 32 * g;
+    const float* vrow = pk.V[t < R ? t : 0] + 32 * g;
+    const float* mrow = mu + 32 * g;
+    f32x4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) cc[j] = 0.f;
-    for (int d = 0; d < kD; d += 2) {
-      const uint32_t kw = key_pair(tk, d);
-      const float2 m = *reinterpret_cast<const float2*>(&mu[d]);
-      const float xa = bf16_lo(kw) - m.x, xb = bf16_hi(kw) - m.y;
+    for (int s = 0; s < 4; ++s) {
+      const uint4 kv = *reinterpret_cast<const uint4*>(kp + 8 * s);
+      const uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
+      const float4 m0 = *reinterpret_cast<const float4*>(mrow + 8 * s);
+      const float4 m1 = *reinterpret_cast<const float4*>(mrow + 8 * s + 4);
+      const float4 v0 = *reinterpret_cast<const float4*>(vrow + 8 * s);
+      const float4 v1 = *reinterpret_cast<const float4*>(vrow + 8 * s + 4);
+      const float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) cc[j] = fmaf(xa, pk.V[k0 + j][d], cc[j]);
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) cc[j] = fmaf(xb, pk.V[k0 + j][d + 1], cc[j]);
+      for (int e = 0; e < 8; ++e) {
+        const float x = ((e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1])) - m[e];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x, t < R ? v[e] : 0.f, acc, 0, 0, 0);
+      }
     }
+    if (t < R) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) pk.C[tk][k0 + j] = cc[j];
+      for (int r = 0; r < 4; ++r) pk.C[4 * g + r][t] = acc[r];
+    }
   }
   __syncthreads();
 
@@ -573,7 +586,7 @@ __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ 
         reinterpret_cast<uint32_t*>(summ + ((size_t)kvh * num_blocks + blk[p]) * RL::kBytes);
     float* r = raw ? raw + ((size_t)(kBuildPages * blockIdx.x + p) * hkv + kvh) * raw_floats(R)
                    : nullptr;
-    coeffs_and_pack<R>(key_pair, sm.pk, dst, r);
+    coeffs_and_pack<R>(kpage, ts, sm.pk, dst, r);
   }
 }
 
@@ -603,11 +616,8 @@ __global__ __launch_bounds__(64) void build_basis_kernel(const uint16_t* __restr
     pk.V[k][d0 + 1] = bk[k * kD + d0 + 1];
   }
   __syncthreads();
-  auto key_pair = [&](int tt, int d) {
-    return *reinterpret_cast<const uint32_t*>(kpage + (size_t)tt * ts + d);
-  };
   uint32_t* dst = reinterpret_cast<uint32_t*>(summ + ((size_t)kvh * num_blocks + blk) * RL::kBytes);
-  coeffs_and_pack<R>(key_pair, pk, dst, nullptr);
+  coeffs_and_pack<R>(kpage, ts, pk, dst, nullptr);
 }
 
 template <int R>
