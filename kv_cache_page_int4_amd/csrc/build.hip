@@ -499,9 +499,10 @@ constexpr int64_t kDppOnlyMaxWorkgroups = 1024;
 // KV head blockIdx.y) per one-wave workgroup: phases 1-2 page by page, the
 // Jacobi sweeps of all four at once (16 lanes each, no lane duplicating
 // another's work), then phases 4-6 page by page.  LDS: the Gram matrices
-// until the sweeps have read them, then the eigenvectors; the packing
-// buffers are reused from page to page.  DPP2: the Jacobi's lane exchanges
-// by DPP moves only.
+// until the sweeps have read them, then in the same bytes the packing
+// buffers, reused from page to page; the top-r eigenvectors and eigenvalues
+// of the four pages apart.  DPP2: the Jacobi's lane exchanges by DPP moves
+// only.
 template <int R, bool DPP2>
 __global__ __launch_bounds__(64) void build_kernel(const uint16_t* __restrict__ kc, int64_t bs,
                                                    int64_t hs, int64_t ts, BlockSource src,
