@@ -131,6 +131,10 @@ size_t locks_attend_workspace_bytes(const locks_dims* dims, int32_t batch,
  *   [82r+128, 84r+128) [784,800) fp16 coefficient scales s_c[r];
  *   [84r+128, +2)     [800,802) fp16 centroid scale; zero to the record end.
  *   Dequantized: mu = s_mu*mu_q, v_k = s_V[k]*V_q[:,k], c_ik = s_c[k]*C_q[i,k].
+ * A record depends only on its page-head's keys: the same bytes whatever else
+ * the call lists, in whatever order, and the same as locks_finalize_pages
+ * writes for that page.  Block ids outside [0, num_blocks) are skipped;
+ * a block listed twice gets the same record twice.
  */
 locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
                                    locks_kv_layout layout, const int32_t* block_ids,
