@@ -46,9 +46,11 @@ struct AttendParams {
 };
 
 // Global -> LDS copy of 16 bytes per lane: lane l writes LDS bytes
-// [lds + 16 l, +16) from sbase + voff.  M0 carries the LDS address and is
-// declared clobbered, so the compiler keeps no value of its own in M0 across
-// the copy.
+// [lds + 16 l, +16) from sbase + voff.  M0 carries the LDS address.  M0 is a
+// register the compiler reserves, so listing it as clobbered is only a note
+// to the reader (the compiler warns that it does not act on it): what makes
+// this safe is that nothing else in these kernels uses M0 -- the generated
+// code writes M0 only here, right before each copy.
 // The copy is non-temporal: each K/V page is read once per step, and
 // streaming it past the cache's normal allocation raises the read rate
 // (each instruction reads one contiguous kilobyte, so no line is split

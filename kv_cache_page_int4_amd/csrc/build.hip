@@ -598,7 +598,7 @@ template <int R>
 __global__ __launch_bounds__(64) void build_basis_kernel(const uint16_t* __restrict__ kc,
                                                          int64_t bs, int64_t hs, int64_t ts,
                                                          BlockSource src, int32_t n_items,
-                                                         int32_t num_blocks, int32_t hkv,
+                                                         int32_t num_blocks,
                                                          uint8_t* __restrict__ summ,
                                                          const float* __restrict__ basis) {
   using RL = RecLayout<R>;
@@ -629,7 +629,7 @@ hipError_t launch_build_r(const uint16_t* k_cache, int64_t block_stride, int64_t
   if (basis) {
     hipLaunchKernelGGL(build_basis_kernel<R>, dim3(n_items, hkv, n_layers), dim3(64), 0, stream,
                        k_cache, block_stride, head_stride, token_stride, src, n_items,
-                       num_blocks, hkv, summaries, basis);
+                       num_blocks, summaries, basis);
   } else {
     const int32_t wgs = (n_items + kBuildPages - 1) / kBuildPages;
     const bool dpp_only = (int64_t)wgs * hkv * n_layers <= kDppOnlyMaxWorkgroups;

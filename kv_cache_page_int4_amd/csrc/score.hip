@@ -115,8 +115,10 @@ struct ScoreParams {
 
 // Global -> LDS copy of 16 bytes per active lane: lane l writes LDS bytes
 // [lds + 16 l, lds + 16 l + 16) from sbase + voff.  M0 carries the LDS
-// address and is declared clobbered, so the compiler keeps no value of its
-// own in M0 across the copy.
+// address.  M0 is a register the compiler reserves, so listing it as
+// clobbered is only a note to the reader (the compiler warns that it does not
+// act on it): what makes this safe is that nothing else in the kernel uses
+// M0 -- the generated code writes M0 only here, right before each copy.
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff),
                "s"(sbase), "s"(lds)
@@ -132,9 +134,12 @@ __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_c
 
 // NSUB: 4-head sub-passes per step (2 for a group of 8 heads, else 1).
 // Waves per SIMD the register budget is cut for: 7 (at most 72 registers)
-// for one head pass; a group of 8 heads at rank 8 needs a little more than
-// 96 registers and is held to 96 (5 waves instead of 4).
-constexpr int score_waves(int r, int nsub) { return nsub == 1 || r == 4 ? 7 : (r == 8 ? 5 : 3); }
+// for one head pass at ranks 4 and 8; rank 16 needs 96 registers for one
+// pass (5 waves); a group of 8 heads at rank 8 needs a little more than 96
+// registers and is held to 96 (5 waves instead of 4).
+constexpr int score_waves(int r, int nsub) {
+  return nsub == 1 ? (r == 16 ? 5 : 7) : (r == 4 ? 7 : (r == 8 ? 5 : 3));
+}
 
 template <int R, int NSUB>
 __global__ __launch_bounds__(64 * kScoreWaves) __attribute__((
@@ -247,7 +252,7 @@ score_kernel(ScoreParams p) {
       v.w = ((unsigned)v.w < nbk) ? v.w : -1;
       return v;
     };
-    auto issue = [&](int k, int4 bb) {
+    auto issue = [&](int4 bb) {
       const uint32_t slot = ring0;
       const int bi[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
@@ -265,7 +270,7 @@ score_kernel(ScoreParams p) {
     const int4 none = make_int4(-1, -1, -1, -1);
     int4 b0 = step_bids(0);
     int4 b1 = (n > 1) ? step_bids(1) : none;
-    issue(0, b0);
+    issue(b0);
     for (int k = 0; k < n; ++k) {
       const int4 bcur = b0;
       const bool more = k + 1 < n;
@@ -312,7 +317,7 @@ score_kernel(ScoreParams p) {
         cw[3] = c4.w;
       }
       wait_lgkm0();
-      if (more) issue(k + 1, b1);
+      if (more) issue(b1);
       b0 = b1;
       b1 = (k + 2 < n) ? step_bids(k + 2) : none;
 
