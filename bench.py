@@ -78,9 +78,25 @@ def parse():
     return ap.parse_args()
 
 
-def timed(fn, reps, warm=1):
+def warm_graph(g, min_reps=3, min_seconds=0.025):
+    """Replay a freshly captured graph until at least `min_reps` replays and
+    `min_seconds` of wall time have passed.  The first replays of a new graph
+    run slower before the launches settle (the scorer's 32 launches at 1M:
+    77-83 us per launch over the first 5 to 9 replays, then 74-75 us), so
+    timing starts after that."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_reps or time.perf_counter() - t0 < min_seconds:
+        g.replay()
+        torch.cuda.synchronize()
+        n += 1
+    return n
+
+
+def timed(fn, reps):
     """Average ms of fn() replayed from a captured graph (device time, not host
-    launch rate), HIP events on the launch stream."""
+    launch rate), HIP events on the launch stream, after warm_graph."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -91,9 +107,7 @@ def timed(fn, reps, warm=1):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         fn()
-    for _ in range(warm):
-        g.replay()
-    torch.cuda.synchronize()
+    warm_graph(g)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -104,9 +118,10 @@ def timed(fn, reps, warm=1):
     return e0.elapsed_time(e1) / reps
 
 
-def timed_replays(fn, reps, warm=1):
+def timed_replays(fn, reps):
     """ms of each of `reps` replays of fn() captured in one graph, each replay
-    between its own pair of HIP events on the launch stream."""
+    between its own pair of HIP events on the launch stream, after
+    warm_graph."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -117,9 +132,7 @@ def timed_replays(fn, reps, warm=1):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         fn()
-    for _ in range(warm):
-        g.replay()
-    torch.cuda.synchronize()
+    warm_graph(g)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
     for a, b in ev:
@@ -867,7 +880,8 @@ def main():
                      "bytes_per_launch": page_heads * SCORE_BYTES_PER_PAGE_HEAD,
                      "timing": ("mean over graph replays of every layer's "
                                 "locks_score_pages launch, back to back, each replay between "
-                                "its own HIP events on the launch stream")},
+                                "its own HIP events on the launch stream, after at least 25 ms "
+                                "of warm-up replays of the same graph")},
         "attention": {"achieved": round(attend_gbs, 1), "unit": "GB/s",
                       "frac": round(attend_gbs / PEAK_HBM_GBS, 4),
                       "kernel_us": round(attend_us, 3),
